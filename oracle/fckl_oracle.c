@@ -1,0 +1,304 @@
+/*
+ * fckl_oracle.c -- CPU oracle for the offline top-K distillation KL loss.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, plain, obviously correct
+ * statement of what the fused chunked loss computes.  It is used by the test
+ * suite, by the smoke check and by the benchmark's CPU-baseline leg, and by
+ * nothing else: the product library never links, loads or calls it, and it
+ * shares no code, header, table or helper with the GPU library.
+ *
+ * What is computed (all arithmetic in IEEE double):
+ *
+ *   The teacher cache holds, per token i, K logits tl[i,k] and their vocabulary
+ *   indices idx[i,k] ("Preparing Offline Top-K Logits", getaibook.com; "Breaking
+ *   the Bottleneck with Offline Caching and Chunked Loss", axbrief.com: the top
+ *   100 logits are extracted once and stored).
+ *
+ *   1. Teacher distribution over the K cached entries, at temperature T:
+ *        lp[k] = tl[k]/T - log sum_j exp(tl[j]/T),   p[k] = exp(lp[k]).
+ *      The pages do not say how the mass outside the top-K is handled; the
+ *      reading taken here renormalises over the K cached entries (no tail bucket).
+ *   2. Student logits over the full vocabulary: the output projection is part of
+ *      the loss ("What actually changed?", calcaas.com: the fused loss folds the
+ *      model's output projection into the loss):
+ *        z[i,v] = sum_j h[i,j] * W[v,j].
+ *   3. lse[i] = log sum_v exp(z[i,v]/T)   (natural log, max-shifted).
+ *   4. log q[i,k] = z[i,idx[i,k]]/T - lse[i].
+ *   5. loss[i] = T^2 * sum_k p[k] * (lp[k] - log q[i,k])   -- forward KL(p || q),
+ *      the KL divergence the pages name ("Configuring Fused Chunked KL Loss",
+ *      getaibook.com) taken from the teacher's cached distribution to the student's.
+ *      The reported loss is the mean of loss[i] over the N tokens.
+ *   6. Gradient of (grad_scale * mean loss) with respect to z:
+ *        g[i,v] = grad_scale * (T/N) * ( (sum_k p[k]) * exp(z[i,v]/T - lse[i])
+ *                                        - sum_k p[k] * [idx[i,k] == v] ).
+ *   7. dH[i,:] = sum_v g[i,v] * W[v,:];   dW[v,:] = sum_i g[i,v] * h[i,:].
+ *
+ * The chunking of the method changes where and when these numbers are formed,
+ * not their values, so the oracle does not chunk ("Breaking the Bottleneck ...",
+ * axbrief.com: one slice of the sequence at a time, then discarded).
+ *
+ * Inputs are double arrays, row-major: h[N*H], W[V*H], idx[N*K] (int32),
+ * tl[N*K].  A row list (rows, nrows) selects which tokens are evaluated; rows ==
+ * NULL means all N tokens in order.  Return value 0 on success, negative on a
+ * rejected argument (see the ORACLE_E* codes below); outputs are then untouched.
+ */
+#include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EARG (-1)   /* bad sizes, T <= 0, NULL pointers */
+#define ORACLE_EIDX (-2)   /* a cached index outside [0, V) */
+#define ORACLE_EMEM (-3)   /* host allocation failed */
+
+static int check_args(int64_t N, int64_t H, int64_t V, int64_t K, double T,
+                      const double *h, const double *W, const int32_t *idx,
+                      const double *tl, int64_t nrows, const int64_t *rows)
+{
+    if (N < 0 || H <= 0 || V <= 0 || K <= 0 || !(T > 0.0) || isinf(T))
+        return ORACLE_EARG;
+    if (!h || !W || !idx || !tl || nrows < 0)
+        return ORACLE_EARG;
+    if (!rows && nrows != N)
+        return ORACLE_EARG;
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t i = rows ? rows[r] : r;
+        if (i < 0 || i >= N)
+            return ORACLE_EARG;
+        for (int64_t k = 0; k < K; ++k) {
+            int32_t v = idx[i * K + k];
+            if (v < 0 || (int64_t)v >= V)
+                return ORACLE_EIDX;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Step 1: teacher probabilities p and log-probabilities lp over the K entries. */
+static void teacher_distribution(int64_t K, double T, const double *tl, double *p, double *lp)
+{
+    double m = -INFINITY;
+    for (int64_t k = 0; k < K; ++k)
+        if (tl[k] / T > m)
+            m = tl[k] / T;
+    double s = 0.0;
+    for (int64_t k = 0; k < K; ++k)
+        s += exp(tl[k] / T - m);
+    double log_norm = m + log(s);
+    for (int64_t k = 0; k < K; ++k) {
+        lp[k] = tl[k] / T - log_norm;
+        p[k] = exp(lp[k]);
+    }
+}
+
+/* Step 2: student logits of one token over the whole vocabulary. */
+static void student_logits(int64_t H, int64_t V, const double *h_row, const double *W, double *z)
+{
+    for (int64_t v = 0; v < V; ++v) {
+        const double *w = W + v * H;
+        double acc = 0.0;
+        for (int64_t j = 0; j < H; ++j)
+            acc += h_row[j] * w[j];
+        z[v] = acc;
+    }
+}
+
+/* Step 3: log sum_v exp(z[v]/T), shifted by the maximum. */
+static double logsumexp_over_vocab(int64_t V, double T, const double *z)
+{
+    double m = -INFINITY;
+    for (int64_t v = 0; v < V; ++v)
+        if (z[v] / T > m)
+            m = z[v] / T;
+    double s = 0.0;
+    for (int64_t v = 0; v < V; ++v)
+        s += exp(z[v] / T - m);
+    return m + log(s);
+}
+
+/*
+ * Forward: per-token loss (steps 1-5) and lse (step 3) for the selected rows.
+ * loss_out[r], lse_out[r] refer to row rows[r] (or r).  Either output may be NULL.
+ */
+int fckl_oracle_forward(int64_t N, int64_t H, int64_t V, int64_t K, double T,
+                        const double *h, const double *W, const int32_t *idx,
+                        const double *tl, int64_t nrows, const int64_t *rows,
+                        double *loss_out, double *lse_out)
+{
+    int rc = check_args(N, H, V, K, T, h, W, idx, tl, nrows, rows);
+    if (rc)
+        return rc;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *z = (double *)malloc(sizeof(double) * (size_t)V);
+        double *p = (double *)malloc(sizeof(double) * (size_t)K);
+        double *lp = (double *)malloc(sizeof(double) * (size_t)K);
+        int have = (z && p && lp);
+        if (!have) {
+#pragma omp atomic write
+            failed = 1;
+        }
+        /* Every thread reaches the worksharing loop; one without buffers skips its rows. */
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nrows; ++r) {
+            if (!have)
+                continue;
+            {
+                int64_t i = rows ? rows[r] : r;
+                teacher_distribution(K, T, tl + i * K, p, lp);
+                student_logits(H, V, h + i * H, W, z);
+                double lse = logsumexp_over_vocab(V, T, z);
+                double kl = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    double log_q = z[idx[i * K + k]] / T - lse;
+                    kl += p[k] * (lp[k] - log_q);
+                }
+                if (loss_out)
+                    loss_out[r] = T * T * kl;
+                if (lse_out)
+                    lse_out[r] = lse;
+            }
+        }
+        free(z);
+        free(p);
+        free(lp);
+    }
+    return failed ? ORACLE_EMEM : ORACLE_OK;
+}
+
+/* Mean of the per-token loss over all N tokens (the reduction of step 5). */
+int fckl_oracle_loss_mean(int64_t N, int64_t H, int64_t V, int64_t K, double T,
+                          const double *h, const double *W, const int32_t *idx,
+                          const double *tl, double *mean_out)
+{
+    if (N <= 0 || !mean_out)
+        return ORACLE_EARG;
+    double *loss = (double *)malloc(sizeof(double) * (size_t)N);
+    if (!loss)
+        return ORACLE_EMEM;
+    int rc = fckl_oracle_forward(N, H, V, K, T, h, W, idx, tl, N, NULL, loss, NULL);
+    if (rc == ORACLE_OK) {
+        double s = 0.0;
+        for (int64_t i = 0; i < N; ++i)
+            s += loss[i];
+        *mean_out = s / (double)N;
+    }
+    free(loss);
+    return rc;
+}
+
+/*
+ * Backward (steps 6-7) of grad_scale * (1/n_norm) * sum over the selected rows
+ * of loss[i].  With rows == NULL and n_norm == N this is the gradient of
+ * grad_scale * mean loss.  dH_out[r*H + j] is the gradient for row rows[r];
+ * dW_out[V*H] receives the sum over the selected rows only (it is overwritten).
+ * Either output may be NULL.
+ */
+int fckl_oracle_backward(int64_t N, int64_t H, int64_t V, int64_t K, double T,
+                         const double *h, const double *W, const int32_t *idx,
+                         const double *tl, double grad_scale, int64_t n_norm,
+                         int64_t nrows, const int64_t *rows,
+                         double *dH_out, double *dW_out)
+{
+    int rc = check_args(N, H, V, K, T, h, W, idx, tl, nrows, rows);
+    if (rc)
+        return rc;
+    if (n_norm <= 0)
+        return ORACLE_EARG;
+    /* g for every selected row, held whole: nrows * V doubles. */
+    double *g = (double *)malloc(sizeof(double) * (size_t)(nrows > 0 ? nrows : 1) * (size_t)V);
+    if (!g)
+        return ORACLE_EMEM;
+    const double scale = grad_scale * T / (double)n_norm;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *z = (double *)malloc(sizeof(double) * (size_t)V);
+        double *p = (double *)malloc(sizeof(double) * (size_t)K);
+        double *lp = (double *)malloc(sizeof(double) * (size_t)K);
+        int have = (z && p && lp);
+        if (!have) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nrows; ++r) {
+            if (!have)
+                continue;
+            {
+                int64_t i = rows ? rows[r] : r;
+                teacher_distribution(K, T, tl + i * K, p, lp);
+                student_logits(H, V, h + i * H, W, z);
+                double lse = logsumexp_over_vocab(V, T, z);
+                double psum = 0.0;
+                for (int64_t k = 0; k < K; ++k)
+                    psum += p[k];
+                double *gr = g + r * V;
+                for (int64_t v = 0; v < V; ++v)
+                    gr[v] = scale * psum * exp(z[v] / T - lse);
+                for (int64_t k = 0; k < K; ++k)
+                    gr[idx[i * K + k]] -= scale * p[k];
+            }
+        }
+        free(z);
+        free(p);
+        free(lp);
+    }
+    if (failed) {
+        free(g);
+        return ORACLE_EMEM;
+    }
+    if (dH_out) {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nrows; ++r) {
+            double *out = dH_out + r * H;
+            for (int64_t j = 0; j < H; ++j)
+                out[j] = 0.0;
+            for (int64_t v = 0; v < V; ++v) {
+                double gv = g[r * V + v];
+                const double *w = W + v * H;
+                for (int64_t j = 0; j < H; ++j)
+                    out[j] += gv * w[j];
+            }
+        }
+    }
+    if (dW_out) {
+        /* Each vocabulary row is owned by one thread: no shared accumulation. */
+#pragma omp parallel for schedule(static)
+        for (int64_t v = 0; v < V; ++v) {
+            double *out = dW_out + v * H;
+            for (int64_t j = 0; j < H; ++j)
+                out[j] = 0.0;
+            for (int64_t r = 0; r < nrows; ++r) {
+                int64_t i = rows ? rows[r] : r;
+                double gv = g[r * V + v];
+                const double *hr = h + i * H;
+                for (int64_t j = 0; j < H; ++j)
+                    out[j] += gv * hr[j];
+            }
+        }
+    }
+    free(g);
+    return ORACLE_OK;
+}
+
+/* Number of OpenMP threads a parallel region of the oracle uses. */
+int fckl_oracle_num_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        {
+#ifdef _OPENMP
+            n = omp_get_num_threads();
+#endif
+        }
+    }
+    return n;
+}

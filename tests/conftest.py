@@ -1,0 +1,16 @@
+"""pytest configuration: the `gpu` marker and the import path.
+
+Tests marked ``gpu`` need an MI355X (gfx950) and the built HIP library; every
+other test runs on the host alone.
+"""
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: a long-running case (large workload)")
