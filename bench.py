@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused chunked top-K KL loss, forward + backward, on one MI355X.
+
+One step = fckl_forward + fckl_backward over the whole batch (N tokens) of the
+GPT-OSS-20B-shaped workload at 32K tokens: N=32768, H=2880, V=201088, K=100, T=1,
+bf16 h / W / teacher logits, fp32 accumulation.  Inputs are synthetic (seeded
+generators in synth/, same shapes and distributions; the teacher cache is the exact
+top-100 of a perturbed copy of the LM head) and resident in HBM before timing.
+
+Prints one JSON line.  `value` is tokens/s of whole fwd+bwd steps.  `roofline` is
+the dominant kernel's achieved bf16 MFMA rate: its algorithmic flops per launch
+(2 * tokens * V * H) over its mean launch time, taken with HIP events that the
+library records around each launch on its own stream during the timed steps.
+`cpu_baseline` times the CPU oracle (fp64) on a small sample of the same tokens.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s fwd+bwd of fused top-K KL (MFMA % of peak) + peak GiB, N=32K V=201088"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+GiB = float(1 << 30)
+
+
+class HipEvents:
+    """hipEvent_t handles from libamdhip64 (the library records them on its stream)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            arr[i] = e.value
+        return arr
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float(0)
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, arr):
+        for e in arr:
+            self.hip.hipEventDestroy(e)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="c3", help="synth workload key (default c3: the 32K-token GPT-OSS-20B shape)")
+    ap.add_argument("--tokens", type=int, default=0, help="override N (for quick runs)")
+    ap.add_argument("--chunk", type=int, default=0, help="tokens per chunk (0 = library scheduler)")
+    ap.add_argument("--cpu-tokens", type=int, default=32, help="oracle sample size for cpu_baseline (0 = skip)")
+    ap.add_argument("--dense", action="store_true", help="also measure peak memory of a dense torch KL baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import chunked_top_kl_chunk_amd as fckl
+    import synth
+
+    fckl.load()
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[args.workload]
+    if args.tokens:
+        wl = wl.with_tokens(args.tokens)
+    N, H, V, K, T = wl.N, wl.H, wl.V, wl.K, wl.T
+    log("workload %s N=%d H=%d V=%d K=%d T=%g: generating inputs" % (wl.name, N, H, V, K, T))
+    t0 = time.time()
+    x = synth.make_inputs(wl, device=dev)
+    log("inputs ready in %.1fs" % (time.time() - t0))
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
+    h = torch.from_numpy(x.h_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    W = torch.from_numpy(x.W_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    idx = torch.from_numpy(np.ascontiguousarray(x.idx)).to(dev)
+    tl = torch.from_numpy(x.tl_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    desc = fckl.desc_for(h, W, idx, tl, T, args.chunk)
+    chunk, ws_bytes = fckl.plan(desc) if args.chunk == 0 else (args.chunk, fckl.workspace_size(desc, args.chunk))
+    nchunks = -(-N // chunk)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    loss = torch.empty(N, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    mean = torch.empty(1, dtype=torch.float32, device=dev)
+    dH = torch.empty(N, H, dtype=torch.float32, device=dev)
+    dW = torch.empty(V, H, dtype=torch.float32, device=dev)
+    log("chunk %d (%d chunks), workspace %.2f GiB" % (chunk, nchunks, ws_bytes / GiB))
+
+    def step(profile=None):
+        fckl.forward(h, W, idx, tl, T=T, chunk=chunk, ws=ws, loss_tok=loss, lse=lse, loss_mean=mean,
+                     profile=profile)
+        fckl.backward(h, W, idx, tl, lse, T=T, chunk=chunk, ws=ws, dH=dH, dW=dW, profile=profile)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log("warmup step %d done" % i)
+    peak_bytes = torch.cuda.max_memory_allocated()
+
+    # Per-kernel HIP events, recorded by the library on its stream during the timed steps.
+    ev = HipEvents()
+    per_step = nchunks * 8 + 1
+    cap = per_step * max(args.steps, 1)
+    events = ev.create(2 * cap)
+    kid = (ctypes.c_int32 * cap)()
+    work = (ctypes.c_int32 * cap)()
+    prof = fckl.Profile((1 << len(fckl.KERNELS)) - 1, cap, 0, events, kid, work)
+
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step(prof)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_step = elapsed * 1e3 / args.steps
+    tokens_per_s = N * args.steps / elapsed
+    log("timed %d steps: %.2f ms/step, %.0f tokens/s" % (args.steps, ms_step, tokens_per_s))
+
+    kernels = {}
+    for i in range(prof.count):
+        name = fckl.KERNELS[kid[i]]
+        d = kernels.setdefault(name, {"launches": 0, "ms": 0.0, "tokens": 0})
+        d["launches"] += 1
+        d["ms"] += ev.elapsed_ms(events[2 * i], events[2 * i + 1])
+        d["tokens"] += work[i]
+    ev.destroy(events)
+    gemms = ("fwd_logits", "bwd_logits", "dh", "dw")
+    for name, d in kernels.items():
+        d["avg_ms"] = d["ms"] / d["launches"]
+        d["ms_per_step"] = d["ms"] / args.steps
+        if name in gemms:
+            flops = 2.0 * d["tokens"] * V * H
+            d["tflops"] = flops / (d["ms"] * 1e-3) / 1e12
+            d["mfma_frac"] = d["tflops"] / PEAK_BF16_TFLOPS
+    dom = max(gemms, key=lambda n: kernels[n]["ms"])
+    kd = kernels[dom]
+    flops_per_launch = 2.0 * (kd["tokens"] / kd["launches"]) * V * H
+    achieved = flops_per_launch / (kd["avg_ms"] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_launch_ms": round(kd["avg_ms"], 4),
+                "flops_per_launch": flops_per_launch}
+    step_tflops = 8.0 * N * V * H / (ms_step * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "N": N, "H": H, "V": V, "K": K, "T": T, "chunk": chunk,
+                   "chunks": nchunks},
+        "roofline": roofline,
+        "mfma_frac_step": round(step_tflops / PEAK_BF16_TFLOPS, 4),
+        "step_tflops": round(step_tflops, 1),
+        "peak_gib": round(peak_bytes / GiB, 3),
+        "workspace_gib": round(ws_bytes / GiB, 3),
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+    }
+
+    if args.dense:
+        out["dense_baseline"] = dense_baseline(h, W, idx, tl, T)
+
+    if args.cpu_tokens > 0:
+        out["cpu_baseline"] = cpu_baseline(x, wl, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+def dense_baseline(h, W, idx, tl, T):
+    """Peak memory of the dense loss: the full N x V logits materialised by torch."""
+    import torch
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    try:
+        Wg = W.detach().clone().requires_grad_(True)
+        hg = h.detach().clone().requires_grad_(True)
+        z = (hg @ Wg.t()).float() / T
+        logq = torch.log_softmax(z, dim=1)
+        logp = torch.log_softmax(tl.float() / T, dim=1)
+        per_tok = (T * T) * (logp.exp() * (logp - torch.gather(logq, 1, idx.long()))).sum(1)
+        per_tok.mean().backward()
+        torch.cuda.synchronize()
+        res = {"peak_gib": round(torch.cuda.max_memory_allocated() / GiB, 3),
+               "inputs_gib": round(base / GiB, 3), "ok": True}
+    except torch.cuda.OutOfMemoryError:
+        res = {"ok": False, "error": "out of memory"}
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(x, wl, S):
+    """The CPU oracle (fp64, OpenMP) on S sampled tokens: forward, then backward with
+    those tokens' dH rows and their dW contribution -- 8*V*H flop per token."""
+    import numpy as np
+    import oracle
+    import synth
+    rows = synth.sample_rows(wl, S)
+    h64 = x.h.astype(np.float64)
+    W64 = x.W.astype(np.float64)
+    tl64 = x.tl.astype(np.float64)
+    threads = oracle.num_threads()
+    log("cpu baseline: oracle on %d tokens, %d threads" % (S, threads))
+    t0 = time.perf_counter()
+    oracle.forward(h64, W64, x.idx, tl64, wl.T, rows=rows)
+    oracle.backward(h64, W64, x.idx, tl64, wl.T, rows=rows, n_norm=wl.N)
+    dt = time.perf_counter() - t0
+    return {"value": round(S / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d seeded-sampled tokens of the %d-token workload: forward and backward (dH rows and "
+                      "their dW contribution), fp64, %.1f s" % (S, wl.N, dt)}
+
+
+if __name__ == "__main__":
+    main()

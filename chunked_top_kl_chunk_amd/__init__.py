@@ -1,0 +1,218 @@
+"""Fused chunked top-K KL distillation loss on AMD MI355X (gfx950).
+
+Thin binding over the C ABI in ``include/fckl.h`` (``libfckl.so``, built in-tree by
+``python -m chunked_top_kl_chunk_amd.build``).  This module only marshals
+arguments: torch supplies device memory and the stream, and every step of the
+loss runs in the library's HIP kernels.  There is no CPU or eager fallback; if
+the library is missing every call raises.
+
+    import chunked_top_kl_chunk_amd as fckl
+    loss_tok, lse, loss_mean = fckl.forward(h, W, topk_idx, topk_logit, T=1.0)
+    dH, dW = fckl.backward(h, W, topk_idx, topk_logit, lse, T=1.0)
+
+Shapes: h [N,H] bf16, W [V,H] bf16, topk_idx [N,K] int32, topk_logit [N,K] bf16 or
+float32, all contiguous on one HIP device.  Outputs are float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfckl.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_INDEX, ERR_HIP = range(6)
+DTYPE_BF16, DTYPE_F32 = 0, 1
+FLAG_VALIDATE, FLAG_DW_ACCUMULATE = 1, 2
+
+# Every symbol include/fckl.h declares.
+EXPORTS = ("fckl_plan", "fckl_workspace_size", "fckl_forward", "fckl_backward",
+           "fckl_status_string", "fckl_version")
+
+
+KERNELS = ("prepare", "fwd_logits", "combine", "mean", "bwd_logits", "dh", "dh_reduce", "dw")
+
+
+class Profile(ctypes.Structure):
+    """Mirror of struct fckl_profile (per-kernel hipEvent brackets)."""
+    _fields_ = [("kernel_mask", ctypes.c_uint32), ("capacity", ctypes.c_int32), ("count", ctypes.c_int32),
+                ("events", ctypes.POINTER(ctypes.c_void_p)), ("kernel_ids", ctypes.POINTER(ctypes.c_int32)),
+                ("work", ctypes.POINTER(ctypes.c_int32))]
+
+
+class Desc(ctypes.Structure):
+    """Mirror of struct fckl_desc."""
+    _fields_ = [("N", ctypes.c_int64), ("H", ctypes.c_int32), ("V", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("T", ctypes.c_float), ("chunk", ctypes.c_int32), ("logit_dtype", ctypes.c_int32),
+                ("flags", ctypes.c_uint32), ("profile", ctypes.POINTER(Profile))]
+
+
+class FCKLError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, status_string(status), status))
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libfckl.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libfckl.so not found at %s; build it with `python -m chunked_top_kl_chunk_amd.build`"
+                          % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, vp, sz = ctypes.POINTER, ctypes.c_void_p, ctypes.c_size_t
+    lib.fckl_plan.argtypes = [P(Desc), sz, P(ctypes.c_int32), P(sz)]
+    lib.fckl_workspace_size.argtypes = [P(Desc), ctypes.c_int32, P(sz)]
+    lib.fckl_forward.argtypes = [P(Desc), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.fckl_backward.argtypes = [P(Desc), vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
+    lib.fckl_status_string.argtypes = [ctypes.c_int]
+    lib.fckl_status_string.restype = ctypes.c_char_p
+    lib.fckl_version.argtypes = []
+    lib.fckl_version.restype = ctypes.c_int32
+    for f in ("fckl_plan", "fckl_workspace_size", "fckl_forward", "fckl_backward"):
+        getattr(lib, f).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().fckl_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(load().fckl_version())
+
+
+def make_desc(N: int, H: int, V: int, K: int, T: float = 1.0, chunk: int = 0, logit_dtype: int = DTYPE_BF16,
+              flags: int = 0, profile: Optional[Profile] = None) -> Desc:
+    d = Desc(int(N), int(H), int(V), int(K), float(T), int(chunk), int(logit_dtype), int(flags))
+    if profile is not None:
+        d.profile = ctypes.pointer(profile)
+    return d
+
+
+def _call(name: str, *args) -> None:
+    st = getattr(load(), name)(*args)
+    if st != OK:
+        raise FCKLError(st, name)
+
+
+def plan(desc: Desc, budget_bytes: int = 0) -> Tuple[int, int]:
+    """(tokens per chunk, workspace bytes) chosen by the library's chunk scheduler."""
+    c, ws = ctypes.c_int32(0), ctypes.c_size_t(0)
+    _call("fckl_plan", ctypes.byref(desc), ctypes.c_size_t(budget_bytes), ctypes.byref(c), ctypes.byref(ws))
+    return int(c.value), int(ws.value)
+
+
+def workspace_size(desc: Desc, chunk: int) -> int:
+    ws = ctypes.c_size_t(0)
+    _call("fckl_workspace_size", ctypes.byref(desc), ctypes.c_int32(chunk), ctypes.byref(ws))
+    return int(ws.value)
+
+
+# ---------------------------------------------------------------- torch-facing calls
+
+def _check_inputs(h, W, topk_idx, topk_logit):
+    import torch
+    for name, t in (("h", h), ("W", W), ("topk_idx", topk_idx), ("topk_logit", topk_logit)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError("%s must be a device tensor" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if h.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
+        raise ValueError("h and W must be bfloat16")
+    if topk_idx.dtype != torch.int32:
+        raise ValueError("topk_idx must be int32")
+    if topk_logit.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("topk_logit must be bfloat16 or float32")
+    if h.dim() != 2 or W.dim() != 2 or topk_idx.dim() != 2 or topk_logit.shape != topk_idx.shape:
+        raise ValueError("expected h[N,H], W[V,H], topk_idx[N,K], topk_logit[N,K]")
+    if W.shape[1] != h.shape[1] or topk_idx.shape[0] != h.shape[0]:
+        raise ValueError("shape mismatch: h%s W%s topk_idx%s" % (tuple(h.shape), tuple(W.shape),
+                                                                tuple(topk_idx.shape)))
+    devs = {t.device for t in (h, W, topk_idx, topk_logit)}
+    if len(devs) != 1:
+        raise ValueError("all tensors must be on one device")
+
+
+def desc_for(h, W, topk_idx, topk_logit, T: float, chunk: int = 0, flags: int = 0,
+             profile: Optional[Profile] = None) -> Desc:
+    import torch
+    ld = DTYPE_F32 if topk_logit.dtype == torch.float32 else DTYPE_BF16
+    return make_desc(h.shape[0], h.shape[1], W.shape[0], topk_idx.shape[1], T, chunk, ld, flags, profile)
+
+
+def _stream_handle(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _out(t, shape, device, name):
+    import torch
+    if t is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or t.device != device:
+        raise ValueError("%s must be a contiguous float32 tensor of shape %s on %s" % (name, shape, device))
+    return t
+
+
+def _workspace(desc: Desc, ws, device):
+    import torch
+    if desc.chunk == 0:
+        chunk, need = plan(desc)
+        desc.chunk = chunk
+    else:
+        need = workspace_size(desc, desc.chunk)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    if ws.numel() * ws.element_size() < need or not ws.is_contiguous():
+        raise ValueError("workspace of %d bytes needed" % need)
+    return ws
+
+
+def forward(h, W, topk_idx, topk_logit, T: float = 1.0, chunk: int = 0, ws=None, validate: bool = False,
+            loss_tok=None, lse=None, loss_mean=None, stream=None, profile: Optional[Profile] = None):
+    """Per-token loss, saved lse (log-sum-exp of z/T) and the mean loss, via fckl_forward."""
+    _check_inputs(h, W, topk_idx, topk_logit)
+    dev = h.device
+    desc = desc_for(h, W, topk_idx, topk_logit, T, chunk, FLAG_VALIDATE if validate else 0, profile)
+    ws = _workspace(desc, ws, dev)
+    N = h.shape[0]
+    loss_tok = _out(loss_tok, (N,), dev, "loss_tok")
+    lse = _out(lse, (N,), dev, "lse")
+    loss_mean = _out(loss_mean, (1,), dev, "loss_mean")
+    _call("fckl_forward", ctypes.byref(desc), h.data_ptr(), W.data_ptr(), topk_idx.data_ptr(),
+          topk_logit.data_ptr(), loss_tok.data_ptr(), lse.data_ptr(), loss_mean.data_ptr(), ws.data_ptr(),
+          ctypes.c_size_t(ws.numel() * ws.element_size()), _stream_handle(stream))
+    return loss_tok, lse, loss_mean
+
+
+def backward(h, W, topk_idx, topk_logit, lse, T: float = 1.0, grad_scale: float = 1.0, chunk: int = 0, ws=None,
+             dH=None, dW=None, accumulate: bool = False, validate: bool = False, stream=None,
+             profile: Optional[Profile] = None):
+    """dH [N,H] and dW [V,H] (float32) of grad_scale * mean loss, via fckl_backward."""
+    import torch
+    _check_inputs(h, W, topk_idx, topk_logit)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (h.shape[0],) or lse.device != h.device:
+        raise ValueError("lse must be float32 [N] on the inputs' device")
+    dev = h.device
+    flags = (FLAG_VALIDATE if validate else 0) | (FLAG_DW_ACCUMULATE if accumulate else 0)
+    desc = desc_for(h, W, topk_idx, topk_logit, T, chunk, flags, profile)
+    ws = _workspace(desc, ws, dev)
+    dH = _out(dH, tuple(h.shape), dev, "dH")
+    dW = _out(dW, tuple(W.shape), dev, "dW")
+    _call("fckl_backward", ctypes.byref(desc), h.data_ptr(), W.data_ptr(), topk_idx.data_ptr(),
+          topk_logit.data_ptr(), lse.data_ptr(), ctypes.c_float(grad_scale), dH.data_ptr(), dW.data_ptr(),
+          ws.data_ptr(), ctypes.c_size_t(ws.numel() * ws.element_size()), _stream_handle(stream))
+    return dH, dW
+
+
+__all__ = ["Desc", "Profile", "KERNELS", "FCKLError", "load", "plan", "workspace_size", "forward", "backward", "make_desc",
+           "desc_for", "status_string", "version", "EXPORTS", "LIB_PATH"]

@@ -1,0 +1,240 @@
+// fckl_api.cpp -- the C ABI declared in include/fckl.h: argument checks, the chunk
+// loop and the launch sequence.  No device memory is allocated here; every buffer,
+// including the workspace, belongs to the caller.
+#include <hip/hip_runtime.h>
+
+#include "fckl_internal.h"
+
+using namespace fckl;
+
+namespace {
+
+fckl_status common_checks(const fckl_desc *d, const void *h, const void *W, const int32_t *idx, const void *tl,
+                          void *ws, size_t ws_bytes, Layout *L)
+{
+    fckl_status st = check_desc(d);
+    if (st != FCKL_OK)
+        return st;
+    if (!h || !W || !idx || !tl || !ws)
+        return FCKL_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || (reinterpret_cast<uintptr_t>(h) & 15u) != 0 ||
+        (reinterpret_cast<uintptr_t>(W) & 15u) != 0)
+        return FCKL_ERR_INVALID_ARG;
+    st = plan_chunk(d, ws_bytes, L);
+    if (st != FCKL_OK)
+        return st;
+    if (L->total > ws_bytes)
+        return FCKL_ERR_WORKSPACE;
+    return FCKL_OK;
+}
+
+ChunkArgs chunk_args(const fckl_desc *d, const void *h, const void *W, const int32_t *idx, const void *tl,
+                     void *ws, const Layout *L, int64_t c0)
+{
+    ChunkArgs a;
+    const size_t esz = d->logit_dtype == FCKL_DTYPE_F32 ? 4 : 2;
+    a.h = reinterpret_cast<const uint16_t *>(h) + (size_t)c0 * d->H;
+    a.W = reinterpret_cast<const uint16_t *>(W);
+    a.idx = idx + (size_t)c0 * d->K;
+    a.tl = reinterpret_cast<const char *>(tl) + (size_t)c0 * d->K * esz;
+    a.logit_f32 = d->logit_dtype == FCKL_DTYPE_F32;
+    a.rows = (int32_t)((d->N - c0) < L->C ? (d->N - c0) : L->C);
+    a.H = d->H;
+    a.V = d->V;
+    a.K = d->K;
+    a.T = d->T;
+    a.ws = reinterpret_cast<char *>(ws);
+    a.L = L;
+    return a;
+}
+
+// FCKL_FLAG_VALIDATE: run the teacher preparation of every chunk with the index check
+// on, then read the flag back (the only host synchronisation in the library).
+fckl_status validate_indices(const fckl_desc *d, const void *h, const void *W, const int32_t *idx,
+                             const void *tl, void *ws, const Layout &L, void *stream)
+{
+    uint32_t *flag = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(ws) + L.off_err);
+    if (launch_zero_flag(flag, stream))
+        return FCKL_ERR_HIP;
+    for (int64_t c0 = 0; c0 < d->N; c0 += L.C) {
+        ChunkArgs a = chunk_args(d, h, W, idx, tl, ws, &L, c0);
+        if (launch_prepare(a, true, stream))
+            return FCKL_ERR_HIP;
+    }
+    uint32_t host = 0;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(&host, flag, sizeof(host), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return FCKL_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess)
+        return FCKL_ERR_HIP;
+    return host ? FCKL_ERR_INDEX : FCKL_OK;
+}
+
+// Brackets one launch with the caller's events when fckl_desc.profile selects it.
+class Timed {
+  public:
+    Timed(const fckl_desc *d, int kernel, int work, void *stream)
+        : p_(d->profile), s_(reinterpret_cast<hipStream_t>(stream))
+    {
+        if (p_ && p_->events && ((p_->kernel_mask >> kernel) & 1u) && p_->count >= 0 &&
+            p_->count < p_->capacity) {
+            slot_ = p_->count++;
+            if (p_->kernel_ids)
+                p_->kernel_ids[slot_] = kernel;
+            if (p_->work)
+                p_->work[slot_] = work;
+            (void)hipEventRecord(reinterpret_cast<hipEvent_t>(p_->events[2 * slot_]), s_);
+        }
+    }
+    ~Timed()
+    {
+        if (slot_ >= 0)
+            (void)hipEventRecord(reinterpret_cast<hipEvent_t>(p_->events[2 * slot_ + 1]), s_);
+    }
+
+  private:
+    fckl_profile *p_;
+    hipStream_t s_;
+    int slot_ = -1;
+};
+
+}  // namespace
+
+extern "C" {
+
+fckl_status fckl_plan(const fckl_desc *desc, size_t budget_bytes, int32_t *chunk_out, size_t *ws_bytes_out)
+{
+    Layout L;
+    fckl_status st = plan_chunk(desc, budget_bytes, &L);
+    if (st != FCKL_OK)
+        return st;
+    if (chunk_out)
+        *chunk_out = L.C;
+    if (ws_bytes_out)
+        *ws_bytes_out = L.total;
+    return FCKL_OK;
+}
+
+fckl_status fckl_workspace_size(const fckl_desc *desc, int32_t chunk, size_t *ws_bytes_out)
+{
+    Layout L;
+    fckl_status st = make_layout(desc, chunk, &L);
+    if (st != FCKL_OK)
+        return st;
+    if (ws_bytes_out)
+        *ws_bytes_out = L.total;
+    return FCKL_OK;
+}
+
+fckl_status fckl_forward(const fckl_desc *desc, const void *h, const void *W, const int32_t *topk_idx,
+                         const void *topk_logit, float *loss_tok, float *lse, float *loss_mean, void *ws,
+                         size_t ws_bytes, void *stream)
+{
+    Layout L;
+    fckl_status st = common_checks(desc, h, W, topk_idx, topk_logit, ws, ws_bytes, &L);
+    if (st != FCKL_OK)
+        return st;
+    if (!loss_tok || !lse)
+        return FCKL_ERR_INVALID_ARG;
+    if (desc->flags & FCKL_FLAG_VALIDATE) {
+        st = validate_indices(desc, h, W, topk_idx, topk_logit, ws, L, stream);
+        if (st != FCKL_OK)
+            return st;
+    }
+    for (int64_t c0 = 0; c0 < desc->N; c0 += L.C) {
+        ChunkArgs a = chunk_args(desc, h, W, topk_idx, topk_logit, ws, &L, c0);
+        {
+            Timed t(desc, FCKL_KERNEL_PREPARE, a.rows, stream);
+            if (launch_prepare(a, false, stream))
+                return FCKL_ERR_HIP;
+        }
+        {
+            Timed t(desc, FCKL_KERNEL_FWD_LOGITS, a.rows, stream);
+            if (launch_forward_logits(a, stream))
+                return FCKL_ERR_HIP;
+        }
+        {
+            Timed t(desc, FCKL_KERNEL_COMBINE, a.rows, stream);
+            if (launch_combine(a, loss_tok + c0, lse + c0, stream))
+                return FCKL_ERR_HIP;
+        }
+    }
+    if (loss_mean) {
+        Timed t(desc, FCKL_KERNEL_MEAN, (int)desc->N, stream);
+        if (launch_mean(loss_tok, desc->N, loss_mean, stream))
+            return FCKL_ERR_HIP;
+    }
+    return FCKL_OK;
+}
+
+fckl_status fckl_backward(const fckl_desc *desc, const void *h, const void *W, const int32_t *topk_idx,
+                          const void *topk_logit, const float *lse, float grad_scale, float *dH, float *dW,
+                          void *ws, size_t ws_bytes, void *stream)
+{
+    Layout L;
+    fckl_status st = common_checks(desc, h, W, topk_idx, topk_logit, ws, ws_bytes, &L);
+    if (st != FCKL_OK)
+        return st;
+    if (!lse || !dH || !dW)
+        return FCKL_ERR_INVALID_ARG;
+    if (desc->flags & FCKL_FLAG_VALIDATE) {
+        st = validate_indices(desc, h, W, topk_idx, topk_logit, ws, L, stream);
+        if (st != FCKL_OK)
+            return st;
+    }
+    // d(grad_scale * mean loss)/dz = grad_scale * (T/N) * ((sum p) q - scatter p)
+    const float coef = (float)((double)grad_scale * (double)desc->T / (double)desc->N);
+    const bool acc0 = (desc->flags & FCKL_FLAG_DW_ACCUMULATE) != 0;
+    for (int64_t c0 = 0; c0 < desc->N; c0 += L.C) {
+        ChunkArgs a = chunk_args(desc, h, W, topk_idx, topk_logit, ws, &L, c0);
+        {
+            Timed t(desc, FCKL_KERNEL_PREPARE, a.rows, stream);
+            if (launch_prepare(a, false, stream))
+                return FCKL_ERR_HIP;
+        }
+        {
+            Timed t(desc, FCKL_KERNEL_BWD_LOGITS, a.rows, stream);
+            if (launch_backward_logits(a, lse + c0, coef, stream))
+                return FCKL_ERR_HIP;
+        }
+        {
+            Timed t(desc, FCKL_KERNEL_DH, a.rows, stream);
+            if (launch_dh(a, stream))
+                return FCKL_ERR_HIP;
+        }
+        {
+            Timed t(desc, FCKL_KERNEL_DH_REDUCE, a.rows, stream);
+            if (launch_dh_reduce(a, dH + (size_t)c0 * desc->H, stream))
+                return FCKL_ERR_HIP;
+        }
+        {
+            Timed t(desc, FCKL_KERNEL_DW, a.rows, stream);
+            if (launch_dw(a, dW, acc0 || c0 > 0, stream))
+                return FCKL_ERR_HIP;
+        }
+    }
+    return FCKL_OK;
+}
+
+const char *fckl_status_string(fckl_status s)
+{
+    switch (s) {
+    case FCKL_OK:
+        return "success";
+    case FCKL_ERR_INVALID_ARG:
+        return "invalid argument";
+    case FCKL_ERR_UNSUPPORTED:
+        return "unsupported shape or option";
+    case FCKL_ERR_WORKSPACE:
+        return "workspace too small";
+    case FCKL_ERR_INDEX:
+        return "cached index out of range or repeated";
+    case FCKL_ERR_HIP:
+        return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int32_t fckl_version(void) { return 100; }
+
+}  // extern "C"

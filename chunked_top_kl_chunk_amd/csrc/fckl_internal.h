@@ -1,0 +1,71 @@
+// fckl_internal.h -- host-side plan, workspace layout and kernel launchers (not part of the ABI).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fckl.h"
+
+namespace fckl {
+
+// Token tile and vocabulary tile of the logit GEMMs (rows of W x tokens of h).
+constexpr int kVocabTile = 256;
+constexpr int kTokenTile = 256;
+constexpr int kMaxK = 128;
+constexpr int32_t kMaxChunk = 16384;
+constexpr size_t kDefaultBudget = size_t(4) << 30;   // 4 GiB of the 288 GB HBM3E
+
+// Where each per-chunk buffer lives inside the caller's workspace.  Every buffer is
+// sized by the chunk, never by N.
+struct Layout {
+    int32_t C = 0;          // tokens per chunk
+    int32_t Cpad = 0;       // C rounded up to kTokenTile
+    int32_t nVt = 0;        // vocabulary tiles: ceil(V / kVocabTile)
+    int32_t Vpad = 0;       // nVt * kVocabTile (row pitch of g)
+    int32_t cnt_stride = 0; // bytes per token of the per-tile entry-count table
+    int32_t dh_bn = 0;      // hidden-dimension tile of the dH / dW products (192 or 256)
+    int32_t dh_splits = 0;  // vocabulary splits of the dH product
+    size_t off_idx = 0;     // int32 [Cpad, K]   cached indices, sorted ascending per token
+    size_t off_p = 0;       // f32   [Cpad, K]   teacher probabilities in the same order
+    size_t off_zk = 0;      // f32   [Cpad, K]   student logit at each sorted index
+    size_t off_psum = 0;    // f32   [Cpad]      sum_k p
+    size_t off_negent = 0;  // f32   [Cpad]      sum_k p log p
+    size_t off_cnt = 0;     // u8    [Cpad, cnt_stride] entries below each vocabulary tile start
+    size_t off_part = 0;    // f32x2 [nVt, Cpad] per-tile (max, sum exp) of z/T, base 2
+    size_t off_g = 0;       // bf16  [Cpad, Vpad] chunk gradient w.r.t. the logits
+    size_t off_dhp = 0;     // f32   [dh_splits, Cpad, H] split partial sums of dH
+    size_t off_err = 0;     // u32   [4]         index-check flag
+    size_t total = 0;
+};
+
+fckl_status check_desc(const fckl_desc *d);
+fckl_status make_layout(const fckl_desc *d, int32_t chunk, Layout *L);
+fckl_status plan_chunk(const fckl_desc *d, size_t budget, Layout *L);
+
+// ------------------------------------------------------------------ launchers
+// All return hipSuccess (0) or the launch error; they never synchronise.
+
+struct ChunkArgs {
+    const uint16_t *h;          // chunk's first row of h [.., H]
+    const uint16_t *W;          // [V, H]
+    const int32_t *idx;         // chunk's first row of topk_idx [.., K]
+    const void *tl;             // chunk's first row of topk_logit
+    int logit_f32;
+    int32_t rows;               // valid tokens in this chunk (<= C)
+    int32_t H, V, K;
+    float T;
+    char *ws;
+    const Layout *L;
+};
+
+int launch_prepare(const ChunkArgs &a, bool validate, void *stream);
+int launch_forward_logits(const ChunkArgs &a, void *stream);
+int launch_combine(const ChunkArgs &a, float *loss_tok, float *lse, void *stream);
+int launch_mean(const float *loss_tok, int64_t N, float *loss_mean, void *stream);
+int launch_backward_logits(const ChunkArgs &a, const float *lse, float coef, void *stream);
+int launch_dh(const ChunkArgs &a, void *stream);
+int launch_dh_reduce(const ChunkArgs &a, float *dH, void *stream);
+int launch_dw(const ChunkArgs &a, float *dW, bool accumulate, void *stream);
+int launch_zero_flag(uint32_t *flag, void *stream);
+
+}  // namespace fckl

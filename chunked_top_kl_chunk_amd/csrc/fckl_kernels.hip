@@ -1,0 +1,975 @@
+// fckl_kernels.hip -- gfx950 kernels of the fused chunked top-K KL loss.
+//
+// Per chunk of tokens (one slice of the sequence at a time, "Breaking the Bottleneck
+// with Offline Caching and Chunked Loss", axbrief.com; the output projection is folded
+// into the loss, "What actually changed?", calcaas.com):
+//
+//   prepare          teacher softmax over the K cached logits, entries sorted by index,
+//                    per-vocabulary-tile entry counts
+//   forward_logits   z^T tile = W_tile . h_tile^T on MFMA (bf16 in, fp32 accumulate);
+//                    the epilogue keeps z in registers, reduces max / sum exp(z/T) over
+//                    the tile's 256 vocabulary rows per token and picks z at the cached
+//                    indices owned by the tile.  Only (max, sum) per tile and the K
+//                    picked logits per token leave the chip.
+//   combine          per token: logsumexp over the tiles, the KL term, the loss
+//   backward_logits  the same MFMA tiles recompute z (the extra projection in the
+//                    backward pass that the chunked loss pays for, axbrief.com);
+//                    the epilogue forms g = c((sum p) softmax(z/T) - scatter(p, idx)),
+//                    rounds it to bf16 and writes the chunk's g [C, V]
+//   dh               dH_chunk = g . W   (split over the vocabulary, fixed-order reduce)
+//   dw               dW += g^T . h_chunk (fp32 read-modify-write, chunk after chunk)
+//
+// GEMM core: 256 x 256 (or 256 x 192) tiles, 512 threads = 8 wave64s, each wave owns a
+// 128 x 64 (or 64 x 96) block of v_mfma_f32_32x32x16_bf16 accumulators.  Operands are
+// staged global -> registers -> LDS (two stages, one barrier per 64-deep k-step).  LDS
+// rows hold 64 bf16 along k with an XOR swizzle of the 16-byte chunk index.  Operands
+// whose contiguous dimension is not k (W and h in the backward products, g in dW) are
+// transposed in registers (8 k-rows x 4 columns per thread) before the LDS write.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fckl_internal.h"
+
+namespace fckl {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 512;
+constexpr int kBK = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// ------------------------------------------------------------------ small helpers
+
+// LDS operand tiles: one row = 64 bf16 along k = eight 16-byte chunks.  The chunk
+// index is XOR-ed with row bits 0-2 and 3-5 so that 8 consecutive rows at one chunk
+// (the MFMA operand read) and 8 rows 8 apart (the transposed write) hit 8 distinct
+// 16-byte bank groups.
+__device__ __forceinline__ int swz(int row, int kc)
+{
+    return (row << 3) + (kc ^ (row & 7) ^ ((row >> 3) & 7));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// float -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return 0x7fc0u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v += __shfl_xor(v, o);
+    return v;
+}
+
+// Merge two (max, sum) pairs of base-2 exponentials: sum_a 2^(x-ma) + sum_b 2^(x-mb).
+__device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2)
+{
+    float M = fmaxf(m, m2);
+    if (M == kNegInf)
+        return;
+    s = s * fast_exp2(m - M) + s2 * fast_exp2(m2 - M);
+    m = M;
+}
+
+// Work-group id -> (tile along M, tile along N).  Work-groups are dealt to the eight
+// XCDs round-robin; renumber them so that each XCD runs a contiguous range, then walk
+// that range in groups of GM tiles along M x all tiles along N, so that the tiles in
+// flight on one XCD share operand rows in its L2.
+__device__ __forceinline__ void map_tile(int bid, int nM, int nN, int GM, int &tm, int &tn)
+{
+    const int total = nM * nN;
+    const int per = total >> 3;
+    int id = bid;
+    if (bid < (per << 3))
+        id = (bid & 7) * per + (bid >> 3);
+    const int group = GM * nN;
+    const int g = id / group;
+    const int first = g * GM;
+    const int gm = min(nM - first, GM);
+    const int r = id - g * group;
+    tm = first + r % gm;
+    tn = r / gm;
+}
+
+// ------------------------------------------------------------------ operand loaders
+
+// Operand whose k dimension is contiguous in memory: element (row, k) at base[row*ld + k].
+template <int ROWS>
+struct KMajorLoad {
+    static_assert((ROWS * 8) % kThreads == 0, "tile rows");
+    static constexpr int kPer = ROWS * 8 / kThreads;
+    u32x4 r[kPer];
+
+    __device__ __forceinline__ void load(const uint16_t *base, int64_t ld, int row0, int rows_valid, int k0,
+                                         int k_valid)
+    {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int c = threadIdx.x + i * kThreads;
+            const int row = c >> 3, kc = c & 7;
+            const int grow = row0 + row, gk = k0 + kc * 8;
+            if (grow < rows_valid && gk < k_valid)
+                r[i] = *reinterpret_cast<const u32x4 *>(base + (int64_t)grow * ld + gk);
+            else
+                r[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    __device__ __forceinline__ void store(char *lds) const
+    {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int c = threadIdx.x + i * kThreads;
+            *reinterpret_cast<u32x4 *>(lds + swz(c >> 3, c & 7) * 16) = r[i];
+        }
+    }
+};
+
+// Operand whose row dimension is contiguous: element (row, k) at base[k*ld + row].
+// Each thread loads 8 consecutive k-rows x 4 consecutive columns (8 bytes per row) and
+// transposes them into four 16-byte k-vectors.
+template <int ROWS>
+struct RowMajorLoad {
+    static constexpr int kQuads = ROWS / 4;
+    static constexpr int kBlocks = 8 * kQuads;
+    static_assert(kBlocks <= kThreads, "tile rows");
+    u32x2 r[8];
+
+    __device__ __forceinline__ void load(const uint16_t *base, int64_t ld, int row0, int rows_valid, int k0,
+                                         int k_valid)
+    {
+        const int t = threadIdx.x;
+        const int kg = t / kQuads, q = t - (t / kQuads) * kQuads;
+        const int grow = row0 + q * 4;
+        const bool ok = (t < kBlocks) && (grow < rows_valid);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int gk = k0 + kg * 8 + i;
+            if (ok && gk < k_valid)
+                r[i] = *reinterpret_cast<const u32x2 *>(base + (int64_t)gk * ld + grow);
+            else
+                r[i] = u32x2{0u, 0u};
+        }
+    }
+    __device__ __forceinline__ void store(char *lds) const
+    {
+        const int t = threadIdx.x;
+        if (t >= kBlocks)
+            return;
+        const int kg = t / kQuads, q = t - (t / kQuads) * kQuads;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            u32x4 o;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t lo = r[2 * d][c >> 1], hi = r[2 * d + 1][c >> 1];
+                o[d] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+            }
+            *reinterpret_cast<u32x4 *>(lds + swz(q * 4 + c, kg) * 16) = o;
+        }
+    }
+};
+
+template <bool KMAJ, int ROWS>
+struct LoaderOf {
+    using type = KMajorLoad<ROWS>;
+};
+template <int ROWS>
+struct LoaderOf<false, ROWS> {
+    using type = RowMajorLoad<ROWS>;
+};
+
+// ------------------------------------------------------------------ GEMM core
+
+// C[m, n] = sum_k A(m, k) * B(n, k) for one BM x BN tile; the result stays in
+// registers: acc[mb][nb][r] is row m0 + wm*WTM + mb*32 + 8*(r/4) + 4*(lane/32) + r%4,
+// column n0 + wn*WTN + nb*32 + lane%32.
+template <int BM_, int BN_, int WM_, int WN_, bool AK, bool BKM>
+struct Gemm {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static_assert(WM * WN * 64 == kThreads, "8 waves");
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
+    static constexpr int MB = WTM / 32, NB = WTN / 32;
+    static_assert(MB * 32 == WTM && NB * 32 == WTN, "wave tile");
+    static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int LDS_BYTES = 2 * STAGE;
+    using ALoad = typename LoaderOf<AK, BM>::type;
+    using BLoad = typename LoaderOf<BKM, BN>::type;
+
+    __device__ __forceinline__ static int row_of(int wm, int mb, int r, int lane)
+    {
+        return wm * WTM + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    }
+    __device__ __forceinline__ static int col_of(int wn, int nb, int lane) { return wn * WTN + nb * 32 + (lane & 31); }
+
+    __device__ static void run(char *smem, const uint16_t *A, int64_t lda, int m0, int m_valid,
+                               const uint16_t *B, int64_t ldb, int n0, int n_valid, int k_begin, int k_end,
+                               f32x16 (&acc)[MB][NB])
+    {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int wm = wave / WN, wn = wave % WN;
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[i][j][r] = 0.0f;
+        const int nk = (k_end - k_begin + kBK - 1) / kBK;
+        if (nk <= 0)
+            return;
+        ALoad la;
+        BLoad lb;
+        la.load(A, lda, m0, m_valid, k_begin, k_end);
+        lb.load(B, ldb, n0, n_valid, k_begin, k_end);
+        la.store(smem);
+        lb.store(smem + A_BYTES);
+        __syncthreads();
+        for (int kb = 0; kb < nk; ++kb) {
+            char *cur = smem + (kb & 1) * STAGE;
+            const bool more = kb + 1 < nk;
+            if (more) {
+                la.load(A, lda, m0, m_valid, k_begin + (kb + 1) * kBK, k_end);
+                lb.load(B, ldb, n0, n_valid, k_begin + (kb + 1) * kBK, k_end);
+            }
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int kc = ks * 2 + (lane >> 5);
+                bf16x8 af[MB], bfrag[NB];
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+                    af[i] = *reinterpret_cast<const bf16x8 *>(cur + swz(wm * WTM + i * 32 + (lane & 31), kc) * 16);
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    bfrag[j] = *reinterpret_cast<const bf16x8 *>(cur + A_BYTES +
+                                                                  swz(wn * WTN + j * 32 + (lane & 31), kc) * 16);
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+#pragma unroll
+                    for (int j = 0; j < NB; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfrag[j], acc[i][j], 0, 0, 0);
+            }
+            if (more) {
+                char *nxt = smem + ((kb + 1) & 1) * STAGE;
+                la.store(nxt);
+                lb.store(nxt + A_BYTES);
+            }
+            __syncthreads();
+        }
+    }
+};
+
+// The logit GEMM: rows = vocabulary (W), columns = tokens (h), k = hidden.
+using LogitGemm = Gemm<256, 256, 2, 4, true, true>;
+constexpr int kGStagePitch = 256 * 2 + 16;   // bytes per token row of the bf16 g staging tile
+constexpr int kLogitLds = (LogitGemm::LDS_BYTES > 256 * kGStagePitch) ? LogitGemm::LDS_BYTES : 256 * kGStagePitch;
+
+// Select acc[mb][nb][r] for a run-time (mb*16 + r) without indexing registers.
+template <int MB, int NB>
+__device__ __forceinline__ float pick(const f32x16 (&acc)[MB][NB], int nb, int sel)
+{
+    float v = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+        if (j == nb) {
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    v = (i * 16 + r == sel) ? acc[i][j][r] : v;
+        }
+    return v;
+}
+
+template <int MB, int NB>
+__device__ __forceinline__ void sub_at(f32x16 (&acc)[MB][NB], int nb, int sel, float d)
+{
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+        if (j == nb) {
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[i][j][r] = (i * 16 + r == sel) ? acc[i][j][r] - d : acc[i][j][r];
+        }
+}
+
+// ------------------------------------------------------------------ prepare
+
+struct PrepParams {
+    const int32_t *idx;     // [rows, K] chunk's cached indices
+    const void *tl;         // [rows, K] chunk's cached logits
+    int logit_f32;
+    int rows, K, V, nVt, cnt_stride;
+    float scale2;           // log2(e) / T
+    int32_t *idx_s;         // [Cpad, K] out
+    float *p_s;             // [Cpad, K] out
+    float *zk;              // [Cpad, K] out: NaN until the forward epilogue fills it
+    float *psum;            // [Cpad] out
+    float *negent;          // [Cpad] out: sum_k p log p (natural log)
+    uint8_t *cnt;           // [Cpad, cnt_stride] out
+    uint32_t *err;          // index-check flag (validate only)
+    int validate;
+};
+
+// One wave per token.  Teacher distribution p = softmax(tl/T) over the K entries
+// ("Preparing Offline Top-K Logits", getaibook.com: the cache holds the top-K logits
+// and their indices); entries are sorted by vocabulary index (rank = number of entries
+// with a smaller index, ties by position) so that each vocabulary tile owns one
+// contiguous range of them, whose bounds cnt[] records.
+__global__ __launch_bounds__(256) void prepare_kernel(PrepParams p)
+{
+    __shared__ int s_idx[4][kMaxK];
+    __shared__ int s_sorted[4][kMaxK];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + w;
+    const bool live = t < p.rows;
+    const int K = p.K;
+    float a[2], pr[2];
+    int ix[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int e = lane + 64 * h;
+        a[h] = kNegInf;
+        ix[h] = 0x7fffffff;
+        if (live && e < K) {
+            const size_t o = (size_t)t * K + e;
+            const float x = p.logit_f32 ? reinterpret_cast<const float *>(p.tl)[o]
+                                        : bf16_to_f32(reinterpret_cast<const uint16_t *>(p.tl)[o]);
+            a[h] = x * p.scale2;
+            ix[h] = p.idx[o];
+        }
+        if (e < kMaxK)
+            s_idx[w][e] = ix[h];
+    }
+    const float m = wave_max(fmaxf(a[0], a[1]));
+    const float ms = (m == kNegInf) ? 0.0f : m;
+    const float s = wave_sum(fast_exp2(a[0] - ms) + fast_exp2(a[1] - ms));
+    const float lse2 = ms + log2f(s);
+    float ps = 0.0f, ne = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const bool in = lane + 64 * h < K;
+        pr[h] = in ? fast_exp2(a[h] - lse2) : 0.0f;
+        ps += pr[h];
+        ne += in ? pr[h] * (a[h] - lse2) * kLn2 : 0.0f;
+    }
+    ps = wave_sum(ps);
+    ne = wave_sum(ne);
+    __syncthreads();
+    bool bad = false;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int e = lane + 64 * h;
+        if (live && e < K) {
+            const int v = ix[h];
+            int rank = 0;
+            for (int j = 0; j < K; ++j) {
+                const int u = s_idx[w][j];
+                rank += (u < v || (u == v && j < e)) ? 1 : 0;
+                bad |= (u == v && j != e);
+            }
+            bad |= (v < 0 || v >= p.V);
+            const size_t o = (size_t)t * K + rank;
+            p.idx_s[o] = v;
+            p.p_s[o] = pr[h];
+            p.zk[o] = __builtin_nanf("");
+            s_sorted[w][rank] = v;
+        }
+    }
+    if (live && lane == 0) {
+        p.psum[t] = ps;
+        p.negent[t] = ne;
+    }
+    if (p.validate && bad)
+        *p.err = 1u;
+    __syncthreads();
+    if (!live)
+        return;
+    // cnt[vt] = number of sorted entries below vt * 256 (lower bound in s_sorted).
+    uint8_t *crow = p.cnt + (size_t)t * p.cnt_stride;
+    for (int vt = lane; vt <= p.nVt; vt += 64) {
+        const int key = vt * kVocabTile;
+        int lo = 0, hi = K;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (s_sorted[w][mid] < key)
+                lo = mid + 1;
+            else
+                hi = mid;
+        }
+        crow[vt] = (uint8_t)lo;
+    }
+}
+
+// ------------------------------------------------------------------ forward logits
+
+struct FwdParams {
+    const uint16_t *W;      // [V, H]
+    const uint16_t *h;      // [rows, H] chunk
+    int H, V, rows, Cpad, K, nVt, nNt, cnt_stride;
+    float scale2;           // log2(e) / T
+    const int32_t *idx_s;
+    const uint8_t *cnt;
+    float *zk;
+    float2 *part;           // [nVt, Cpad]
+};
+
+__global__ __launch_bounds__(kThreads) void forward_logits_kernel(FwdParams p)
+{
+    using G = LogitGemm;
+    __shared__ __attribute__((aligned(16))) char smem[kLogitLds];
+    int tm, tn;
+    map_tile(blockIdx.x, p.nVt, p.nNt, 4, tm, tn);
+    const int m0 = tm * G::BM, n0 = tn * G::BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / G::WN, wn = wave % G::WN;
+
+    // Entry range of this vocabulary tile for each of the lane's tokens.
+    int cs[G::NB], ce[G::NB];
+#pragma unroll
+    for (int j = 0; j < G::NB; ++j) {
+        const int tok = n0 + G::col_of(wn, j, lane);
+        cs[j] = ce[j] = 0;
+        if (tok < p.rows) {
+            const uint8_t *c = p.cnt + (size_t)tok * p.cnt_stride + tm;
+            cs[j] = c[0];
+            ce[j] = c[1];
+        }
+    }
+
+    f32x16 acc[G::MB][G::NB];
+    G::run(smem, p.W, p.H, m0, p.V, p.h, p.H, n0, p.rows, 0, p.H, acc);
+
+    // Per token, over the wave's 128 vocabulary rows: max and sum of 2^(z*log2e/T - max).
+    float *red = reinterpret_cast<float *>(smem);   // [WM][BN][2]
+#pragma unroll
+    for (int j = 0; j < G::NB; ++j) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int i = 0; i < G::MB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const bool in = m0 + G::row_of(wm, i, r, lane) < p.V;
+                mx = fmaxf(mx, in ? acc[i][j][r] * p.scale2 : kNegInf);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float ms = (mx == kNegInf) ? 0.0f : mx;
+        float sum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < G::MB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const bool in = m0 + G::row_of(wm, i, r, lane) < p.V;
+                sum += in ? fast_exp2(acc[i][j][r] * p.scale2 - ms) : 0.0f;
+            }
+        sum += __shfl_xor(sum, 32);
+        if (lane < 32) {
+            const int nl = G::col_of(wn, j, lane);
+            red[(wm * G::BN + nl) * 2 + 0] = mx;
+            red[(wm * G::BN + nl) * 2 + 1] = sum;
+        }
+    }
+    __syncthreads();
+    for (int nl = threadIdx.x; nl < G::BN; nl += kThreads) {
+        if (n0 + nl < p.rows) {
+            float m = red[nl * 2 + 0], s = red[nl * 2 + 1];
+#pragma unroll
+            for (int w2 = 1; w2 < G::WM; ++w2)
+                lse_merge(m, s, red[(w2 * G::BN + nl) * 2 + 0], red[(w2 * G::BN + nl) * 2 + 1]);
+            p.part[(size_t)tm * p.Cpad + n0 + nl] = make_float2(m, s);
+        }
+    }
+    // Pick z at the cached indices this tile owns: the lane holding that row writes it.
+    const int wrow0 = m0 + wm * G::WTM;
+#pragma unroll
+    for (int j = 0; j < G::NB; ++j) {
+        const int tok = n0 + G::col_of(wn, j, lane);
+        for (int e = cs[j]; e < ce[j]; ++e) {
+            const int v = p.idx_s[(size_t)tok * p.K + e];
+            const int row = v - wrow0;
+            if (row >= 0 && row < G::WTM && v < p.V) {
+                const int r32 = row & 31;
+                if (((r32 >> 2) & 1) == (lane >> 5)) {
+                    const int sel = (row >> 5) * 16 + ((r32 >> 3) << 2) + (r32 & 3);
+                    p.zk[(size_t)tok * p.K + e] = pick(acc, j, sel);
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ combine
+
+struct CombineParams {
+    const float2 *part;
+    const float *zk, *p_s, *psum, *negent;
+    int rows, Cpad, nVt, K;
+    float T;
+    float *loss_tok;        // chunk's first token
+    float *lse;             // chunk's first token
+};
+
+// 32 tokens x 8 slices of the vocabulary tiles per block.
+__global__ __launch_bounds__(256) void combine_kernel(CombineParams p)
+{
+    __shared__ float s_m[8][32], s_s[8][32], s_d[8][32];
+    const int tl = threadIdx.x & 31, sp = threadIdx.x >> 5;
+    const int t = blockIdx.x * 32 + tl;
+    float m = kNegInf, s = 0.0f, d = 0.0f;
+    if (t < p.rows) {
+        for (int vt = sp; vt < p.nVt; vt += 8) {
+            const float2 q = p.part[(size_t)vt * p.Cpad + t];
+            lse_merge(m, s, q.x, q.y);
+        }
+        for (int e = sp; e < p.K; e += 8)
+            d += p.p_s[(size_t)t * p.K + e] * p.zk[(size_t)t * p.K + e];
+    }
+    s_m[sp][tl] = m;
+    s_s[sp][tl] = s;
+    s_d[sp][tl] = d;
+    __syncthreads();
+    if (sp == 0 && t < p.rows) {
+#pragma unroll
+        for (int k = 1; k < 8; ++k) {
+            lse_merge(m, s, s_m[k][tl], s_s[k][tl]);
+            d += s_d[k][tl];
+        }
+        const float lse = (m + log2f(s)) * kLn2;    // log sum_v exp(z_v / T)
+        // T^2 * sum_k p (log p - z_k/T + lse)
+        const float loss = p.T * p.T * (p.negent[t] - d / p.T + p.psum[t] * lse);
+        p.loss_tok[t] = loss;
+        p.lse[t] = lse;
+    }
+}
+
+// ------------------------------------------------------------------ mean
+
+__global__ __launch_bounds__(1024) void mean_kernel(const float *x, int64_t n, float *out)
+{
+    __shared__ double s[1024];
+    double a = 0.0;
+    for (int64_t i = threadIdx.x; i < n; i += 1024)
+        a += (double)x[i];
+    s[threadIdx.x] = a;
+    __syncthreads();
+    for (int o = 512; o >= 1; o >>= 1) {
+        if ((int)threadIdx.x < o)
+            s[threadIdx.x] += s[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0)
+        *out = (float)(s[0] / (double)n);
+}
+
+// ------------------------------------------------------------------ backward logits
+
+struct BwdParams {
+    const uint16_t *W, *h;
+    int H, V, rows, Cpad, Vpad, K, nVt, nNt, cnt_stride;
+    float scale2;           // log2(e) / T
+    float coef;             // grad_scale * T / N
+    const float *lse;       // chunk's first token (natural log, z/T units)
+    const int32_t *idx_s;
+    const float *p_s, *psum;
+    const uint8_t *cnt;
+    uint16_t *g;            // [Cpad, Vpad] bf16
+};
+
+__global__ __launch_bounds__(kThreads) void backward_logits_kernel(BwdParams p)
+{
+    using G = LogitGemm;
+    __shared__ __attribute__((aligned(16))) char smem[kLogitLds];
+    int tm, tn;
+    map_tile(blockIdx.x, p.nVt, p.nNt, 4, tm, tn);
+    const int m0 = tm * G::BM, n0 = tn * G::BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / G::WN, wn = wave % G::WN;
+
+    int cs[G::NB], ce[G::NB];
+    float l2[G::NB], amp[G::NB];
+#pragma unroll
+    for (int j = 0; j < G::NB; ++j) {
+        const int tok = n0 + G::col_of(wn, j, lane);
+        cs[j] = ce[j] = 0;
+        l2[j] = 0.0f;
+        amp[j] = 0.0f;
+        if (tok < p.rows) {
+            const uint8_t *c = p.cnt + (size_t)tok * p.cnt_stride + tm;
+            cs[j] = c[0];
+            ce[j] = c[1];
+            l2[j] = p.lse[tok] * kLog2e;
+            amp[j] = p.coef * p.psum[tok];
+        }
+    }
+
+    f32x16 acc[G::MB][G::NB];
+    G::run(smem, p.W, p.H, m0, p.V, p.h, p.H, n0, p.rows, 0, p.H, acc);
+
+    // g = coef * ((sum p) * exp(z/T - lse) - scatter(p, idx)); zero outside [0,V) x [0,rows).
+#pragma unroll
+    for (int j = 0; j < G::NB; ++j) {
+        const bool tok_in = n0 + G::col_of(wn, j, lane) < p.rows;
+#pragma unroll
+        for (int i = 0; i < G::MB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const bool in = tok_in && (m0 + G::row_of(wm, i, r, lane) < p.V);
+                acc[i][j][r] = in ? amp[j] * fast_exp2(acc[i][j][r] * p.scale2 - l2[j]) : 0.0f;
+            }
+    }
+    const int wrow0 = m0 + wm * G::WTM;
+#pragma unroll
+    for (int j = 0; j < G::NB; ++j) {
+        const int tok = n0 + G::col_of(wn, j, lane);
+        for (int e = cs[j]; e < ce[j]; ++e) {
+            const int v = p.idx_s[(size_t)tok * p.K + e];
+            const int row = v - wrow0;
+            if (row >= 0 && row < G::WTM && v < p.V) {
+                const int r32 = row & 31;
+                if (((r32 >> 2) & 1) == (lane >> 5)) {
+                    const int sel = (row >> 5) * 16 + ((r32 >> 3) << 2) + (r32 & 3);
+                    sub_at(acc, j, sel, p.coef * p.p_s[(size_t)tok * p.K + e]);
+                }
+            }
+        }
+    }
+    // Stage the bf16 tile as [token][vocab] in LDS, then write whole 16-byte pieces.
+    // (The main loop ended with a barrier, so the operand buffers are free.)
+#pragma unroll
+    for (int j = 0; j < G::NB; ++j) {
+        const int nl = G::col_of(wn, j, lane);
+#pragma unroll
+        for (int i = 0; i < G::MB; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int ml = G::row_of(wm, i, 4 * q, lane);
+                u32x2 pk;
+                pk[0] = bf16_rne(acc[i][j][4 * q + 0]) | (bf16_rne(acc[i][j][4 * q + 1]) << 16);
+                pk[1] = bf16_rne(acc[i][j][4 * q + 2]) | (bf16_rne(acc[i][j][4 * q + 3]) << 16);
+                *reinterpret_cast<u32x2 *>(smem + nl * kGStagePitch + ml * 2) = pk;
+            }
+    }
+    __syncthreads();
+    constexpr int kChunks = G::BN * (G::BM * 2 / 16);
+#pragma unroll 4
+    for (int c = threadIdx.x; c < kChunks; c += kThreads) {
+        const int nl = c >> 5, col = (c & 31) * 8;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + nl * kGStagePitch + col * 2);
+        *reinterpret_cast<u32x4 *>(p.g + (size_t)(n0 + nl) * p.Vpad + m0 + col) = v;
+    }
+}
+
+// ------------------------------------------------------------------ dH = g . W
+
+struct DhParams {
+    const uint16_t *g;      // [Cpad, Vpad]
+    const uint16_t *W;      // [V, H]
+    int H, V, Vpad, rows, Cpad, nMt, nNt, ksplit;
+    float *part;            // [splits, Cpad, H]
+};
+
+template <class G>
+__global__ __launch_bounds__(kThreads) void dh_kernel(DhParams p)
+{
+    __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
+    int tm, tn;
+    map_tile(blockIdx.x, p.nMt, p.nNt, 1, tm, tn);
+    const int m0 = tm * G::BM, n0 = tn * G::BN;
+    const int k_begin = blockIdx.y * p.ksplit;
+    const int k_end = min(p.V, k_begin + p.ksplit);
+    f32x16 acc[G::MB][G::NB];
+    // A(m = token, k = vocab) = g[m][k]; B(n = hidden, k = vocab) = W[k][n].
+    G::run(smem, p.g, p.Vpad, m0, p.rows, p.W, p.H, n0, p.H, k_begin, k_end, acc);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / G::WN, wn = wave % G::WN;
+    float *out = p.part + (size_t)blockIdx.y * p.Cpad * p.H;
+#pragma unroll
+    for (int j = 0; j < G::NB; ++j) {
+        const int col = n0 + G::col_of(wn, j, lane);
+        if (col < p.H) {
+#pragma unroll
+            for (int i = 0; i < G::MB; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + G::row_of(wm, i, r, lane);
+                    if (row < p.rows)
+                        out[(size_t)row * p.H + col] = acc[i][j][r];
+                }
+        }
+    }
+}
+
+// dH[row] = sum over splits, in split order.
+__global__ __launch_bounds__(256) void dh_reduce_kernel(const float *part, int splits, size_t split_stride,
+                                                         size_t n4, float *dH)
+{
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4)
+        return;
+    float4 a = reinterpret_cast<const float4 *>(part)[i];
+    for (int s = 1; s < splits; ++s) {
+        const float4 b = reinterpret_cast<const float4 *>(part + s * split_stride)[i];
+        a.x += b.x;
+        a.y += b.y;
+        a.z += b.z;
+        a.w += b.w;
+    }
+    reinterpret_cast<float4 *>(dH)[i] = a;
+}
+
+// ------------------------------------------------------------------ dW += g^T . h
+
+struct DwParams {
+    const uint16_t *g;      // [Cpad, Vpad]
+    const uint16_t *h;      // [rows, H] chunk
+    int H, V, Vpad, rows, nMt, nNt, accumulate;
+    float *dW;              // [V, H]
+};
+
+template <class G>
+__global__ __launch_bounds__(kThreads) void dw_kernel(DwParams p)
+{
+    __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
+    int tm, tn;
+    map_tile(blockIdx.x, p.nMt, p.nNt, 1, tm, tn);
+    const int m0 = tm * G::BM, n0 = tn * G::BN;
+    f32x16 acc[G::MB][G::NB];
+    // A(m = vocab, k = token) = g[k][m]; B(n = hidden, k = token) = h[k][n].
+    G::run(smem, p.g, p.Vpad, m0, p.Vpad, p.h, p.H, n0, p.H, 0, p.rows, acc);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / G::WN, wn = wave % G::WN;
+#pragma unroll
+    for (int j = 0; j < G::NB; ++j) {
+        const int col = n0 + G::col_of(wn, j, lane);
+        if (col < p.H) {
+#pragma unroll
+            for (int i = 0; i < G::MB; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + G::row_of(wm, i, r, lane);
+                    if (row < p.V) {
+                        float *d = p.dW + (size_t)row * p.H + col;
+                        *d = p.accumulate ? *d + acc[i][j][r] : acc[i][j][r];
+                    }
+                }
+        }
+    }
+}
+
+using DGemm256 = Gemm<256, 256, 2, 4, true, false>;   // dH, hidden tile 256
+using DGemm192 = Gemm<256, 192, 4, 2, true, false>;   // dH, hidden tile 192
+using WGemm256 = Gemm<256, 256, 2, 4, false, false>;  // dW, hidden tile 256
+using WGemm192 = Gemm<256, 192, 4, 2, false, false>;  // dW, hidden tile 192
+
+__global__ void zero_u32_kernel(uint32_t *p, int n)
+{
+    if ((int)threadIdx.x < n)
+        p[threadIdx.x] = 0u;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ launchers
+
+static inline hipStream_t S(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+int launch_prepare(const ChunkArgs &a, bool validate, void *stream)
+{
+    const Layout &L = *a.L;
+    PrepParams p;
+    p.idx = a.idx;
+    p.tl = a.tl;
+    p.logit_f32 = a.logit_f32;
+    p.rows = a.rows;
+    p.K = a.K;
+    p.V = a.V;
+    p.nVt = L.nVt;
+    p.cnt_stride = L.cnt_stride;
+    p.scale2 = kLog2e / a.T;
+    p.idx_s = reinterpret_cast<int32_t *>(a.ws + L.off_idx);
+    p.p_s = reinterpret_cast<float *>(a.ws + L.off_p);
+    p.zk = reinterpret_cast<float *>(a.ws + L.off_zk);
+    p.psum = reinterpret_cast<float *>(a.ws + L.off_psum);
+    p.negent = reinterpret_cast<float *>(a.ws + L.off_negent);
+    p.cnt = reinterpret_cast<uint8_t *>(a.ws + L.off_cnt);
+    p.err = reinterpret_cast<uint32_t *>(a.ws + L.off_err);
+    p.validate = validate ? 1 : 0;
+    hipLaunchKernelGGL(prepare_kernel, dim3((a.rows + 3) / 4), dim3(256), 0, S(stream), p);
+    return (int)hipGetLastError();
+}
+
+int launch_forward_logits(const ChunkArgs &a, void *stream)
+{
+    const Layout &L = *a.L;
+    FwdParams p;
+    p.W = a.W;
+    p.h = a.h;
+    p.H = a.H;
+    p.V = a.V;
+    p.rows = a.rows;
+    p.Cpad = L.Cpad;
+    p.K = a.K;
+    p.nVt = L.nVt;
+    p.nNt = (a.rows + kTokenTile - 1) / kTokenTile;
+    p.cnt_stride = L.cnt_stride;
+    p.scale2 = kLog2e / a.T;
+    p.idx_s = reinterpret_cast<const int32_t *>(a.ws + L.off_idx);
+    p.cnt = reinterpret_cast<const uint8_t *>(a.ws + L.off_cnt);
+    p.zk = reinterpret_cast<float *>(a.ws + L.off_zk);
+    p.part = reinterpret_cast<float2 *>(a.ws + L.off_part);
+    hipLaunchKernelGGL(forward_logits_kernel, dim3(p.nVt * p.nNt), dim3(kThreads), 0, S(stream), p);
+    return (int)hipGetLastError();
+}
+
+int launch_combine(const ChunkArgs &a, float *loss_tok, float *lse, void *stream)
+{
+    const Layout &L = *a.L;
+    CombineParams p;
+    p.part = reinterpret_cast<const float2 *>(a.ws + L.off_part);
+    p.zk = reinterpret_cast<const float *>(a.ws + L.off_zk);
+    p.p_s = reinterpret_cast<const float *>(a.ws + L.off_p);
+    p.psum = reinterpret_cast<const float *>(a.ws + L.off_psum);
+    p.negent = reinterpret_cast<const float *>(a.ws + L.off_negent);
+    p.rows = a.rows;
+    p.Cpad = L.Cpad;
+    p.nVt = L.nVt;
+    p.K = a.K;
+    p.T = a.T;
+    p.loss_tok = loss_tok;
+    p.lse = lse;
+    hipLaunchKernelGGL(combine_kernel, dim3((a.rows + 31) / 32), dim3(256), 0, S(stream), p);
+    return (int)hipGetLastError();
+}
+
+int launch_mean(const float *loss_tok, int64_t N, float *loss_mean, void *stream)
+{
+    hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(1024), 0, S(stream), loss_tok, N, loss_mean);
+    return (int)hipGetLastError();
+}
+
+int launch_backward_logits(const ChunkArgs &a, const float *lse, float coef, void *stream)
+{
+    const Layout &L = *a.L;
+    BwdParams p;
+    p.W = a.W;
+    p.h = a.h;
+    p.H = a.H;
+    p.V = a.V;
+    p.rows = a.rows;
+    p.Cpad = L.Cpad;
+    p.Vpad = L.Vpad;
+    p.K = a.K;
+    p.nVt = L.nVt;
+    p.nNt = (a.rows + kTokenTile - 1) / kTokenTile;
+    p.cnt_stride = L.cnt_stride;
+    p.scale2 = kLog2e / a.T;
+    p.coef = coef;
+    p.lse = lse;
+    p.idx_s = reinterpret_cast<const int32_t *>(a.ws + L.off_idx);
+    p.p_s = reinterpret_cast<const float *>(a.ws + L.off_p);
+    p.psum = reinterpret_cast<const float *>(a.ws + L.off_psum);
+    p.cnt = reinterpret_cast<const uint8_t *>(a.ws + L.off_cnt);
+    p.g = reinterpret_cast<uint16_t *>(a.ws + L.off_g);
+    hipLaunchKernelGGL(backward_logits_kernel, dim3(p.nVt * p.nNt), dim3(kThreads), 0, S(stream), p);
+    return (int)hipGetLastError();
+}
+
+// Vocabulary splits of the dH product: rows of W per split (a multiple of the k-step)
+// and the number of splits that hold at least one row.
+static void dh_splits(const ChunkArgs &a, int &ksplit, int &used)
+{
+    const Layout &L = *a.L;
+    ksplit = ((L.Vpad + L.dh_splits - 1) / L.dh_splits + kBK - 1) / kBK * kBK;
+    used = (a.V + ksplit - 1) / ksplit;
+}
+
+int launch_dh(const ChunkArgs &a, void *stream)
+{
+    const Layout &L = *a.L;
+    DhParams p;
+    p.g = reinterpret_cast<const uint16_t *>(a.ws + L.off_g);
+    p.W = a.W;
+    p.H = a.H;
+    p.V = a.V;
+    p.Vpad = L.Vpad;
+    p.rows = a.rows;
+    p.Cpad = L.Cpad;
+    p.nMt = (a.rows + 255) / 256;
+    p.nNt = (a.H + L.dh_bn - 1) / L.dh_bn;
+    int used = 0;
+    dh_splits(a, p.ksplit, used);
+    p.part = reinterpret_cast<float *>(a.ws + L.off_dhp);
+    dim3 grid(p.nMt * p.nNt, used);
+    if (L.dh_bn == 256)
+        hipLaunchKernelGGL(dh_kernel<DGemm256>, grid, dim3(kThreads), 0, S(stream), p);
+    else
+        hipLaunchKernelGGL(dh_kernel<DGemm192>, grid, dim3(kThreads), 0, S(stream), p);
+    return (int)hipGetLastError();
+}
+
+int launch_dh_reduce(const ChunkArgs &a, float *dH, void *stream)
+{
+    const Layout &L = *a.L;
+    int ksplit = 0, used = 0;
+    dh_splits(a, ksplit, used);
+    const float *part = reinterpret_cast<const float *>(a.ws + L.off_dhp);
+    const size_t n4 = (size_t)a.rows * a.H / 4;
+    hipLaunchKernelGGL(dh_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, S(stream), part, used,
+                       (size_t)L.Cpad * a.H, n4, dH);
+    return (int)hipGetLastError();
+}
+
+int launch_dw(const ChunkArgs &a, float *dW, bool accumulate, void *stream)
+{
+    const Layout &L = *a.L;
+    DwParams p;
+    p.g = reinterpret_cast<const uint16_t *>(a.ws + L.off_g);
+    p.h = a.h;
+    p.H = a.H;
+    p.V = a.V;
+    p.Vpad = L.Vpad;
+    p.rows = a.rows;
+    p.nMt = L.nVt;
+    p.nNt = (a.H + L.dh_bn - 1) / L.dh_bn;
+    p.accumulate = accumulate ? 1 : 0;
+    p.dW = dW;
+    dim3 grid(p.nMt * p.nNt);
+    if (L.dh_bn == 256)
+        hipLaunchKernelGGL(dw_kernel<WGemm256>, grid, dim3(kThreads), 0, S(stream), p);
+    else
+        hipLaunchKernelGGL(dw_kernel<WGemm192>, grid, dim3(kThreads), 0, S(stream), p);
+    return (int)hipGetLastError();
+}
+
+int launch_zero_flag(uint32_t *flag, void *stream)
+{
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, S(stream), flag, 4);
+    return (int)hipGetLastError();
+}
+
+}  // namespace fckl

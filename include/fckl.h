@@ -1,0 +1,185 @@
+/*
+ * fckl.h -- C ABI of the fused chunked top-K KL distillation loss (gfx950 / MI355X).
+ *
+ * The operation.  A student's final hidden states h[N,H] are projected through its
+ * LM head W[V,H] (no bias) and each token's KL divergence is taken against a teacher
+ * cache that holds, per token, K logits and their vocabulary indices.  The
+ * projection is part of the loss and the tokens are processed one chunk at a time,
+ * so the N x V logit grid is never stored, forward or backward.  Sources (the web
+ * pages the method is described on):
+ *   - "What actually changed?", calcaas.com: the fused chunked loss folds the output
+ *     projection into the loss and processes one slice of the sequence at a time, so
+ *     the vocabulary-by-sequence grid is never built;
+ *   - "Breaking the Bottleneck with Offline Caching and Chunked Loss", axbrief.com:
+ *     the teacher's top-100 logits are cached once; the loss takes one chunk,
+ *     computes its part and discards it; the backward pass re-projects each chunk;
+ *   - "Preparing Offline Top-K Logits", getaibook.com: the cache stores the top-K
+ *     logits together with their indices, K configurable (10 and 100 are named);
+ *   - "Two Architectural Innovations", keepingupwith.ai: gradients are processed in
+ *     small tiles rather than over the full vocabulary x sequence tensor.
+ *
+ * Definition (IEEE real arithmetic; the GPU computes it with bf16 inputs and fp32
+ * accumulation):
+ *   p[i,k]  = softmax_k(topk_logit[i,:] / T)           (renormalised over the K entries)
+ *   z[i,v]  = sum_j h[i,j] * W[v,j]
+ *   lse[i]  = log sum_v exp(z[i,v] / T)
+ *   loss[i] = T^2 * sum_k p[i,k] * (log p[i,k] - (z[i, idx[i,k]] / T - lse[i]))
+ *   loss_mean = (1/N) * sum_i loss[i]
+ *   g[i,v]  = grad_scale * (T/N) * ((sum_k p[i,k]) * exp(z[i,v]/T - lse[i])
+ *                                   - sum_k p[i,k] * [idx[i,k] == v])
+ *   dH = g W,  dW = g^T h          (the gradients of grad_scale * loss_mean)
+ *
+ * Conventions for every entry point:
+ *   - All tensors are dense and row-major.  Pointers marked "device" are device
+ *     memory of the current HIP device; the library reads and writes them only from
+ *     kernels launched on `stream`.  The caller owns every buffer, including the
+ *     workspace; the library allocates no device memory and keeps no global state.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls are
+ *     asynchronous: outputs are valid once the stream has reached the call.  The only
+ *     host synchronisation is the index check requested by FCKL_FLAG_VALIDATE.
+ *   - Errors are returned as status codes; nothing throws across the ABI.  Argument
+ *     errors are detected before any HIP call and leave every output untouched.
+ *   - Limits of this version: 1 <= K <= 128, K <= V, H % 8 == 0, H <= 65536,
+ *     V <= 2^30, N <= 2^31 - 1, T finite and > 0.  Cached indices must be distinct
+ *     within a token and lie in [0, V); with FCKL_FLAG_VALIDATE the call checks them
+ *     and returns FCKL_ERR_INDEX, otherwise results for such inputs are undefined
+ *     (no out-of-bounds memory access is made either way).
+ */
+#ifndef FCKL_H
+#define FCKL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fckl_status {
+    FCKL_OK = 0,
+    FCKL_ERR_INVALID_ARG = 1,   /* null pointer, bad size, T <= 0, unsupported shape */
+    FCKL_ERR_UNSUPPORTED = 2,   /* a valid request outside this version's limits */
+    FCKL_ERR_WORKSPACE = 3,     /* workspace too small for the chosen chunk */
+    FCKL_ERR_INDEX = 4,         /* FCKL_FLAG_VALIDATE found an index out of range or repeated */
+    FCKL_ERR_HIP = 5            /* a HIP runtime call failed (launch, sync, copy) */
+} fckl_status;
+
+/* Element type of topk_logit. */
+enum { FCKL_DTYPE_BF16 = 0, FCKL_DTYPE_F32 = 1 };
+
+/* Flags (bitwise or). */
+enum {
+    FCKL_FLAG_VALIDATE = 1u,       /* check indices on the GPU and report FCKL_ERR_INDEX (syncs the stream) */
+    FCKL_FLAG_DW_ACCUMULATE = 2u   /* backward adds into dW instead of overwriting it */
+};
+
+/* Kernels of the path, for fckl_profile.kernel_mask (bit 1u << id). */
+enum {
+    FCKL_KERNEL_PREPARE = 0,       /* teacher softmax over the K entries, entries sorted by index */
+    FCKL_KERNEL_FWD_LOGITS = 1,    /* forward logit GEMM + online logsumexp / pick epilogue */
+    FCKL_KERNEL_COMBINE = 2,       /* per-token logsumexp over tiles and KL */
+    FCKL_KERNEL_MEAN = 3,          /* mean of the per-token loss */
+    FCKL_KERNEL_BWD_LOGITS = 4,    /* recompute GEMM + gradient epilogue, writes g */
+    FCKL_KERNEL_DH = 5,            /* dH = g W (vocabulary splits) */
+    FCKL_KERNEL_DH_REDUCE = 6,     /* fixed-order sum of the dH splits */
+    FCKL_KERNEL_DW = 7,            /* dW += g^T h */
+    FCKL_KERNEL_COUNT = 8
+};
+
+/*
+ * Optional per-kernel timing (caller-owned).  When fckl_desc.profile is not NULL, every
+ * launch of a kernel selected by kernel_mask is bracketed by two hipEventRecord calls on
+ * the call's stream, using events[2*i] and events[2*i+1] for the i-th bracketed launch
+ * (i = count, then count is incremented; launches beyond capacity are not timed).  The
+ * caller creates the hipEvent_t handles (passed as void*) and reads the elapsed times
+ * after synchronising.  kernel_ids[i] receives the FCKL_KERNEL_* id of launch i and
+ * work[i] the number of tokens that launch processed.
+ */
+typedef struct fckl_profile {
+    uint32_t kernel_mask;
+    int32_t capacity;
+    int32_t count;
+    void **events;           /* host array of 2 * capacity hipEvent_t */
+    int32_t *kernel_ids;     /* host array of capacity */
+    int32_t *work;           /* host array of capacity */
+} fckl_profile;
+
+/* Problem description shared by every call. */
+typedef struct fckl_desc {
+    int64_t N;            /* tokens (batch x sequence, flattened) */
+    int32_t H;            /* hidden size */
+    int32_t V;            /* vocabulary size */
+    int32_t K;            /* cached teacher entries per token */
+    float T;              /* temperature (student and teacher logits are divided by it) */
+    int32_t chunk;        /* tokens per chunk; 0 = let fckl_plan choose */
+    int32_t logit_dtype;  /* FCKL_DTYPE_BF16 or FCKL_DTYPE_F32 */
+    uint32_t flags;       /* FCKL_FLAG_* */
+    fckl_profile *profile;/* optional kernel timing, NULL = none */
+} fckl_desc;
+
+/*
+ * Chunk scheduler ("processes one chunk ... then discards it", axbrief.com; sized
+ * here for the 288 GB of HBM3E of one MI355X).  Pure host function, no HIP call.
+ * Chooses the number of tokens per chunk for `desc` so that the workspace fits in
+ * `budget_bytes` (0 = the library default, 4 GiB), preferring the largest chunk up to
+ * 16384 tokens and then evening out the chunks.  If desc->chunk > 0 that chunk is
+ * kept and only its workspace size is reported.
+ *   chunk_out    host, may be NULL: tokens per chunk.
+ *   ws_bytes_out host, may be NULL: workspace bytes fckl_forward/fckl_backward need.
+ * Returns FCKL_ERR_WORKSPACE when even the smallest chunk does not fit.
+ */
+fckl_status fckl_plan(const fckl_desc *desc, size_t budget_bytes, int32_t *chunk_out,
+                      size_t *ws_bytes_out);
+
+/*
+ * Workspace bytes needed for `desc` run with `chunk` tokens per chunk (chunk >= 1).
+ * The workspace depends on chunk, H, V and K only, never on N: peak memory has no
+ * N x V term.  Pure host function.
+ */
+fckl_status fckl_workspace_size(const fckl_desc *desc, int32_t chunk, size_t *ws_bytes_out);
+
+/*
+ * Forward pass: per-token loss, saved lse, and the mean loss.
+ *   h          device, bf16 [N,H]      student hidden states
+ *   W          device, bf16 [V,H]      student LM head
+ *   topk_idx   device, int32 [N,K]     teacher's cached vocabulary indices
+ *   topk_logit device, bf16 or f32 [N,K] (desc->logit_dtype) teacher's cached logits
+ *   loss_tok   device, f32 [N]         out: loss[i]
+ *   lse        device, f32 [N]         out: log sum_v exp(z[i,v]/T), kept for fckl_backward
+ *   loss_mean  device, f32 [1]         out: mean of loss_tok (may be NULL)
+ *   ws         device, ws_bytes bytes, 256-byte aligned; contents on entry are ignored
+ * Chunk: desc->chunk, or fckl_plan(desc, ws_bytes) when it is 0.
+ * Deterministic: the same inputs give bit-identical outputs.
+ */
+fckl_status fckl_forward(const fckl_desc *desc, const void *h, const void *W,
+                         const int32_t *topk_idx, const void *topk_logit,
+                         float *loss_tok, float *lse, float *loss_mean,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Backward pass: gradients of grad_scale * loss_mean with respect to h and W.  Each
+ * chunk's logits are recomputed with the same tiles as the forward pass; the chunk's
+ * gradient g (bf16, in the workspace) feeds the dH and dW products.
+ *   lse        device, f32 [N]         the lse written by fckl_forward for these inputs
+ *   grad_scale                         upstream gradient of loss_mean (1 for a plain loss)
+ *   dH         device, f32 [N,H]       out: overwritten
+ *   dW         device, f32 [V,H]       out: overwritten, or added to with FCKL_FLAG_DW_ACCUMULATE;
+ *                                      accumulated in fp32 across chunks in chunk order
+ * Other arguments as in fckl_forward.  Deterministic.
+ */
+fckl_status fckl_backward(const fckl_desc *desc, const void *h, const void *W,
+                          const int32_t *topk_idx, const void *topk_logit, const float *lse,
+                          float grad_scale, float *dH, float *dW,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *fckl_status_string(fckl_status status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t fckl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FCKL_H */

@@ -1,0 +1,159 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, element by element.
+
+Sizes are ones the oracle finishes in seconds while still spanning several vocabulary
+and token tiles, ragged tails in every dimension, several chunks and the edge cases
+(one token, one cached entry, the largest K, high temperature, rows with large
+norms).  Tolerances: see tests/gpu_util.py.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import chunked_top_kl_chunk_amd as fckl
+import oracle
+import synth
+from gpu_util import (GRAD_TOL, LOSS_RTOL, LSE_ATOL, arrays, check_grad, check_loss, device, rel_max, run, say,
+                      upload)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
+
+
+def synthetic(seed, N, H, V, K, T, tl_sigma=2.0, z_sigma=2.0, scaled_frac=0.0):
+    """h ~ N(0,1), W ~ N(0, (z_sigma^2)/H) so that logits spread over a few units, teacher
+    logits N(0, tl_sigma^2) sorted descending on K distinct random indices; bf16 values."""
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((N, H)).astype(np.float32)
+    if scaled_frac > 0:
+        pick = rng.permutation(N)[:max(1, int(round(scaled_frac * N)))]
+        h[pick] *= 20.0
+    W = (rng.standard_normal((V, H)) * (z_sigma / math.sqrt(H))).astype(np.float32)
+    idx = synth.distinct_indices(seed + 1, N, K, V)
+    tl = -np.sort(-rng.standard_normal((N, K)).astype(np.float32) * tl_sigma, axis=1)
+    return synth.round_bf16(h), synth.round_bf16(W), idx, synth.round_bf16(tl)
+
+
+def compare_all(g, h, W, idx, tl, T, grad_scale=1.0, what=""):
+    ref_loss, ref_lse = oracle.forward(h, W, idx, tl, T)
+    ref_dH, ref_dW = oracle.backward(h, W, idx, tl, T, grad_scale=grad_scale)
+    e_loss = check_loss(g["loss"], ref_loss, what)
+    e_lse = float(np.abs(g["lse"] - ref_lse).max())
+    assert e_lse <= LSE_ATOL, "%s lse abs err %.3e" % (what, e_lse)
+    e_mean = abs(float(g["mean"][0]) - ref_loss.mean()) / abs(ref_loss.mean())
+    assert e_mean <= LOSS_RTOL, "%s mean loss rel err %.3e" % (what, e_mean)
+    e_dH = check_grad(g["dH"], ref_dH, what + " dH")
+    e_dW = check_grad(g["dW"], ref_dW, what + " dW")
+    say("%s: loss %.2e lse %.2e mean %.2e dH %.2e dW %.2e" % (what, e_loss, e_lse, e_mean, e_dH, e_dW))
+
+
+def test_tiny_workload_full_parity():
+    """The tiny CPU-checkable workload: N=512, H=256, V=4096, K=10, T=1, 4 chunks of 128."""
+    wl = synth.WORKLOADS["c1"]
+    x = synth.make_inputs(wl)
+    say("case: tiny workload", wl)
+    g = run(*upload(x, device()), T=wl.T, chunk=wl.chunk)
+    compare_all(g, x.h, x.W, x.idx, x.tl, wl.T, what="tiny")
+    # for information: the same GPU result against the oracle on the unrounded fp32 draws
+    ref_loss, _ = oracle.forward(x.h_raw, x.W_raw, x.idx, x.tl_raw, wl.T)
+    say("tiny vs unrounded fp32 inputs: max per-token loss rel err %.3e"
+        % float((np.abs(g["loss"] - ref_loss) / ref_loss).max()))
+
+
+CASES = [
+    # seed, N, H, V, K, T, chunk, extra
+    (1, 1000, 200, 4100, 7, 1.7, 384, {}),
+    (2, 1, 64, 300, 3, 1.0, 0, {}),
+    (3, 257, 136, 1000, 128, 0.5, 256, {}),
+    (4, 600, 256, 2048, 1, 3.0, 0, {}),
+    (5, 300, 2880, 777, 20, 2.0, 100, {}),
+    (6, 512, 512, 3000, 10, 4.0, 0, {"scaled_frac": 0.01, "tl_sigma": 1.0}),
+    (7, 700, 1024, 5000, 100, 1.0, 512, {"z_sigma": 4.0}),
+    (8, 130, 3072, 513, 16, 1.0, 0, {}),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=["ragged", "one-token", "K128", "K1", "H2880", "scaled-rows",
+                                             "K100", "H3072"])
+def test_parity_shapes(case):
+    seed, N, H, V, K, T, chunk, extra = case
+    say("case:", case)
+    h, W, idx, tl = synthetic(seed, N, H, V, K, T, **extra)
+    g = run(*arrays(h, W, idx, tl), T=T, chunk=chunk, grad_scale=1.0)
+    compare_all(g, h, W, idx, tl, T, what="shape%d" % seed)
+
+
+def test_grad_scale_and_f32_logits():
+    h, W, idx, tl = synthetic(11, 300, 128, 1500, 12, 1.3)
+    dh, dW_, di, dt = arrays(h, W, idx, tl)
+    g = run(dh, dW_, di, dt, T=1.3, grad_scale=-2.5)
+    compare_all(g, h, W, idx, tl, 1.3, grad_scale=-2.5, what="grad_scale")
+    # the same logits given as float32 give the same results
+    g32 = run(dh, dW_, di, dt.float().contiguous(), T=1.3, grad_scale=-2.5)
+    for k in g:
+        np.testing.assert_array_equal(g[k], g32[k])
+
+
+def test_deterministic_and_chunk_invariant():
+    h, W, idx, tl = synthetic(12, 1100, 256, 3000, 10, 1.0)
+    t = arrays(h, W, idx, tl)
+    a = run(*t, T=1.0, chunk=256)
+    b = run(*t, T=1.0, chunk=256)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+    for chunk in (128, 512, 1100, 0):
+        c = run(*t, T=1.0, chunk=chunk)
+        # per-token results do not depend on how tokens are grouped into chunks
+        np.testing.assert_array_equal(c["loss"], a["loss"])
+        np.testing.assert_array_equal(c["lse"], a["lse"])
+        assert rel_max(c["dH"], a["dH"]) < 1e-5
+        assert rel_max(c["dW"], a["dW"]) < 1e-5
+
+
+def test_loss_nonnegative():
+    h, W, idx, tl = synthetic(13, 800, 256, 2000, 50, 2.0, z_sigma=6.0)
+    g = run(*arrays(h, W, idx, tl), T=2.0, backward=False)
+    assert (g["loss"] >= -1e-5 * np.abs(g["loss"]).max()).all()
+
+
+def test_zero_head_closed_form_on_gpu():
+    """W = 0 and equal teacher logits: loss = T^2 log(V/K) per token (closed form)."""
+    cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")))
+    for c in cases["uniform_teacher_zero_head"]:
+        V, K, T = c["V"], c["K"], c["T"]
+        N, H = 300, 64
+        rng = np.random.default_rng(14)
+        h = rng.standard_normal((N, H)).astype(np.float32)
+        idx = synth.distinct_indices(15, N, K, V)
+        g = run(*arrays(h, np.zeros((V, H), np.float32), idx, np.full((N, K), 0.5, np.float32)), T=T)
+        np.testing.assert_allclose(g["loss"], c["loss"], rtol=1e-5, atol=1e-5)
+        np.testing.assert_allclose(g["lse"], math.log(V), rtol=1e-6)
+        assert np.abs(g["dH"]).max() == 0.0
+
+
+def test_dw_accumulate_and_validate():
+    h, W, idx, tl = synthetic(16, 400, 128, 1200, 8, 1.0)
+    dh, dW_, di, dt = arrays(h, W, idx, tl)
+    loss, lse, _ = fckl.forward(dh, dW_, di, dt, T=1.0, validate=True)
+    _, dW1 = fckl.backward(dh, dW_, di, dt, lse, T=1.0)
+    dW2 = dW1.clone()
+    fckl.backward(dh, dW_, di, dt, lse, T=1.0, dW=dW2, accumulate=True)
+    torch.cuda.synchronize()
+    a, b = dW2.cpu().numpy(), dW1.cpu().numpy()
+    assert np.abs(a - 2 * b).max() <= 1e-6 * np.abs(b).max()
+    for bad_value in (1200, -1, None):
+        bad = di.clone()
+        if bad_value is None:
+            bad[5, 3] = bad[5, 1]          # a repeated index within one token
+        else:
+            bad[7, 2] = bad_value
+        for fn in ("forward", "backward"):
+            with pytest.raises(fckl.FCKLError) as e:
+                if fn == "forward":
+                    fckl.forward(dh, dW_, bad, dt, T=1.0, validate=True)
+                else:
+                    fckl.backward(dh, dW_, bad, dt, lse, T=1.0, validate=True)
+            assert e.value.status == fckl.ERR_INDEX

@@ -1,0 +1,151 @@
+"""Host-side checks of libfckl.so: it loads, exports what include/fckl.h declares, and
+its scheduler and argument checks behave -- all without touching a GPU (the calls
+here return before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunked_top_kl_chunk_amd as fckl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fckl.h")
+GiB = 1 << 30
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fckl_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fckl.load()
+    names = declared_functions()
+    assert set(names) == set(fckl.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    assert fckl.status_string(fckl.OK) == "success"
+    assert "workspace" in fckl.status_string(fckl.ERR_WORKSPACE)
+    assert "index" in fckl.status_string(fckl.ERR_INDEX)
+    assert fckl.status_string(99) == "unknown status"
+    assert fckl.version() >= 100
+
+
+C3 = dict(N=32768, H=2880, V=201088, K=100, T=1.0)
+
+
+def test_plan_fits_budget_and_is_even():
+    d = fckl.make_desc(**C3)
+    for budget in (0, 1 * GiB, 2 * GiB, 8 * GiB):
+        chunk, ws = fckl.plan(d, budget)
+        assert ws <= (budget or 4 * GiB)
+        assert chunk % 256 == 0 and 256 <= chunk <= 16384
+        nchunks = -(-C3["N"] // chunk)
+        assert nchunks * chunk - C3["N"] < 256 * nchunks
+
+
+def test_workspace_independent_of_tokens():
+    sizes = set()
+    for N in (4096, 32768, 262144, 2 ** 31 - 1):
+        d = fckl.make_desc(N, 2880, 201088, 100, 1.0)
+        sizes.add(fckl.workspace_size(d, 4096))
+    assert len(sizes) == 1
+
+
+def test_workspace_grows_with_chunk():
+    d = fckl.make_desc(**C3)
+    w = [fckl.workspace_size(d, c) for c in (256, 1024, 4096, 8192, 16384)]
+    assert all(a < b for a, b in zip(w, w[1:]))
+    # dominated by the bf16 chunk gradient g[C, V]: about 2*C*V bytes
+    assert 2 * 4096 * 201088 < w[2] < 3 * 4096 * 201088
+
+
+def test_plan_explicit_chunk_and_small_budget():
+    d = fckl.make_desc(**dict(C3, chunk=1000))
+    chunk, ws = fckl.plan(d, 0)
+    assert chunk == 1000 and ws == fckl.workspace_size(d, 1000)
+    d = fckl.make_desc(**C3)
+    with pytest.raises(fckl.FCKLError) as e:
+        fckl.plan(d, 1 << 20)
+    assert e.value.status == fckl.ERR_WORKSPACE
+    # a small N plans a single chunk covering it
+    chunk, _ = fckl.plan(fckl.make_desc(300, 256, 4096, 10, 1.0), 0)
+    assert chunk == 512
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(N=0), fckl.ERR_INVALID_ARG),
+    (dict(T=0.0), fckl.ERR_INVALID_ARG),
+    (dict(T=-1.0), fckl.ERR_INVALID_ARG),
+    (dict(T=float("nan")), fckl.ERR_INVALID_ARG),
+    (dict(T=float("inf")), fckl.ERR_INVALID_ARG),
+    (dict(K=0), fckl.ERR_INVALID_ARG),
+    (dict(K=5000, V=4096), fckl.ERR_INVALID_ARG),
+    (dict(chunk=-3), fckl.ERR_INVALID_ARG),
+    (dict(logit_dtype=7), fckl.ERR_INVALID_ARG),
+    (dict(flags=64), fckl.ERR_INVALID_ARG),
+    (dict(H=260), fckl.ERR_UNSUPPORTED),
+    (dict(K=129), fckl.ERR_UNSUPPORTED),
+])
+def test_invalid_descriptions_rejected(bad, status):
+    args = dict(N=512, H=256, V=4096, K=10, T=1.0)
+    args.update(bad)
+    d = fckl.make_desc(**args)
+    with pytest.raises(fckl.FCKLError) as e:
+        fckl.plan(d, 0)
+    assert e.value.status == status
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_entry_points_reject_before_any_hip_call():
+    """Null or misaligned pointers and a short workspace are refused up front.
+
+    The pointers are never dereferenced: every case returns before a kernel launch,
+    so this runs without a GPU.
+    """
+    lib = fckl.load()
+    d = fckl.make_desc(512, 256, 4096, 10, 1.0, chunk=128)
+    need = fckl.workspace_size(d, 128)
+    P = 1 << 40  # a 256-aligned address that is never touched
+    ok = [_fake(P), _fake(P), _fake(P), _fake(P)]
+    # null input
+    st = lib.fckl_forward(ctypes.byref(d), None, *ok[1:], _fake(P), _fake(P), None, _fake(P), need, None)
+    assert st == fckl.ERR_INVALID_ARG
+    # null outputs
+    st = lib.fckl_forward(ctypes.byref(d), *ok, None, _fake(P), None, _fake(P), need, None)
+    assert st == fckl.ERR_INVALID_ARG
+    st = lib.fckl_backward(ctypes.byref(d), *ok, _fake(P), ctypes.c_float(1.0), None, _fake(P), _fake(P), need, None)
+    assert st == fckl.ERR_INVALID_ARG
+    # misaligned workspace
+    st = lib.fckl_forward(ctypes.byref(d), *ok, _fake(P), _fake(P), None, _fake(P + 8), need, None)
+    assert st == fckl.ERR_INVALID_ARG
+    # workspace too small
+    st = lib.fckl_forward(ctypes.byref(d), *ok, _fake(P), _fake(P), None, _fake(P), need - 1, None)
+    assert st == fckl.ERR_WORKSPACE
+    st = lib.fckl_backward(ctypes.byref(d), *ok, _fake(P), ctypes.c_float(1.0), _fake(P), _fake(P), _fake(P),
+                           need - 256, None)
+    assert st == fckl.ERR_WORKSPACE
+    # bad description through the entry point
+    bad = fckl.make_desc(512, 256, 4096, 10, 0.0, chunk=128)
+    st = lib.fckl_forward(ctypes.byref(bad), *ok, _fake(P), _fake(P), None, _fake(P), need, None)
+    assert st == fckl.ERR_INVALID_ARG
+    st = lib.fckl_forward(None, *ok, _fake(P), _fake(P), None, _fake(P), need, None)
+    assert st == fckl.ERR_INVALID_ARG
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    h = torch.zeros(4, 8, dtype=torch.bfloat16)
+    W = torch.zeros(16, 8, dtype=torch.bfloat16)
+    idx = torch.zeros(4, 2, dtype=torch.int32)
+    tl = torch.zeros(4, 2, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fckl.forward(h, W, idx, tl)
