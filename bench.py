@@ -71,7 +71,7 @@ def main():
     ap.add_argument("--workload", default="c3", help="synth workload key (default c3: the 32K-token GPT-OSS-20B shape)")
     ap.add_argument("--tokens", type=int, default=0, help="override N (for quick runs)")
     ap.add_argument("--chunk", type=int, default=0, help="tokens per chunk (0 = library scheduler)")
-    ap.add_argument("--cpu-tokens", type=int, default=32, help="oracle sample size for cpu_baseline (0 = skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=48, help="oracle sample size for cpu_baseline (0 = skip)")
     ap.add_argument("--dense", action="store_true", help="also measure peak memory of a dense torch KL baseline")
     args = ap.parse_args()
     if args.gpus != 1:

@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fckl_internal.h"
 
 namespace fckl {
@@ -38,7 +40,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 512;
 constexpr int kBK = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -117,10 +118,10 @@ __device__ __forceinline__ void map_tile(int bid, int nM, int nN, int GM, int &t
 // ------------------------------------------------------------------ operand loaders
 
 // Operand whose k dimension is contiguous in memory: element (row, k) at base[row*ld + k].
-template <int ROWS>
+template <int ROWS, int NT>
 struct KMajorLoad {
-    static_assert((ROWS * 8) % kThreads == 0, "tile rows");
-    static constexpr int kPer = ROWS * 8 / kThreads;
+    static_assert((ROWS * 8) % NT == 0, "tile rows");
+    static constexpr int kPer = ROWS * 8 / NT;
     u32x4 r[kPer];
 
     __device__ __forceinline__ void load(const uint16_t *base, int64_t ld, int row0, int rows_valid, int k0,
@@ -128,7 +129,7 @@ struct KMajorLoad {
     {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
-            const int c = threadIdx.x + i * kThreads;
+            const int c = threadIdx.x + i * NT;
             const int row = c >> 3, kc = c & 7;
             const int grow = row0 + row, gk = k0 + kc * 8;
             if (grow < rows_valid && gk < k_valid)
@@ -141,64 +142,70 @@ struct KMajorLoad {
     {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
-            const int c = threadIdx.x + i * kThreads;
+            const int c = threadIdx.x + i * NT;
             *reinterpret_cast<u32x4 *>(lds + swz(c >> 3, c & 7) * 16) = r[i];
         }
     }
 };
 
 // Operand whose row dimension is contiguous: element (row, k) at base[k*ld + row].
-// Each thread loads 8 consecutive k-rows x 4 consecutive columns (8 bytes per row) and
-// transposes them into four 16-byte k-vectors.
-template <int ROWS>
+// A block is 8 consecutive k-rows x 4 consecutive columns (8 bytes per k-row); each
+// thread loads kPer blocks and transposes each into four 16-byte k-vectors.
+template <int ROWS, int NT>
 struct RowMajorLoad {
     static constexpr int kQuads = ROWS / 4;
     static constexpr int kBlocks = 8 * kQuads;
-    static_assert(kBlocks <= kThreads, "tile rows");
-    u32x2 r[8];
+    static constexpr int kPer = (kBlocks + NT - 1) / NT;
+    u32x2 r[kPer][8];
 
     __device__ __forceinline__ void load(const uint16_t *base, int64_t ld, int row0, int rows_valid, int k0,
                                          int k_valid)
     {
-        const int t = threadIdx.x;
-        const int kg = t / kQuads, q = t - (t / kQuads) * kQuads;
-        const int grow = row0 + q * 4;
-        const bool ok = (t < kBlocks) && (grow < rows_valid);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int gk = k0 + kg * 8 + i;
-            if (ok && gk < k_valid)
-                r[i] = *reinterpret_cast<const u32x2 *>(base + (int64_t)gk * ld + grow);
-            else
-                r[i] = u32x2{0u, 0u};
+        for (int b = 0; b < kPer; ++b) {
+            const int t = threadIdx.x + b * NT;
+            const int kg = t / kQuads, q = t - (t / kQuads) * kQuads;
+            const int grow = row0 + q * 4;
+            const bool ok = (t < kBlocks) && (grow < rows_valid);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int gk = k0 + kg * 8 + i;
+                if (ok && gk < k_valid)
+                    r[b][i] = *reinterpret_cast<const u32x2 *>(base + (int64_t)gk * ld + grow);
+                else
+                    r[b][i] = u32x2{0u, 0u};
+            }
         }
     }
     __device__ __forceinline__ void store(char *lds) const
     {
-        const int t = threadIdx.x;
-        if (t >= kBlocks)
-            return;
-        const int kg = t / kQuads, q = t - (t / kQuads) * kQuads;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            u32x4 o;
+        for (int b = 0; b < kPer; ++b) {
+            const int t = threadIdx.x + b * NT;
+            if (t >= kBlocks)
+                continue;
+            const int kg = t / kQuads, q = t - (t / kQuads) * kQuads;
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const uint32_t lo = r[2 * d][c >> 1], hi = r[2 * d + 1][c >> 1];
-                o[d] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+            for (int c = 0; c < 4; ++c) {
+                u32x4 o;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t lo = r[b][2 * d][c >> 1], hi = r[b][2 * d + 1][c >> 1];
+                    o[d] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+                }
+                *reinterpret_cast<u32x4 *>(lds + swz(q * 4 + c, kg) * 16) = o;
             }
-            *reinterpret_cast<u32x4 *>(lds + swz(q * 4 + c, kg) * 16) = o;
         }
     }
 };
 
-template <bool KMAJ, int ROWS>
+template <bool KMAJ, int ROWS, int NT>
 struct LoaderOf {
-    using type = KMajorLoad<ROWS>;
+    using type = KMajorLoad<ROWS, NT>;
 };
-template <int ROWS>
-struct LoaderOf<false, ROWS> {
-    using type = RowMajorLoad<ROWS>;
+template <int ROWS, int NT>
+struct LoaderOf<false, ROWS, NT> {
+    using type = RowMajorLoad<ROWS, NT>;
 };
 
 // ------------------------------------------------------------------ GEMM core
@@ -209,15 +216,15 @@ struct LoaderOf<false, ROWS> {
 template <int BM_, int BN_, int WM_, int WN_, bool AK, bool BKM>
 struct Gemm {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-    static_assert(WM * WN * 64 == kThreads, "8 waves");
+    static constexpr int NT = WM * WN * 64;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int MB = WTM / 32, NB = WTN / 32;
     static_assert(MB * 32 == WTM && NB * 32 == WTN, "wave tile");
     static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = 2 * STAGE;
-    using ALoad = typename LoaderOf<AK, BM>::type;
-    using BLoad = typename LoaderOf<BKM, BN>::type;
+    using ALoad = typename LoaderOf<AK, BM, NT>::type;
+    using BLoad = typename LoaderOf<BKM, BN, NT>::type;
 
     __device__ __forceinline__ static int row_of(int wm, int mb, int r, int lane)
     {
@@ -282,8 +289,350 @@ struct Gemm {
     }
 };
 
+// ------------------------------------------------------------------ GEMM core, direct-to-LDS
+
+// Lanes whose 16-byte piece of an operand lies outside it (rows past the end, k past
+// the reduction length) load these zeros instead, so partial tiles need no branches.
+__device__ __attribute__((aligned(16))) const uint32_t kZeroPage[4] = {0u, 0u, 0u, 0u};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// global_load_lds_dwordx4: each lane of the wave copies 16 bytes from `src` to LDS at
+// lds_wave_base + 16 * lane (lds_wave_base is the same for the whole wave).
+__device__ __forceinline__ void copy16_to_lds(const void *src, char *lds_wave_base)
+{
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)lds_wave_base, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt bits 3:0
+// and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time unrolled).
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+
+// s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt at their no-wait maxima).
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+// Operand tile whose k dimension is contiguous: ROWS rows x BKK k, one row = BKK/8
+// 16-byte chunks.  gfx950's LDS serves 256 bytes (64 banks) per cycle, i.e. 16 lanes
+// of a ds_read_b128; the fragment read has those 16 lanes on 16 consecutive rows at
+// one chunk, so the chunk index is XOR-swizzled with the row to spread them over all
+// 16 bank groups.
+template <int ROWS, int BKK, int NT>
+struct KTile {
+    static constexpr int CPR = BKK / 8;
+    static constexpr int CHUNKS = ROWS * CPR;
+    static_assert(CHUNKS % NT == 0, "whole wave instructions");
+    static constexpr int PER = CHUNKS / NT;
+    static constexpr int BYTES = CHUNKS * 16;
+
+    static_assert(CPR == 8 || CPR == 4, "k-step of 64 or 32");
+    __device__ __forceinline__ static int sw(int row)
+    {
+        return CPR == 8 ? ((row & 7) ^ ((row >> 3) & 1)) : ((row >> 2) & 3);
+    }
+
+    // Per-thread source state: for each of the PER 16-byte pieces, the row's base
+    // pointer (already offset by the piece's k) and whether the row exists.
+    struct Src {
+        const uint16_t *p[PER];
+        int kc8[PER];
+        bool ok[PER];
+    };
+    __device__ __forceinline__ static void init(Src &s, const uint16_t *base, int64_t ld, int row0, int rows_valid)
+    {
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int pslot = (i * (NT / 64) + wave) * 64 + lane;
+            const int row = pslot / CPR, pc = pslot % CPR;
+            const int kc = pc ^ sw(row);
+            const int grow = row0 + row;
+            s.ok[i] = grow < rows_valid;
+            s.kc8[i] = kc * 8;
+            s.p[i] = base + (int64_t)(s.ok[i] ? grow : 0) * ld + kc * 8;
+        }
+    }
+    // Piece i of the k-slice [k0, k0 + BKK) into `tile` (a piece past k_valid or past
+    // the last row comes from the zero page).
+    __device__ __forceinline__ static void issue_one(Src &s, int i, int k0, int k_valid, int64_t, char *tile)
+    {
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const bool ok = s.ok[i] && (k0 + s.kc8[i] < k_valid);
+        const void *src = ok ? static_cast<const void *>(s.p[i] + k0) : static_cast<const void *>(kZeroPage);
+        copy16_to_lds(src, tile + (i * (NT / 64) + wave) * 1024);
+    }
+    // 8 k-values (chunk kc) of tile row `row`, the MFMA operand of one lane.
+    __device__ __forceinline__ static bf16x8 frag(const char *tile, int row, int kc)
+    {
+        return *reinterpret_cast<const bf16x8 *>(tile + (row * CPR + (kc ^ sw(row))) * 16);
+    }
+};
+
+// Operand tile whose row (m or n) dimension is contiguous: BKK k-rows x COLS columns.
+// The MFMA operand (8 consecutive k of one column per lane) is gathered with two
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane l receives element l%4 of the
+// 8-byte pieces addressed by lanes l/4, 4 + l/4, 8 + l/4 and 12 + l/4, so lanes
+// addressing k-rows kb..kb+3 at columns c..c+15 hand each lane 4 k-values of one
+// column.  One LDS cycle serves 32 lanes (256 bytes): four k-rows x four 16-byte
+// chunks; the chunk index is XOR-swizzled by a function of k so that the four rows
+// land in four distinct 64-byte bank groups.
+template <int COLS, int BKK, int NT>
+struct MNTile {
+    static constexpr int CPR = COLS / 8;
+    static constexpr int CHUNKS = BKK * CPR;
+    static_assert(CHUNKS % NT == 0, "whole wave instructions");
+    static constexpr int PER = CHUNKS / NT;
+    static constexpr int BYTES = CHUNKS * 16;
+
+    static_assert(CPR == 32 || CPR == 24, "256 or 192 columns");
+    // 512-byte rows: XOR by 4*(k%4).  384-byte rows alternate between the two halves
+    // of the 256-byte bank window, so XOR by 4*((k/2)%2) suffices.
+    __device__ __forceinline__ static int sw(int k) { return CPR == 32 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); }
+
+    // Per-thread source state: for each piece, the pointer at k-row (k_begin + k),
+    // the piece's k-row within the tile and whether its columns exist.
+    struct Src {
+        const uint16_t *p[PER];
+        int k[PER];
+        bool ok[PER];
+    };
+    __device__ __forceinline__ static void init(Src &s, const uint16_t *base, int64_t ld, int col0, int cols_valid,
+                                                int k_begin)
+    {
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int pslot = (i * (NT / 64) + wave) * 64 + lane;
+            const int k = pslot / CPR, pc = pslot % CPR;
+            const int gc = col0 + (pc ^ sw(k)) * 8;
+            s.ok[i] = gc < cols_valid;
+            s.k[i] = k;
+            s.p[i] = base + (int64_t)(k_begin + k) * ld + (s.ok[i] ? gc : 0);
+        }
+    }
+    // Piece i of k-rows [k0, k0 + BKK) into `tile`.  Each piece's pointer advances by
+    // BKK rows per call, so the k-steps of one piece must be issued in order.
+    __device__ __forceinline__ static void issue_one(Src &s, int i, int k0, int k_valid, int64_t ld, char *tile)
+    {
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const bool ok = s.ok[i] && (k0 + s.k[i] < k_valid);
+        const void *src = ok ? static_cast<const void *>(s.p[i]) : static_cast<const void *>(kZeroPage);
+        copy16_to_lds(src, tile + (i * (NT / 64) + wave) * 1024);
+        s.p[i] += (int64_t)BKK * ld;
+    }
+    // Operand of one lane for the 32-column block starting at `col`, k-step ks (16 k).
+    __device__ __forceinline__ static bf16x8 frag(const char *tile, int col, int ks)
+    {
+        const int lane = threadIdx.x & 63;
+        const int s = lane & 15;
+        const int c = col + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+        const int kb = ks * 16 + 8 * (lane >> 5) + (s >> 2);
+        i16x4 v[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int k = kb + 4 * r;
+            const char *a = tile + (k * CPR + ((c >> 3) ^ sw(k))) * 16 + ((c >> 2) & 1) * 8;
+            v[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(a));
+        }
+        i16x4 lo = v[0], hi = v[1];
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8, w);
+    }
+};
+
+template <bool KMAJ, int ROWS, int BKK, int NT>
+struct TileOf {
+    using type = KTile<ROWS, BKK, NT>;
+};
+template <int ROWS, int BKK, int NT>
+struct TileOf<false, ROWS, BKK, NT> {
+    using type = MNTile<ROWS, BKK, NT>;
+};
+
+// C[m, n] = sum_k A(m, k) * B(n, k) for one BM x BN tile, operands streamed
+// global -> LDS by the DMA path with S stages in flight (no staging registers).
+// Accumulator layout as in Gemm.  A k-major: A(m,k) = A[m*lda + k]; otherwise
+// A(m,k) = A[k*lda + m]; the same for B.
+template <int BM_, int BN_, int WM_, int WN_, bool AK, bool BKM, int BKK, int S>
+struct GemmD {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int NT = WM * WN * 64;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
+    static constexpr int MB = WTM / 32, NB = WTN / 32;
+    static_assert(MB * 32 == WTM && NB * 32 == WTN, "wave tile");
+    using AT = typename TileOf<AK, BM, BKK, NT>::type;
+    using BT = typename TileOf<BKM, BN, BKK, NT>::type;
+    static constexpr int STAGE = AT::BYTES + BT::BYTES;
+    static constexpr int LDS_BYTES = S * STAGE;
+    static constexpr int L = AT::PER + BT::PER;     // DMA loads per thread per k-step
+    static_assert(S >= 2 && (S - 2) * L < 64, "stages");
+
+    __device__ __forceinline__ static int row_of(int wm, int mb, int r, int lane)
+    {
+        return wm * WTM + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    }
+    __device__ __forceinline__ static int col_of(int wn, int nb, int lane) { return wn * WTN + nb * 32 + (lane & 31); }
+
+    struct Frags {
+        bf16x8 a[MB], b[NB];
+    };
+
+    __device__ __forceinline__ static void load_frags(const char *stage, int ks, int wm, int wn, int lane, Frags &f)
+    {
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            if constexpr (AK)
+                f.a[i] = AT::frag(stage, wm * WTM + i * 32 + (lane & 31), ks * 2 + (lane >> 5));
+            else
+                f.a[i] = AT::frag(stage, wm * WTM + i * 32, ks);
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            if constexpr (BKM)
+                f.b[j] = BT::frag(stage + AT::BYTES, wn * WTN + j * 32 + (lane & 31), ks * 2 + (lane >> 5));
+            else
+                f.b[j] = BT::frag(stage + AT::BYTES, wn * WTN + j * 32, ks);
+        }
+    }
+
+    __device__ __forceinline__ static void mma(const Frags &f, f32x16 (&acc)[MB][NB])
+    {
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+    }
+
+    // DS-read instructions per fragment set (a transposed fragment takes two reads).
+    static constexpr int DS_PER_SUB = (AK ? MB : 2 * MB) + (BKM ? NB : 2 * NB);
+    static constexpr int SUB = BKK / 16;
+    // The L loads of one k-step are spread over the first ISSUE_SUBS substeps of the
+    // step before, P per substep.
+    static constexpr int ISSUE_SUBS = (S == 2 && SUB > 2) ? SUB / 2 : SUB;
+    static constexpr int P = (L + ISSUE_SUBS - 1) / ISSUE_SUBS;
+
+    // Scheduling hint for one substep: MFMAs interleaved one-for-one with the LDS reads
+    // of the next substep's fragments and with this substep's global->LDS loads.
+    template <int NDS, int NVM>
+    __device__ __forceinline__ static void interleave()
+    {
+#pragma unroll
+        for (int i = 0; i < MB * NB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+            if (i < NDS)
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+            if (i < NVM)
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read (to LDS)
+        }
+        if constexpr (NDS > MB * NB)
+            __builtin_amdgcn_sched_group_barrier(0x100, NDS - MB * NB, 0);
+        if constexpr (NVM > MB * NB)
+            __builtin_amdgcn_sched_group_barrier(0x020, NVM - MB * NB, 0);
+    }
+
+    // S LDS stages.  While k-step kb is computed, the loads of step kb + S - 1 are issued
+    // (a few per substep, interleaved with the MFMAs) into the stage step kb - 1 used.
+    // At the end of step kb the wave waits for step kb + 1 (steps kb+2 .. kb+S-1 may
+    // stay in flight) and the barrier retires stage kb.  Fragments are read one 16-deep
+    // substep ahead of the MFMAs that use them.  Steps past the end load zeros, which
+    // keeps the wait counts uniform.
+    __device__ static void run(char *smem, const uint16_t *A, int64_t lda, int m0, int m_valid, int ka_valid,
+                               const uint16_t *B, int64_t ldb, int n0, int n_valid, int kb_valid, int k_begin,
+                               int k_end, f32x16 (&acc)[MB][NB])
+    {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int wm = wave / WN, wn = wave % WN;
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[i][j][r] = 0.0f;
+        const int nk = (k_end - k_begin + BKK - 1) / BKK;
+        if (nk <= 0) {
+            __syncthreads();
+            return;
+        }
+        typename AT::Src sa;
+        typename BT::Src sb;
+        if constexpr (AK)
+            AT::init(sa, A, lda, m0, m_valid);
+        else
+            AT::init(sa, A, lda, m0, m_valid, k_begin);
+        if constexpr (BKM)
+            BT::init(sb, B, ldb, n0, n_valid);
+        else
+            BT::init(sb, B, ldb, n0, n_valid, k_begin);
+        // loads [first, last) of k-step `step` (0..L-1: A pieces, then B pieces)
+        auto issue = [&](int step, auto first_c, auto last_c) {
+            constexpr int first = decltype(first_c)::value, last = decltype(last_c)::value;
+            char *st = smem + (step % S) * STAGE;
+            const int k0 = k_begin + step * BKK;
+#pragma unroll
+            for (int x = first; x < last; ++x) {
+                if (x < AT::PER)
+                    AT::issue_one(sa, x, k0, ka_valid, lda, st);
+                else
+                    BT::issue_one(sb, x - AT::PER, k0, kb_valid, ldb, st + AT::BYTES);
+            }
+        };
+#pragma unroll
+        for (int st = 0; st + 1 < S; ++st)
+            issue(st, std::integral_constant<int, 0>{}, std::integral_constant<int, L>{});
+        wait_vmcnt<(S - 2) * L>();
+        __builtin_amdgcn_s_barrier();
+        Frags f, fn;
+        load_frags(smem, 0, wm, wn, lane, f);
+        for (int kb = 0; kb < nk; ++kb) {
+            const char *cur = smem + (kb % S) * STAGE;
+            const int next = kb + S - 1;
+            static_for<SUB>([&](auto ssc) {
+                constexpr int ss = decltype(ssc)::value;
+                constexpr int lo = ss * P < L ? ss * P : L;
+                constexpr int hi = (ss + 1) * P < L ? (ss + 1) * P : L;
+                if constexpr (ss + 1 < SUB)
+                    load_frags(cur, ss + 1, wm, wn, lane, fn);
+                if constexpr (lo < hi)
+                    issue(next, std::integral_constant<int, lo>{}, std::integral_constant<int, hi>{});
+                mma(f, acc);
+                interleave<(ss + 1 < SUB) ? DS_PER_SUB : 0, hi - lo>();
+                if constexpr (ss + 1 < SUB)
+                    f = fn;
+            });
+            if (kb + 1 < nk) {
+                // step kb+1 has landed and this wave's reads of stage kb are done
+                wait_vmcnt<(S - 2) * L>();
+                wait_lgkmcnt0();
+                __builtin_amdgcn_s_barrier();
+                load_frags(smem + ((kb + 1) % S) * STAGE, 0, wm, wn, lane, f);
+            }
+        }
+        // every wave is done reading LDS (and no load is in flight) before the caller reuses it
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+};
+
 // The logit GEMM: rows = vocabulary (W), columns = tokens (h), k = hidden.
-using LogitGemm = Gemm<256, 256, 2, 4, true, true>;
+using LogitGemm = GemmD<256, 256, 2, 4, true, true, 64, 2>;
 constexpr int kGStagePitch = 256 * 2 + 16;   // bytes per token row of the bf16 g staging tile
 constexpr int kLogitLds = (LogitGemm::LDS_BYTES > 256 * kGStagePitch) ? LogitGemm::LDS_BYTES : 256 * kGStagePitch;
 
@@ -439,7 +788,7 @@ struct FwdParams {
     float2 *part;           // [nVt, Cpad]
 };
 
-__global__ __launch_bounds__(kThreads) void forward_logits_kernel(FwdParams p)
+__global__ __launch_bounds__(LogitGemm::NT) void forward_logits_kernel(FwdParams p)
 {
     using G = LogitGemm;
     __shared__ __attribute__((aligned(16))) char smem[kLogitLds];
@@ -463,7 +812,7 @@ __global__ __launch_bounds__(kThreads) void forward_logits_kernel(FwdParams p)
     }
 
     f32x16 acc[G::MB][G::NB];
-    G::run(smem, p.W, p.H, m0, p.V, p.h, p.H, n0, p.rows, 0, p.H, acc);
+    G::run(smem, p.W, p.H, m0, p.V, p.H, p.h, p.H, n0, p.rows, p.H, 0, p.H, acc);
 
     // Per token, over the wave's 128 vocabulary rows: max and sum of 2^(z*log2e/T - max).
     float *red = reinterpret_cast<float *>(smem);   // [WM][BN][2]
@@ -495,7 +844,7 @@ __global__ __launch_bounds__(kThreads) void forward_logits_kernel(FwdParams p)
         }
     }
     __syncthreads();
-    for (int nl = threadIdx.x; nl < G::BN; nl += kThreads) {
+    for (int nl = threadIdx.x; nl < G::BN; nl += G::NT) {
         if (n0 + nl < p.rows) {
             float m = red[nl * 2 + 0], s = red[nl * 2 + 1];
 #pragma unroll
@@ -600,7 +949,7 @@ struct BwdParams {
     uint16_t *g;            // [Cpad, Vpad] bf16
 };
 
-__global__ __launch_bounds__(kThreads) void backward_logits_kernel(BwdParams p)
+__global__ __launch_bounds__(LogitGemm::NT) void backward_logits_kernel(BwdParams p)
 {
     using G = LogitGemm;
     __shared__ __attribute__((aligned(16))) char smem[kLogitLds];
@@ -628,7 +977,7 @@ __global__ __launch_bounds__(kThreads) void backward_logits_kernel(BwdParams p)
     }
 
     f32x16 acc[G::MB][G::NB];
-    G::run(smem, p.W, p.H, m0, p.V, p.h, p.H, n0, p.rows, 0, p.H, acc);
+    G::run(smem, p.W, p.H, m0, p.V, p.H, p.h, p.H, n0, p.rows, p.H, 0, p.H, acc);
 
     // g = coef * ((sum p) * exp(z/T - lse) - scatter(p, idx)); zero outside [0,V) x [0,rows).
 #pragma unroll
@@ -677,7 +1026,7 @@ __global__ __launch_bounds__(kThreads) void backward_logits_kernel(BwdParams p)
     __syncthreads();
     constexpr int kChunks = G::BN * (G::BM * 2 / 16);
 #pragma unroll 4
-    for (int c = threadIdx.x; c < kChunks; c += kThreads) {
+    for (int c = threadIdx.x; c < kChunks; c += G::NT) {
         const int nl = c >> 5, col = (c & 31) * 8;
         const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + nl * kGStagePitch + col * 2);
         *reinterpret_cast<u32x4 *>(p.g + (size_t)(n0 + nl) * p.Vpad + m0 + col) = v;
@@ -694,7 +1043,7 @@ struct DhParams {
 };
 
 template <class G>
-__global__ __launch_bounds__(kThreads) void dh_kernel(DhParams p)
+__global__ __launch_bounds__(G::NT) void dh_kernel(DhParams p)
 {
     __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
     int tm, tn;
@@ -704,7 +1053,7 @@ __global__ __launch_bounds__(kThreads) void dh_kernel(DhParams p)
     const int k_end = min(p.V, k_begin + p.ksplit);
     f32x16 acc[G::MB][G::NB];
     // A(m = token, k = vocab) = g[m][k]; B(n = hidden, k = vocab) = W[k][n].
-    G::run(smem, p.g, p.Vpad, m0, p.rows, p.W, p.H, n0, p.H, k_begin, k_end, acc);
+    G::run(smem, p.g, p.Vpad, m0, p.rows, k_end, p.W, p.H, n0, p.H, k_end, k_begin, k_end, acc);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / G::WN, wn = wave % G::WN;
     float *out = p.part + (size_t)blockIdx.y * p.Cpad * p.H;
@@ -752,7 +1101,7 @@ struct DwParams {
 };
 
 template <class G>
-__global__ __launch_bounds__(kThreads) void dw_kernel(DwParams p)
+__global__ __launch_bounds__(G::NT) void dw_kernel(DwParams p)
 {
     __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
     int tm, tn;
@@ -760,7 +1109,7 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(DwParams p)
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     f32x16 acc[G::MB][G::NB];
     // A(m = vocab, k = token) = g[k][m]; B(n = hidden, k = token) = h[k][n].
-    G::run(smem, p.g, p.Vpad, m0, p.Vpad, p.h, p.H, n0, p.H, 0, p.rows, acc);
+    G::run(smem, p.g, p.Vpad, m0, p.Vpad, p.rows, p.h, p.H, n0, p.H, p.rows, 0, p.rows, acc);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / G::WN, wn = wave % G::WN;
 #pragma unroll
@@ -781,10 +1130,10 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(DwParams p)
     }
 }
 
-using DGemm256 = Gemm<256, 256, 2, 4, true, false>;   // dH, hidden tile 256
-using DGemm192 = Gemm<256, 192, 4, 2, true, false>;   // dH, hidden tile 192
-using WGemm256 = Gemm<256, 256, 2, 4, false, false>;  // dW, hidden tile 256
-using WGemm192 = Gemm<256, 192, 4, 2, false, false>;  // dW, hidden tile 192
+using DGemm256 = GemmD<256, 256, 2, 4, true, false, 64, 2>;   // dH, hidden tile 256
+using DGemm192 = GemmD<256, 192, 4, 2, true, false, 64, 2>;   // dH, hidden tile 192
+using WGemm256 = GemmD<256, 256, 2, 4, false, false, 64, 2>;  // dW, hidden tile 256
+using WGemm192 = GemmD<256, 192, 4, 2, false, false, 64, 2>;  // dW, hidden tile 192
 
 __global__ void zero_u32_kernel(uint32_t *p, int n)
 {
@@ -842,7 +1191,7 @@ int launch_forward_logits(const ChunkArgs &a, void *stream)
     p.cnt = reinterpret_cast<const uint8_t *>(a.ws + L.off_cnt);
     p.zk = reinterpret_cast<float *>(a.ws + L.off_zk);
     p.part = reinterpret_cast<float2 *>(a.ws + L.off_part);
-    hipLaunchKernelGGL(forward_logits_kernel, dim3(p.nVt * p.nNt), dim3(kThreads), 0, S(stream), p);
+    hipLaunchKernelGGL(forward_logits_kernel, dim3(p.nVt * p.nNt), dim3(LogitGemm::NT), 0, S(stream), p);
     return (int)hipGetLastError();
 }
 
@@ -895,7 +1244,7 @@ int launch_backward_logits(const ChunkArgs &a, const float *lse, float coef, voi
     p.psum = reinterpret_cast<const float *>(a.ws + L.off_psum);
     p.cnt = reinterpret_cast<const uint8_t *>(a.ws + L.off_cnt);
     p.g = reinterpret_cast<uint16_t *>(a.ws + L.off_g);
-    hipLaunchKernelGGL(backward_logits_kernel, dim3(p.nVt * p.nNt), dim3(kThreads), 0, S(stream), p);
+    hipLaunchKernelGGL(backward_logits_kernel, dim3(p.nVt * p.nNt), dim3(LogitGemm::NT), 0, S(stream), p);
     return (int)hipGetLastError();
 }
 
@@ -926,9 +1275,9 @@ int launch_dh(const ChunkArgs &a, void *stream)
     p.part = reinterpret_cast<float *>(a.ws + L.off_dhp);
     dim3 grid(p.nMt * p.nNt, used);
     if (L.dh_bn == 256)
-        hipLaunchKernelGGL(dh_kernel<DGemm256>, grid, dim3(kThreads), 0, S(stream), p);
+        hipLaunchKernelGGL(dh_kernel<DGemm256>, grid, dim3(DGemm256::NT), 0, S(stream), p);
     else
-        hipLaunchKernelGGL(dh_kernel<DGemm192>, grid, dim3(kThreads), 0, S(stream), p);
+        hipLaunchKernelGGL(dh_kernel<DGemm192>, grid, dim3(DGemm192::NT), 0, S(stream), p);
     return (int)hipGetLastError();
 }
 
@@ -960,9 +1309,9 @@ int launch_dw(const ChunkArgs &a, float *dW, bool accumulate, void *stream)
     p.dW = dW;
     dim3 grid(p.nMt * p.nNt);
     if (L.dh_bn == 256)
-        hipLaunchKernelGGL(dw_kernel<WGemm256>, grid, dim3(kThreads), 0, S(stream), p);
+        hipLaunchKernelGGL(dw_kernel<WGemm256>, grid, dim3(WGemm256::NT), 0, S(stream), p);
     else
-        hipLaunchKernelGGL(dw_kernel<WGemm192>, grid, dim3(kThreads), 0, S(stream), p);
+        hipLaunchKernelGGL(dw_kernel<WGemm192>, grid, dim3(WGemm192::NT), 0, S(stream), p);
     return (int)hipGetLastError();
 }
 
