@@ -126,7 +126,7 @@ def main():
 
     # Per-kernel HIP events, recorded by the library on its stream during the timed steps.
     ev = HipEvents()
-    per_step = nchunks * 8 + 1
+    per_step = nchunks * len(fckl.KERNELS) + 2
     cap = per_step * max(args.steps, 1)
     events = ev.create(2 * cap)
     kid = (ctypes.c_int32 * cap)()

@@ -31,7 +31,7 @@ EXPORTS = ("fckl_plan", "fckl_workspace_size", "fckl_forward", "fckl_backward",
            "fckl_status_string", "fckl_version")
 
 
-KERNELS = ("prepare", "fwd_logits", "combine", "mean", "bwd_logits", "dh", "dh_reduce", "dw")
+KERNELS = ("prepare", "fwd_logits", "combine", "mean", "bwd_logits", "dh", "dh_reduce", "dw", "transpose")
 
 
 class Profile(ctypes.Structure):

@@ -185,11 +185,23 @@ fckl_status fckl_backward(const fckl_desc *desc, const void *h, const void *W, c
     // d(grad_scale * mean loss)/dz = grad_scale * (T/N) * ((sum p) q - scatter p)
     const float coef = (float)((double)grad_scale * (double)desc->T / (double)desc->N);
     const bool acc0 = (desc->flags & FCKL_FLAG_DW_ACCUMULATE) != 0;
+    {
+        // W^T once per call: the dH product reduces over the vocabulary
+        ChunkArgs a = chunk_args(desc, h, W, topk_idx, topk_logit, ws, &L, 0);
+        Timed t(desc, FCKL_KERNEL_TRANSPOSE, 0, stream);
+        if (launch_transpose_head(a, stream))
+            return FCKL_ERR_HIP;
+    }
     for (int64_t c0 = 0; c0 < desc->N; c0 += L.C) {
         ChunkArgs a = chunk_args(desc, h, W, topk_idx, topk_logit, ws, &L, c0);
         {
             Timed t(desc, FCKL_KERNEL_PREPARE, a.rows, stream);
             if (launch_prepare(a, false, stream))
+                return FCKL_ERR_HIP;
+        }
+        {
+            Timed t(desc, FCKL_KERNEL_TRANSPOSE, a.rows, stream);
+            if (launch_transpose_chunk(a, stream))
                 return FCKL_ERR_HIP;
         }
         {

@@ -13,7 +13,7 @@ constexpr int kVocabTile = 256;
 constexpr int kTokenTile = 256;
 constexpr int kMaxK = 128;
 constexpr int32_t kMaxChunk = 16384;
-constexpr size_t kDefaultBudget = size_t(4) << 30;   // 4 GiB of the 288 GB HBM3E
+constexpr size_t kDefaultBudget = size_t(12) << 30;  // 12 GiB of the 288 GB HBM3E
 
 // Where each per-chunk buffer lives inside the caller's workspace.  Every buffer is
 // sized by the chunk, never by N.
@@ -33,6 +33,9 @@ struct Layout {
     size_t off_cnt = 0;     // u8    [Cpad, cnt_stride] entries below each vocabulary tile start
     size_t off_part = 0;    // f32x2 [nVt, Cpad] per-tile (max, sum exp) of z/T, base 2
     size_t off_g = 0;       // bf16  [Cpad, Vpad] chunk gradient w.r.t. the logits
+    size_t off_gT = 0;      // bf16  [Vpad, Cpad] the same, transposed (dW operand)
+    size_t off_hT = 0;      // bf16  [H, Cpad]    chunk hidden states, transposed (dW operand)
+    size_t off_WT = 0;      // bf16  [H, Vpad]    LM head, transposed (dH operand)
     size_t off_dhp = 0;     // f32   [dh_splits, Cpad, H] split partial sums of dH
     size_t off_err = 0;     // u32   [4]         index-check flag
     size_t total = 0;
@@ -66,6 +69,8 @@ int launch_backward_logits(const ChunkArgs &a, const float *lse, float coef, voi
 int launch_dh(const ChunkArgs &a, void *stream);
 int launch_dh_reduce(const ChunkArgs &a, float *dH, void *stream);
 int launch_dw(const ChunkArgs &a, float *dW, bool accumulate, void *stream);
+int launch_transpose_head(const ChunkArgs &a, void *stream);
+int launch_transpose_chunk(const ChunkArgs &a, void *stream);
 int launch_zero_flag(uint32_t *flag, void *stream);
 
 }  // namespace fckl

@@ -346,36 +346,40 @@ struct KTile {
         return CPR == 8 ? ((row & 7) ^ ((row >> 3) & 1)) : ((row >> 2) & 3);
     }
 
-    // Per-thread source state: for each of the PER 16-byte pieces, the row's base
-    // pointer (already offset by the piece's k) and whether the row exists.
+    // Source state.  `base` (uniform) points at row row0, column k0 of the current
+    // k-slice; per piece, a lane keeps its 32-bit element offset from there and a
+    // check value: the piece's k offset, or a huge number when its row does not exist.
     struct Src {
-        const uint16_t *p[PER];
-        int kc8[PER];
-        bool ok[PER];
+        const uint16_t *base;
+        uint32_t off[PER];
+        int kchk[PER];
     };
-    __device__ __forceinline__ static void init(Src &s, const uint16_t *base, int64_t ld, int row0, int rows_valid)
+    __device__ __forceinline__ static void init(Src &s, const uint16_t *base, int64_t ld, int row0, int rows_valid,
+                                                int k_begin)
     {
         const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        s.base = base + (int64_t)row0 * ld + k_begin;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int pslot = (i * (NT / 64) + wave) * 64 + lane;
             const int row = pslot / CPR, pc = pslot % CPR;
             const int kc = pc ^ sw(row);
-            const int grow = row0 + row;
-            s.ok[i] = grow < rows_valid;
-            s.kc8[i] = kc * 8;
-            s.p[i] = base + (int64_t)(s.ok[i] ? grow : 0) * ld + kc * 8;
+            const bool ok = row0 + row < rows_valid;
+            s.off[i] = ok ? (uint32_t)(row * ld + kc * 8) : 0u;
+            s.kchk[i] = ok ? kc * 8 : (1 << 30);
         }
     }
     // Piece i of the k-slice [k0, k0 + BKK) into `tile` (a piece past k_valid or past
     // the last row comes from the zero page).
-    __device__ __forceinline__ static void issue_one(Src &s, int i, int k0, int k_valid, int64_t, char *tile)
+    __device__ __forceinline__ static void issue_one(const Src &s, int i, int k0, int k_valid, char *tile)
     {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        const bool ok = s.ok[i] && (k0 + s.kc8[i] < k_valid);
-        const void *src = ok ? static_cast<const void *>(s.p[i] + k0) : static_cast<const void *>(kZeroPage);
+        const bool ok = k0 + s.kchk[i] < k_valid;
+        const void *src = ok ? static_cast<const void *>(s.base + s.off[i]) : static_cast<const void *>(kZeroPage);
         copy16_to_lds(src, tile + (i * (NT / 64) + wave) * 1024);
     }
+    // Move the source to the next k-slice.
+    __device__ __forceinline__ static void advance(Src &s, int64_t) { s.base += BKK; }
     // 8 k-values (chunk kc) of tile row `row`, the MFMA operand of one lane.
     __device__ __forceinline__ static bf16x8 frag(const char *tile, int row, int kc)
     {
@@ -399,42 +403,50 @@ struct MNTile {
     static constexpr int PER = CHUNKS / NT;
     static constexpr int BYTES = CHUNKS * 16;
 
-    static_assert(CPR == 32 || CPR == 24, "256 or 192 columns");
-    // 512-byte rows: XOR by 4*(k%4).  384-byte rows alternate between the two halves
-    // of the 256-byte bank window, so XOR by 4*((k/2)%2) suffices.
-    __device__ __forceinline__ static int sw(int k) { return CPR == 32 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); }
+    static_assert((CPR * 16) % 256 == 0 || (CPR * 16) % 256 == 128, "row pitch a multiple of 128 bytes");
+    static_assert(CPR % 8 == 0, "XOR swizzle stays inside the row");
+    // Rows whose pitch is a multiple of 256 bytes: XOR by 4*(k%4).  Rows of an odd
+    // multiple of 128 bytes alternate between the two halves of the 256-byte bank
+    // window, so XOR by 4*((k/2)%2) suffices.
+    __device__ __forceinline__ static int sw(int k)
+    {
+        return (CPR * 16) % 256 == 0 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
+    }
 
-    // Per-thread source state: for each piece, the pointer at k-row (k_begin + k),
-    // the piece's k-row within the tile and whether its columns exist.
+    // Source state.  `base` (uniform) points at k-row k0 of the current slice, column
+    // col0; per piece, a lane keeps its 32-bit element offset from there and a check
+    // value: the piece's k-row in the slice, or a huge number when its columns do not
+    // exist.
     struct Src {
-        const uint16_t *p[PER];
-        int k[PER];
-        bool ok[PER];
+        const uint16_t *base;
+        uint32_t off[PER];
+        int kchk[PER];
     };
     __device__ __forceinline__ static void init(Src &s, const uint16_t *base, int64_t ld, int col0, int cols_valid,
                                                 int k_begin)
     {
         const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        s.base = base + (int64_t)k_begin * ld + col0;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int pslot = (i * (NT / 64) + wave) * 64 + lane;
             const int k = pslot / CPR, pc = pslot % CPR;
-            const int gc = col0 + (pc ^ sw(k)) * 8;
-            s.ok[i] = gc < cols_valid;
-            s.k[i] = k;
-            s.p[i] = base + (int64_t)(k_begin + k) * ld + (s.ok[i] ? gc : 0);
+            const int c = (pc ^ sw(k)) * 8;
+            const bool ok = col0 + c < cols_valid;
+            s.off[i] = ok ? (uint32_t)(k * ld + c) : 0u;
+            s.kchk[i] = ok ? k : (1 << 30);
         }
     }
-    // Piece i of k-rows [k0, k0 + BKK) into `tile`.  Each piece's pointer advances by
-    // BKK rows per call, so the k-steps of one piece must be issued in order.
-    __device__ __forceinline__ static void issue_one(Src &s, int i, int k0, int k_valid, int64_t ld, char *tile)
+    // Piece i of k-rows [k0, k0 + BKK) into `tile`.
+    __device__ __forceinline__ static void issue_one(const Src &s, int i, int k0, int k_valid, char *tile)
     {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        const bool ok = s.ok[i] && (k0 + s.k[i] < k_valid);
-        const void *src = ok ? static_cast<const void *>(s.p[i]) : static_cast<const void *>(kZeroPage);
+        const bool ok = k0 + s.kchk[i] < k_valid;
+        const void *src = ok ? static_cast<const void *>(s.base + s.off[i]) : static_cast<const void *>(kZeroPage);
         copy16_to_lds(src, tile + (i * (NT / 64) + wave) * 1024);
-        s.p[i] += (int64_t)BKK * ld;
     }
+    // Move the source to the next k-slice.
+    __device__ __forceinline__ static void advance(Src &s, int64_t ld) { s.base += (int64_t)BKK * ld; }
     // Operand of one lane for the 32-column block starting at `col`, k-step ks (16 k).
     __device__ __forceinline__ static bf16x8 frag(const char *tile, int col, int ks)
     {
@@ -573,15 +585,10 @@ struct GemmD {
         }
         typename AT::Src sa;
         typename BT::Src sb;
-        if constexpr (AK)
-            AT::init(sa, A, lda, m0, m_valid);
-        else
-            AT::init(sa, A, lda, m0, m_valid, k_begin);
-        if constexpr (BKM)
-            BT::init(sb, B, ldb, n0, n_valid);
-        else
-            BT::init(sb, B, ldb, n0, n_valid, k_begin);
-        // loads [first, last) of k-step `step` (0..L-1: A pieces, then B pieces)
+        AT::init(sa, A, lda, m0, m_valid, k_begin);
+        BT::init(sb, B, ldb, n0, n_valid, k_begin);
+        // Loads [first, last) of k-step `step` (0..L-1: A pieces, then B pieces).  The
+        // k-steps are issued in order; the sources advance after a step's last load.
         auto issue = [&](int step, auto first_c, auto last_c) {
             constexpr int first = decltype(first_c)::value, last = decltype(last_c)::value;
             char *st = smem + (step % S) * STAGE;
@@ -589,9 +596,13 @@ struct GemmD {
 #pragma unroll
             for (int x = first; x < last; ++x) {
                 if (x < AT::PER)
-                    AT::issue_one(sa, x, k0, ka_valid, lda, st);
+                    AT::issue_one(sa, x, k0, ka_valid, st);
                 else
-                    BT::issue_one(sb, x - AT::PER, k0, kb_valid, ldb, st + AT::BYTES);
+                    BT::issue_one(sb, x - AT::PER, k0, kb_valid, st + AT::BYTES);
+            }
+            if constexpr (last == L) {
+                AT::advance(sa, lda);
+                BT::advance(sb, ldb);
             }
         };
 #pragma unroll
@@ -947,6 +958,7 @@ struct BwdParams {
     const float *p_s, *psum;
     const uint8_t *cnt;
     uint16_t *g;            // [Cpad, Vpad] bf16
+    uint16_t *gT;           // [Vpad, Cpad] bf16
 };
 
 __global__ __launch_bounds__(LogitGemm::NT) void backward_logits_kernel(BwdParams p)
@@ -1031,13 +1043,33 @@ __global__ __launch_bounds__(LogitGemm::NT) void backward_logits_kernel(BwdParam
         const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + nl * kGStagePitch + col * 2);
         *reinterpret_cast<u32x4 *>(p.g + (size_t)(n0 + nl) * p.Vpad + m0 + col) = v;
     }
+    // The same tile transposed, [vocab][token], for the dW product.
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < G::NB; ++j) {
+        const int nl = G::col_of(wn, j, lane);
+#pragma unroll
+        for (int i = 0; i < G::MB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int ml = G::row_of(wm, i, r, lane);
+                *reinterpret_cast<uint16_t *>(smem + ml * kGStagePitch + nl * 2) = (uint16_t)bf16_rne(acc[i][j][r]);
+            }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int c = threadIdx.x; c < kChunks; c += G::NT) {
+        const int ml = c >> 5, col = (c & 31) * 8;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + ml * kGStagePitch + col * 2);
+        *reinterpret_cast<u32x4 *>(p.gT + (size_t)(m0 + ml) * p.Cpad + n0 + col) = v;
+    }
 }
 
 // ------------------------------------------------------------------ dH = g . W
 
 struct DhParams {
     const uint16_t *g;      // [Cpad, Vpad]
-    const uint16_t *W;      // [V, H]
+    const uint16_t *WT;     // [H, Vpad]
     int H, V, Vpad, rows, Cpad, nMt, nNt, ksplit;
     float *part;            // [splits, Cpad, H]
 };
@@ -1052,8 +1084,8 @@ __global__ __launch_bounds__(G::NT) void dh_kernel(DhParams p)
     const int k_begin = blockIdx.y * p.ksplit;
     const int k_end = min(p.V, k_begin + p.ksplit);
     f32x16 acc[G::MB][G::NB];
-    // A(m = token, k = vocab) = g[m][k]; B(n = hidden, k = vocab) = W[k][n].
-    G::run(smem, p.g, p.Vpad, m0, p.rows, k_end, p.W, p.H, n0, p.H, k_end, k_begin, k_end, acc);
+    // A(m = token, k = vocab) = g[m][k]; B(n = hidden, k = vocab) = WT[n][k].
+    G::run(smem, p.g, p.Vpad, m0, p.rows, k_end, p.WT, p.Vpad, n0, p.H, k_end, k_begin, k_end, acc);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / G::WN, wn = wave % G::WN;
     float *out = p.part + (size_t)blockIdx.y * p.Cpad * p.H;
@@ -1094,9 +1126,9 @@ __global__ __launch_bounds__(256) void dh_reduce_kernel(const float *part, int s
 // ------------------------------------------------------------------ dW += g^T . h
 
 struct DwParams {
-    const uint16_t *g;      // [Cpad, Vpad]
-    const uint16_t *h;      // [rows, H] chunk
-    int H, V, Vpad, rows, nMt, nNt, accumulate;
+    const uint16_t *gT;     // [Vpad, Cpad]
+    const uint16_t *hT;     // [H, Cpad]
+    int H, V, Vpad, Cpad, rows, nMt, nNt, accumulate;
     float *dW;              // [V, H]
 };
 
@@ -1108,8 +1140,8 @@ __global__ __launch_bounds__(G::NT) void dw_kernel(DwParams p)
     map_tile(blockIdx.x, p.nMt, p.nNt, 1, tm, tn);
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     f32x16 acc[G::MB][G::NB];
-    // A(m = vocab, k = token) = g[k][m]; B(n = hidden, k = token) = h[k][n].
-    G::run(smem, p.g, p.Vpad, m0, p.Vpad, p.rows, p.h, p.H, n0, p.H, p.rows, 0, p.rows, acc);
+    // A(m = vocab, k = token) = gT[m][k]; B(n = hidden, k = token) = hT[n][k].
+    G::run(smem, p.gT, p.Cpad, m0, p.Vpad, p.rows, p.hT, p.Cpad, n0, p.H, p.rows, 0, p.rows, acc);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / G::WN, wn = wave % G::WN;
 #pragma unroll
@@ -1130,10 +1162,29 @@ __global__ __launch_bounds__(G::NT) void dw_kernel(DwParams p)
     }
 }
 
-using DGemm256 = GemmD<256, 256, 2, 4, true, false, 64, 2>;   // dH, hidden tile 256
-using DGemm192 = GemmD<256, 192, 4, 2, true, false, 64, 2>;   // dH, hidden tile 192
-using WGemm256 = GemmD<256, 256, 2, 4, false, false, 64, 2>;  // dW, hidden tile 256
-using WGemm192 = GemmD<256, 192, 4, 2, false, false, 64, 2>;  // dW, hidden tile 192
+using DGemm256 = GemmD<256, 256, 2, 4, true, true, 64, 2>;   // dH, hidden tile 256
+using DGemm192 = GemmD<256, 192, 4, 2, true, true, 64, 2>;   // dH, hidden tile 192
+using WGemm256 = GemmD<256, 256, 2, 4, true, true, 64, 2>;   // dW, hidden tile 256
+using WGemm192 = GemmD<256, 192, 4, 2, true, true, 64, 2>;   // dW, hidden tile 192
+
+// dst[c][r] = src[r][c] for r < rows, c < cols; dst[c][r] = 0 for rows <= r < rpad.
+// 64 x 64 tiles through LDS so that both sides are read and written along rows.
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t *src, int64_t ld_src, int rows, int cols,
+                                                        uint16_t *dst, int64_t ld_dst, int rpad)
+{
+    __shared__ uint16_t t[64][66];
+    const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+        const int r = e >> 6, c = e & 63;
+        t[r][c] = (r0 + r < rows && c0 + c < cols) ? src[(int64_t)(r0 + r) * ld_src + c0 + c] : (uint16_t)0;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+        const int c = e >> 6, r = e & 63;
+        if (c0 + c < cols && r0 + r < rpad)
+            dst[(int64_t)(c0 + c) * ld_dst + r0 + r] = t[r][c];
+    }
+}
 
 __global__ void zero_u32_kernel(uint32_t *p, int n)
 {
@@ -1244,6 +1295,7 @@ int launch_backward_logits(const ChunkArgs &a, const float *lse, float coef, voi
     p.psum = reinterpret_cast<const float *>(a.ws + L.off_psum);
     p.cnt = reinterpret_cast<const uint8_t *>(a.ws + L.off_cnt);
     p.g = reinterpret_cast<uint16_t *>(a.ws + L.off_g);
+    p.gT = reinterpret_cast<uint16_t *>(a.ws + L.off_gT);
     hipLaunchKernelGGL(backward_logits_kernel, dim3(p.nVt * p.nNt), dim3(LogitGemm::NT), 0, S(stream), p);
     return (int)hipGetLastError();
 }
@@ -1262,7 +1314,7 @@ int launch_dh(const ChunkArgs &a, void *stream)
     const Layout &L = *a.L;
     DhParams p;
     p.g = reinterpret_cast<const uint16_t *>(a.ws + L.off_g);
-    p.W = a.W;
+    p.WT = reinterpret_cast<const uint16_t *>(a.ws + L.off_WT);
     p.H = a.H;
     p.V = a.V;
     p.Vpad = L.Vpad;
@@ -1297,11 +1349,12 @@ int launch_dw(const ChunkArgs &a, float *dW, bool accumulate, void *stream)
 {
     const Layout &L = *a.L;
     DwParams p;
-    p.g = reinterpret_cast<const uint16_t *>(a.ws + L.off_g);
-    p.h = a.h;
+    p.gT = reinterpret_cast<const uint16_t *>(a.ws + L.off_gT);
+    p.hT = reinterpret_cast<const uint16_t *>(a.ws + L.off_hT);
     p.H = a.H;
     p.V = a.V;
     p.Vpad = L.Vpad;
+    p.Cpad = L.Cpad;
     p.rows = a.rows;
     p.nMt = L.nVt;
     p.nNt = (a.H + L.dh_bn - 1) / L.dh_bn;
@@ -1312,6 +1365,28 @@ int launch_dw(const ChunkArgs &a, float *dW, bool accumulate, void *stream)
         hipLaunchKernelGGL(dw_kernel<WGemm256>, grid, dim3(WGemm256::NT), 0, S(stream), p);
     else
         hipLaunchKernelGGL(dw_kernel<WGemm192>, grid, dim3(WGemm192::NT), 0, S(stream), p);
+    return (int)hipGetLastError();
+}
+
+// W [V, H] -> WT [H, Vpad] (columns V..Vpad-1 zero).
+int launch_transpose_head(const ChunkArgs &a, void *stream)
+{
+    const Layout &L = *a.L;
+    uint16_t *WT = reinterpret_cast<uint16_t *>(a.ws + L.off_WT);
+    dim3 grid((L.Vpad + 63) / 64, (a.H + 63) / 64);
+    hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, S(stream), a.W, (int64_t)a.H, a.V, a.H, WT,
+                       (int64_t)L.Vpad, L.Vpad);
+    return (int)hipGetLastError();
+}
+
+// chunk's h [rows, H] -> hT [H, Cpad] (columns rows..Cpad-1 zero).
+int launch_transpose_chunk(const ChunkArgs &a, void *stream)
+{
+    const Layout &L = *a.L;
+    uint16_t *hT = reinterpret_cast<uint16_t *>(a.ws + L.off_hT);
+    dim3 grid((L.Cpad + 63) / 64, (a.H + 63) / 64);
+    hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, S(stream), a.h, (int64_t)a.H, a.rows, a.H, hT,
+                       (int64_t)L.Cpad, L.Cpad);
     return (int)hipGetLastError();
 }
 

@@ -37,18 +37,44 @@ fckl_status check_desc(const fckl_desc *d)
     return FCKL_OK;
 }
 
-// Number of vocabulary splits of the dH product: enough work-groups to cover the
-// 256 compute units several times over, but at least 4 k-steps of 64 per split.
+// Hidden-dimension tile of the dH / dW products: 256 when it divides H, else 192 when
+// that does, else 256 with a masked tail.
+static int32_t hidden_tile(int32_t H)
+{
+    if (H % 256 == 0)
+        return 256;
+    if (H % 192 == 0)
+        return 192;
+    return 256;
+}
+
+// Number of vocabulary splits of the dH product (its reduction runs over V).  Each
+// split streams a V/S slice of W; enough splits keep that slice inside the 256 MB
+// last-level cache, and among the candidates the one whose work-group count
+// best fills whole waves of the 256 compute units wins.  At least 4 k-steps of 64 per
+// split; at most 32 splits.
 static int32_t dh_split_count(int32_t Cpad, int32_t H, int32_t bn, int32_t Vpad)
 {
-    int64_t tiles = (int64_t)(Cpad / kTokenTile) * ((H + bn - 1) / bn);
-    int64_t s = (1024 + tiles - 1) / tiles;
-    int64_t smax = Vpad / 256;
-    if (s > smax)
-        s = smax;
-    if (s > 64)
-        s = 64;
-    return (int32_t)(s < 1 ? 1 : s);
+    const int64_t tiles = (int64_t)(Cpad / kTokenTile) * ((H + bn - 1) / bn);
+    const int64_t slice_cap = (int64_t)192 << 20;                    // bytes of W per split
+    int64_t smin = ((int64_t)Vpad * H * 2 + slice_cap - 1) / slice_cap;
+    int64_t smax = std::min<int64_t>(32, Vpad / 256);
+    smin = std::max<int64_t>(1, std::min(smin, smax));
+    // the smallest split count from smin that fills 97% of its waves, else the best fill
+    int64_t best = smin;
+    double best_eff = -1.0;
+    for (int64_t s = smin; s <= smax; ++s) {
+        const int64_t wgs = tiles * s;
+        const int64_t waves = (wgs + 255) / 256;
+        const double eff = (double)wgs / (double)(waves * 256);
+        if (eff >= 0.97)
+            return (int32_t)s;
+        if (eff > best_eff + 1e-9) {
+            best_eff = eff;
+            best = s;
+        }
+    }
+    return (int32_t)best;
 }
 
 fckl_status make_layout(const fckl_desc *d, int32_t chunk, Layout *L)
@@ -64,7 +90,7 @@ fckl_status make_layout(const fckl_desc *d, int32_t chunk, Layout *L)
     o.nVt = (d->V + kVocabTile - 1) / kVocabTile;
     o.Vpad = o.nVt * kVocabTile;
     o.cnt_stride = (int32_t)align_up((size_t)o.nVt + 1, 16);
-    o.dh_bn = (d->H % 256 == 0) ? 256 : (d->H % 192 == 0 ? 192 : 256);
+    o.dh_bn = hidden_tile(d->H);
     o.dh_splits = dh_split_count(o.Cpad, d->H, o.dh_bn, o.Vpad);
     const size_t Cp = (size_t)o.Cpad, K = (size_t)d->K;
     size_t off = 0;
@@ -81,6 +107,9 @@ fckl_status make_layout(const fckl_desc *d, int32_t chunk, Layout *L)
     o.off_cnt = take(Cp * (size_t)o.cnt_stride);
     o.off_part = take((size_t)o.nVt * Cp * 8);
     o.off_g = take(Cp * (size_t)o.Vpad * 2);
+    o.off_gT = take(Cp * (size_t)o.Vpad * 2);
+    o.off_hT = take(Cp * (size_t)d->H * 2);
+    o.off_WT = take((size_t)o.Vpad * (size_t)d->H * 2);
     o.off_dhp = take((size_t)o.dh_splits * Cp * (size_t)d->H * 4);
     o.off_err = take(16);
     o.total = off;
@@ -109,12 +138,20 @@ fckl_status plan_chunk(const fckl_desc *d, size_t budget, Layout *L)
     }
     if (best == 0)
         return FCKL_ERR_WORKSPACE;
-    // Even the chunks out: same number of chunks, as few padded tokens as possible.
-    int64_t nchunks = (d->N + best - 1) / best;
-    int32_t c = (int32_t)align_up((size_t)((d->N + nchunks - 1) / nchunks), kTokenTile);
-    if (c > best)
-        c = best;
-    return make_layout(d, c, L);
+    // Even the chunks out: the fewest chunks of equal size (up to the token tile) whose
+    // layout fits.  (The workspace is not monotone in the chunk: the dH split count
+    // depends on it.)
+    for (int64_t nchunks = (d->N + best - 1) / best;; ++nchunks) {
+        const int32_t c = (int32_t)align_up((size_t)((d->N + nchunks - 1) / nchunks), kTokenTile);
+        Layout even;
+        if (c <= best && make_layout(d, c, &even) == FCKL_OK && even.total <= budget) {
+            *L = even;
+            return FCKL_OK;
+        }
+        if (c <= kTokenTile)
+            break;
+    }
+    return make_layout(d, best, L);
 }
 
 }  // namespace fckl

@@ -83,7 +83,8 @@ enum {
     FCKL_KERNEL_DH = 5,            /* dH = g W (vocabulary splits) */
     FCKL_KERNEL_DH_REDUCE = 6,     /* fixed-order sum of the dH splits */
     FCKL_KERNEL_DW = 7,            /* dW += g^T h */
-    FCKL_KERNEL_COUNT = 8
+    FCKL_KERNEL_TRANSPOSE = 8,     /* W^T once per backward call, h^T once per chunk */
+    FCKL_KERNEL_COUNT = 9
 };
 
 /*
@@ -121,7 +122,7 @@ typedef struct fckl_desc {
  * Chunk scheduler ("processes one chunk ... then discards it", axbrief.com; sized
  * here for the 288 GB of HBM3E of one MI355X).  Pure host function, no HIP call.
  * Chooses the number of tokens per chunk for `desc` so that the workspace fits in
- * `budget_bytes` (0 = the library default, 4 GiB), preferring the largest chunk up to
+ * `budget_bytes` (0 = the library default, 12 GiB), preferring the largest chunk up to
  * 16384 tokens and then evening out the chunks.  If desc->chunk > 0 that chunk is
  * kept and only its workspace size is reported.
  *   chunk_out    host, may be NULL: tokens per chunk.
