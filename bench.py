@@ -73,6 +73,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=0, help="tokens per chunk (0 = library scheduler)")
     ap.add_argument("--cpu-tokens", type=int, default=48, help="oracle sample size for cpu_baseline (0 = skip)")
     ap.add_argument("--dense", action="store_true", help="also measure peak memory of a dense torch KL baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one plain 1 GiB device copy first (reference dispatch for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
@@ -86,6 +88,14 @@ def main():
 
     fckl.load()
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
     wl = synth.WORKLOADS[args.workload]
     if args.tokens:
         wl = wl.with_tokens(args.tokens)

@@ -1,0 +1,128 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark uses
+(the library's own chunk choice for its default workspace budget).
+
+At these sizes the oracle cannot run every token, so:
+  * per-token outputs (loss, lse and dH rows) are compared with the oracle on a seeded
+    sample of tokens (the oracle computes each token on its own, normalising dH by
+    the full N); the sample includes the large-norm rows of the stress workload;
+  * dW is compared element by element, over the full vocabulary and hidden size, on a
+    separate run of the same shapes restricted to a sampled subset of tokens;
+  * at full size, properties that hold at any size are checked: every per-token loss
+    is >= 0, the mean equals the average of the per-token losses, the rows of dW sum
+    to zero (the softmax part of the gradient sums to the teacher mass it removes),
+    and <dW, W> = <dH, h> (both equal sum_i <g_i, z_i>).
+"""
+import numpy as np
+import pytest
+import torch
+
+import chunked_top_kl_chunk_amd as fckl
+import oracle
+import synth
+from gpu_util import GRAD_TOL, LOSS_RTOL, LSE_ATOL, check_grad, check_loss, device, rel_max, say, upload
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
+
+SAMPLE_ROWS = 48
+DW_TOKENS = 48
+
+
+def _run_full(wl, x):
+    dev = device()
+    h, W, idx, tl = upload(x, dev)
+    desc = fckl.desc_for(h, W, idx, tl, wl.T)
+    chunk, ws_bytes = fckl.plan(desc)
+    say("workload %s N=%d H=%d V=%d K=%d T=%g: chunk %d, workspace %.2f GiB"
+        % (wl.name, wl.N, wl.H, wl.V, wl.K, wl.T, chunk, ws_bytes / 2 ** 30))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    loss, lse, mean = fckl.forward(h, W, idx, tl, T=wl.T, chunk=chunk, ws=ws)
+    dH, dW = fckl.backward(h, W, idx, tl, lse, T=wl.T, chunk=chunk, ws=ws)
+    torch.cuda.synchronize()
+    # size-independent identities, evaluated on the GPU in float64
+    sum_rows = dW.double().sum(0).abs().max().item()
+    scale_rows = dW.double().abs().sum(0).max().item()
+    ip_w = (dW.double() * W.double()).sum().item()
+    ip_h = (dH.double() * h.double()).sum().item()
+    out = dict(loss=loss.cpu().numpy(), lse=lse.cpu().numpy(), mean=float(mean.item()), chunk=chunk,
+               sum_rows=sum_rows, scale_rows=scale_rows, ip_w=ip_w, ip_h=ip_h)
+    rows = synth.sample_rows(wl, SAMPLE_ROWS, must_include=synth.scaled_rows(wl)[:8])
+    out["rows"] = rows
+    out["dH_rows"] = dH[torch.from_numpy(rows).to(dev)].cpu().numpy()
+    del dH, dW, ws, h, W, idx, tl, loss, lse
+    torch.cuda.empty_cache()
+    return out
+
+
+def _check_workload(key):
+    wl = synth.WORKLOADS[key]
+    say("case: full workload", key, wl.name)
+    x = synth.make_inputs(wl, device=device())
+    g = _run_full(wl, x)
+    # properties at full size
+    assert np.isfinite(g["loss"]).all()
+    assert (g["loss"] >= -1e-5 * np.abs(g["loss"]).max()).all()
+    assert abs(g["mean"] - g["loss"].astype(np.float64).mean()) <= 1e-5 * abs(g["mean"])
+    assert g["sum_rows"] <= 1e-3 * g["scale_rows"], (g["sum_rows"], g["scale_rows"])
+    assert abs(g["ip_w"] - g["ip_h"]) <= 2e-2 * max(abs(g["ip_w"]), abs(g["ip_h"]), 1e-30), (g["ip_w"], g["ip_h"])
+    # sampled tokens against the oracle
+    rows = g["rows"]
+    hs, idxs, tls = x.h[rows], x.idx[rows], x.tl[rows]
+    W64 = x.W.astype(np.float64)
+    ref_loss, ref_lse = oracle.forward(hs, W64, idxs, tls, wl.T)
+    e_loss = check_loss(g["loss"][rows], ref_loss, key)
+    e_lse = float(np.abs(g["lse"][rows] - ref_lse).max())
+    assert e_lse <= LSE_ATOL, "%s lse abs err %.3e" % (key, e_lse)
+    ref_dH, _ = oracle.backward(hs, W64, idxs, tls, wl.T, n_norm=wl.N, want_dW=False)
+    e_dH = check_grad(g["dH_rows"], ref_dH, key + " dH rows")
+    say("%s: chunk %d, sampled %d rows: loss %.2e lse %.2e dH %.2e; sum_v dW %.1e of %.1e; <dW,W> %.6e <dH,h> %.6e"
+        % (key, g["chunk"], rows.size, e_loss, e_lse, e_dH, g["sum_rows"], g["scale_rows"], g["ip_w"], g["ip_h"]))
+    # dW over the full vocabulary x hidden size, on a token subset
+    sub = synth.sample_rows(wl, DW_TOKENS)
+    dev = device()
+    hb = torch.from_numpy(x.h_bits[sub].view(np.int16)).to(dev).view(torch.bfloat16)
+    Wb = torch.from_numpy(x.W_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    ib = torch.from_numpy(np.ascontiguousarray(x.idx[sub])).to(dev)
+    tb = torch.from_numpy(x.tl_bits[sub].view(np.int16)).to(dev).view(torch.bfloat16)
+    _, lse_s, _ = fckl.forward(hb, Wb, ib, tb, T=wl.T, chunk=g["chunk"])
+    dH_s, dW_s = fckl.backward(hb, Wb, ib, tb, lse_s, T=wl.T, chunk=g["chunk"])
+    torch.cuda.synchronize()
+    ref_dHs, ref_dWs = oracle.backward(x.h[sub], W64, x.idx[sub], x.tl[sub], wl.T)
+    e_dHs = check_grad(dH_s.cpu().numpy(), ref_dHs, key + " subset dH")
+    e_dWs = check_grad(dW_s.cpu().numpy(), ref_dWs, key + " subset dW")
+    say("%s: %d-token subset, full V x H: dH %.2e dW %.2e" % (key, sub.size, e_dHs, e_dWs))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("key", ["c2", "c3", "c4", "c5"])
+def test_full_workload(key):
+    _check_workload(key)
+
+
+def test_peak_memory_has_no_tokens_times_vocab_term():
+    """Peak device memory of fwd+bwd at the 32K shape's H, V, K for growing N, fixed chunk:
+    linear in N with the per-token cost of the inputs and outputs only."""
+    dev = device()
+    H, V, K, chunk = 2880, 201088, 100, 4096
+    W = (torch.randn(V, H, device=dev) * 0.02).to(torch.bfloat16)
+    peaks = []
+    Ns = (4096, 16384, 32768)
+    for N in Ns:
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        h = torch.randn(N, H, device=dev, dtype=torch.bfloat16)
+        idx = torch.randint(0, V, (N, K), device=dev, dtype=torch.int32)
+        tl = torch.randn(N, K, device=dev, dtype=torch.bfloat16)
+        loss, lse, _ = fckl.forward(h, W, idx, tl, T=1.0, chunk=chunk)
+        dH, dW = fckl.backward(h, W, idx, tl, lse, T=1.0, chunk=chunk)
+        torch.cuda.synchronize()
+        peaks.append(torch.cuda.max_memory_allocated() - base)
+        del h, idx, tl, loss, lse, dH, dW
+    per_token = [(peaks[i + 1] - peaks[i]) / (Ns[i + 1] - Ns[i]) for i in range(len(Ns) - 1)]
+    expect = 2 * H + 4 * H + K * (4 + 2) + 4 + 4          # h, dH, idx, logits, loss, lse
+    say("peak bytes %s, per-token slope %s (expected %d, an N x V term would add %d)"
+        % (peaks, per_token, expect, 4 * V))
+    for s in per_token:
+        assert 0.9 * expect <= s <= 1.1 * expect
