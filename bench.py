@@ -71,7 +71,7 @@ def main():
     ap.add_argument("--workload", default="c3", help="synth workload key (default c3: the 32K-token GPT-OSS-20B shape)")
     ap.add_argument("--tokens", type=int, default=0, help="override N (for quick runs)")
     ap.add_argument("--chunk", type=int, default=0, help="tokens per chunk (0 = library scheduler)")
-    ap.add_argument("--cpu-tokens", type=int, default=48, help="oracle sample size for cpu_baseline (0 = skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=256, help="oracle sample size for cpu_baseline (0 = skip)")
     ap.add_argument("--dense", action="store_true", help="also measure peak memory of a dense torch KL baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (reference dispatch for HBM byte counters)")
@@ -174,7 +174,8 @@ def main():
     flops_per_launch = 2.0 * (kd["tokens"] / kd["launches"]) * V * H
     achieved = flops_per_launch / (kd["avg_ms"] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(wl.name, chunk, dom),
                 "avg_launch_ms": round(kd["avg_ms"], 4),
                 "flops_per_launch": flops_per_launch}
     step_tflops = 8.0 * N * V * H / (ms_step * 1e-3) / 1e12
@@ -195,11 +196,36 @@ def main():
     }
 
     if args.dense:
+        # the fused path's workspace and outputs are released first: the dense loss is
+        # measured with only the inputs resident
+        del ws, loss, lse, mean, dH, dW
         out["dense_baseline"] = dense_baseline(h, W, idx, tl, T)
 
     if args.cpu_tokens > 0:
         out["cpu_baseline"] = cpu_baseline(x, wl, args.cpu_tokens)
     print(json.dumps(out), flush=True)
+
+
+KERNEL_NAMES = {"fwd_logits": "forward_logits_kernel", "bwd_logits": "backward_logits_kernel",
+                "dh": "dh_kernel", "dw": "dw_kernel"}
+
+
+def measured_traffic(workload, chunk, kernel):
+    """HBM bytes (read + written) per launch of `kernel`, from the rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs summarised in profiles/, scaled by the reference copy; None when no
+    summary exists for this workload and chunk or the kernels changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_bytes_%s.json" % workload)
+    src = os.path.join(ROOT, "chunked_top_kl_chunk_amd", "csrc", "fckl_kernels.hip")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("chunk") != chunk or rec.get("kernels_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    for name, v in rec["kernels"].items():
+        if name.startswith(KERNEL_NAMES[kernel]):
+            return round(v["read_bytes"] + v["write_bytes"])
+    return None
 
 
 def dense_baseline(h, W, idx, tl, T):

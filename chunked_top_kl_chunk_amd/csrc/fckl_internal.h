@@ -12,7 +12,7 @@ namespace fckl {
 constexpr int kVocabTile = 256;
 constexpr int kTokenTile = 256;
 constexpr int kMaxK = 128;
-constexpr int32_t kMaxChunk = 16384;
+constexpr int32_t kMaxChunk = 8192;
 constexpr size_t kDefaultBudget = size_t(12) << 30;  // 12 GiB of the 288 GB HBM3E
 
 // Where each per-chunk buffer lives inside the caller's workspace.  Every buffer is

@@ -119,12 +119,15 @@ typedef struct fckl_desc {
 } fckl_desc;
 
 /*
- * Chunk scheduler ("processes one chunk ... then discards it", axbrief.com; sized
- * here for the 288 GB of HBM3E of one MI355X).  Pure host function, no HIP call.
+ * Chunk scheduler (the method handles one slice of the tokens at a time and drops its
+ * intermediates before the next: axbrief.com, "Breaking the Bottleneck with Offline
+ * Caching and Chunked Loss"; sized here for the 288 GB of HBM3E of one MI355X).  Pure
+ * host function, no HIP call.
  * Chooses the number of tokens per chunk for `desc` so that the workspace fits in
  * `budget_bytes` (0 = the library default, 12 GiB), preferring the largest chunk up to
- * 16384 tokens and then evening out the chunks.  If desc->chunk > 0 that chunk is
- * kept and only its workspace size is reported.
+ * 8192 tokens (beyond that the saving in re-streamed W and dW read-modify-write is
+ * small and the chunk gradient keeps growing) and then evening out the chunks.  If
+ * desc->chunk > 0 that chunk is kept and only its workspace size is reported.
  *   chunk_out    host, may be NULL: tokens per chunk.
  *   ws_bytes_out host, may be NULL: workspace bytes fckl_forward/fckl_backward need.
  * Returns FCKL_ERR_WORKSPACE when even the smallest chunk does not fit.

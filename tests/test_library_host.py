@@ -45,7 +45,7 @@ def test_plan_fits_budget_and_is_even():
     for budget in (0, 2 * GiB, 3 * GiB, 8 * GiB):
         chunk, ws = fckl.plan(d, budget)
         assert ws <= (budget or DEFAULT_BUDGET)
-        assert chunk % 256 == 0 and 256 <= chunk <= 16384
+        assert chunk % 256 == 0 and 256 <= chunk <= 8192
         nchunks = -(-C3["N"] // chunk)
         assert nchunks * chunk - C3["N"] < 256 * nchunks
 
