@@ -644,7 +644,10 @@ struct GemmD {
 
 // The logit GEMM: rows = vocabulary (W), columns = tokens (h), k = hidden.
 using LogitGemm = GemmD<256, 256, 2, 4, true, true, 64, 2>;
-constexpr int kGStagePitch = 256 * 2 + 16;   // bytes per token row of the bf16 g staging tile
+static_assert(LogitGemm::BM == kVocabTile, "entry counts are kept per 256-row vocabulary tile");
+static_assert(kTokenTile % LogitGemm::BN == 0, "chunk padding covers whole token tiles");
+constexpr int kGStagePitch = 256 * 2 + 16;   // bytes per row of the bf16 g / g^T staging tiles
+static_assert(LogitGemm::BM <= 256 && LogitGemm::BN <= 256, "staging tile");
 constexpr int kLogitLds = (LogitGemm::LDS_BYTES > 256 * kGStagePitch) ? LogitGemm::LDS_BYTES : 256 * kGStagePitch;
 
 // Select acc[mb][nb][r] for a run-time (mb*16 + r) without indexing registers.
@@ -1037,9 +1040,10 @@ __global__ __launch_bounds__(LogitGemm::NT) void backward_logits_kernel(BwdParam
     }
     __syncthreads();
     constexpr int kChunks = G::BN * (G::BM * 2 / 16);
+    constexpr int kRowChunks = G::BM / 8;       // 16-byte pieces per token row of the tile
 #pragma unroll 4
     for (int c = threadIdx.x; c < kChunks; c += G::NT) {
-        const int nl = c >> 5, col = (c & 31) * 8;
+        const int nl = c / kRowChunks, col = (c % kRowChunks) * 8;
         const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + nl * kGStagePitch + col * 2);
         *reinterpret_cast<u32x4 *>(p.g + (size_t)(n0 + nl) * p.Vpad + m0 + col) = v;
     }
@@ -1057,9 +1061,10 @@ __global__ __launch_bounds__(LogitGemm::NT) void backward_logits_kernel(BwdParam
             }
     }
     __syncthreads();
+    constexpr int kColChunks = G::BN / 8;       // 16-byte pieces per vocabulary row of the tile
 #pragma unroll 4
     for (int c = threadIdx.x; c < kChunks; c += G::NT) {
-        const int ml = c >> 5, col = (c & 31) * 8;
+        const int ml = c / kColChunks, col = (c % kColChunks) * 8;
         const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + ml * kGStagePitch + col * 2);
         *reinterpret_cast<u32x4 *>(p.gT + (size_t)(m0 + ml) * p.Cpad + n0 + col) = v;
     }
@@ -1235,7 +1240,7 @@ int launch_forward_logits(const ChunkArgs &a, void *stream)
     p.Cpad = L.Cpad;
     p.K = a.K;
     p.nVt = L.nVt;
-    p.nNt = (a.rows + kTokenTile - 1) / kTokenTile;
+    p.nNt = (a.rows + LogitGemm::BN - 1) / LogitGemm::BN;
     p.cnt_stride = L.cnt_stride;
     p.scale2 = kLog2e / a.T;
     p.idx_s = reinterpret_cast<const int32_t *>(a.ws + L.off_idx);
@@ -1285,7 +1290,7 @@ int launch_backward_logits(const ChunkArgs &a, const float *lse, float coef, voi
     p.Vpad = L.Vpad;
     p.K = a.K;
     p.nVt = L.nVt;
-    p.nNt = (a.rows + kTokenTile - 1) / kTokenTile;
+    p.nNt = (a.rows + LogitGemm::BN - 1) / LogitGemm::BN;
     p.cnt_stride = L.cnt_stride;
     p.scale2 = kLog2e / a.T;
     p.coef = coef;
