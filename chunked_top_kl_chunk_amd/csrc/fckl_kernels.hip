@@ -15,16 +15,19 @@
 //   backward_logits  the same MFMA tiles recompute z (the extra projection in the
 //                    backward pass that the chunked loss pays for, axbrief.com);
 //                    the epilogue forms g = c((sum p) softmax(z/T) - scatter(p, idx)),
-//                    rounds it to bf16 and writes the chunk's g [C, V]
+//                    rounds it to bf16 and writes the chunk's g twice: [C, V] for the
+//                    dH product and [V, C] for the dW product
 //   dh               dH_chunk = g . W   (split over the vocabulary, fixed-order reduce)
 //   dw               dW += g^T . h_chunk (fp32 read-modify-write, chunk after chunk)
+//   transpose        W -> W^T once per backward call, h_chunk -> h_chunk^T per chunk
 //
 // GEMM core: 256 x 256 (or 256 x 192) tiles, 512 threads = 8 wave64s, each wave owns a
-// 128 x 64 (or 64 x 96) block of v_mfma_f32_32x32x16_bf16 accumulators.  Operands are
-// staged global -> registers -> LDS (two stages, one barrier per 64-deep k-step).  LDS
-// rows hold 64 bf16 along k with an XOR swizzle of the 16-byte chunk index.  Operands
-// whose contiguous dimension is not k (W and h in the backward products, g in dW) are
-// transposed in registers (8 k-rows x 4 columns per thread) before the LDS write.
+// 128 x 64 (or 64 x 96) block of v_mfma_f32_32x32x16_bf16 accumulators.  Every operand
+// is read k-major (contiguous along the reduction), which is why the backward products
+// use W^T, h_chunk^T and the second layout of g.  Each lane's 16-byte piece goes from
+// global memory straight into LDS (global_load_lds_dwordx4, no register staging); two
+// LDS stages of 64-deep k-steps, one barrier per step, and an XOR swizzle of the
+// 16-byte chunks that keeps the MFMA operand reads free of bank conflicts.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -46,15 +49,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
 
 // ------------------------------------------------------------------ small helpers
-
-// LDS operand tiles: one row = 64 bf16 along k = eight 16-byte chunks.  The chunk
-// index is XOR-ed with row bits 0-2 and 3-5 so that 8 consecutive rows at one chunk
-// (the MFMA operand read) and 8 rows 8 apart (the transposed write) hit 8 distinct
-// 16-byte bank groups.
-__device__ __forceinline__ int swz(int row, int kc)
-{
-    return (row << 3) + (kc ^ (row & 7) ^ ((row >> 3) & 7));
-}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -114,180 +108,6 @@ __device__ __forceinline__ void map_tile(int bid, int nM, int nN, int GM, int &t
     tm = first + r % gm;
     tn = r / gm;
 }
-
-// ------------------------------------------------------------------ operand loaders
-
-// Operand whose k dimension is contiguous in memory: element (row, k) at base[row*ld + k].
-template <int ROWS, int NT>
-struct KMajorLoad {
-    static_assert((ROWS * 8) % NT == 0, "tile rows");
-    static constexpr int kPer = ROWS * 8 / NT;
-    u32x4 r[kPer];
-
-    __device__ __forceinline__ void load(const uint16_t *base, int64_t ld, int row0, int rows_valid, int k0,
-                                         int k_valid)
-    {
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int c = threadIdx.x + i * NT;
-            const int row = c >> 3, kc = c & 7;
-            const int grow = row0 + row, gk = k0 + kc * 8;
-            if (grow < rows_valid && gk < k_valid)
-                r[i] = *reinterpret_cast<const u32x4 *>(base + (int64_t)grow * ld + gk);
-            else
-                r[i] = u32x4{0u, 0u, 0u, 0u};
-        }
-    }
-    __device__ __forceinline__ void store(char *lds) const
-    {
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int c = threadIdx.x + i * NT;
-            *reinterpret_cast<u32x4 *>(lds + swz(c >> 3, c & 7) * 16) = r[i];
-        }
-    }
-};
-
-// Operand whose row dimension is contiguous: element (row, k) at base[k*ld + row].
-// A block is 8 consecutive k-rows x 4 consecutive columns (8 bytes per k-row); each
-// thread loads kPer blocks and transposes each into four 16-byte k-vectors.
-template <int ROWS, int NT>
-struct RowMajorLoad {
-    static constexpr int kQuads = ROWS / 4;
-    static constexpr int kBlocks = 8 * kQuads;
-    static constexpr int kPer = (kBlocks + NT - 1) / NT;
-    u32x2 r[kPer][8];
-
-    __device__ __forceinline__ void load(const uint16_t *base, int64_t ld, int row0, int rows_valid, int k0,
-                                         int k_valid)
-    {
-#pragma unroll
-        for (int b = 0; b < kPer; ++b) {
-            const int t = threadIdx.x + b * NT;
-            const int kg = t / kQuads, q = t - (t / kQuads) * kQuads;
-            const int grow = row0 + q * 4;
-            const bool ok = (t < kBlocks) && (grow < rows_valid);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int gk = k0 + kg * 8 + i;
-                if (ok && gk < k_valid)
-                    r[b][i] = *reinterpret_cast<const u32x2 *>(base + (int64_t)gk * ld + grow);
-                else
-                    r[b][i] = u32x2{0u, 0u};
-            }
-        }
-    }
-    __device__ __forceinline__ void store(char *lds) const
-    {
-#pragma unroll
-        for (int b = 0; b < kPer; ++b) {
-            const int t = threadIdx.x + b * NT;
-            if (t >= kBlocks)
-                continue;
-            const int kg = t / kQuads, q = t - (t / kQuads) * kQuads;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                u32x4 o;
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const uint32_t lo = r[b][2 * d][c >> 1], hi = r[b][2 * d + 1][c >> 1];
-                    o[d] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-                }
-                *reinterpret_cast<u32x4 *>(lds + swz(q * 4 + c, kg) * 16) = o;
-            }
-        }
-    }
-};
-
-template <bool KMAJ, int ROWS, int NT>
-struct LoaderOf {
-    using type = KMajorLoad<ROWS, NT>;
-};
-template <int ROWS, int NT>
-struct LoaderOf<false, ROWS, NT> {
-    using type = RowMajorLoad<ROWS, NT>;
-};
-
-// ------------------------------------------------------------------ GEMM core
-
-// C[m, n] = sum_k A(m, k) * B(n, k) for one BM x BN tile; the result stays in
-// registers: acc[mb][nb][r] is row m0 + wm*WTM + mb*32 + 8*(r/4) + 4*(lane/32) + r%4,
-// column n0 + wn*WTN + nb*32 + lane%32.
-template <int BM_, int BN_, int WM_, int WN_, bool AK, bool BKM>
-struct Gemm {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-    static constexpr int NT = WM * WN * 64;
-    static constexpr int WTM = BM / WM, WTN = BN / WN;
-    static constexpr int MB = WTM / 32, NB = WTN / 32;
-    static_assert(MB * 32 == WTM && NB * 32 == WTN, "wave tile");
-    static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
-    static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int LDS_BYTES = 2 * STAGE;
-    using ALoad = typename LoaderOf<AK, BM, NT>::type;
-    using BLoad = typename LoaderOf<BKM, BN, NT>::type;
-
-    __device__ __forceinline__ static int row_of(int wm, int mb, int r, int lane)
-    {
-        return wm * WTM + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    }
-    __device__ __forceinline__ static int col_of(int wn, int nb, int lane) { return wn * WTN + nb * 32 + (lane & 31); }
-
-    __device__ static void run(char *smem, const uint16_t *A, int64_t lda, int m0, int m_valid,
-                               const uint16_t *B, int64_t ldb, int n0, int n_valid, int k_begin, int k_end,
-                               f32x16 (&acc)[MB][NB])
-    {
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-        const int wm = wave / WN, wn = wave % WN;
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    acc[i][j][r] = 0.0f;
-        const int nk = (k_end - k_begin + kBK - 1) / kBK;
-        if (nk <= 0)
-            return;
-        ALoad la;
-        BLoad lb;
-        la.load(A, lda, m0, m_valid, k_begin, k_end);
-        lb.load(B, ldb, n0, n_valid, k_begin, k_end);
-        la.store(smem);
-        lb.store(smem + A_BYTES);
-        __syncthreads();
-        for (int kb = 0; kb < nk; ++kb) {
-            char *cur = smem + (kb & 1) * STAGE;
-            const bool more = kb + 1 < nk;
-            if (more) {
-                la.load(A, lda, m0, m_valid, k_begin + (kb + 1) * kBK, k_end);
-                lb.load(B, ldb, n0, n_valid, k_begin + (kb + 1) * kBK, k_end);
-            }
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int kc = ks * 2 + (lane >> 5);
-                bf16x8 af[MB], bfrag[NB];
-#pragma unroll
-                for (int i = 0; i < MB; ++i)
-                    af[i] = *reinterpret_cast<const bf16x8 *>(cur + swz(wm * WTM + i * 32 + (lane & 31), kc) * 16);
-#pragma unroll
-                for (int j = 0; j < NB; ++j)
-                    bfrag[j] = *reinterpret_cast<const bf16x8 *>(cur + A_BYTES +
-                                                                  swz(wn * WTN + j * 32 + (lane & 31), kc) * 16);
-#pragma unroll
-                for (int i = 0; i < MB; ++i)
-#pragma unroll
-                    for (int j = 0; j < NB; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfrag[j], acc[i][j], 0, 0, 0);
-            }
-            if (more) {
-                char *nxt = smem + ((kb + 1) & 1) * STAGE;
-                la.store(nxt);
-                lb.store(nxt + A_BYTES);
-            }
-            __syncthreads();
-        }
-    }
-};
 
 // ------------------------------------------------------------------ GEMM core, direct-to-LDS
 
@@ -561,10 +381,12 @@ struct GemmD {
 
     // S LDS stages.  While k-step kb is computed, the loads of step kb + S - 1 are issued
     // (a few per substep, interleaved with the MFMAs) into the stage step kb - 1 used.
-    // At the end of step kb the wave waits for step kb + 1 (steps kb+2 .. kb+S-1 may
-    // stay in flight) and the barrier retires stage kb.  Fragments are read one 16-deep
-    // substep ahead of the MFMAs that use them.  Steps past the end load zeros, which
-    // keeps the wait counts uniform.
+    // Fragments are read one 16-deep substep ahead of the MFMAs that use them.  Before
+    // the last substep's MFMAs the wave waits for step kb + 1 (steps kb+2 .. kb+S-1 may
+    // stay in flight) and the barrier retires stage kb (its last fragments are already
+    // in registers); those MFMAs then run while the first fragments of step kb + 1 are
+    // read, so no wave starts a step waiting on LDS.  Steps past the end load zeros,
+    // which keeps the wait counts uniform.
     __device__ static void run(char *smem, const uint16_t *A, int64_t lda, int m0, int m_valid, int ka_valid,
                                const uint16_t *B, int64_t ldb, int n0, int n_valid, int kb_valid, int k_begin,
                                int k_end, f32x16 (&acc)[MB][NB])
@@ -612,30 +434,37 @@ struct GemmD {
         __builtin_amdgcn_s_barrier();
         Frags f, fn;
         load_frags(smem, 0, wm, wn, lane, f);
-        for (int kb = 0; kb < nk; ++kb) {
+        auto step = [&](int kb, auto last_c) {
+            constexpr bool last = decltype(last_c)::value;
             const char *cur = smem + (kb % S) * STAGE;
             const int next = kb + S - 1;
             static_for<SUB>([&](auto ssc) {
                 constexpr int ss = decltype(ssc)::value;
                 constexpr int lo = ss * P < L ? ss * P : L;
                 constexpr int hi = (ss + 1) * P < L ? (ss + 1) * P : L;
-                if constexpr (ss + 1 < SUB)
-                    load_frags(cur, ss + 1, wm, wn, lane, fn);
                 if constexpr (lo < hi)
                     issue(next, std::integral_constant<int, lo>{}, std::integral_constant<int, hi>{});
-                mma(f, acc);
-                interleave<(ss + 1 < SUB) ? DS_PER_SUB : 0, hi - lo>();
-                if constexpr (ss + 1 < SUB)
+                if constexpr (ss + 1 < SUB) {
+                    load_frags(cur, ss + 1, wm, wn, lane, fn);
+                    mma(f, acc);
+                    interleave<DS_PER_SUB, hi - lo>();
                     f = fn;
+                } else if constexpr (!last) {
+                    wait_vmcnt<(S - 2) * L>();
+                    wait_lgkmcnt0();
+                    __builtin_amdgcn_s_barrier();
+                    load_frags(smem + ((kb + 1) % S) * STAGE, 0, wm, wn, lane, fn);
+                    mma(f, acc);
+                    interleave<DS_PER_SUB, 0>();
+                    f = fn;
+                } else {
+                    mma(f, acc);
+                }
             });
-            if (kb + 1 < nk) {
-                // step kb+1 has landed and this wave's reads of stage kb are done
-                wait_vmcnt<(S - 2) * L>();
-                wait_lgkmcnt0();
-                __builtin_amdgcn_s_barrier();
-                load_frags(smem + ((kb + 1) % S) * STAGE, 0, wm, wn, lane, f);
-            }
-        }
+        };
+        for (int kb = 0; kb + 1 < nk; ++kb)
+            step(kb, std::false_type{});
+        step(nk - 1, std::true_type{});
         // every wave is done reading LDS (and no load is in flight) before the caller reuses it
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -1149,19 +978,29 @@ __global__ __launch_bounds__(G::NT) void dw_kernel(DwParams p)
     G::run(smem, p.gT, p.Cpad, m0, p.Vpad, p.rows, p.hT, p.Cpad, n0, p.H, p.rows, 0, p.rows, acc);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / G::WN, wn = wave % G::WN;
+    // Each lane owns one hidden column of 16 * MB rows per fragment column.  When
+    // accumulating, all old values of a fragment column are read before any is written,
+    // so the reads are in flight together instead of each waiting behind the store
+    // before it.
 #pragma unroll
     for (int j = 0; j < G::NB; ++j) {
         const int col = n0 + G::col_of(wn, j, lane);
         if (col < p.H) {
+            float old[G::MB][16];
 #pragma unroll
             for (int i = 0; i < G::MB; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = m0 + G::row_of(wm, i, r, lane);
-                    if (row < p.V) {
-                        float *d = p.dW + (size_t)row * p.H + col;
-                        *d = p.accumulate ? *d + acc[i][j][r] : acc[i][j][r];
-                    }
+                    old[i][r] = (p.accumulate && row < p.V) ? p.dW[(size_t)row * p.H + col] : 0.0f;
+                }
+#pragma unroll
+            for (int i = 0; i < G::MB; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + G::row_of(wm, i, r, lane);
+                    if (row < p.V)
+                        p.dW[(size_t)row * p.H + col] = old[i][r] + acc[i][j][r];
                 }
         }
     }
