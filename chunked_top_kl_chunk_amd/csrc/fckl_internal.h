@@ -11,6 +11,11 @@ namespace fckl {
 // Token tile and vocabulary tile of the logit GEMMs (rows of W x tokens of h).
 constexpr int kVocabTile = 256;
 constexpr int kTokenTile = 256;
+// Hidden-dimension tile of the dH and dW products.  A hidden size that is not a
+// multiple (2880) leaves the last tile partly masked; measured on the 32K-token,
+// 201088-entry vocabulary shape, 256-wide tiles with that waste beat exact 192-wide ones
+// for dH (higher operand reuse per loaded byte) and tie for dW.
+constexpr int kHiddenTile = 256;
 constexpr int kMaxK = 128;
 constexpr int32_t kMaxChunk = 8192;
 constexpr size_t kDefaultBudget = size_t(12) << 30;  // 12 GiB of the 288 GB HBM3E
@@ -23,7 +28,6 @@ struct Layout {
     int32_t nVt = 0;        // vocabulary tiles: ceil(V / kVocabTile)
     int32_t Vpad = 0;       // nVt * kVocabTile (row pitch of g)
     int32_t cnt_stride = 0; // bytes per token of the per-tile entry-count table
-    int32_t dh_bn = 0;      // hidden-dimension tile of the dH / dW products (192 or 256)
     int32_t dh_splits = 0;  // vocabulary splits of the dH product
     size_t off_idx = 0;     // int32 [Cpad, K]   cached indices, sorted ascending per token
     size_t off_p = 0;       // f32   [Cpad, K]   teacher probabilities in the same order

@@ -21,8 +21,8 @@
 //   dw               dW += g^T . h_chunk (fp32 read-modify-write, chunk after chunk)
 //   transpose        W -> W^T once per backward call, h_chunk -> h_chunk^T per chunk
 //
-// GEMM core: 256 x 256 (or 256 x 192) tiles, 512 threads = 8 wave64s, each wave owns a
-// 128 x 64 (or 64 x 96) block of v_mfma_f32_32x32x16_bf16 accumulators.  Every operand
+// GEMM core: 256 x 256 tiles, 512 threads = 8 wave64s, each wave owns a 128 x 64 block
+// of v_mfma_f32_32x32x16_bf16 accumulators.  Every operand
 // is read k-major (contiguous along the reduction), which is why the backward products
 // use W^T, h_chunk^T and the second layout of g.  Each lane's 16-byte piece goes from
 // global memory straight into LDS (global_load_lds_dwordx4, no register staging); two
@@ -43,7 +43,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBK = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
@@ -52,13 +51,13 @@ constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// float -> bf16 bits, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint32_t bf16_rne(float f)
+// Two fp32 values -> packed bf16 pair (lo in bits 0-15), rounded to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return 0x7fc0u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -123,6 +122,12 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void copy16_to_lds(const void *src, char *lds_wave_base)
 {
     __builtin_amdgcn_global_load_lds(src, (lds_void_t *)lds_wave_base, 16, 0, 0);
+}
+
+// global_load_lds_dword: 4 bytes per lane to lds_wave_base + 4 * lane.
+__device__ __forceinline__ void copy4_to_lds(const void *src, char *lds_wave_base)
+{
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)lds_wave_base, 4, 0, 0);
 }
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt bits 3:0
@@ -301,9 +306,13 @@ struct TileOf<false, ROWS, BKK, NT> {
 // global -> LDS by the DMA path with S stages in flight (no staging registers).
 // Accumulator layout as in Gemm.  A k-major: A(m,k) = A[m*lda + k]; otherwise
 // A(m,k) = A[k*lda + m]; the same for B.
+struct NoHook {
+    __device__ __forceinline__ void operator()() const {}
+};
+
 template <int BM_, int BN_, int WM_, int WN_, bool AK, bool BKM, int BKK, int S>
 struct GemmD {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BKK;
     static constexpr int NT = WM * WN * 64;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int MB = WTM / 32, NB = WTN / 32;
@@ -386,10 +395,13 @@ struct GemmD {
     // stay in flight) and the barrier retires stage kb (its last fragments are already
     // in registers); those MFMAs then run while the first fragments of step kb + 1 are
     // read, so no wave starts a step waiting on LDS.  Steps past the end load zeros,
-    // which keeps the wait counts uniform.
+    // which keeps the wait counts uniform.  `hook` runs once, right after the first
+    // stage has landed: loads it issues are older than every k-step load, so the first
+    // step's wait covers them.
+    template <class Hook = NoHook>
     __device__ static void run(char *smem, const uint16_t *A, int64_t lda, int m0, int m_valid, int ka_valid,
                                const uint16_t *B, int64_t ldb, int n0, int n_valid, int kb_valid, int k_begin,
-                               int k_end, f32x16 (&acc)[MB][NB])
+                               int k_end, f32x16 (&acc)[MB][NB], const Hook &hook = Hook())
     {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int wm = wave / WN, wn = wave % WN;
@@ -402,6 +414,8 @@ struct GemmD {
                     acc[i][j][r] = 0.0f;
         const int nk = (k_end - k_begin + BKK - 1) / BKK;
         if (nk <= 0) {
+            hook();
+            __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             return;
         }
@@ -432,6 +446,7 @@ struct GemmD {
             issue(st, std::integral_constant<int, 0>{}, std::integral_constant<int, L>{});
         wait_vmcnt<(S - 2) * L>();
         __builtin_amdgcn_s_barrier();
+        hook();
         Frags f, fn;
         load_frags(smem, 0, wm, wn, lane, f);
         auto step = [&](int kb, auto last_c) {
@@ -475,9 +490,49 @@ struct GemmD {
 using LogitGemm = GemmD<256, 256, 2, 4, true, true, 64, 2>;
 static_assert(LogitGemm::BM == kVocabTile, "entry counts are kept per 256-row vocabulary tile");
 static_assert(kTokenTile % LogitGemm::BN == 0, "chunk padding covers whole token tiles");
-constexpr int kGStagePitch = 256 * 2 + 16;   // bytes per row of the bf16 g / g^T staging tiles
+constexpr int kGStagePitch = 256 * 2 + 16;   // bytes per token row of the staged bf16 g tile
 static_assert(LogitGemm::BM <= 256 && LogitGemm::BN <= 256, "staging tile");
 constexpr int kLogitLds = (LogitGemm::LDS_BYTES > 256 * kGStagePitch) ? LogitGemm::LDS_BYTES : 256 * kGStagePitch;
+
+// The first kPre cached entries of every token of a logit tile that fall into the tile's
+// vocabulary rows (index and, for the backward, teacher probability) are copied into
+// LDS, behind the GEMM operands, while the main loop runs.  The epilogues then find
+// them without a global load that has to wait for the entry count first; a token with
+// more entries in one tile (rare) reads the rest from global memory.
+constexpr int kPre = LogitGemm::NT / LogitGemm::BN;
+constexpr int kPreLds = 2 * LogitGemm::NT * 4;
+static_assert(kPre * LogitGemm::BN == LogitGemm::NT, "one prefetched entry per thread");
+static_assert(kLogitLds + kPreLds <= 160 * 1024, "LDS");
+
+struct EntryPrefetch {
+    const void *src_idx = nullptr, *src_p = nullptr;
+
+    // Thread t takes entry (start + t / BN) of token n0 + t % BN.
+    __device__ __forceinline__ void init(const uint8_t *cnt, int cnt_stride, int tm, int n0, int rows, int K,
+                                         const int32_t *idx_s, const float *p_s)
+    {
+        const int nl = threadIdx.x % LogitGemm::BN, slot = threadIdx.x / LogitGemm::BN;
+        const int tok = n0 + nl;
+        if (tok < rows) {
+            const uint8_t *c = cnt + (size_t)tok * cnt_stride + tm;
+            const int e = c[0] + slot;
+            if (e < c[1]) {
+                src_idx = idx_s + (size_t)tok * K + e;
+                if (p_s)
+                    src_p = p_s + (size_t)tok * K + e;
+            }
+        }
+    }
+    // Copies into pre[0 .. NT) (indices) and pre[NT .. 2 NT) (probabilities).
+    __device__ __forceinline__ void issue(char *pre) const
+    {
+        char *base = pre + (threadIdx.x & ~63) * 4;
+        if (src_idx)
+            copy4_to_lds(src_idx, base);
+        if (src_p)
+            copy4_to_lds(src_p, base + LogitGemm::NT * 4);
+    }
+};
 
 // Select acc[mb][nb][r] for a run-time (mb*16 + r) without indexing registers.
 template <int MB, int NB>
@@ -634,12 +689,15 @@ struct FwdParams {
 __global__ __launch_bounds__(LogitGemm::NT) void forward_logits_kernel(FwdParams p)
 {
     using G = LogitGemm;
-    __shared__ __attribute__((aligned(16))) char smem[kLogitLds];
+    __shared__ __attribute__((aligned(16))) char smem[kLogitLds + kPreLds];
     int tm, tn;
     map_tile(blockIdx.x, p.nVt, p.nNt, 4, tm, tn);
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / G::WN, wn = wave % G::WN;
+    char *pre = smem + kLogitLds;
+    EntryPrefetch pf;
+    pf.init(p.cnt, p.cnt_stride, tm, n0, p.rows, p.K, p.idx_s, nullptr);
 
     // Entry range of this vocabulary tile for each of the lane's tokens.
     int cs[G::NB], ce[G::NB];
@@ -655,7 +713,7 @@ __global__ __launch_bounds__(LogitGemm::NT) void forward_logits_kernel(FwdParams
     }
 
     f32x16 acc[G::MB][G::NB];
-    G::run(smem, p.W, p.H, m0, p.V, p.H, p.h, p.H, n0, p.rows, p.H, 0, p.H, acc);
+    G::run(smem, p.W, p.H, m0, p.V, p.H, p.h, p.H, n0, p.rows, p.H, 0, p.H, acc, [&] { pf.issue(pre); });
 
     // Per token, over the wave's 128 vocabulary rows: max and sum of 2^(z*log2e/T - max).
     float *red = reinterpret_cast<float *>(smem);   // [WM][BN][2]
@@ -698,11 +756,12 @@ __global__ __launch_bounds__(LogitGemm::NT) void forward_logits_kernel(FwdParams
     }
     // Pick z at the cached indices this tile owns: the lane holding that row writes it.
     const int wrow0 = m0 + wm * G::WTM;
+    const int32_t *pre_idx = reinterpret_cast<const int32_t *>(pre);
 #pragma unroll
     for (int j = 0; j < G::NB; ++j) {
-        const int tok = n0 + G::col_of(wn, j, lane);
+        const int nl = G::col_of(wn, j, lane), tok = n0 + nl;
         for (int e = cs[j]; e < ce[j]; ++e) {
-            const int v = p.idx_s[(size_t)tok * p.K + e];
+            const int v = (e - cs[j] < kPre) ? pre_idx[(e - cs[j]) * G::BN + nl] : p.idx_s[(size_t)tok * p.K + e];
             const int row = v - wrow0;
             if (row >= 0 && row < G::WTM && v < p.V) {
                 const int r32 = row & 31;
@@ -796,12 +855,15 @@ struct BwdParams {
 __global__ __launch_bounds__(LogitGemm::NT) void backward_logits_kernel(BwdParams p)
 {
     using G = LogitGemm;
-    __shared__ __attribute__((aligned(16))) char smem[kLogitLds];
+    __shared__ __attribute__((aligned(16))) char smem[kLogitLds + kPreLds];
     int tm, tn;
     map_tile(blockIdx.x, p.nVt, p.nNt, 4, tm, tn);
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / G::WN, wn = wave % G::WN;
+    char *pre = smem + kLogitLds;
+    EntryPrefetch pf;
+    pf.init(p.cnt, p.cnt_stride, tm, n0, p.rows, p.K, p.idx_s, p.p_s);
 
     int cs[G::NB], ce[G::NB];
     float l2[G::NB], amp[G::NB];
@@ -821,7 +883,7 @@ __global__ __launch_bounds__(LogitGemm::NT) void backward_logits_kernel(BwdParam
     }
 
     f32x16 acc[G::MB][G::NB];
-    G::run(smem, p.W, p.H, m0, p.V, p.H, p.h, p.H, n0, p.rows, p.H, 0, p.H, acc);
+    G::run(smem, p.W, p.H, m0, p.V, p.H, p.h, p.H, n0, p.rows, p.H, 0, p.H, acc, [&] { pf.issue(pre); });
 
     // g = coef * ((sum p) * exp(z/T - lse) - scatter(p, idx)); zero outside [0,V) x [0,rows).
 #pragma unroll
@@ -836,17 +898,21 @@ __global__ __launch_bounds__(LogitGemm::NT) void backward_logits_kernel(BwdParam
             }
     }
     const int wrow0 = m0 + wm * G::WTM;
+    const int32_t *pre_idx = reinterpret_cast<const int32_t *>(pre);
+    const float *pre_p = reinterpret_cast<const float *>(pre + G::NT * 4);
 #pragma unroll
     for (int j = 0; j < G::NB; ++j) {
-        const int tok = n0 + G::col_of(wn, j, lane);
+        const int nl = G::col_of(wn, j, lane), tok = n0 + nl;
         for (int e = cs[j]; e < ce[j]; ++e) {
-            const int v = p.idx_s[(size_t)tok * p.K + e];
+            const bool in_lds = e - cs[j] < kPre;
+            const int v = in_lds ? pre_idx[(e - cs[j]) * G::BN + nl] : p.idx_s[(size_t)tok * p.K + e];
             const int row = v - wrow0;
             if (row >= 0 && row < G::WTM && v < p.V) {
                 const int r32 = row & 31;
                 if (((r32 >> 2) & 1) == (lane >> 5)) {
                     const int sel = (row >> 5) * 16 + ((r32 >> 3) << 2) + (r32 & 3);
-                    sub_at(acc, j, sel, p.coef * p.p_s[(size_t)tok * p.K + e]);
+                    const float pe = in_lds ? pre_p[(e - cs[j]) * G::BN + nl] : p.p_s[(size_t)tok * p.K + e];
+                    sub_at(acc, j, sel, p.coef * pe);
                 }
             }
         }
@@ -862,8 +928,8 @@ __global__ __launch_bounds__(LogitGemm::NT) void backward_logits_kernel(BwdParam
             for (int q = 0; q < 4; ++q) {
                 const int ml = G::row_of(wm, i, 4 * q, lane);
                 u32x2 pk;
-                pk[0] = bf16_rne(acc[i][j][4 * q + 0]) | (bf16_rne(acc[i][j][4 * q + 1]) << 16);
-                pk[1] = bf16_rne(acc[i][j][4 * q + 2]) | (bf16_rne(acc[i][j][4 * q + 3]) << 16);
+                pk[0] = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
+                pk[1] = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
                 *reinterpret_cast<u32x2 *>(smem + nl * kGStagePitch + ml * 2) = pk;
             }
     }
@@ -876,26 +942,28 @@ __global__ __launch_bounds__(LogitGemm::NT) void backward_logits_kernel(BwdParam
         const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + nl * kGStagePitch + col * 2);
         *reinterpret_cast<u32x4 *>(p.g + (size_t)(n0 + nl) * p.Vpad + m0 + col) = v;
     }
-    // The same tile transposed, [vocab][token], for the dW product.
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < G::NB; ++j) {
-        const int nl = G::col_of(wn, j, lane);
-#pragma unroll
-        for (int i = 0; i < G::MB; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int ml = G::row_of(wm, i, r, lane);
-                *reinterpret_cast<uint16_t *>(smem + ml * kGStagePitch + nl * 2) = (uint16_t)bf16_rne(acc[i][j][r]);
-            }
-    }
-    __syncthreads();
-    constexpr int kColChunks = G::BN / 8;       // 16-byte pieces per vocabulary row of the tile
-#pragma unroll 4
-    for (int c = threadIdx.x; c < kChunks; c += G::NT) {
-        const int ml = c / kColChunks, col = (c % kColChunks) * 8;
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + ml * kGStagePitch + col * 2);
-        *reinterpret_cast<u32x4 *>(p.gT + (size_t)(m0 + ml) * p.Cpad + n0 + col) = v;
+    // The same tile transposed, [vocab][token], for the dW product, read back from the
+    // staged [token][vocab] tile with transposing LDS reads: in a 16-lane group, lane l
+    // addresses the 8-byte piece of token row t + l/4 at vocabulary columns v + 4(l%4),
+    // and every lane receives 4 consecutive tokens of vocabulary column v + l.  Two such
+    // reads give a lane 8 tokens = one 16-byte piece of a g^T row.  A wave covers 16
+    // vocabulary rows x 32 tokens per step (its 4 groups take 8 tokens each).
+    constexpr int kTokBlocks = G::BN / 32;
+    constexpr int kBlocks = (G::BM / 16) * kTokBlocks;
+    const int grp = lane >> 4, gl = lane & 15;
+#pragma unroll 2
+    for (int b = wave; b < kBlocks; b += G::NT / 64) {
+        const int vb = (b / kTokBlocks) * 16, tb = (b % kTokBlocks) * 32 + grp * 8;
+        const char *src = smem + (tb + (gl >> 2)) * kGStagePitch + (vb + 4 * (gl & 3)) * 2;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(src));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4 *)(src + 4 * kGStagePitch));
+        u32x4 v;
+        v[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+        v[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+        v[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+        v[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+        *reinterpret_cast<u32x4 *>(p.gT + (size_t)(m0 + vb + gl) * p.Cpad + n0 + tb) = v;
     }
 }
 
@@ -1006,10 +1074,8 @@ __global__ __launch_bounds__(G::NT) void dw_kernel(DwParams p)
     }
 }
 
-using DGemm256 = GemmD<256, 256, 2, 4, true, true, 64, 2>;   // dH, hidden tile 256
-using DGemm192 = GemmD<256, 192, 4, 2, true, true, 64, 2>;   // dH, hidden tile 192
-using WGemm256 = GemmD<256, 256, 2, 4, true, true, 64, 2>;   // dW, hidden tile 256
-using WGemm192 = GemmD<256, 192, 4, 2, true, true, 64, 2>;   // dW, hidden tile 192
+using DGemm = GemmD<256, kHiddenTile, 2, 4, true, true, 64, 2>;   // dH: tokens x hidden, k = vocabulary
+using WGemm = GemmD<256, kHiddenTile, 2, 4, true, true, 64, 2>;   // dW: vocabulary x hidden, k = tokens
 
 // dst[c][r] = src[r][c] for r < rows, c < cols; dst[c][r] = 0 for rows <= r < rpad.
 // 64 x 64 tiles through LDS so that both sides are read and written along rows.
@@ -1149,7 +1215,7 @@ int launch_backward_logits(const ChunkArgs &a, const float *lse, float coef, voi
 static void dh_splits(const ChunkArgs &a, int &ksplit, int &used)
 {
     const Layout &L = *a.L;
-    ksplit = ((L.Vpad + L.dh_splits - 1) / L.dh_splits + kBK - 1) / kBK * kBK;
+    ksplit = ((L.Vpad + L.dh_splits - 1) / L.dh_splits + DGemm::BK - 1) / DGemm::BK * DGemm::BK;
     used = (a.V + ksplit - 1) / ksplit;
 }
 
@@ -1165,15 +1231,12 @@ int launch_dh(const ChunkArgs &a, void *stream)
     p.rows = a.rows;
     p.Cpad = L.Cpad;
     p.nMt = (a.rows + 255) / 256;
-    p.nNt = (a.H + L.dh_bn - 1) / L.dh_bn;
+    p.nNt = (a.H + kHiddenTile - 1) / kHiddenTile;
     int used = 0;
     dh_splits(a, p.ksplit, used);
     p.part = reinterpret_cast<float *>(a.ws + L.off_dhp);
     dim3 grid(p.nMt * p.nNt, used);
-    if (L.dh_bn == 256)
-        hipLaunchKernelGGL(dh_kernel<DGemm256>, grid, dim3(DGemm256::NT), 0, S(stream), p);
-    else
-        hipLaunchKernelGGL(dh_kernel<DGemm192>, grid, dim3(DGemm192::NT), 0, S(stream), p);
+    hipLaunchKernelGGL(dh_kernel<DGemm>, grid, dim3(DGemm::NT), 0, S(stream), p);
     return (int)hipGetLastError();
 }
 
@@ -1201,14 +1264,11 @@ int launch_dw(const ChunkArgs &a, float *dW, bool accumulate, void *stream)
     p.Cpad = L.Cpad;
     p.rows = a.rows;
     p.nMt = L.nVt;
-    p.nNt = (a.H + L.dh_bn - 1) / L.dh_bn;
+    p.nNt = (a.H + kHiddenTile - 1) / kHiddenTile;
     p.accumulate = accumulate ? 1 : 0;
     p.dW = dW;
     dim3 grid(p.nMt * p.nNt);
-    if (L.dh_bn == 256)
-        hipLaunchKernelGGL(dw_kernel<WGemm256>, grid, dim3(WGemm256::NT), 0, S(stream), p);
-    else
-        hipLaunchKernelGGL(dw_kernel<WGemm192>, grid, dim3(WGemm192::NT), 0, S(stream), p);
+    hipLaunchKernelGGL(dw_kernel<WGemm>, grid, dim3(WGemm::NT), 0, S(stream), p);
     return (int)hipGetLastError();
 }
 

@@ -37,25 +37,14 @@ fckl_status check_desc(const fckl_desc *d)
     return FCKL_OK;
 }
 
-// Hidden-dimension tile of the dH / dW products: 256 when it divides H, else 192 when
-// that does, else 256 with a masked tail.
-static int32_t hidden_tile(int32_t H)
-{
-    if (H % 256 == 0)
-        return 256;
-    if (H % 192 == 0)
-        return 192;
-    return 256;
-}
-
 // Number of vocabulary splits of the dH product (its reduction runs over V).  Each
 // split streams a V/S slice of W; enough splits keep that slice inside the 256 MB
 // last-level cache, and among the candidates the one whose work-group count
 // best fills whole waves of the 256 compute units wins.  At least 4 k-steps of 64 per
 // split; at most 32 splits.
-static int32_t dh_split_count(int32_t Cpad, int32_t H, int32_t bn, int32_t Vpad)
+static int32_t dh_split_count(int32_t Cpad, int32_t H, int32_t Vpad)
 {
-    const int64_t tiles = (int64_t)(Cpad / kTokenTile) * ((H + bn - 1) / bn);
+    const int64_t tiles = (int64_t)(Cpad / kTokenTile) * ((H + kHiddenTile - 1) / kHiddenTile);
     const int64_t slice_cap = (int64_t)192 << 20;                    // bytes of W per split
     int64_t smin = ((int64_t)Vpad * H * 2 + slice_cap - 1) / slice_cap;
     int64_t smax = std::min<int64_t>(32, Vpad / 256);
@@ -90,8 +79,7 @@ fckl_status make_layout(const fckl_desc *d, int32_t chunk, Layout *L)
     o.nVt = (d->V + kVocabTile - 1) / kVocabTile;
     o.Vpad = o.nVt * kVocabTile;
     o.cnt_stride = (int32_t)align_up((size_t)o.nVt + 1, 16);
-    o.dh_bn = hidden_tile(d->H);
-    o.dh_splits = dh_split_count(o.Cpad, d->H, o.dh_bn, o.Vpad);
+    o.dh_splits = dh_split_count(o.Cpad, d->H, o.Vpad);
     const size_t Cp = (size_t)o.Cpad, K = (size_t)d->K;
     size_t off = 0;
     auto take = [&](size_t bytes) {
