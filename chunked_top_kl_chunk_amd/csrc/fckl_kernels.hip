@@ -716,34 +716,42 @@ __global__ __launch_bounds__(LogitGemm::NT) void forward_logits_kernel(FwdParams
     G::run(smem, p.W, p.H, m0, p.V, p.H, p.h, p.H, n0, p.rows, p.H, 0, p.H, acc, [&] { pf.issue(pre); });
 
     // Per token, over the wave's 128 vocabulary rows: max and sum of 2^(z*log2e/T - max).
+    // Every tile but the last vocabulary tile skips the row check.
     float *red = reinterpret_cast<float *>(smem);   // [WM][BN][2]
+    auto reduce = [&](auto interior_c) {
+        constexpr bool interior = decltype(interior_c)::value;
 #pragma unroll
-    for (int j = 0; j < G::NB; ++j) {
-        float mx = kNegInf;
+        for (int j = 0; j < G::NB; ++j) {
+            float mx = kNegInf;
 #pragma unroll
-        for (int i = 0; i < G::MB; ++i)
+            for (int i = 0; i < G::MB; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const bool in = m0 + G::row_of(wm, i, r, lane) < p.V;
-                mx = fmaxf(mx, in ? acc[i][j][r] * p.scale2 : kNegInf);
+                for (int r = 0; r < 16; ++r) {
+                    const bool in = interior || m0 + G::row_of(wm, i, r, lane) < p.V;
+                    mx = fmaxf(mx, in ? acc[i][j][r] * p.scale2 : kNegInf);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float ms = (mx == kNegInf) ? 0.0f : mx;
+            float sum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < G::MB; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const bool in = interior || m0 + G::row_of(wm, i, r, lane) < p.V;
+                    sum += in ? fast_exp2(acc[i][j][r] * p.scale2 - ms) : 0.0f;
+                }
+            sum += __shfl_xor(sum, 32);
+            if (lane < 32) {
+                const int nl = G::col_of(wn, j, lane);
+                red[(wm * G::BN + nl) * 2 + 0] = mx;
+                red[(wm * G::BN + nl) * 2 + 1] = sum;
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float ms = (mx == kNegInf) ? 0.0f : mx;
-        float sum = 0.0f;
-#pragma unroll
-        for (int i = 0; i < G::MB; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const bool in = m0 + G::row_of(wm, i, r, lane) < p.V;
-                sum += in ? fast_exp2(acc[i][j][r] * p.scale2 - ms) : 0.0f;
-            }
-        sum += __shfl_xor(sum, 32);
-        if (lane < 32) {
-            const int nl = G::col_of(wn, j, lane);
-            red[(wm * G::BN + nl) * 2 + 0] = mx;
-            red[(wm * G::BN + nl) * 2 + 1] = sum;
         }
-    }
+    };
+    if (m0 + G::BM <= p.V)
+        reduce(std::true_type{});
+    else
+        reduce(std::false_type{});
     __syncthreads();
     for (int nl = threadIdx.x; nl < G::BN; nl += G::NT) {
         if (n0 + nl < p.rows) {
@@ -886,14 +894,18 @@ __global__ __launch_bounds__(LogitGemm::NT) void backward_logits_kernel(BwdParam
     G::run(smem, p.W, p.H, m0, p.V, p.H, p.h, p.H, n0, p.rows, p.H, 0, p.H, acc, [&] { pf.issue(pre); });
 
     // g = coef * ((sum p) * exp(z/T - lse) - scatter(p, idx)); zero outside [0,V) x [0,rows).
+    // The row test is against a per-lane limit: element (i, r) sits row_of(wm, i, r, lane)
+    // = row_of(wm, 0, 0, lane) + 32 i + 8 (r / 4) + r % 4, so it is inside when that
+    // constant offset is below V - m0 - row_of(wm, 0, 0, lane) (and -1 for a padded token).
 #pragma unroll
     for (int j = 0; j < G::NB; ++j) {
         const bool tok_in = n0 + G::col_of(wn, j, lane) < p.rows;
+        const int lim = tok_in ? p.V - m0 - G::row_of(wm, 0, 0, lane) : -1;
 #pragma unroll
         for (int i = 0; i < G::MB; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const bool in = tok_in && (m0 + G::row_of(wm, i, r, lane) < p.V);
+                const bool in = 32 * i + 8 * (r >> 2) + (r & 3) < lim;
                 acc[i][j][r] = in ? amp[j] * fast_exp2(acc[i][j][r] * p.scale2 - l2[j]) : 0.0f;
             }
     }
