@@ -28,6 +28,8 @@
 // global memory straight into LDS (global_load_lds_dwordx4, no register staging); two
 // LDS stages of 64-deep k-steps, one barrier per step, and an XOR swizzle of the
 // 16-byte chunks that keeps the MFMA operand reads free of bank conflicts.
+// The two logit kernels are persistent (one work-group per compute unit looping over
+// tiles), which removes the per-work-group dispatch gap between tiles.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -686,12 +688,11 @@ struct FwdParams {
     float2 *part;           // [nVt, Cpad]
 };
 
-__global__ __launch_bounds__(LogitGemm::NT) void forward_logits_kernel(FwdParams p)
+__device__ __forceinline__ void forward_tile(const FwdParams &p, char *smem, int t)
 {
     using G = LogitGemm;
-    __shared__ __attribute__((aligned(16))) char smem[kLogitLds + kPreLds];
     int tm, tn;
-    map_tile(blockIdx.x, p.nVt, p.nNt, 4, tm, tn);
+    map_tile(t, p.nVt, p.nNt, 4, tm, tn);
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / G::WN, wn = wave % G::WN;
@@ -782,6 +783,19 @@ __global__ __launch_bounds__(LogitGemm::NT) void forward_logits_kernel(FwdParams
     }
 }
 
+// Persistent: one work-group per compute unit walks the tiles b, b + grid, ...  The
+// grid is a multiple of 8, so all tiles of a work-group map to its own XCD, and the
+// XCD's work-groups move through its tile range together, as one wave of
+// non-persistent work-groups would.
+__global__ __launch_bounds__(LogitGemm::NT) void forward_logits_kernel(FwdParams p)
+{
+    __shared__ __attribute__((aligned(16))) char smem[kLogitLds + kPreLds];
+    for (int t = blockIdx.x; t < p.nVt * p.nNt; t += gridDim.x) {
+        forward_tile(p, smem, t);
+        __syncthreads();    // every wave is done with LDS before the next tile's loads land
+    }
+}
+
 // ------------------------------------------------------------------ combine
 
 struct CombineParams {
@@ -860,12 +874,11 @@ struct BwdParams {
     uint16_t *gT;           // [Vpad, Cpad] bf16
 };
 
-__global__ __launch_bounds__(LogitGemm::NT) void backward_logits_kernel(BwdParams p)
+__device__ __forceinline__ void backward_tile(const BwdParams &p, char *smem, int t)
 {
     using G = LogitGemm;
-    __shared__ __attribute__((aligned(16))) char smem[kLogitLds + kPreLds];
     int tm, tn;
-    map_tile(blockIdx.x, p.nVt, p.nNt, 4, tm, tn);
+    map_tile(t, p.nVt, p.nNt, 4, tm, tn);
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / G::WN, wn = wave % G::WN;
@@ -976,6 +989,15 @@ __global__ __launch_bounds__(LogitGemm::NT) void backward_logits_kernel(BwdParam
         v[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
         v[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
         *reinterpret_cast<u32x4 *>(p.gT + (size_t)(m0 + vb + gl) * p.Cpad + n0 + tb) = v;
+    }
+}
+
+__global__ __launch_bounds__(LogitGemm::NT) void backward_logits_kernel(BwdParams p)
+{
+    __shared__ __attribute__((aligned(16))) char smem[kLogitLds + kPreLds];
+    for (int t = blockIdx.x; t < p.nVt * p.nNt; t += gridDim.x) {
+        backward_tile(p, smem, t);
+        __syncthreads();
     }
 }
 
@@ -1120,6 +1142,25 @@ __global__ void zero_u32_kernel(uint32_t *p, int n)
 
 static inline hipStream_t S(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Work-groups of a persistent logit kernel: one per compute unit of the current device
+// (rounded up to a multiple of the 8 XCDs), never more than there are tiles.
+static int persistent_grid(int tiles)
+{
+    static int cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        dev = -1;
+    int n = dev >= 0 ? cus[dev] : 0;
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess || n <= 0)
+            n = 256;
+        n = (n + 7) / 8 * 8;
+        if (dev >= 0)
+            cus[dev] = n;
+    }
+    return tiles < n ? tiles : n;
+}
+
 int launch_prepare(const ChunkArgs &a, bool validate, void *stream)
 {
     const Layout &L = *a.L;
@@ -1164,7 +1205,7 @@ int launch_forward_logits(const ChunkArgs &a, void *stream)
     p.cnt = reinterpret_cast<const uint8_t *>(a.ws + L.off_cnt);
     p.zk = reinterpret_cast<float *>(a.ws + L.off_zk);
     p.part = reinterpret_cast<float2 *>(a.ws + L.off_part);
-    hipLaunchKernelGGL(forward_logits_kernel, dim3(p.nVt * p.nNt), dim3(LogitGemm::NT), 0, S(stream), p);
+    hipLaunchKernelGGL(forward_logits_kernel, dim3(persistent_grid(p.nVt * p.nNt)), dim3(LogitGemm::NT), 0, S(stream), p);
     return (int)hipGetLastError();
 }
 
@@ -1218,7 +1259,7 @@ int launch_backward_logits(const ChunkArgs &a, const float *lse, float coef, voi
     p.cnt = reinterpret_cast<const uint8_t *>(a.ws + L.off_cnt);
     p.g = reinterpret_cast<uint16_t *>(a.ws + L.off_g);
     p.gT = reinterpret_cast<uint16_t *>(a.ws + L.off_gT);
-    hipLaunchKernelGGL(backward_logits_kernel, dim3(p.nVt * p.nNt), dim3(LogitGemm::NT), 0, S(stream), p);
+    hipLaunchKernelGGL(backward_logits_kernel, dim3(persistent_grid(p.nVt * p.nNt)), dim3(LogitGemm::NT), 0, S(stream), p);
     return (int)hipGetLastError();
 }
 
