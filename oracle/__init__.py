@@ -58,6 +58,11 @@ def _load() -> ctypes.CDLL:
         lib.fckl_oracle_loss_mean.restype = ctypes.c_int
         lib.fckl_oracle_backward.argtypes = [i64, i64, i64, i64, f64, vp, vp, vp, vp, f64, i64, i64, vp, vp, vp]
         lib.fckl_oracle_backward.restype = ctypes.c_int
+        lib.fckl_oracle_weighted_mean.argtypes = [i64, i64, i64, i64, f64, vp, vp, vp, vp, vp, vp]
+        lib.fckl_oracle_weighted_mean.restype = ctypes.c_int
+        lib.fckl_oracle_weighted_backward.argtypes = [i64, i64, i64, i64, f64, vp, vp, vp, vp, vp, f64, i64, vp,
+                                                      vp, vp]
+        lib.fckl_oracle_weighted_backward.restype = ctypes.c_int
         lib.fckl_oracle_num_threads.argtypes = []
         lib.fckl_oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -132,6 +137,37 @@ def backward(h, W, idx, tl, T: float, grad_scale: float = 1.0, n_norm: Optional[
     _check(_load().fckl_oracle_backward(N, H, V, K, float(T), _ptr(h), _ptr(W), _ptr(idx), _ptr(tl),
                                         float(grad_scale), int(N if n_norm is None else n_norm),
                                         nrows, _ptr(r), _ptr(dH), _ptr(dW)))
+    return dH, dW
+
+
+def weighted_mean(h, W, idx, tl, T: float, w) -> float:
+    """sum_i w[i] loss[i] / sum_i w[i] over all tokens (0 when every weight is 0)."""
+    h, W, idx, tl, w = _f64(h), _f64(W), _i32(idx), _f64(tl), _f64(w)
+    N, H, V, K = _shapes(h, W, idx, tl)
+    if w.shape != (N,):
+        raise ValueError("weights must have shape (N,)")
+    out = np.zeros(1, np.float64)
+    _check(_load().fckl_oracle_weighted_mean(N, H, V, K, float(T), _ptr(h), _ptr(W), _ptr(idx), _ptr(tl), _ptr(w),
+                                             _ptr(out)))
+    return float(out[0])
+
+
+def weighted_backward(h, W, idx, tl, T: float, w, grad_scale: float = 1.0, rows=None, want_dH: bool = True,
+                      want_dW: bool = True):
+    """Gradients of grad_scale * weighted mean loss; row i scaled by w[i] / sum_j w[j].
+
+    Returns (dH[nrows, H] or None, dW[V, H] or None), float64; dW sums the selected rows.
+    """
+    h, W, idx, tl, w = _f64(h), _f64(W), _i32(idx), _f64(tl), _f64(w)
+    N, H, V, K = _shapes(h, W, idx, tl)
+    if w.shape != (N,):
+        raise ValueError("weights must have shape (N,)")
+    r = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    nrows = N if r is None else r.shape[0]
+    dH = np.empty((nrows, H), np.float64) if want_dH else None
+    dW = np.empty((V, H), np.float64) if want_dW else None
+    _check(_load().fckl_oracle_weighted_backward(N, H, V, K, float(T), _ptr(h), _ptr(W), _ptr(idx), _ptr(tl),
+                                                 _ptr(w), float(grad_scale), nrows, _ptr(r), _ptr(dH), _ptr(dW)))
     return dH, dW
 
 

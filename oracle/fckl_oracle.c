@@ -37,6 +37,13 @@
  * not their values, so the oracle does not chunk ("Breaking the Bottleneck ...",
  * axbrief.com: one slice of the sequence at a time, then discarded).
  *
+ * Token masks and per-token weights (the weighted reduction below) change only the
+ * reduction: with weights w[i] >= 0 the reported loss is
+ *      sum_i w[i] loss[i] / sum_i w[i]     (0 when every weight is 0),
+ * a masked token being one with w[i] = 0, and step 6 scales row i by
+ * grad_scale * T * w[i] / sum_j w[j] instead of grad_scale * T / N.  All weights 1
+ * give the plain mean.
+ *
  * Inputs are double arrays, row-major: h[N*H], W[V*H], idx[N*K] (int32),
  * tl[N*K].  A row list (rows, nrows) selects which tokens are evaluated; rows ==
  * NULL means all N tokens in order.  Return value 0 on success, negative on a
@@ -193,28 +200,22 @@ int fckl_oracle_loss_mean(int64_t N, int64_t H, int64_t V, int64_t K, double T,
 }
 
 /*
- * Backward (steps 6-7) of grad_scale * (1/n_norm) * sum over the selected rows
- * of loss[i].  With rows == NULL and n_norm == N this is the gradient of
- * grad_scale * mean loss.  dH_out[r*H + j] is the gradient for row rows[r];
- * dW_out[V*H] receives the sum over the selected rows only (it is overwritten).
- * Either output may be NULL.
+ * Steps 6-7 for the selected rows, row r's gradient scaled by row_scale[r]:
+ *   g[r,v] = row_scale[r] * ( (sum_k p[k]) exp(z[v]/T - lse) - sum_k p[k] [idx[k] == v] ).
+ * dH_out[r*H + j] is the gradient for row rows[r]; dW_out[V*H] receives the sum over
+ * the selected rows only (it is overwritten).  Either output may be NULL.
  */
-int fckl_oracle_backward(int64_t N, int64_t H, int64_t V, int64_t K, double T,
+static int backward_rows(int64_t N, int64_t H, int64_t V, int64_t K, double T,
                          const double *h, const double *W, const int32_t *idx,
-                         const double *tl, double grad_scale, int64_t n_norm,
+                         const double *tl, const double *row_scale,
                          int64_t nrows, const int64_t *rows,
                          double *dH_out, double *dW_out)
 {
-    int rc = check_args(N, H, V, K, T, h, W, idx, tl, nrows, rows);
-    if (rc)
-        return rc;
-    if (n_norm <= 0)
-        return ORACLE_EARG;
+    (void)N;
     /* g for every selected row, held whole: nrows * V doubles. */
     double *g = (double *)malloc(sizeof(double) * (size_t)(nrows > 0 ? nrows : 1) * (size_t)V);
     if (!g)
         return ORACLE_EMEM;
-    const double scale = grad_scale * T / (double)n_norm;
     int failed = 0;
 #pragma omp parallel
     {
@@ -232,6 +233,7 @@ int fckl_oracle_backward(int64_t N, int64_t H, int64_t V, int64_t K, double T,
                 continue;
             {
                 int64_t i = rows ? rows[r] : r;
+                const double scale = row_scale[r];
                 teacher_distribution(K, T, tl + i * K, p, lp);
                 student_logits(H, V, h + i * H, W, z);
                 double lse = logsumexp_over_vocab(V, T, z);
@@ -285,6 +287,102 @@ int fckl_oracle_backward(int64_t N, int64_t H, int64_t V, int64_t K, double T,
     }
     free(g);
     return ORACLE_OK;
+}
+
+/*
+ * Backward (steps 6-7) of grad_scale * (1/n_norm) * sum over the selected rows
+ * of loss[i].  With rows == NULL and n_norm == N this is the gradient of
+ * grad_scale * mean loss.
+ */
+int fckl_oracle_backward(int64_t N, int64_t H, int64_t V, int64_t K, double T,
+                         const double *h, const double *W, const int32_t *idx,
+                         const double *tl, double grad_scale, int64_t n_norm,
+                         int64_t nrows, const int64_t *rows,
+                         double *dH_out, double *dW_out)
+{
+    int rc = check_args(N, H, V, K, T, h, W, idx, tl, nrows, rows);
+    if (rc)
+        return rc;
+    if (n_norm <= 0)
+        return ORACLE_EARG;
+    double *scale = (double *)malloc(sizeof(double) * (size_t)(nrows > 0 ? nrows : 1));
+    if (!scale)
+        return ORACLE_EMEM;
+    for (int64_t r = 0; r < nrows; ++r)
+        scale[r] = grad_scale * T / (double)n_norm;
+    rc = backward_rows(N, H, V, K, T, h, W, idx, tl, scale, nrows, rows, dH_out, dW_out);
+    free(scale);
+    return rc;
+}
+
+/* sum_i w[i] over all N tokens; ORACLE_EARG for a negative or non-finite weight. */
+static int weight_sum(int64_t N, const double *w, double *sum)
+{
+    if (!w)
+        return ORACLE_EARG;
+    double s = 0.0;
+    for (int64_t i = 0; i < N; ++i) {
+        if (!(w[i] >= 0.0) || isinf(w[i]))
+            return ORACLE_EARG;
+        s += w[i];
+    }
+    *sum = s;
+    return ORACLE_OK;
+}
+
+/* Weighted mean of the per-token loss: sum_i w[i] loss[i] / sum_i w[i] (0 if all w are 0). */
+int fckl_oracle_weighted_mean(int64_t N, int64_t H, int64_t V, int64_t K, double T,
+                              const double *h, const double *W, const int32_t *idx,
+                              const double *tl, const double *w, double *mean_out)
+{
+    if (N <= 0 || !mean_out)
+        return ORACLE_EARG;
+    double wsum = 0.0;
+    int rc = weight_sum(N, w, &wsum);
+    if (rc)
+        return rc;
+    double *loss = (double *)malloc(sizeof(double) * (size_t)N);
+    if (!loss)
+        return ORACLE_EMEM;
+    rc = fckl_oracle_forward(N, H, V, K, T, h, W, idx, tl, N, NULL, loss, NULL);
+    if (rc == ORACLE_OK) {
+        double s = 0.0;
+        for (int64_t i = 0; i < N; ++i)
+            s += w[i] * loss[i];
+        *mean_out = wsum > 0.0 ? s / wsum : 0.0;
+    }
+    free(loss);
+    return rc;
+}
+
+/*
+ * Gradient of grad_scale * (weighted mean loss) for the selected rows: row i is
+ * scaled by grad_scale * T * w[i] / sum_j w[j] (the sum over all N tokens), and by 0
+ * when every weight is 0.
+ */
+int fckl_oracle_weighted_backward(int64_t N, int64_t H, int64_t V, int64_t K, double T,
+                                  const double *h, const double *W, const int32_t *idx,
+                                  const double *tl, const double *w, double grad_scale,
+                                  int64_t nrows, const int64_t *rows,
+                                  double *dH_out, double *dW_out)
+{
+    int rc = check_args(N, H, V, K, T, h, W, idx, tl, nrows, rows);
+    if (rc)
+        return rc;
+    double wsum = 0.0;
+    rc = weight_sum(N, w, &wsum);
+    if (rc)
+        return rc;
+    double *scale = (double *)malloc(sizeof(double) * (size_t)(nrows > 0 ? nrows : 1));
+    if (!scale)
+        return ORACLE_EMEM;
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t i = rows ? rows[r] : r;
+        scale[r] = wsum > 0.0 ? grad_scale * T * w[i] / wsum : 0.0;
+    }
+    rc = backward_rows(N, H, V, K, T, h, W, idx, tl, scale, nrows, rows, dH_out, dW_out);
+    free(scale);
+    return rc;
 }
 
 /* Number of OpenMP threads a parallel region of the oracle uses. */

@@ -25,12 +25,16 @@ MUTANTS = {
                               "double log_q = z[idx[i * K + (K - 1 - k)]] / T - lse;"),
     "lse_temperature_dropped": ("s += exp(z[v] / T - m);", "s += exp(z[v] - m);"),
     "scatter_sign_flipped": ("gr[idx[i * K + k]] -= scale * p[k];", "gr[idx[i * K + k]] += scale * p[k];"),
-    "grad_temperature_dropped": ("const double scale = grad_scale * T / (double)n_norm;",
-                                 "const double scale = grad_scale / (double)n_norm;"),
+    "grad_temperature_dropped": ("scale[r] = grad_scale * T / (double)n_norm;",
+                                 "scale[r] = grad_scale / (double)n_norm;"),
     "dW_vocab_index_wrong": ("double gv = g[r * V + v];\n                const double *hr",
                              "double gv = g[r * V + (V - 1 - v)];\n                const double *hr"),
     "dH_uses_softmax_only": ("gr[v] = scale * psum * exp(z[v] / T - lse);",
                              "gr[v] = scale * psum * exp(z[v] - lse);"),
+    "weighted_mean_over_count": ("*mean_out = wsum > 0.0 ? s / wsum : 0.0;",
+                                 "*mean_out = wsum > 0.0 ? s / (double)N : 0.0;"),
+    "weighted_grad_row_weight_dropped": ("scale[r] = wsum > 0.0 ? grad_scale * T * w[i] / wsum : 0.0;",
+                                         "scale[r] = wsum > 0.0 ? grad_scale * T / wsum : 0.0;"),
 }
 
 

@@ -301,3 +301,96 @@ def test_rejects_bad_arguments():
             oracle.forward(h, W, idx, tl, badT)
     with pytest.raises(oracle.OracleError):
         oracle.forward(h, W, idx, tl, T, rows=[h.shape[0]])
+
+
+# ---------------------------------------------------------------- token weights and masks
+#
+# The weighted reduction: mean_w = sum_i w_i loss_i / sum_i w_i; a masked token has w = 0.
+
+def torch_weighted_reference(h, W, idx, tl, T, w, grad_scale=1.0):
+    """The weighted mean and its gradients through torch autograd (CPU, float64)."""
+    ht = torch.tensor(h, dtype=torch.float64, requires_grad=True)
+    Wt = torch.tensor(W, dtype=torch.float64, requires_grad=True)
+    logq = torch.gather(torch.log_softmax((ht @ Wt.t()) / T, dim=1), 1, torch.tensor(idx, dtype=torch.int64))
+    logp = torch.log_softmax(torch.tensor(tl, dtype=torch.float64) / T, dim=1)
+    per_tok = (T * T) * (logp.exp() * (logp - logq)).sum(dim=1)
+    wt = torch.tensor(w, dtype=torch.float64)
+    mean = (wt * per_tok).sum() / wt.sum()
+    (grad_scale * mean).backward()
+    return mean.item(), ht.grad.numpy(), Wt.grad.numpy()
+
+
+@pytest.mark.parametrize("seed,T,gs", [(30, 1.0, 1.0), (31, 2.0, -0.5)])
+def test_weighted_matches_torch_autograd(seed, T, gs):
+    h, W, idx, tl, _ = rand_problem(seed, N=9, T=T)
+    w = np.random.default_rng(seed + 1).uniform(0.0, 2.0, size=h.shape[0])
+    w[3] = 0.0
+    ref_mean, ref_dH, ref_dW = torch_weighted_reference(h, W, idx, tl, T, w, gs)
+    mean = oracle.weighted_mean(h, W, idx, tl, T, w)
+    dH, dW = oracle.weighted_backward(h, W, idx, tl, T, w, grad_scale=gs)
+    assert abs(mean - ref_mean) <= 1e-12 * abs(ref_mean)
+    np.testing.assert_allclose(dH, ref_dH, rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(dW, ref_dW, rtol=1e-10, atol=1e-14)
+
+
+def test_unit_weights_are_the_plain_mean():
+    h, W, idx, tl, T = rand_problem(32)
+    w = np.ones(h.shape[0])
+    assert abs(oracle.weighted_mean(h, W, idx, tl, T, w) - oracle.loss_mean(h, W, idx, tl, T)) <= 1e-14
+    dH, dW = oracle.weighted_backward(h, W, idx, tl, T, w, grad_scale=1.7)
+    dH0, dW0 = oracle.backward(h, W, idx, tl, T, grad_scale=1.7)
+    np.testing.assert_allclose(dH, dH0, rtol=1e-13, atol=1e-17)
+    np.testing.assert_allclose(dW, dW0, rtol=1e-13, atol=1e-17)
+
+
+def test_mask_is_the_plain_mean_of_the_kept_tokens():
+    """A 0/1 mask gives the unweighted loss of the kept tokens alone; masked rows get no gradient."""
+    h, W, idx, tl, T = rand_problem(33, N=10)
+    keep = np.array([1, 0, 1, 1, 0, 0, 1, 1, 0, 1], dtype=bool)
+    w = keep.astype(np.float64)
+    mean = oracle.weighted_mean(h, W, idx, tl, T, w)
+    assert abs(mean - oracle.loss_mean(h[keep], W, idx[keep], tl[keep], T)) <= 1e-13 * abs(mean)
+    dH, dW = oracle.weighted_backward(h, W, idx, tl, T, w)
+    dHs, dWs = oracle.backward(h[keep], W, idx[keep], tl[keep], T)
+    np.testing.assert_allclose(dH[keep], dHs, rtol=1e-12, atol=1e-17)
+    assert np.abs(dH[~keep]).max() == 0.0
+    np.testing.assert_allclose(dW, dWs, rtol=1e-12, atol=1e-17)
+
+
+def test_integer_weights_are_repeated_tokens():
+    """Weight m on a token equals that token appearing m times in a plain mean."""
+    h, W, idx, tl, T = rand_problem(34, N=6)
+    m = np.array([2, 1, 3, 0, 1, 4])
+    rep = np.repeat(np.arange(h.shape[0]), m)
+    mean = oracle.weighted_mean(h, W, idx, tl, T, m.astype(np.float64))
+    assert abs(mean - oracle.loss_mean(h[rep], W, idx[rep], tl[rep], T)) <= 1e-13 * abs(mean)
+    dH, dW = oracle.weighted_backward(h, W, idx, tl, T, m.astype(np.float64), grad_scale=0.6)
+    dHr, dWr = oracle.backward(h[rep], W, idx[rep], tl[rep], T, grad_scale=0.6)
+    np.testing.assert_allclose(dW, dWr, rtol=1e-12, atol=1e-17)
+    # each copy of token i carries the same gradient; the weighted row is their sum
+    summed = np.zeros_like(dH)
+    np.add.at(summed, rep, dHr)
+    np.testing.assert_allclose(dH, summed, rtol=1e-12, atol=1e-17)
+
+
+def test_weight_scale_invariance_and_all_masked():
+    h, W, idx, tl, T = rand_problem(35)
+    w = np.random.default_rng(36).uniform(0.1, 1.0, size=h.shape[0])
+    a = oracle.weighted_mean(h, W, idx, tl, T, w)
+    b = oracle.weighted_mean(h, W, idx, tl, T, 8.0 * w)
+    assert abs(a - b) <= 1e-13 * abs(a)
+    dHa, dWa = oracle.weighted_backward(h, W, idx, tl, T, w)
+    dHb, dWb = oracle.weighted_backward(h, W, idx, tl, T, 8.0 * w)
+    np.testing.assert_allclose(dHa, dHb, rtol=1e-12, atol=1e-17)
+    np.testing.assert_allclose(dWa, dWb, rtol=1e-12, atol=1e-17)
+    z = np.zeros(h.shape[0])
+    assert oracle.weighted_mean(h, W, idx, tl, T, z) == 0.0
+    dH0, dW0 = oracle.weighted_backward(h, W, idx, tl, T, z)
+    assert np.abs(dH0).max() == 0.0 and np.abs(dW0).max() == 0.0
+    bad = w.copy()
+    bad[2] = -1.0
+    with pytest.raises(oracle.OracleError):
+        oracle.weighted_mean(h, W, idx, tl, T, bad)
+    bad[2] = float("nan")
+    with pytest.raises(oracle.OracleError):
+        oracle.weighted_backward(h, W, idx, tl, T, bad)
