@@ -12,6 +12,9 @@ the dominant kernel's achieved bf16 MFMA rate: its algorithmic flops per launch
 (2 * tokens * V * H) over its mean launch time, taken with HIP events that the
 library records around each launch on its own stream during the timed steps.
 `cpu_baseline` times the CPU oracle (fp64) on a small sample of the same tokens.
+`single_call` times the same step done by fckl_forward_backward, which forms each
+chunk's logits once (6 N V H flop); it is reported beside the main line, which times
+the two passes of the method as defined (8 N V H flop).
 """
 from __future__ import annotations
 
@@ -73,6 +76,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=0, help="tokens per chunk (0 = library scheduler)")
     ap.add_argument("--cpu-tokens", type=int, default=256, help="oracle sample size for cpu_baseline (0 = skip)")
     ap.add_argument("--dense", action="store_true", help="also measure peak memory of a dense torch KL baseline")
+    ap.add_argument("--no-single-call", action="store_true",
+                    help="skip timing fckl_forward_backward (the single-call path) after the main measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (reference dispatch for HBM byte counters)")
     args = ap.parse_args()
@@ -134,33 +139,9 @@ def main():
         log("warmup step %d done" % i)
     peak_bytes = torch.cuda.max_memory_allocated()
 
-    # Per-kernel HIP events, recorded by the library on its stream during the timed steps.
-    ev = HipEvents()
-    per_step = nchunks * len(fckl.KERNELS) + 2
-    cap = per_step * max(args.steps, 1)
-    events = ev.create(2 * cap)
-    kid = (ctypes.c_int32 * cap)()
-    work = (ctypes.c_int32 * cap)()
-    prof = fckl.Profile((1 << len(fckl.KERNELS)) - 1, cap, 0, events, kid, work)
-
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for _ in range(args.steps):
-        step(prof)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    ms_step = elapsed * 1e3 / args.steps
-    tokens_per_s = N * args.steps / elapsed
+    ms_step, kernels = timed_steps(fckl, step, args.steps, nchunks)
+    tokens_per_s = N * 1e3 / ms_step
     log("timed %d steps: %.2f ms/step, %.0f tokens/s" % (args.steps, ms_step, tokens_per_s))
-
-    kernels = {}
-    for i in range(prof.count):
-        name = fckl.KERNELS[kid[i]]
-        d = kernels.setdefault(name, {"launches": 0, "ms": 0.0, "tokens": 0})
-        d["launches"] += 1
-        d["ms"] += ev.elapsed_ms(events[2 * i], events[2 * i + 1])
-        d["tokens"] += work[i]
-    ev.destroy(events)
     gemms = ("fwd_logits", "bwd_logits", "dh", "dw")
     for name, d in kernels.items():
         d["avg_ms"] = d["ms"] / d["launches"]
@@ -195,6 +176,25 @@ def main():
                     for k, v in kernels.items()},
     }
 
+    if not args.no_single_call:
+        # The same step as one fckl_forward_backward call: each chunk's logits are formed
+        # once (6 N V H flop instead of 8).  Reported beside the main line, which times
+        # the two passes the method defines.
+        def single(profile=None):
+            fckl.forward_backward(h, W, idx, tl, T=T, chunk=chunk, ws=ws, loss_tok=loss, lse=lse, loss_mean=mean,
+                                  dH=dH, dW=dW, profile=profile)
+        single()
+        torch.cuda.synchronize()
+        ms1, k1 = timed_steps(fckl, single, args.steps, nchunks)
+        log("single call: %.2f ms/step, %.0f tokens/s" % (ms1, N * 1e3 / ms1))
+        out["single_call"] = {
+            "value": round(N * 1e3 / ms1, 1), "unit": "tokens/s", "ms_per_step": round(ms1, 3),
+            "flops_per_step": 6.0 * N * V * H,
+            "mfma_frac": round(6.0 * N * V * H / (ms1 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "kernels": {k: {"launches": v["launches"], "ms_per_step": round(v["ms"] / args.steps, 4)}
+                        for k, v in k1.items()},
+        }
+
     if args.dense:
         # the fused path's workspace and outputs are released first: the dense loss is
         # measured with only the inputs resident
@@ -204,6 +204,35 @@ def main():
     if args.cpu_tokens > 0:
         out["cpu_baseline"] = cpu_baseline(x, wl, args.cpu_tokens)
     print(json.dumps(out), flush=True)
+
+
+def timed_steps(fckl, step, steps, nchunks):
+    """Time `steps` calls of step(profile) between two device syncs; the library records
+    HIP events around each of its kernel launches on its stream.  Returns (ms per step,
+    per-kernel {launches, ms, tokens})."""
+    import torch
+    ev = HipEvents()
+    per_step = nchunks * len(fckl.KERNELS) + 4
+    cap = per_step * max(steps, 1)
+    events = ev.create(2 * cap)
+    kid = (ctypes.c_int32 * cap)()
+    work = (ctypes.c_int32 * cap)()
+    prof = fckl.Profile((1 << len(fckl.KERNELS)) - 1, cap, 0, events, kid, work)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(steps):
+        step(prof)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    kernels = {}
+    for i in range(prof.count):
+        name = fckl.KERNELS[kid[i]]
+        d = kernels.setdefault(name, {"launches": 0, "ms": 0.0, "tokens": 0})
+        d["launches"] += 1
+        d["ms"] += ev.elapsed_ms(events[2 * i], events[2 * i + 1])
+        d["tokens"] += work[i]
+    ev.destroy(events)
+    return elapsed * 1e3 / steps, kernels
 
 
 KERNEL_NAMES = {"fwd_logits": "forward_logits_kernel", "bwd_logits": "backward_logits_kernel",

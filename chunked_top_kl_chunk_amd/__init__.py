@@ -9,6 +9,12 @@ the library is missing every call raises.
     import chunked_top_kl_chunk_amd as fckl
     loss_tok, lse, loss_mean = fckl.forward(h, W, topk_idx, topk_logit, T=1.0)
     dH, dW = fckl.backward(h, W, topk_idx, topk_logit, lse, T=1.0)
+    # or both in one call (the loss is the last operation of the step):
+    loss_tok, lse, loss_mean, dH, dW = fckl.forward_backward(h, W, topk_idx, topk_logit, T=1.0)
+
+Optional per-token ``weights`` (float32 [N], 0 masks a token) make the mean
+sum_i w_i loss_i / sum_i w_i.  ``FusedChunkedKLLoss`` (``chunked_top_kl_chunk_amd.loss``)
+wraps the two passes as a torch autograd module.
 
 Shapes: h [N,H] bf16, W [V,H] bf16, topk_idx [N,K] int32, topk_logit [N,K] bf16 or
 float32, all contiguous on one HIP device.  Outputs are float32.
@@ -27,11 +33,12 @@ DTYPE_BF16, DTYPE_F32 = 0, 1
 FLAG_VALIDATE, FLAG_DW_ACCUMULATE = 1, 2
 
 # Every symbol include/fckl.h declares.
-EXPORTS = ("fckl_plan", "fckl_workspace_size", "fckl_forward", "fckl_backward",
-           "fckl_status_string", "fckl_version")
+EXPORTS = ("fckl_plan", "fckl_workspace_size", "fckl_forward", "fckl_backward", "fckl_forward_ex",
+           "fckl_backward_ex", "fckl_forward_backward", "fckl_status_string", "fckl_version")
 
 
-KERNELS = ("prepare", "fwd_logits", "combine", "mean", "bwd_logits", "dh", "dh_reduce", "dw", "transpose")
+KERNELS = ("prepare", "fwd_logits", "combine", "mean", "bwd_logits", "dh", "dh_reduce", "dw", "transpose",
+           "softmax_grad", "weights")
 
 
 class Profile(ctypes.Structure):
@@ -71,11 +78,16 @@ def load() -> ctypes.CDLL:
     lib.fckl_workspace_size.argtypes = [P(Desc), ctypes.c_int32, P(sz)]
     lib.fckl_forward.argtypes = [P(Desc), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.fckl_backward.argtypes = [P(Desc), vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
+    lib.fckl_forward_ex.argtypes = [P(Desc), vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.fckl_backward_ex.argtypes = [P(Desc), vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
+    lib.fckl_forward_backward.argtypes = [P(Desc), vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp,
+                                          sz, vp]
     lib.fckl_status_string.argtypes = [ctypes.c_int]
     lib.fckl_status_string.restype = ctypes.c_char_p
     lib.fckl_version.argtypes = []
     lib.fckl_version.restype = ctypes.c_int32
-    for f in ("fckl_plan", "fckl_workspace_size", "fckl_forward", "fckl_backward"):
+    for f in ("fckl_plan", "fckl_workspace_size", "fckl_forward", "fckl_backward", "fckl_forward_ex",
+              "fckl_backward_ex", "fckl_forward_backward"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -177,27 +189,51 @@ def _workspace(desc: Desc, ws, device):
     return ws
 
 
+def _weights(weights, N, device):
+    """None, or a contiguous float32 [N] tensor on `device` (its pointer is passed as is)."""
+    import torch
+    if weights is None:
+        return None
+    if (not isinstance(weights, torch.Tensor) or weights.dtype != torch.float32 or tuple(weights.shape) != (N,)
+            or not weights.is_contiguous() or weights.device != device):
+        raise ValueError("weights must be a contiguous float32 tensor of shape (%d,) on %s" % (N, device))
+    return weights
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
 def forward(h, W, topk_idx, topk_logit, T: float = 1.0, chunk: int = 0, ws=None, validate: bool = False,
-            loss_tok=None, lse=None, loss_mean=None, stream=None, profile: Optional[Profile] = None):
-    """Per-token loss, saved lse (log-sum-exp of z/T) and the mean loss, via fckl_forward."""
+            loss_tok=None, lse=None, loss_mean=None, stream=None, profile: Optional[Profile] = None,
+            weights=None):
+    """Per-token loss, saved lse (log-sum-exp of z/T) and the mean loss (weighted when
+    `weights` is given), via fckl_forward / fckl_forward_ex."""
     _check_inputs(h, W, topk_idx, topk_logit)
     dev = h.device
     desc = desc_for(h, W, topk_idx, topk_logit, T, chunk, FLAG_VALIDATE if validate else 0, profile)
     ws = _workspace(desc, ws, dev)
     N = h.shape[0]
+    weights = _weights(weights, N, dev)
     loss_tok = _out(loss_tok, (N,), dev, "loss_tok")
     lse = _out(lse, (N,), dev, "lse")
     loss_mean = _out(loss_mean, (1,), dev, "loss_mean")
-    _call("fckl_forward", ctypes.byref(desc), h.data_ptr(), W.data_ptr(), topk_idx.data_ptr(),
-          topk_logit.data_ptr(), loss_tok.data_ptr(), lse.data_ptr(), loss_mean.data_ptr(), ws.data_ptr(),
-          ctypes.c_size_t(ws.numel() * ws.element_size()), _stream_handle(stream))
+    common = (h.data_ptr(), W.data_ptr(), topk_idx.data_ptr(), topk_logit.data_ptr())
+    tail = (loss_tok.data_ptr(), lse.data_ptr(), loss_mean.data_ptr(), ws.data_ptr(),
+            ctypes.c_size_t(ws.numel() * ws.element_size()), _stream_handle(stream))
+    if weights is None:
+        _call("fckl_forward", ctypes.byref(desc), *common, *tail)
+    else:
+        _call("fckl_forward_ex", ctypes.byref(desc), *common, weights.data_ptr(), *tail)
     return loss_tok, lse, loss_mean
 
 
 def backward(h, W, topk_idx, topk_logit, lse, T: float = 1.0, grad_scale: float = 1.0, chunk: int = 0, ws=None,
              dH=None, dW=None, accumulate: bool = False, validate: bool = False, stream=None,
-             profile: Optional[Profile] = None):
-    """dH [N,H] and dW [V,H] (float32) of grad_scale * mean loss, via fckl_backward."""
+             profile: Optional[Profile] = None, weights=None, grad_scale_dev=None):
+    """dH [N,H] and dW [V,H] (float32) of grad_scale * (weighted) mean loss, via
+    fckl_backward / fckl_backward_ex.  grad_scale_dev (float32 [1] on the device) further
+    multiplies grad_scale without a host read-back."""
     import torch
     _check_inputs(h, W, topk_idx, topk_logit)
     if lse.dtype != torch.float32 or tuple(lse.shape) != (h.shape[0],) or lse.device != h.device:
@@ -206,13 +242,47 @@ def backward(h, W, topk_idx, topk_logit, lse, T: float = 1.0, grad_scale: float 
     flags = (FLAG_VALIDATE if validate else 0) | (FLAG_DW_ACCUMULATE if accumulate else 0)
     desc = desc_for(h, W, topk_idx, topk_logit, T, chunk, flags, profile)
     ws = _workspace(desc, ws, dev)
+    weights = _weights(weights, h.shape[0], dev)
+    if grad_scale_dev is not None and (grad_scale_dev.dtype != torch.float32 or grad_scale_dev.numel() != 1
+                                       or grad_scale_dev.device != dev):
+        raise ValueError("grad_scale_dev must be a float32 scalar tensor on the inputs' device")
     dH = _out(dH, tuple(h.shape), dev, "dH")
     dW = _out(dW, tuple(W.shape), dev, "dW")
-    _call("fckl_backward", ctypes.byref(desc), h.data_ptr(), W.data_ptr(), topk_idx.data_ptr(),
-          topk_logit.data_ptr(), lse.data_ptr(), ctypes.c_float(grad_scale), dH.data_ptr(), dW.data_ptr(),
-          ws.data_ptr(), ctypes.c_size_t(ws.numel() * ws.element_size()), _stream_handle(stream))
+    common = (h.data_ptr(), W.data_ptr(), topk_idx.data_ptr(), topk_logit.data_ptr())
+    tail = (dH.data_ptr(), dW.data_ptr(), ws.data_ptr(), ctypes.c_size_t(ws.numel() * ws.element_size()),
+            _stream_handle(stream))
+    if weights is None and grad_scale_dev is None:
+        _call("fckl_backward", ctypes.byref(desc), *common, lse.data_ptr(), ctypes.c_float(grad_scale), *tail)
+    else:
+        _call("fckl_backward_ex", ctypes.byref(desc), *common, _ptr(weights), lse.data_ptr(),
+              ctypes.c_float(grad_scale), _ptr(grad_scale_dev), *tail)
     return dH, dW
 
 
-__all__ = ["Desc", "Profile", "KERNELS", "FCKLError", "load", "plan", "workspace_size", "forward", "backward", "make_desc",
-           "desc_for", "status_string", "version", "EXPORTS", "LIB_PATH"]
+def forward_backward(h, W, topk_idx, topk_logit, T: float = 1.0, grad_scale: float = 1.0, weights=None,
+                     chunk: int = 0, ws=None, loss_tok=None, lse=None, loss_mean=None, dH=None, dW=None,
+                     accumulate: bool = False, validate: bool = False, stream=None,
+                     profile: Optional[Profile] = None):
+    """Loss and gradients in one call (fckl_forward_backward): the logits of each chunk
+    are formed once.  Returns (loss_tok, lse, loss_mean, dH, dW)."""
+    _check_inputs(h, W, topk_idx, topk_logit)
+    dev = h.device
+    flags = (FLAG_VALIDATE if validate else 0) | (FLAG_DW_ACCUMULATE if accumulate else 0)
+    desc = desc_for(h, W, topk_idx, topk_logit, T, chunk, flags, profile)
+    ws = _workspace(desc, ws, dev)
+    N = h.shape[0]
+    weights = _weights(weights, N, dev)
+    loss_tok = _out(loss_tok, (N,), dev, "loss_tok")
+    lse = _out(lse, (N,), dev, "lse")
+    loss_mean = _out(loss_mean, (1,), dev, "loss_mean")
+    dH = _out(dH, tuple(h.shape), dev, "dH")
+    dW = _out(dW, tuple(W.shape), dev, "dW")
+    _call("fckl_forward_backward", ctypes.byref(desc), h.data_ptr(), W.data_ptr(), topk_idx.data_ptr(),
+          topk_logit.data_ptr(), _ptr(weights), ctypes.c_float(grad_scale), loss_tok.data_ptr(), lse.data_ptr(),
+          loss_mean.data_ptr(), dH.data_ptr(), dW.data_ptr(), ws.data_ptr(),
+          ctypes.c_size_t(ws.numel() * ws.element_size()), _stream_handle(stream))
+    return loss_tok, lse, loss_mean, dH, dW
+
+
+__all__ = ["Desc", "Profile", "KERNELS", "FCKLError", "load", "plan", "workspace_size", "forward", "backward",
+           "forward_backward", "make_desc", "desc_for", "status_string", "version", "EXPORTS", "LIB_PATH"]

@@ -98,6 +98,149 @@ class Timed {
     int slot_ = -1;
 };
 
+// Sum of the weights and its inverse, into the workspace (weights != NULL).
+fckl_status weight_sum(const fckl_desc *desc, const float *weights, void *ws, const Layout &L, void *stream,
+                       float **wsum)
+{
+    *wsum = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + L.off_wsum);
+    Timed t(desc, FCKL_KERNEL_WEIGHTS, (int)desc->N, stream);
+    return launch_weight_sum(weights, desc->N, *wsum, stream) ? FCKL_ERR_HIP : FCKL_OK;
+}
+
+// The gradient scale of the chunk starting at token c0 (see GradScale).
+GradScale chunk_scale(const fckl_desc *desc, float grad_scale, const float *weights, const float *wsum, int64_t c0)
+{
+    GradScale gs;
+    if (weights) {
+        gs.coef = (float)((double)grad_scale * (double)desc->T);
+        gs.w = weights + c0;
+        gs.inv_wsum = wsum + 1;
+    } else {
+        // d(grad_scale * mean loss)/dz = grad_scale * (T/N) * ((sum p) q - scatter p)
+        gs.coef = (float)((double)grad_scale * (double)desc->T / (double)desc->N);
+    }
+    return gs;
+}
+
+fckl_status mean_of(const fckl_desc *desc, const float *loss_tok, const float *weights, float *loss_mean,
+                    void *stream)
+{
+    Timed t(desc, FCKL_KERNEL_MEAN, (int)desc->N, stream);
+    const int rc = weights ? launch_weighted_mean(loss_tok, weights, desc->N, loss_mean, stream)
+                           : launch_mean(loss_tok, desc->N, loss_mean, stream);
+    return rc ? FCKL_ERR_HIP : FCKL_OK;
+}
+
+fckl_status forward_impl(const fckl_desc *desc, const void *h, const void *W, const int32_t *topk_idx,
+                         const void *topk_logit, const float *weights, float *loss_tok, float *lse,
+                         float *loss_mean, void *ws, size_t ws_bytes, void *stream)
+{
+    Layout L;
+    fckl_status st = common_checks(desc, h, W, topk_idx, topk_logit, ws, ws_bytes, &L);
+    if (st != FCKL_OK)
+        return st;
+    if (!loss_tok || !lse)
+        return FCKL_ERR_INVALID_ARG;
+    if (desc->flags & FCKL_FLAG_VALIDATE) {
+        st = validate_indices(desc, h, W, topk_idx, topk_logit, ws, L, stream);
+        if (st != FCKL_OK)
+            return st;
+    }
+    for (int64_t c0 = 0; c0 < desc->N; c0 += L.C) {
+        ChunkArgs a = chunk_args(desc, h, W, topk_idx, topk_logit, ws, &L, c0);
+        {
+            Timed t(desc, FCKL_KERNEL_PREPARE, a.rows, stream);
+            if (launch_prepare(a, false, stream))
+                return FCKL_ERR_HIP;
+        }
+        {
+            Timed t(desc, FCKL_KERNEL_FWD_LOGITS, a.rows, stream);
+            if (launch_forward_logits(a, stream))
+                return FCKL_ERR_HIP;
+        }
+        {
+            Timed t(desc, FCKL_KERNEL_COMBINE, a.rows, stream);
+            if (launch_combine(a, loss_tok + c0, lse + c0, stream))
+                return FCKL_ERR_HIP;
+        }
+    }
+    return loss_mean ? mean_of(desc, loss_tok, weights, loss_mean, stream) : FCKL_OK;
+}
+
+// dH, dH reduce and dW of one chunk whose g (both layouts) and h^T are in the workspace.
+fckl_status chunk_products(const fckl_desc *desc, const ChunkArgs &a, int64_t c0, float *dH, float *dW,
+                           void *stream)
+{
+    {
+        Timed t(desc, FCKL_KERNEL_DH, a.rows, stream);
+        if (launch_dh(a, stream))
+            return FCKL_ERR_HIP;
+    }
+    {
+        Timed t(desc, FCKL_KERNEL_DH_REDUCE, a.rows, stream);
+        if (launch_dh_reduce(a, dH + (size_t)c0 * desc->H, stream))
+            return FCKL_ERR_HIP;
+    }
+    {
+        Timed t(desc, FCKL_KERNEL_DW, a.rows, stream);
+        const bool accumulate = (desc->flags & FCKL_FLAG_DW_ACCUMULATE) != 0 || c0 > 0;
+        if (launch_dw(a, dW, accumulate, stream))
+            return FCKL_ERR_HIP;
+    }
+    return FCKL_OK;
+}
+
+fckl_status backward_impl(const fckl_desc *desc, const void *h, const void *W, const int32_t *topk_idx,
+                          const void *topk_logit, const float *weights, const float *lse, float grad_scale,
+                          const float *grad_scale_dev, float *dH, float *dW, void *ws, size_t ws_bytes,
+                          void *stream)
+{
+    Layout L;
+    fckl_status st = common_checks(desc, h, W, topk_idx, topk_logit, ws, ws_bytes, &L);
+    if (st != FCKL_OK)
+        return st;
+    if (!lse || !dH || !dW)
+        return FCKL_ERR_INVALID_ARG;
+    if (desc->flags & FCKL_FLAG_VALIDATE) {
+        st = validate_indices(desc, h, W, topk_idx, topk_logit, ws, L, stream);
+        if (st != FCKL_OK)
+            return st;
+    }
+    float *wsum = nullptr;
+    if (weights && (st = weight_sum(desc, weights, ws, L, stream, &wsum)) != FCKL_OK)
+        return st;
+    {
+        // W^T once per call: the dH product reduces over the vocabulary
+        ChunkArgs a = chunk_args(desc, h, W, topk_idx, topk_logit, ws, &L, 0);
+        Timed t(desc, FCKL_KERNEL_TRANSPOSE, 0, stream);
+        if (launch_transpose_head(a, stream))
+            return FCKL_ERR_HIP;
+    }
+    for (int64_t c0 = 0; c0 < desc->N; c0 += L.C) {
+        ChunkArgs a = chunk_args(desc, h, W, topk_idx, topk_logit, ws, &L, c0);
+        GradScale gs = chunk_scale(desc, grad_scale, weights, wsum, c0);
+        gs.mul = grad_scale_dev;
+        {
+            Timed t(desc, FCKL_KERNEL_PREPARE, a.rows, stream);
+            if (launch_prepare(a, false, stream, &gs))
+                return FCKL_ERR_HIP;
+        }
+        {
+            Timed t(desc, FCKL_KERNEL_TRANSPOSE, a.rows, stream);
+            if (launch_transpose_chunk(a, stream))
+                return FCKL_ERR_HIP;
+        }
+        {
+            Timed t(desc, FCKL_KERNEL_BWD_LOGITS, a.rows, stream);
+            if (launch_backward_logits(a, lse + c0, stream))
+                return FCKL_ERR_HIP;
+        }
+        if ((st = chunk_products(desc, a, c0, dH, dW, stream)) != FCKL_OK)
+            return st;
+    }
+    return FCKL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -130,63 +273,53 @@ fckl_status fckl_forward(const fckl_desc *desc, const void *h, const void *W, co
                          const void *topk_logit, float *loss_tok, float *lse, float *loss_mean, void *ws,
                          size_t ws_bytes, void *stream)
 {
-    Layout L;
-    fckl_status st = common_checks(desc, h, W, topk_idx, topk_logit, ws, ws_bytes, &L);
-    if (st != FCKL_OK)
-        return st;
-    if (!loss_tok || !lse)
-        return FCKL_ERR_INVALID_ARG;
-    if (desc->flags & FCKL_FLAG_VALIDATE) {
-        st = validate_indices(desc, h, W, topk_idx, topk_logit, ws, L, stream);
-        if (st != FCKL_OK)
-            return st;
-    }
-    for (int64_t c0 = 0; c0 < desc->N; c0 += L.C) {
-        ChunkArgs a = chunk_args(desc, h, W, topk_idx, topk_logit, ws, &L, c0);
-        {
-            Timed t(desc, FCKL_KERNEL_PREPARE, a.rows, stream);
-            if (launch_prepare(a, false, stream))
-                return FCKL_ERR_HIP;
-        }
-        {
-            Timed t(desc, FCKL_KERNEL_FWD_LOGITS, a.rows, stream);
-            if (launch_forward_logits(a, stream))
-                return FCKL_ERR_HIP;
-        }
-        {
-            Timed t(desc, FCKL_KERNEL_COMBINE, a.rows, stream);
-            if (launch_combine(a, loss_tok + c0, lse + c0, stream))
-                return FCKL_ERR_HIP;
-        }
-    }
-    if (loss_mean) {
-        Timed t(desc, FCKL_KERNEL_MEAN, (int)desc->N, stream);
-        if (launch_mean(loss_tok, desc->N, loss_mean, stream))
-            return FCKL_ERR_HIP;
-    }
-    return FCKL_OK;
+    return forward_impl(desc, h, W, topk_idx, topk_logit, nullptr, loss_tok, lse, loss_mean, ws, ws_bytes, stream);
+}
+
+fckl_status fckl_forward_ex(const fckl_desc *desc, const void *h, const void *W, const int32_t *topk_idx,
+                            const void *topk_logit, const float *weights, float *loss_tok, float *lse,
+                            float *loss_mean, void *ws, size_t ws_bytes, void *stream)
+{
+    return forward_impl(desc, h, W, topk_idx, topk_logit, weights, loss_tok, lse, loss_mean, ws, ws_bytes, stream);
 }
 
 fckl_status fckl_backward(const fckl_desc *desc, const void *h, const void *W, const int32_t *topk_idx,
                           const void *topk_logit, const float *lse, float grad_scale, float *dH, float *dW,
                           void *ws, size_t ws_bytes, void *stream)
 {
+    return backward_impl(desc, h, W, topk_idx, topk_logit, nullptr, lse, grad_scale, nullptr, dH, dW, ws, ws_bytes,
+                         stream);
+}
+
+fckl_status fckl_backward_ex(const fckl_desc *desc, const void *h, const void *W, const int32_t *topk_idx,
+                             const void *topk_logit, const float *weights, const float *lse, float grad_scale,
+                             const float *grad_scale_dev, float *dH, float *dW, void *ws, size_t ws_bytes,
+                             void *stream)
+{
+    return backward_impl(desc, h, W, topk_idx, topk_logit, weights, lse, grad_scale, grad_scale_dev, dH, dW, ws,
+                         ws_bytes, stream);
+}
+
+fckl_status fckl_forward_backward(const fckl_desc *desc, const void *h, const void *W, const int32_t *topk_idx,
+                                  const void *topk_logit, const float *weights, float grad_scale,
+                                  float *loss_tok, float *lse, float *loss_mean, float *dH, float *dW, void *ws,
+                                  size_t ws_bytes, void *stream)
+{
     Layout L;
     fckl_status st = common_checks(desc, h, W, topk_idx, topk_logit, ws, ws_bytes, &L);
     if (st != FCKL_OK)
         return st;
-    if (!lse || !dH || !dW)
+    if (!loss_tok || !lse || !dH || !dW)
         return FCKL_ERR_INVALID_ARG;
     if (desc->flags & FCKL_FLAG_VALIDATE) {
         st = validate_indices(desc, h, W, topk_idx, topk_logit, ws, L, stream);
         if (st != FCKL_OK)
             return st;
     }
-    // d(grad_scale * mean loss)/dz = grad_scale * (T/N) * ((sum p) q - scatter p)
-    const float coef = (float)((double)grad_scale * (double)desc->T / (double)desc->N);
-    const bool acc0 = (desc->flags & FCKL_FLAG_DW_ACCUMULATE) != 0;
+    float *wsum = nullptr;
+    if (weights && (st = weight_sum(desc, weights, ws, L, stream, &wsum)) != FCKL_OK)
+        return st;
     {
-        // W^T once per call: the dH product reduces over the vocabulary
         ChunkArgs a = chunk_args(desc, h, W, topk_idx, topk_logit, ws, &L, 0);
         Timed t(desc, FCKL_KERNEL_TRANSPOSE, 0, stream);
         if (launch_transpose_head(a, stream))
@@ -194,9 +327,25 @@ fckl_status fckl_backward(const fckl_desc *desc, const void *h, const void *W, c
     }
     for (int64_t c0 = 0; c0 < desc->N; c0 += L.C) {
         ChunkArgs a = chunk_args(desc, h, W, topk_idx, topk_logit, ws, &L, c0);
+        const GradScale gs = chunk_scale(desc, grad_scale, weights, wsum, c0);
         {
             Timed t(desc, FCKL_KERNEL_PREPARE, a.rows, stream);
             if (launch_prepare(a, false, stream))
+                return FCKL_ERR_HIP;
+        }
+        {
+            Timed t(desc, FCKL_KERNEL_FWD_LOGITS, a.rows, stream);
+            if (launch_forward_logits(a, stream, true))
+                return FCKL_ERR_HIP;
+        }
+        {
+            Timed t(desc, FCKL_KERNEL_COMBINE, a.rows, stream);
+            if (launch_combine(a, loss_tok + c0, lse + c0, stream))
+                return FCKL_ERR_HIP;
+        }
+        {
+            Timed t(desc, FCKL_KERNEL_SOFTMAX_GRAD, a.rows, stream);
+            if (launch_softmax_grad(a, lse + c0, gs, stream))
                 return FCKL_ERR_HIP;
         }
         {
@@ -204,28 +353,10 @@ fckl_status fckl_backward(const fckl_desc *desc, const void *h, const void *W, c
             if (launch_transpose_chunk(a, stream))
                 return FCKL_ERR_HIP;
         }
-        {
-            Timed t(desc, FCKL_KERNEL_BWD_LOGITS, a.rows, stream);
-            if (launch_backward_logits(a, lse + c0, coef, stream))
-                return FCKL_ERR_HIP;
-        }
-        {
-            Timed t(desc, FCKL_KERNEL_DH, a.rows, stream);
-            if (launch_dh(a, stream))
-                return FCKL_ERR_HIP;
-        }
-        {
-            Timed t(desc, FCKL_KERNEL_DH_REDUCE, a.rows, stream);
-            if (launch_dh_reduce(a, dH + (size_t)c0 * desc->H, stream))
-                return FCKL_ERR_HIP;
-        }
-        {
-            Timed t(desc, FCKL_KERNEL_DW, a.rows, stream);
-            if (launch_dw(a, dW, acc0 || c0 > 0, stream))
-                return FCKL_ERR_HIP;
-        }
+        if ((st = chunk_products(desc, a, c0, dH, dW, stream)) != FCKL_OK)
+            return st;
     }
-    return FCKL_OK;
+    return loss_mean ? mean_of(desc, loss_tok, weights, loss_mean, stream) : FCKL_OK;
 }
 
 const char *fckl_status_string(fckl_status s)
@@ -247,6 +378,6 @@ const char *fckl_status_string(fckl_status s)
     return "unknown status";
 }
 
-int32_t fckl_version(void) { return 100; }
+int32_t fckl_version(void) { return 200; }
 
 }  // extern "C"

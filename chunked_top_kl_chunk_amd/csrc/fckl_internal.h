@@ -36,6 +36,9 @@ struct Layout {
     size_t off_negent = 0;  // f32   [Cpad]      sum_k p log p
     size_t off_cnt = 0;     // u8    [Cpad, cnt_stride] entries below each vocabulary tile start
     size_t off_part = 0;    // f32x2 [nVt, Cpad] per-tile (max, sum exp) of z/T, base 2
+    size_t off_mw = 0;      // f32   [2 nVt, Cpad] max of z/T (base 2) per 128-row half tile,
+                            //       kept by the single-call path with the exponentials
+    size_t off_wsum = 0;    // f32   [2]         sum of the token weights and its inverse
     size_t off_g = 0;       // bf16  [Cpad, Vpad] chunk gradient w.r.t. the logits
     size_t off_gT = 0;      // bf16  [Vpad, Cpad] the same, transposed (dW operand)
     size_t off_hT = 0;      // bf16  [H, Cpad]    chunk hidden states, transposed (dW operand)
@@ -65,11 +68,29 @@ struct ChunkArgs {
     const Layout *L;
 };
 
-int launch_prepare(const ChunkArgs &a, bool validate, void *stream);
-int launch_forward_logits(const ChunkArgs &a, void *stream);
+// Per-token scale of the gradient with respect to z: coef * w[i] * (*inv_wsum) with
+// weights, coef alone without (w == NULL), times *mul when mul is set.  coef = grad_scale * T, divided by N when
+// there are no weights.
+struct GradScale {
+    float coef = 0.0f;
+    const float *w = nullptr;         // chunk's first token, or NULL
+    const float *inv_wsum = nullptr;  // device scalar, used with w
+    const float *mul = nullptr;       // device scalar multiplying coef, or NULL
+};
+
+// `gs` != NULL: the teacher probabilities and their sum are stored multiplied by the
+// token's gradient scale (the backward pass uses them only in that form).
+int launch_prepare(const ChunkArgs &a, bool validate, void *stream, const GradScale *gs = nullptr);
+// keep_exp: also write 2^(z/T log2 e - m) in bf16 over the chunk's gradient buffer and
+// the half-tile maxima m (single-call path).
+int launch_forward_logits(const ChunkArgs &a, void *stream, bool keep_exp = false);
 int launch_combine(const ChunkArgs &a, float *loss_tok, float *lse, void *stream);
 int launch_mean(const float *loss_tok, int64_t N, float *loss_mean, void *stream);
-int launch_backward_logits(const ChunkArgs &a, const float *lse, float coef, void *stream);
+int launch_weighted_mean(const float *loss_tok, const float *w, int64_t N, float *loss_mean, void *stream);
+int launch_weight_sum(const float *w, int64_t N, float *out2, void *stream);
+int launch_backward_logits(const ChunkArgs &a, const float *lse, void *stream);
+// Single-call path: g (both layouts) from the kept exponentials, the chunk's lse and gs.
+int launch_softmax_grad(const ChunkArgs &a, const float *lse, const GradScale &gs, void *stream);
 int launch_dh(const ChunkArgs &a, void *stream);
 int launch_dh_reduce(const ChunkArgs &a, float *dH, void *stream);
 int launch_dw(const ChunkArgs &a, float *dW, bool accumulate, void *stream);

@@ -583,6 +583,13 @@ struct PrepParams {
     uint8_t *cnt;           // [Cpad, cnt_stride] out
     uint32_t *err;          // index-check flag (validate only)
     int validate;
+    // scaled != 0: p_s and psum are stored times the token's gradient scale
+    // gcoef * (gw ? gw[t] * *ginv : 1) * (gmul ? *gmul : 1)
+    int scaled;
+    float gcoef;
+    const float *gw;        // chunk's first token, or NULL
+    const float *ginv;      // 1 / sum of all weights (device scalar)
+    const float *gmul;      // device scalar multiplying gcoef, or NULL
 };
 
 // One wave per token.  Teacher distribution p = softmax(tl/T) over the K entries
@@ -629,6 +636,12 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepParams p)
     }
     ps = wave_sum(ps);
     ne = wave_sum(ne);
+    if (p.scaled && live) {
+        const float gsc = (p.gw ? p.gcoef * p.gw[t] * *p.ginv : p.gcoef) * (p.gmul ? *p.gmul : 1.0f);
+        pr[0] *= gsc;
+        pr[1] *= gsc;
+        ps *= gsc;
+    }
     __syncthreads();
     bool bad = false;
 #pragma unroll
@@ -677,6 +690,73 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepParams p)
 
 // ------------------------------------------------------------------ forward logits
 
+// From a bf16 tile staged in LDS as [token][vocab] (TOK token rows of 256 vocabulary
+// columns, row pitch kGStagePitch bytes), writes the transposed tile to
+// dst[(m0 + vocab) * pitch + n0 + token] with 16-byte stores, reading it back with
+// transposing LDS reads: in a 16-lane group, lane l addresses the 8-byte piece of token
+// row t + l/4 at vocabulary columns v + 4(l%4), and every lane receives 4 consecutive
+// tokens of vocabulary column v + l.  Two such reads give a lane 8 tokens = one 16-byte
+// piece of a transposed row.  A wave covers 16 vocabulary rows x 32 tokens per step
+// (its 4 groups take 8 tokens each).
+template <int TOK, int NWAVES>
+__device__ __forceinline__ void store_vocab_major(const char *smem, uint16_t *dst, size_t pitch, int m0, int n0)
+{
+    static_assert(TOK % 32 == 0, "whole 32-token blocks");
+    constexpr int kTokBlocks = TOK / 32;
+    constexpr int kBlocks = (256 / 16) * kTokBlocks;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int grp = lane >> 4, gl = lane & 15;
+#pragma unroll 2
+    for (int b = wave; b < kBlocks; b += NWAVES) {
+        const int vb = (b / kTokBlocks) * 16, tb = (b % kTokBlocks) * 32 + grp * 8;
+        const char *src = smem + (tb + (gl >> 2)) * kGStagePitch + (vb + 4 * (gl & 3)) * 2;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(src));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4 *)(src + 4 * kGStagePitch));
+        u32x4 v;
+        v[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+        v[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+        v[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+        v[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+        *reinterpret_cast<u32x4 *>(dst + (size_t)(m0 + vb + gl) * pitch + n0 + tb) = v;
+    }
+}
+
+// Rounds the tile held in `acc` to bf16, stages it in LDS as [token][vocab] (row pitch
+// kGStagePitch) and writes its rows to dst[(n0 + token) * pitch + m0 + vocab] with
+// 16-byte stores.  The staged tile stays in LDS for the caller; LDS must be free on
+// entry (every wave past its last read of the previous contents).
+template <class G>
+__device__ __forceinline__ void store_token_major(const f32x16 (&acc)[G::MB][G::NB], char *smem, uint16_t *dst,
+                                                  size_t pitch, int m0, int n0)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / G::WN, wn = wave % G::WN;
+#pragma unroll
+    for (int j = 0; j < G::NB; ++j) {
+        const int nl = G::col_of(wn, j, lane);
+#pragma unroll
+        for (int i = 0; i < G::MB; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int ml = G::row_of(wm, i, 4 * q, lane);
+                u32x2 pk;
+                pk[0] = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
+                pk[1] = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                *reinterpret_cast<u32x2 *>(smem + nl * kGStagePitch + ml * 2) = pk;
+            }
+    }
+    __syncthreads();
+    constexpr int kChunks = G::BN * (G::BM * 2 / 16);
+    constexpr int kRowChunks = G::BM / 8;       // 16-byte pieces per token row of the tile
+#pragma unroll 4
+    for (int c = threadIdx.x; c < kChunks; c += G::NT) {
+        const int nl = c / kRowChunks, col = (c % kRowChunks) * 8;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + nl * kGStagePitch + col * 2);
+        *reinterpret_cast<u32x4 *>(dst + (size_t)(n0 + nl) * pitch + m0 + col) = v;
+    }
+}
+
 struct FwdParams {
     const uint16_t *W;      // [V, H]
     const uint16_t *h;      // [rows, H] chunk
@@ -686,8 +766,16 @@ struct FwdParams {
     const uint8_t *cnt;
     float *zk;
     float2 *part;           // [nVt, Cpad]
+    // single-call path only: kept exponentials and their half-tile maxima
+    uint16_t *ex;           // [Cpad, Vpad] bf16
+    float *mw;              // [2 nVt, Cpad]
+    int Vpad;
 };
 
+// KEEP (single-call path): besides the forward outputs, the tile's 2^(z/T log2 e - m)
+// are written in bf16 to p.ex, m being the maximum over the wave's 128 vocabulary rows
+// (stored in p.mw), so that the backward needs no second product.
+template <bool KEEP>
 __device__ __forceinline__ void forward_tile(const FwdParams &p, char *smem, int t)
 {
     using G = LogitGemm;
@@ -716,53 +804,6 @@ __device__ __forceinline__ void forward_tile(const FwdParams &p, char *smem, int
     f32x16 acc[G::MB][G::NB];
     G::run(smem, p.W, p.H, m0, p.V, p.H, p.h, p.H, n0, p.rows, p.H, 0, p.H, acc, [&] { pf.issue(pre); });
 
-    // Per token, over the wave's 128 vocabulary rows: max and sum of 2^(z*log2e/T - max).
-    // Every tile but the last vocabulary tile skips the row check.
-    float *red = reinterpret_cast<float *>(smem);   // [WM][BN][2]
-    auto reduce = [&](auto interior_c) {
-        constexpr bool interior = decltype(interior_c)::value;
-#pragma unroll
-        for (int j = 0; j < G::NB; ++j) {
-            float mx = kNegInf;
-#pragma unroll
-            for (int i = 0; i < G::MB; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const bool in = interior || m0 + G::row_of(wm, i, r, lane) < p.V;
-                    mx = fmaxf(mx, in ? acc[i][j][r] * p.scale2 : kNegInf);
-                }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float ms = (mx == kNegInf) ? 0.0f : mx;
-            float sum = 0.0f;
-#pragma unroll
-            for (int i = 0; i < G::MB; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const bool in = interior || m0 + G::row_of(wm, i, r, lane) < p.V;
-                    sum += in ? fast_exp2(acc[i][j][r] * p.scale2 - ms) : 0.0f;
-                }
-            sum += __shfl_xor(sum, 32);
-            if (lane < 32) {
-                const int nl = G::col_of(wn, j, lane);
-                red[(wm * G::BN + nl) * 2 + 0] = mx;
-                red[(wm * G::BN + nl) * 2 + 1] = sum;
-            }
-        }
-    };
-    if (m0 + G::BM <= p.V)
-        reduce(std::true_type{});
-    else
-        reduce(std::false_type{});
-    __syncthreads();
-    for (int nl = threadIdx.x; nl < G::BN; nl += G::NT) {
-        if (n0 + nl < p.rows) {
-            float m = red[nl * 2 + 0], s = red[nl * 2 + 1];
-#pragma unroll
-            for (int w2 = 1; w2 < G::WM; ++w2)
-                lse_merge(m, s, red[(w2 * G::BN + nl) * 2 + 0], red[(w2 * G::BN + nl) * 2 + 1]);
-            p.part[(size_t)tm * p.Cpad + n0 + nl] = make_float2(m, s);
-        }
-    }
     // Pick z at the cached indices this tile owns: the lane holding that row writes it.
     const int wrow0 = m0 + wm * G::WTM;
     const int32_t *pre_idx = reinterpret_cast<const int32_t *>(pre);
@@ -781,17 +822,78 @@ __device__ __forceinline__ void forward_tile(const FwdParams &p, char *smem, int
             }
         }
     }
+
+    // Per token, over the wave's 128 vocabulary rows: max and sum of 2^(z*log2e/T - max).
+    // Without KEEP every tile but the last vocabulary tile skips the row check.  With
+    // KEEP the accumulators are rewritten, and one code path with a per-lane row limit
+    // (as in the backward epilogue) avoids holding two versions of them.
+    float *red = reinterpret_cast<float *>(smem);   // [WM][BN][2]
+    const int lim = p.V - m0 - G::row_of(wm, 0, 0, lane);
+    auto reduce = [&](auto interior_c) {
+        constexpr bool interior = decltype(interior_c)::value;
+#pragma unroll
+        for (int j = 0; j < G::NB; ++j) {
+            float mx = kNegInf;
+#pragma unroll
+            for (int i = 0; i < G::MB; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const bool in = interior || 32 * i + 8 * (r >> 2) + (r & 3) < lim;
+                    mx = fmaxf(mx, in ? acc[i][j][r] * p.scale2 : kNegInf);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float ms = (mx == kNegInf) ? 0.0f : mx;
+            float sum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < G::MB; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const bool in = interior || 32 * i + 8 * (r >> 2) + (r & 3) < lim;
+                    const float e = in ? fast_exp2(acc[i][j][r] * p.scale2 - ms) : 0.0f;
+                    sum += e;
+                    if constexpr (KEEP)
+                        acc[i][j][r] = e;
+                }
+            sum += __shfl_xor(sum, 32);
+            if (lane < 32) {
+                const int nl = G::col_of(wn, j, lane);
+                red[(wm * G::BN + nl) * 2 + 0] = mx;
+                red[(wm * G::BN + nl) * 2 + 1] = sum;
+                if constexpr (KEEP)
+                    p.mw[(size_t)(2 * tm + wm) * p.Cpad + n0 + nl] = ms;
+            }
+        }
+    };
+    if (!KEEP && m0 + G::BM <= p.V)
+        reduce(std::true_type{});
+    else
+        reduce(std::false_type{});
+    __syncthreads();
+    for (int nl = threadIdx.x; nl < G::BN; nl += G::NT) {
+        if (n0 + nl < p.rows) {
+            float m = red[nl * 2 + 0], s = red[nl * 2 + 1];
+#pragma unroll
+            for (int w2 = 1; w2 < G::WM; ++w2)
+                lse_merge(m, s, red[(w2 * G::BN + nl) * 2 + 0], red[(w2 * G::BN + nl) * 2 + 1]);
+            p.part[(size_t)tm * p.Cpad + n0 + nl] = make_float2(m, s);
+        }
+    }
+    if constexpr (KEEP) {
+        __syncthreads();    // the merge above has read `red` before the staging overwrites it
+        store_token_major<G>(acc, smem, p.ex, (size_t)p.Vpad, m0, n0);
+    }
 }
 
 // Persistent: one work-group per compute unit walks the tiles b, b + grid, ...  The
 // grid is a multiple of 8, so all tiles of a work-group map to its own XCD, and the
 // XCD's work-groups move through its tile range together, as one wave of
 // non-persistent work-groups would.
+template <bool KEEP>
 __global__ __launch_bounds__(LogitGemm::NT) void forward_logits_kernel(FwdParams p)
 {
     __shared__ __attribute__((aligned(16))) char smem[kLogitLds + kPreLds];
     for (int t = blockIdx.x; t < p.nVt * p.nNt; t += gridDim.x) {
-        forward_tile(p, smem, t);
+        forward_tile<KEEP>(p, smem, t);
         __syncthreads();    // every wave is done with LDS before the next tile's loads land
     }
 }
@@ -859,16 +961,58 @@ __global__ __launch_bounds__(1024) void mean_kernel(const float *x, int64_t n, f
         *out = (float)(s[0] / (double)n);
 }
 
+// Weighted mean sum_i w_i x_i / sum_i w_i (0 when the weights sum to 0), fixed order, fp64.
+__global__ __launch_bounds__(1024) void weighted_mean_kernel(const float *x, const float *w, int64_t n, float *out)
+{
+    __shared__ double s[1024], sw[1024];
+    double a = 0.0, b = 0.0;
+    for (int64_t i = threadIdx.x; i < n; i += 1024) {
+        a += (double)w[i] * (double)x[i];
+        b += (double)w[i];
+    }
+    s[threadIdx.x] = a;
+    sw[threadIdx.x] = b;
+    __syncthreads();
+    for (int o = 512; o >= 1; o >>= 1) {
+        if ((int)threadIdx.x < o) {
+            s[threadIdx.x] += s[threadIdx.x + o];
+            sw[threadIdx.x] += sw[threadIdx.x + o];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0)
+        *out = sw[0] > 0.0 ? (float)(s[0] / sw[0]) : 0.0f;
+}
+
+// out2[0] = sum of the weights, out2[1] = its inverse (0 when the sum is 0); fixed order, fp64.
+__global__ __launch_bounds__(1024) void weight_sum_kernel(const float *w, int64_t n, float *out2)
+{
+    __shared__ double s[1024];
+    double a = 0.0;
+    for (int64_t i = threadIdx.x; i < n; i += 1024)
+        a += (double)w[i];
+    s[threadIdx.x] = a;
+    __syncthreads();
+    for (int o = 512; o >= 1; o >>= 1) {
+        if ((int)threadIdx.x < o)
+            s[threadIdx.x] += s[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        out2[0] = (float)s[0];
+        out2[1] = s[0] > 0.0 ? (float)(1.0 / s[0]) : 0.0f;
+    }
+}
+
 // ------------------------------------------------------------------ backward logits
 
 struct BwdParams {
     const uint16_t *W, *h;
     int H, V, rows, Cpad, Vpad, K, nVt, nNt, cnt_stride;
     float scale2;           // log2(e) / T
-    float coef;             // grad_scale * T / N
     const float *lse;       // chunk's first token (natural log, z/T units)
     const int32_t *idx_s;
-    const float *p_s, *psum;
+    const float *p_s, *psum;    // stored times each token's gradient scale
     const uint8_t *cnt;
     uint16_t *g;            // [Cpad, Vpad] bf16
     uint16_t *gT;           // [Vpad, Cpad] bf16
@@ -899,14 +1043,15 @@ __device__ __forceinline__ void backward_tile(const BwdParams &p, char *smem, in
             cs[j] = c[0];
             ce[j] = c[1];
             l2[j] = p.lse[tok] * kLog2e;
-            amp[j] = p.coef * p.psum[tok];
+            amp[j] = p.psum[tok];
         }
     }
 
     f32x16 acc[G::MB][G::NB];
     G::run(smem, p.W, p.H, m0, p.V, p.H, p.h, p.H, n0, p.rows, p.H, 0, p.H, acc, [&] { pf.issue(pre); });
 
-    // g = coef * ((sum p) * exp(z/T - lse) - scatter(p, idx)); zero outside [0,V) x [0,rows).
+    // g = c ((sum p) exp(z/T - lse) - scatter(p, idx)), with the token's gradient scale c
+    // already folded into p and sum p; zero outside [0,V) x [0,rows).
     // The row test is against a per-lane limit: element (i, r) sits row_of(wm, i, r, lane)
     // = row_of(wm, 0, 0, lane) + 32 i + 8 (r / 4) + r % 4, so it is inside when that
     // constant offset is below V - m0 - row_of(wm, 0, 0, lane) (and -1 for a padded token).
@@ -937,59 +1082,15 @@ __device__ __forceinline__ void backward_tile(const BwdParams &p, char *smem, in
                 if (((r32 >> 2) & 1) == (lane >> 5)) {
                     const int sel = (row >> 5) * 16 + ((r32 >> 3) << 2) + (r32 & 3);
                     const float pe = in_lds ? pre_p[(e - cs[j]) * G::BN + nl] : p.p_s[(size_t)tok * p.K + e];
-                    sub_at(acc, j, sel, p.coef * pe);
+                    sub_at(acc, j, sel, pe);
                 }
             }
         }
     }
-    // Stage the bf16 tile as [token][vocab] in LDS, then write whole 16-byte pieces.
-    // (The main loop ended with a barrier, so the operand buffers are free.)
-#pragma unroll
-    for (int j = 0; j < G::NB; ++j) {
-        const int nl = G::col_of(wn, j, lane);
-#pragma unroll
-        for (int i = 0; i < G::MB; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int ml = G::row_of(wm, i, 4 * q, lane);
-                u32x2 pk;
-                pk[0] = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
-                pk[1] = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-                *reinterpret_cast<u32x2 *>(smem + nl * kGStagePitch + ml * 2) = pk;
-            }
-    }
-    __syncthreads();
-    constexpr int kChunks = G::BN * (G::BM * 2 / 16);
-    constexpr int kRowChunks = G::BM / 8;       // 16-byte pieces per token row of the tile
-#pragma unroll 4
-    for (int c = threadIdx.x; c < kChunks; c += G::NT) {
-        const int nl = c / kRowChunks, col = (c % kRowChunks) * 8;
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + nl * kGStagePitch + col * 2);
-        *reinterpret_cast<u32x4 *>(p.g + (size_t)(n0 + nl) * p.Vpad + m0 + col) = v;
-    }
-    // The same tile transposed, [vocab][token], for the dW product, read back from the
-    // staged [token][vocab] tile with transposing LDS reads: in a 16-lane group, lane l
-    // addresses the 8-byte piece of token row t + l/4 at vocabulary columns v + 4(l%4),
-    // and every lane receives 4 consecutive tokens of vocabulary column v + l.  Two such
-    // reads give a lane 8 tokens = one 16-byte piece of a g^T row.  A wave covers 16
-    // vocabulary rows x 32 tokens per step (its 4 groups take 8 tokens each).
-    constexpr int kTokBlocks = G::BN / 32;
-    constexpr int kBlocks = (G::BM / 16) * kTokBlocks;
-    const int grp = lane >> 4, gl = lane & 15;
-#pragma unroll 2
-    for (int b = wave; b < kBlocks; b += G::NT / 64) {
-        const int vb = (b / kTokBlocks) * 16, tb = (b % kTokBlocks) * 32 + grp * 8;
-        const char *src = smem + (tb + (gl >> 2)) * kGStagePitch + (vb + 4 * (gl & 3)) * 2;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(src));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4 *)(src + 4 * kGStagePitch));
-        u32x4 v;
-        v[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
-        v[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
-        v[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
-        v[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
-        *reinterpret_cast<u32x4 *>(p.gT + (size_t)(m0 + vb + gl) * p.Cpad + n0 + tb) = v;
-    }
+    // Both layouts of the bf16 tile: [token][vocab] for the dH product, [vocab][token] for
+    // the dW product.  (The main loop ended with a barrier, so the operand buffers are free.)
+    store_token_major<G>(acc, smem, p.g, (size_t)p.Vpad, m0, n0);
+    store_vocab_major<G::BN, G::NT / 64>(smem, p.gT, (size_t)p.Cpad, m0, n0);
 }
 
 __global__ __launch_bounds__(LogitGemm::NT) void backward_logits_kernel(BwdParams p)
@@ -999,6 +1100,72 @@ __global__ __launch_bounds__(LogitGemm::NT) void backward_logits_kernel(BwdParam
         backward_tile(p, smem, t);
         __syncthreads();
     }
+}
+
+// ------------------------------------------------------------------ single-call gradient
+
+struct SoftGradParams {
+    uint16_t *ex;           // [Cpad, Vpad] bf16: the kept 2^(z/T log2 e - m); overwritten with g
+    uint16_t *gT;           // [Vpad, Cpad] bf16 out
+    const float *mw;        // [2 nVt, Cpad] the half-tile maxima m (base 2)
+    const float *lse;       // chunk's first token (natural log, z/T units)
+    const float *psum;      // [Cpad] sum_k p
+    const int32_t *idx_s;   // [Cpad, K] sorted cached indices
+    const float *p_s;       // [Cpad, K] p in the same order
+    const uint8_t *cnt;     // [Cpad, cnt_stride]
+    int rows, Cpad, Vpad, K, cnt_stride;
+    float coef;             // grad_scale * T (/ N without weights)
+    const float *w;         // chunk's first token, or NULL
+    const float *inv_wsum;  // device scalar, used with w
+    const float *mul;       // device scalar multiplying coef, or NULL
+};
+
+constexpr int kSgTok = 64;  // tokens per block of the gradient kernel
+
+// One block per (256-row vocabulary tile, 64 tokens).  With c the token's gradient scale:
+//   g = c ((sum p) 2^(z/T log2 e - lse log2 e) - scatter(p, idx))
+//     = c ((sum p) E 2^(m - lse log2 e) - scatter(p, idx)),   E the kept value,
+// rounded to bf16, written over E ([token][vocab]) and, through LDS, as g^T.
+__global__ __launch_bounds__(256) void softmax_grad_kernel(SoftGradParams p)
+{
+    __shared__ __attribute__((aligned(16))) char smem[kSgTok * kGStagePitch];
+    const int tm = blockIdx.x, n0 = blockIdx.y * kSgTok, m0 = tm * 256;
+    const int c = threadIdx.x & 31;     // 16-byte piece of the tile row
+    const int half = c >> 4;            // its 128-row half of the vocabulary tile
+    for (int rl = threadIdx.x >> 5; rl < kSgTok; rl += 8) {
+        const int tok = n0 + rl;
+        u32x4 out = {0u, 0u, 0u, 0u};
+        if (tok < p.rows) {
+            const float gsc = (p.w ? p.coef * p.w[tok] * *p.inv_wsum : p.coef) * (p.mul ? *p.mul : 1.0f);
+            const float f = gsc * p.psum[tok] *
+                            fast_exp2(p.mw[(size_t)(2 * tm + half) * p.Cpad + tok] - p.lse[tok] * kLog2e);
+            const u32x4 e = *reinterpret_cast<const u32x4 *>(p.ex + (size_t)tok * p.Vpad + m0 + 8 * c);
+            float v[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                v[2 * q] = f * __uint_as_float(e[q] << 16);
+                v[2 * q + 1] = f * __uint_as_float(e[q] & 0xffff0000u);
+            }
+            // the token's cached entries in this vocabulary tile that fall in this piece
+            const uint8_t *cr = p.cnt + (size_t)tok * p.cnt_stride + tm;
+            for (int k = cr[0]; k < cr[1]; ++k) {
+                const int col = p.idx_s[(size_t)tok * p.K + k] - m0 - 8 * c;
+                if (col >= 0 && col < 8) {
+                    const float d = gsc * p.p_s[(size_t)tok * p.K + k];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        v[q] -= (q == col) ? d : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                out[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
+        }
+        *reinterpret_cast<u32x4 *>(p.ex + (size_t)tok * p.Vpad + m0 + 8 * c) = out;
+        *reinterpret_cast<u32x4 *>(smem + rl * kGStagePitch + 16 * c) = out;
+    }
+    __syncthreads();
+    store_vocab_major<kSgTok, 4>(smem, p.gT, (size_t)p.Cpad, m0, n0);
 }
 
 // ------------------------------------------------------------------ dH = g . W
@@ -1161,7 +1328,7 @@ static int persistent_grid(int tiles)
     return tiles < n ? tiles : n;
 }
 
-int launch_prepare(const ChunkArgs &a, bool validate, void *stream)
+int launch_prepare(const ChunkArgs &a, bool validate, void *stream, const GradScale *gs)
 {
     const Layout &L = *a.L;
     PrepParams p;
@@ -1182,11 +1349,16 @@ int launch_prepare(const ChunkArgs &a, bool validate, void *stream)
     p.cnt = reinterpret_cast<uint8_t *>(a.ws + L.off_cnt);
     p.err = reinterpret_cast<uint32_t *>(a.ws + L.off_err);
     p.validate = validate ? 1 : 0;
+    p.scaled = gs ? 1 : 0;
+    p.gcoef = gs ? gs->coef : 1.0f;
+    p.gw = gs ? gs->w : nullptr;
+    p.ginv = gs ? gs->inv_wsum : nullptr;
+    p.gmul = gs ? gs->mul : nullptr;
     hipLaunchKernelGGL(prepare_kernel, dim3((a.rows + 3) / 4), dim3(256), 0, S(stream), p);
     return (int)hipGetLastError();
 }
 
-int launch_forward_logits(const ChunkArgs &a, void *stream)
+int launch_forward_logits(const ChunkArgs &a, void *stream, bool keep_exp)
 {
     const Layout &L = *a.L;
     FwdParams p;
@@ -1205,7 +1377,14 @@ int launch_forward_logits(const ChunkArgs &a, void *stream)
     p.cnt = reinterpret_cast<const uint8_t *>(a.ws + L.off_cnt);
     p.zk = reinterpret_cast<float *>(a.ws + L.off_zk);
     p.part = reinterpret_cast<float2 *>(a.ws + L.off_part);
-    hipLaunchKernelGGL(forward_logits_kernel, dim3(persistent_grid(p.nVt * p.nNt)), dim3(LogitGemm::NT), 0, S(stream), p);
+    p.ex = reinterpret_cast<uint16_t *>(a.ws + L.off_g);
+    p.mw = reinterpret_cast<float *>(a.ws + L.off_mw);
+    p.Vpad = L.Vpad;
+    const dim3 grid(persistent_grid(p.nVt * p.nNt));
+    if (keep_exp)
+        hipLaunchKernelGGL(forward_logits_kernel<true>, grid, dim3(LogitGemm::NT), 0, S(stream), p);
+    else
+        hipLaunchKernelGGL(forward_logits_kernel<false>, grid, dim3(LogitGemm::NT), 0, S(stream), p);
     return (int)hipGetLastError();
 }
 
@@ -1235,7 +1414,44 @@ int launch_mean(const float *loss_tok, int64_t N, float *loss_mean, void *stream
     return (int)hipGetLastError();
 }
 
-int launch_backward_logits(const ChunkArgs &a, const float *lse, float coef, void *stream)
+int launch_weighted_mean(const float *loss_tok, const float *w, int64_t N, float *loss_mean, void *stream)
+{
+    hipLaunchKernelGGL(weighted_mean_kernel, dim3(1), dim3(1024), 0, S(stream), loss_tok, w, N, loss_mean);
+    return (int)hipGetLastError();
+}
+
+int launch_weight_sum(const float *w, int64_t N, float *out2, void *stream)
+{
+    hipLaunchKernelGGL(weight_sum_kernel, dim3(1), dim3(1024), 0, S(stream), w, N, out2);
+    return (int)hipGetLastError();
+}
+
+int launch_softmax_grad(const ChunkArgs &a, const float *lse, const GradScale &gs, void *stream)
+{
+    const Layout &L = *a.L;
+    SoftGradParams p;
+    p.ex = reinterpret_cast<uint16_t *>(a.ws + L.off_g);
+    p.gT = reinterpret_cast<uint16_t *>(a.ws + L.off_gT);
+    p.mw = reinterpret_cast<const float *>(a.ws + L.off_mw);
+    p.lse = lse;
+    p.psum = reinterpret_cast<const float *>(a.ws + L.off_psum);
+    p.idx_s = reinterpret_cast<const int32_t *>(a.ws + L.off_idx);
+    p.p_s = reinterpret_cast<const float *>(a.ws + L.off_p);
+    p.cnt = reinterpret_cast<const uint8_t *>(a.ws + L.off_cnt);
+    p.rows = a.rows;
+    p.Cpad = L.Cpad;
+    p.Vpad = L.Vpad;
+    p.K = a.K;
+    p.cnt_stride = L.cnt_stride;
+    p.coef = gs.coef;
+    p.w = gs.w;
+    p.inv_wsum = gs.inv_wsum;
+    p.mul = gs.mul;
+    hipLaunchKernelGGL(softmax_grad_kernel, dim3(L.nVt, (a.rows + kSgTok - 1) / kSgTok), dim3(256), 0, S(stream), p);
+    return (int)hipGetLastError();
+}
+
+int launch_backward_logits(const ChunkArgs &a, const float *lse, void *stream)
 {
     const Layout &L = *a.L;
     BwdParams p;
@@ -1251,7 +1467,6 @@ int launch_backward_logits(const ChunkArgs &a, const float *lse, float coef, voi
     p.nNt = (a.rows + LogitGemm::BN - 1) / LogitGemm::BN;
     p.cnt_stride = L.cnt_stride;
     p.scale2 = kLog2e / a.T;
-    p.coef = coef;
     p.lse = lse;
     p.idx_s = reinterpret_cast<const int32_t *>(a.ws + L.off_idx);
     p.p_s = reinterpret_cast<const float *>(a.ws + L.off_p);

@@ -94,6 +94,8 @@ fckl_status make_layout(const fckl_desc *d, int32_t chunk, Layout *L)
     o.off_negent = take(Cp * 4);
     o.off_cnt = take(Cp * (size_t)o.cnt_stride);
     o.off_part = take((size_t)o.nVt * Cp * 8);
+    o.off_mw = take((size_t)o.nVt * 2 * Cp * 4);
+    o.off_wsum = take(16);
     o.off_g = take(Cp * (size_t)o.Vpad * 2);
     o.off_gT = take(Cp * (size_t)o.Vpad * 2);
     o.off_hT = take(Cp * (size_t)d->H * 2);

@@ -1,0 +1,100 @@
+"""torch autograd wrapper of the fused chunked top-K KL loss.
+
+``FusedChunkedKLLoss`` is the module the pages configure in place of a stock PyTorch
+loss ("Configuring Fused Chunked KL Loss", getaibook.com): it takes the student's
+final hidden states and LM head (the output projection is part of the loss,
+"What actually changed?", calcaas.com) and the teacher's cached top-K logits and
+indices.  Its forward pass is ``fckl_forward_ex`` and its backward pass
+``fckl_backward_ex``; the upstream gradient stays on the device.  Both passes run in
+the library's HIP kernels; nothing here computes any part of the loss.
+
+Token masks (padding, ignored positions) and per-token weights enter through the
+weighted mean sum_i w_i loss_i / sum_i w_i; a masked token has w = 0.
+
+The library computes dH and dW in float32; autograd hands them to h and W in those
+tensors' dtype (bf16), as it does for any gradient.  A caller that keeps an fp32
+master copy of W can call ``chunked_top_kl_chunk_amd.backward`` with
+``accumulate=True`` on that buffer instead.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import backward as _backward
+from . import forward as _forward
+
+
+class FusedChunkedKLFunction(torch.autograd.Function):
+    """loss = weighted mean over tokens of T^2 KL(p_teacher || softmax(h W^T / T)) over the K cached entries."""
+
+    @staticmethod
+    def forward(ctx, h, W, topk_idx, topk_logit, weights, T: float, chunk: int):
+        _, lse, mean = _forward(h.detach(), W.detach(), topk_idx, topk_logit, T=T, chunk=chunk, weights=weights)
+        ctx.save_for_backward(h, W, topk_idx, topk_logit, lse)
+        ctx.weights = weights
+        ctx.T, ctx.chunk = T, chunk
+        return mean.reshape(())
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        h, W, topk_idx, topk_logit, lse = ctx.saved_tensors
+        if not (ctx.needs_input_grad[0] or ctx.needs_input_grad[1]):
+            return None, None, None, None, None, None, None
+        g = grad_out.detach().to(torch.float32).reshape(1).contiguous()
+        dH, dW = _backward(h.detach(), W.detach(), topk_idx, topk_logit, lse, T=ctx.T, chunk=ctx.chunk,
+                           weights=ctx.weights, grad_scale=1.0, grad_scale_dev=g)
+        return (dH if ctx.needs_input_grad[0] else None, dW if ctx.needs_input_grad[1] else None,
+                None, None, None, None, None)
+
+
+class FusedChunkedKLLoss(torch.nn.Module):
+    """Fused chunked KL distillation loss against a cached top-K teacher.
+
+    Args:
+        temperature: T; student and teacher logits are divided by it and the loss is
+            scaled by T^2.
+        chunk: tokens per chunk (0 = the library's scheduler).
+        ignore_index: topk_idx rows whose first entry equals this value are masked
+            (their other entries are then not read as indices; they must still be in
+            [0, V) or be replaced by the caller).  None = no such convention.
+
+    forward(hidden [.., H] bf16, lm_head_weight [V, H] bf16, topk_idx [.., K] int32,
+            topk_logit [.., K] bf16/f32, mask [..] bool (True = keep) or None,
+            weights [..] float or None) -> scalar loss (float32).
+    """
+
+    def __init__(self, temperature: float = 1.0, chunk: int = 0, ignore_index: Optional[int] = None):
+        super().__init__()
+        if not temperature > 0:
+            raise ValueError("temperature must be > 0")
+        self.temperature = float(temperature)
+        self.chunk = int(chunk)
+        self.ignore_index = ignore_index
+
+    def forward(self, hidden, lm_head_weight, topk_idx, topk_logit, mask=None, weights=None):
+        H = hidden.shape[-1]
+        K = topk_idx.shape[-1]
+        h = hidden.reshape(-1, H)
+        idx = topk_idx.reshape(-1, K)
+        tl = topk_logit.reshape(-1, K)
+        N = h.shape[0]
+        w = None
+        if weights is not None:
+            w = weights.reshape(N).to(torch.float32)
+        if mask is not None:
+            m = mask.reshape(N).to(torch.float32)
+            w = m if w is None else w * m
+        if self.ignore_index is not None:
+            keep = idx[:, 0] != self.ignore_index
+            if not bool(keep.all()):
+                w = keep.to(torch.float32) if w is None else w * keep.to(torch.float32)
+                # ignored rows get a valid placeholder index row; their weight is 0
+                idx = torch.where(keep[:, None], idx, torch.arange(K, device=idx.device, dtype=idx.dtype)[None, :])
+        return FusedChunkedKLFunction.apply(h.contiguous(), lm_head_weight.contiguous(), idx.contiguous(),
+                                            tl.contiguous(), None if w is None else w.contiguous(),
+                                            self.temperature, self.chunk)
+
+
+__all__ = ["FusedChunkedKLFunction", "FusedChunkedKLLoss"]

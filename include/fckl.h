@@ -84,7 +84,9 @@ enum {
     FCKL_KERNEL_DH_REDUCE = 6,     /* fixed-order sum of the dH splits */
     FCKL_KERNEL_DW = 7,            /* dW += g^T h */
     FCKL_KERNEL_TRANSPOSE = 8,     /* W^T once per backward call, h^T once per chunk */
-    FCKL_KERNEL_COUNT = 9
+    FCKL_KERNEL_SOFTMAX_GRAD = 9,  /* fckl_forward_backward: g from the kept exponentials */
+    FCKL_KERNEL_WEIGHTS = 10,      /* sum of the per-token weights */
+    FCKL_KERNEL_COUNT = 11
 };
 
 /*
@@ -175,6 +177,46 @@ fckl_status fckl_backward(const fckl_desc *desc, const void *h, const void *W,
                           const int32_t *topk_idx, const void *topk_logit, const float *lse,
                           float grad_scale, float *dH, float *dW,
                           void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Token masks and per-token weights (padded batches).  The same passes with weights
+ * w[N] (device, f32; a masked token has w = 0; NULL = every weight 1, which is
+ * fckl_forward / fckl_backward):
+ *   loss_mean = sum_i w[i] loss[i] / sum_i w[i]                  (0 when all w are 0)
+ *   g[i,v]    = grad_scale * T * w[i] / sum_j w[j] * ((sum_k p[i,k]) exp(z[i,v]/T - lse[i])
+ *                                                     - sum_k p[i,k] [idx[i,k] == v])
+ * loss_tok and lse stay per token and unweighted.  The pages speak of no masks; this
+ * is the reduction that losses with ignored positions use.  Weights must be finite and
+ * >= 0 (not checked).  The sums over tokens run in a fixed order in fp64, so results
+ * stay deterministic.  grad_scale_dev (device, f32 [1], may be NULL) multiplies
+ * grad_scale on the device, for an upstream gradient that is itself on the GPU (an
+ * autograd graph) and should not be read back to the host first.
+ */
+fckl_status fckl_forward_ex(const fckl_desc *desc, const void *h, const void *W,
+                            const int32_t *topk_idx, const void *topk_logit, const float *weights,
+                            float *loss_tok, float *lse, float *loss_mean,
+                            void *ws, size_t ws_bytes, void *stream);
+fckl_status fckl_backward_ex(const fckl_desc *desc, const void *h, const void *W,
+                             const int32_t *topk_idx, const void *topk_logit, const float *weights,
+                             const float *lse, float grad_scale, const float *grad_scale_dev,
+                             float *dH, float *dW, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Forward and backward in one call, for a loss that is the last operation of the step,
+ * so that its upstream gradient grad_scale is known before the forward pass runs.  The
+ * outputs are those of fckl_forward_ex followed by fckl_backward_ex (weights may be NULL).
+ * The logits are formed once per chunk instead of twice: the forward epilogue keeps
+ * 2^(z/T log2 e - m) in bf16 in the workspace, with m the maximum over each 128-row half
+ * of a 256-row vocabulary tile, and once the chunk's lse is known a streaming kernel
+ * turns those values into g.  That is 6 N V H flop instead of 8.  g differs from the
+ * two-call path by the bf16 rounding of the kept values, which has the same relative size
+ * as the rounding of g itself.  Workspace: the same size as for the two-call path.
+ */
+fckl_status fckl_forward_backward(const fckl_desc *desc, const void *h, const void *W,
+                                  const int32_t *topk_idx, const void *topk_logit,
+                                  const float *weights, float grad_scale,
+                                  float *loss_tok, float *lse, float *loss_mean,
+                                  float *dH, float *dW, void *ws, size_t ws_bytes, void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *fckl_status_string(fckl_status status);

@@ -6,6 +6,7 @@ the loss bound covers it); dH and dW with max|gpu - oracle| <= 2e-2 * max|oracle
 The GPU path takes bf16 inputs, accumulates in fp32 and rounds the chunk gradient g
 to bf16 before the dH / dW products; the oracle sees the same bf16 values in fp64.
 """
+import math
 import sys
 
 import numpy as np
@@ -78,3 +79,17 @@ def check_grad(gpu, ref, what):
     e = rel_max(gpu, ref)
     assert e <= GRAD_TOL, "%s max-abs error %.3e of max|oracle|" % (what, e)
     return e
+
+
+def synthetic(seed, N, H, V, K, T, tl_sigma=2.0, z_sigma=2.0, scaled_frac=0.0):
+    """h ~ N(0,1), W ~ N(0, (z_sigma^2)/H) so that logits spread over a few units, teacher
+    logits N(0, tl_sigma^2) sorted descending on K distinct random indices; bf16 values."""
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((N, H)).astype(np.float32)
+    if scaled_frac > 0:
+        pick = rng.permutation(N)[:max(1, int(round(scaled_frac * N)))]
+        h[pick] *= 20.0
+    W = (rng.standard_normal((V, H)) * (z_sigma / math.sqrt(H))).astype(np.float32)
+    idx = synth.distinct_indices(seed + 1, N, K, V)
+    tl = -np.sort(-rng.standard_normal((N, K)).astype(np.float32) * tl_sigma, axis=1)
+    return synth.round_bf16(h), synth.round_bf16(W), idx, synth.round_bf16(tl)

@@ -17,24 +17,10 @@ import chunked_top_kl_chunk_amd as fckl
 import oracle
 import synth
 from gpu_util import (GRAD_TOL, LOSS_RTOL, LSE_ATOL, arrays, check_grad, check_loss, device, rel_max, run, say,
-                      upload)
+                      synthetic, upload)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
-
-
-def synthetic(seed, N, H, V, K, T, tl_sigma=2.0, z_sigma=2.0, scaled_frac=0.0):
-    """h ~ N(0,1), W ~ N(0, (z_sigma^2)/H) so that logits spread over a few units, teacher
-    logits N(0, tl_sigma^2) sorted descending on K distinct random indices; bf16 values."""
-    rng = np.random.default_rng(seed)
-    h = rng.standard_normal((N, H)).astype(np.float32)
-    if scaled_frac > 0:
-        pick = rng.permutation(N)[:max(1, int(round(scaled_frac * N)))]
-        h[pick] *= 20.0
-    W = (rng.standard_normal((V, H)) * (z_sigma / math.sqrt(H))).astype(np.float32)
-    idx = synth.distinct_indices(seed + 1, N, K, V)
-    tl = -np.sort(-rng.standard_normal((N, K)).astype(np.float32) * tl_sigma, axis=1)
-    return synth.round_bf16(h), synth.round_bf16(W), idx, synth.round_bf16(tl)
 
 
 def compare_all(g, h, W, idx, tl, T, grad_scale=1.0, what=""):

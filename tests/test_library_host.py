@@ -152,3 +152,56 @@ def test_binding_refuses_host_tensors():
     tl = torch.zeros(4, 2, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fckl.forward(h, W, idx, tl)
+
+
+def test_weighted_and_single_call_entry_points_reject_before_any_hip_call():
+    """The weighted passes and the single-call path check their arguments up front too."""
+    lib = fckl.load()
+    d = fckl.make_desc(512, 256, 4096, 10, 1.0, chunk=128)
+    need = fckl.workspace_size(d, 128)
+    P = 1 << 40
+    ok = [_fake(P), _fake(P), _fake(P), _fake(P)]
+    size = ctypes.c_size_t
+    # fckl_forward_ex: weights may be NULL, outputs may not
+    st = lib.fckl_forward_ex(ctypes.byref(d), *ok, None, None, _fake(P), None, _fake(P), size(need), None)
+    assert st == fckl.ERR_INVALID_ARG
+    st = lib.fckl_forward_ex(ctypes.byref(d), *ok, _fake(P), _fake(P), _fake(P), None, _fake(P), size(need - 1), None)
+    assert st == fckl.ERR_WORKSPACE
+    # fckl_backward_ex
+    st = lib.fckl_backward_ex(ctypes.byref(d), *ok, None, _fake(P), ctypes.c_float(1.0), None, None, _fake(P),
+                              _fake(P), size(need), None)
+    assert st == fckl.ERR_INVALID_ARG
+    st = lib.fckl_backward_ex(ctypes.byref(d), *ok, _fake(P), _fake(P), ctypes.c_float(1.0), None, _fake(P),
+                              _fake(P), _fake(P + 8), size(need), None)
+    assert st == fckl.ERR_INVALID_ARG
+    # fckl_forward_backward: every output is required
+    args = [_fake(P)] * 5
+    for missing in range(5):
+        outs = list(args)
+        outs[missing] = None
+        if missing == 2:        # loss_mean may be NULL
+            continue
+        st = lib.fckl_forward_backward(ctypes.byref(d), *ok, None, ctypes.c_float(1.0), *outs, _fake(P), size(need),
+                                       None)
+        assert st == fckl.ERR_INVALID_ARG, missing
+    st = lib.fckl_forward_backward(ctypes.byref(d), *ok, None, ctypes.c_float(1.0), *args, _fake(P), size(need - 256),
+                                   None)
+    assert st == fckl.ERR_WORKSPACE
+    bad = fckl.make_desc(512, 256, 4096, 10, -1.0, chunk=128)
+    st = lib.fckl_forward_backward(ctypes.byref(bad), *ok, None, ctypes.c_float(1.0), *args, _fake(P), size(need), None)
+    assert st == fckl.ERR_INVALID_ARG
+
+
+def test_module_validates_arguments_without_a_gpu():
+    import torch
+    from chunked_top_kl_chunk_amd.loss import FusedChunkedKLLoss
+    with pytest.raises(ValueError):
+        FusedChunkedKLLoss(temperature=0.0)
+    h = torch.zeros(4, 8, dtype=torch.bfloat16)
+    W = torch.zeros(16, 8, dtype=torch.bfloat16)
+    idx = torch.zeros(4, 2, dtype=torch.int32)
+    tl = torch.zeros(4, 2, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        FusedChunkedKLLoss()(h, W, idx, tl)
+    with pytest.raises(ValueError):
+        fckl.forward_backward(h, W, idx, tl)
