@@ -1120,38 +1120,55 @@ struct SoftGradParams {
     const float *mul;       // device scalar multiplying coef, or NULL
 };
 
-constexpr int kSgTok = 64;  // tokens per block of the gradient kernel
+constexpr int kSgTok = 128;       // tokens per block of the gradient kernel
+constexpr int kSgThreads = 512;   // its threads: 32 per token row, kSgThreads / 32 rows at a time
 
 // One block per (256-row vocabulary tile, 64 tokens).  With c the token's gradient scale:
 //   g = c ((sum p) 2^(z/T log2 e - lse log2 e) - scatter(p, idx))
 //     = c ((sum p) E 2^(m - lse log2 e) - scatter(p, idx)),   E the kept value,
 // rounded to bf16, written over E ([token][vocab]) and, through LDS, as g^T.
-__global__ __launch_bounds__(256) void softmax_grad_kernel(SoftGradParams p)
+__global__ __launch_bounds__(kSgThreads) void softmax_grad_kernel(SoftGradParams p)
 {
     __shared__ __attribute__((aligned(16))) char smem[kSgTok * kGStagePitch];
+    constexpr int kStride = kSgThreads / 32;
+    constexpr int kRows = kSgTok / kStride;     // token rows per thread
     const int tm = blockIdx.x, n0 = blockIdx.y * kSgTok, m0 = tm * 256;
     const int c = threadIdx.x & 31;     // 16-byte piece of the tile row
     const int half = c >> 4;            // its 128-row half of the vocabulary tile
-    for (int rl = threadIdx.x >> 5; rl < kSgTok; rl += 8) {
-        const int tok = n0 + rl;
+    const int r0 = threadIdx.x >> 5;
+    // Every load first: the pieces are rewritten in place below, and loads placed after
+    // those stores would each wait for them.  Rows past the chunk read row 0.
+    u32x4 e[kRows];
+    float f[kRows], gsc[kRows];
+    int ks[kRows], ke[kRows];
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+        const int tok = n0 + r0 + kStride * i;
+        const int t = tok < p.rows ? tok : 0;
+        e[i] = *reinterpret_cast<const u32x4 *>(p.ex + (size_t)t * p.Vpad + m0 + 8 * c);
+        gsc[i] = (p.w ? p.coef * p.w[t] * *p.inv_wsum : p.coef) * (p.mul ? *p.mul : 1.0f);
+        f[i] = p.psum[t] * fast_exp2(p.mw[(size_t)(2 * tm + half) * p.Cpad + t] - p.lse[t] * kLog2e);
+        const uint8_t *cr = p.cnt + (size_t)t * p.cnt_stride + tm;
+        ks[i] = cr[0];
+        ke[i] = tok < p.rows ? cr[1] : cr[0];
+    }
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+        const int rl = r0 + kStride * i, tok = n0 + rl;
         u32x4 out = {0u, 0u, 0u, 0u};
         if (tok < p.rows) {
-            const float gsc = (p.w ? p.coef * p.w[tok] * *p.inv_wsum : p.coef) * (p.mul ? *p.mul : 1.0f);
-            const float f = gsc * p.psum[tok] *
-                            fast_exp2(p.mw[(size_t)(2 * tm + half) * p.Cpad + tok] - p.lse[tok] * kLog2e);
-            const u32x4 e = *reinterpret_cast<const u32x4 *>(p.ex + (size_t)tok * p.Vpad + m0 + 8 * c);
+            const float fs = gsc[i] * f[i];
             float v[8];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                v[2 * q] = f * __uint_as_float(e[q] << 16);
-                v[2 * q + 1] = f * __uint_as_float(e[q] & 0xffff0000u);
+                v[2 * q] = fs * __uint_as_float(e[i][q] << 16);
+                v[2 * q + 1] = fs * __uint_as_float(e[i][q] & 0xffff0000u);
             }
             // the token's cached entries in this vocabulary tile that fall in this piece
-            const uint8_t *cr = p.cnt + (size_t)tok * p.cnt_stride + tm;
-            for (int k = cr[0]; k < cr[1]; ++k) {
+            for (int k = ks[i]; k < ke[i]; ++k) {
                 const int col = p.idx_s[(size_t)tok * p.K + k] - m0 - 8 * c;
                 if (col >= 0 && col < 8) {
-                    const float d = gsc * p.p_s[(size_t)tok * p.K + k];
+                    const float d = gsc[i] * p.p_s[(size_t)tok * p.K + k];
 #pragma unroll
                     for (int q = 0; q < 8; ++q)
                         v[q] -= (q == col) ? d : 0.0f;
@@ -1165,7 +1182,7 @@ __global__ __launch_bounds__(256) void softmax_grad_kernel(SoftGradParams p)
         *reinterpret_cast<u32x4 *>(smem + rl * kGStagePitch + 16 * c) = out;
     }
     __syncthreads();
-    store_vocab_major<kSgTok, 4>(smem, p.gT, (size_t)p.Cpad, m0, n0);
+    store_vocab_major<kSgTok, kSgThreads / 64>(smem, p.gT, (size_t)p.Cpad, m0, n0);
 }
 
 // ------------------------------------------------------------------ dH = g . W
@@ -1447,7 +1464,8 @@ int launch_softmax_grad(const ChunkArgs &a, const float *lse, const GradScale &g
     p.w = gs.w;
     p.inv_wsum = gs.inv_wsum;
     p.mul = gs.mul;
-    hipLaunchKernelGGL(softmax_grad_kernel, dim3(L.nVt, (a.rows + kSgTok - 1) / kSgTok), dim3(256), 0, S(stream), p);
+    hipLaunchKernelGGL(softmax_grad_kernel, dim3(L.nVt, (a.rows + kSgTok - 1) / kSgTok), dim3(kSgThreads), 0,
+                       S(stream), p);
     return (int)hipGetLastError();
 }
 

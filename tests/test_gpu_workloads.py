@@ -99,6 +99,35 @@ def test_full_workload(key):
     _check_workload(key)
 
 
+def test_single_call_at_full_size():
+    """fckl_forward_backward on the 32K-token workload: the forward outputs equal the
+    two-call path's bit for bit, the gradients agree with it to the gradient tolerance,
+    and the size-independent identities hold."""
+    wl = synth.WORKLOADS["c3"]
+    say("case: single call, full workload", wl.name)
+    x = synth.make_inputs(wl, device=device())
+    h, W, idx, tl = upload(x, device())
+    desc = fckl.desc_for(h, W, idx, tl, wl.T)
+    chunk, ws_bytes = fckl.plan(desc)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device())
+    loss1, lse1, mean1, dH1, dW1 = fckl.forward_backward(h, W, idx, tl, T=wl.T, chunk=chunk, ws=ws)
+    loss2, lse2, mean2 = fckl.forward(h, W, idx, tl, T=wl.T, chunk=chunk, ws=ws)
+    assert torch.equal(loss1, loss2) and torch.equal(lse1, lse2) and torch.equal(mean1, mean2)
+    dH2, dW2 = fckl.backward(h, W, idx, tl, lse2, T=wl.T, chunk=chunk, ws=ws)
+    torch.cuda.synchronize()
+    e_dH = float((dH1 - dH2).abs().max() / dH2.abs().max())
+    e_dW = float((dW1 - dW2).abs().max() / dW2.abs().max())
+    sum_rows = dW1.double().sum(0).abs().max().item()
+    scale_rows = dW1.double().abs().sum(0).max().item()
+    ip_w = (dW1.double() * W.double()).sum().item()
+    ip_h = (dH1.double() * h.double()).sum().item()
+    say("single call vs two-call at full size: dH %.2e dW %.2e; sum_v dW %.1e of %.1e; <dW,W> %.6e <dH,h> %.6e"
+        % (e_dH, e_dW, sum_rows, scale_rows, ip_w, ip_h))
+    assert e_dH <= GRAD_TOL and e_dW <= GRAD_TOL
+    assert sum_rows <= 1e-3 * scale_rows
+    assert abs(ip_w - ip_h) <= 2e-2 * max(abs(ip_w), abs(ip_h))
+
+
 def test_peak_memory_has_no_tokens_times_vocab_term():
     """Peak device memory of fwd+bwd at the 32K shape's H, V, K for growing N, fixed chunk:
     linear in N with the per-token cost of the inputs and outputs only."""
