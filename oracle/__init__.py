@@ -63,6 +63,8 @@ def _load() -> ctypes.CDLL:
         lib.fckl_oracle_weighted_backward.argtypes = [i64, i64, i64, i64, f64, vp, vp, vp, vp, vp, f64, i64, vp,
                                                       vp, vp]
         lib.fckl_oracle_weighted_backward.restype = ctypes.c_int
+        lib.fckl_oracle_topk.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp]
+        lib.fckl_oracle_topk.restype = ctypes.c_int
         lib.fckl_oracle_num_threads.argtypes = []
         lib.fckl_oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -169,6 +171,22 @@ def weighted_backward(h, W, idx, tl, T: float, w, grad_scale: float = 1.0, rows=
     _check(_load().fckl_oracle_weighted_backward(N, H, V, K, float(T), _ptr(h), _ptr(W), _ptr(idx), _ptr(tl),
                                                  _ptr(w), float(grad_scale), nrows, _ptr(r), _ptr(dH), _ptr(dW)))
     return dH, dW
+
+
+def topk(h, W, K: int):
+    """Per token, the K largest z = h W^T in descending order, equal values by smaller index.
+
+    Returns (idx[N, K] int32, z[N, K] float64).
+    """
+    h, W = _f64(h), _f64(W)
+    N, H = h.shape
+    V, H2 = W.shape
+    if H2 != H:
+        raise ValueError("inconsistent shapes h%s W%s" % (h.shape, W.shape))
+    idx = np.empty((N, K), np.int32)
+    val = np.empty((N, K), np.float64)
+    _check(_load().fckl_oracle_topk(N, H, V, int(K), _ptr(h), _ptr(W), _ptr(idx), _ptr(val)))
+    return idx, val
 
 
 def num_threads() -> int:

@@ -385,6 +385,72 @@ int fckl_oracle_weighted_backward(int64_t N, int64_t H, int64_t V, int64_t K, do
     return rc;
 }
 
+/*
+ * Teacher-side top-K extraction: the cache the loss reads.  The pages describe the
+ * teacher's top logits (100, or 10) and their vocabulary indices being extracted once
+ * per position and stored ("Preparing Offline Top-K Logits", getaibook.com;
+ * "Breaking the Bottleneck with Offline Caching and Chunked Loss", axbrief.com).
+ * For each token i: z[v] = sum_j h[i,j] W[v,j] over the whole vocabulary, then the K
+ * entries with the largest z, in descending order of z; equal values are ordered by
+ * the smaller index first, which makes the result unique.
+ *   idx_out[N*K] (int32), val_out[N*K] (the z of each entry).
+ */
+typedef struct {
+    double z;
+    int32_t v;
+} ranked_logit;
+
+static int rank_before(const ranked_logit *a, const ranked_logit *b)
+{
+    return a->z > b->z || (a->z == b->z && a->v < b->v);
+}
+
+int fckl_oracle_topk(int64_t N, int64_t H, int64_t V, int64_t K, const double *h, const double *W,
+                     int32_t *idx_out, double *val_out)
+{
+    if (N < 0 || H <= 0 || V <= 0 || K <= 0 || K > V || !h || !W || !idx_out || !val_out)
+        return ORACLE_EARG;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *z = (double *)malloc(sizeof(double) * (size_t)V);
+        ranked_logit *best = (ranked_logit *)malloc(sizeof(ranked_logit) * (size_t)K);
+        int have = (z && best);
+        if (!have) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < N; ++i) {
+            if (!have)
+                continue;
+            student_logits(H, V, h + i * H, W, z);
+            /* insertion into a sorted list of the K best seen so far */
+            int64_t n = 0;
+            for (int64_t v = 0; v < V; ++v) {
+                ranked_logit c = {z[v], (int32_t)v};
+                if (n == K && !rank_before(&c, &best[K - 1]))
+                    continue;
+                int64_t at = n < K ? n : K - 1;
+                while (at > 0 && rank_before(&c, &best[at - 1])) {
+                    best[at] = best[at - 1];
+                    --at;
+                }
+                best[at] = c;
+                if (n < K)
+                    ++n;
+            }
+            for (int64_t k = 0; k < K; ++k) {
+                idx_out[i * K + k] = best[k].v;
+                val_out[i * K + k] = best[k].z;
+            }
+        }
+        free(z);
+        free(best);
+    }
+    return failed ? ORACLE_EMEM : ORACLE_OK;
+}
+
 /* Number of OpenMP threads a parallel region of the oracle uses. */
 int fckl_oracle_num_threads(void)
 {

@@ -33,6 +33,12 @@ MUTANTS = {
                              "gr[v] = scale * psum * exp(z[v] - lse);"),
     "weighted_mean_over_count": ("*mean_out = wsum > 0.0 ? s / wsum : 0.0;",
                                  "*mean_out = wsum > 0.0 ? s / (double)N : 0.0;"),
+    "topk_ties_to_larger_index": ("return a->z > b->z || (a->z == b->z && a->v < b->v);",
+                                  "return a->z > b->z || (a->z == b->z && a->v > b->v);"),
+    "topk_ascending": ("return a->z > b->z || (a->z == b->z && a->v < b->v);",
+                       "return a->z < b->z || (a->z == b->z && a->v < b->v);"),
+    "topk_drops_last_slot": ("if (n == K && !rank_before(&c, &best[K - 1]))",
+                             "if (n == K && !rank_before(&c, &best[K > 1 ? K - 2 : 0]))"),
     "weighted_grad_row_weight_dropped": ("scale[r] = wsum > 0.0 ? grad_scale * T * w[i] / wsum : 0.0;",
                                          "scale[r] = wsum > 0.0 ? grad_scale * T / wsum : 0.0;"),
 }

@@ -394,3 +394,58 @@ def test_weight_scale_invariance_and_all_masked():
     bad[2] = float("nan")
     with pytest.raises(oracle.OracleError):
         oracle.weighted_backward(h, W, idx, tl, T, bad)
+
+
+# ---------------------------------------------------------------- teacher top-K extraction
+
+def brute_topk(h, W, K):
+    """numpy: full logits, then a lexicographic sort (value descending, index ascending)."""
+    z = np.asarray(h, np.float64) @ np.asarray(W, np.float64).T
+    idx = np.empty((z.shape[0], K), np.int64)
+    for i in range(z.shape[0]):
+        order = np.lexsort((np.arange(z.shape[1]), -z[i]))
+        idx[i] = order[:K]
+    return idx, np.take_along_axis(z, idx, axis=1)
+
+
+@pytest.mark.parametrize("seed,K", [(60, 1), (61, 7), (62, 50)])
+def test_topk_matches_a_full_sort(seed, K):
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((9, 16))
+    W = rng.standard_normal((120, 16))
+    idx, val = oracle.topk(h, W, K)
+    ref_idx, ref_val = brute_topk(h, W, K)
+    np.testing.assert_array_equal(idx, ref_idx)
+    np.testing.assert_allclose(val, ref_val, rtol=1e-12, atol=1e-12)
+
+
+def test_topk_ties_go_to_the_smaller_index_and_full_sort():
+    rng = np.random.default_rng(63)
+    h = rng.standard_normal((4, 8))
+    W = rng.standard_normal((30, 8))
+    W[17] = W[4]            # equal logits for 4 and 17 in every token
+    W[25] = W[4]
+    idx, _ = oracle.topk(h, W, 30)
+    for i in range(4):
+        order = list(idx[i])
+        assert order.index(4) < order.index(17) < order.index(25)
+        assert sorted(order) == list(range(30))          # K = V is a permutation
+    idx0, val0 = oracle.topk(h, np.zeros_like(W), 5)     # all logits equal
+    assert (idx0 == np.arange(5)).all() and (val0 == 0).all()
+
+
+def test_topk_invariances():
+    rng = np.random.default_rng(64)
+    h = rng.standard_normal((6, 10))
+    W = rng.standard_normal((80, 10))
+    idx, val = oracle.topk(h, W, 12)
+    perm = rng.permutation(80)                             # W_perm[r] = W[perm[r]]
+    idx_p, val_p = oracle.topk(h, W[perm], 12)
+    np.testing.assert_array_equal(perm[idx_p], idx)
+    np.testing.assert_allclose(val_p, val, rtol=1e-13)
+    idx_s, val_s = oracle.topk(3.0 * h, W, 12)             # positive scaling keeps the order
+    np.testing.assert_array_equal(idx_s, idx)
+    np.testing.assert_allclose(val_s, 3.0 * val, rtol=1e-13)
+    for badK in (0, 81):
+        with pytest.raises(oracle.OracleError):
+            oracle.topk(h, W, badK)
