@@ -14,7 +14,8 @@ library records around each launch on its own stream during the timed steps.
 `cpu_baseline` times the CPU oracle (fp64) on a small sample of the same tokens.
 `single_call` times the same step done by fckl_forward_backward, which forms each
 chunk's logits once (6 N V H flop); it is reported beside the main line, which times
-the two passes of the method as defined (8 N V H flop).
+the two passes of the method as defined (8 N V H flop).  `teacher_topk` times the
+teacher-side extraction of the top-K cache from the same hidden states (fckl_topk).
 """
 from __future__ import annotations
 
@@ -78,6 +79,8 @@ def main():
     ap.add_argument("--dense", action="store_true", help="also measure peak memory of a dense torch KL baseline")
     ap.add_argument("--no-single-call", action="store_true",
                     help="skip timing fckl_forward_backward (the single-call path) after the main measurement")
+    ap.add_argument("--no-topk", action="store_true",
+                    help="skip timing the teacher-side top-K extraction (fckl_topk) of the same hidden states")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (reference dispatch for HBM byte counters)")
     args = ap.parse_args()
@@ -194,6 +197,26 @@ def main():
             "kernels": {k: {"launches": v["launches"], "ms_per_step": round(v["ms"] / args.steps, 4)}
                         for k, v in k1.items()},
         }
+
+    if not args.no_topk:
+        # Teacher-side extraction of the cache the loss reads: top-K of h W^T, two passes
+        # of the logit product (4 N V H flop), on the same tensors.
+        tws = torch.empty(fckl.topk_workspace_size(fckl.make_desc(N, H, V, K)), dtype=torch.uint8, device=dev)
+        ti = torch.empty(N, K, dtype=torch.int32, device=dev)
+        tv = torch.empty(N, K, dtype=torch.bfloat16, device=dev)
+        fckl.topk(h, W, K, ws=tws, topk_idx=ti, topk_logit=tv)
+        torch.cuda.synchronize()
+        reps = max(1, min(args.steps, 3))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fckl.topk(h, W, K, ws=tws, topk_idx=ti, topk_logit=tv)
+        torch.cuda.synchronize()
+        ms_t = (time.perf_counter() - t0) * 1e3 / reps
+        log("teacher top-%d: %.2f ms per call" % (K, ms_t))
+        out["teacher_topk"] = {"K": K, "ms_per_call": round(ms_t, 3), "tokens_per_s": round(N * 1e3 / ms_t, 1),
+                               "flops_per_call": 4.0 * N * V * H,
+                               "mfma_frac": round(4.0 * N * V * H / (ms_t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del tws, ti, tv
 
     if args.dense:
         # the fused path's workspace and outputs are released first: the dense loss is

@@ -34,7 +34,8 @@ FLAG_VALIDATE, FLAG_DW_ACCUMULATE = 1, 2
 
 # Every symbol include/fckl.h declares.
 EXPORTS = ("fckl_plan", "fckl_workspace_size", "fckl_forward", "fckl_backward", "fckl_forward_ex",
-           "fckl_backward_ex", "fckl_forward_backward", "fckl_status_string", "fckl_version")
+           "fckl_backward_ex", "fckl_forward_backward", "fckl_topk_workspace_size", "fckl_topk",
+           "fckl_status_string", "fckl_version")
 
 
 KERNELS = ("prepare", "fwd_logits", "combine", "mean", "bwd_logits", "dh", "dh_reduce", "dw", "transpose",
@@ -86,8 +87,10 @@ def load() -> ctypes.CDLL:
     lib.fckl_status_string.restype = ctypes.c_char_p
     lib.fckl_version.argtypes = []
     lib.fckl_version.restype = ctypes.c_int32
+    lib.fckl_topk_workspace_size.argtypes = [P(Desc), ctypes.c_int32, P(sz)]
+    lib.fckl_topk.argtypes = [P(Desc), vp, vp, vp, vp, vp, sz, vp]
     for f in ("fckl_plan", "fckl_workspace_size", "fckl_forward", "fckl_backward", "fckl_forward_ex",
-              "fckl_backward_ex", "fckl_forward_backward"):
+              "fckl_backward_ex", "fckl_forward_backward", "fckl_topk_workspace_size", "fckl_topk"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -284,5 +287,42 @@ def forward_backward(h, W, topk_idx, topk_logit, T: float = 1.0, grad_scale: flo
     return loss_tok, lse, loss_mean, dH, dW
 
 
+def topk_workspace_size(desc: Desc, chunk: int = 0) -> int:
+    ws = ctypes.c_size_t(0)
+    _call("fckl_topk_workspace_size", ctypes.byref(desc), ctypes.c_int32(chunk), ctypes.byref(ws))
+    return int(ws.value)
+
+
+def topk(h, W, K: int, chunk: int = 0, logits_f32: bool = False, ws=None, topk_idx=None, topk_logit=None,
+         stream=None):
+    """Teacher-side extraction (fckl_topk): per token the K largest z = h W^T, descending,
+    equal values by the smaller index.  Returns (topk_idx int32 [N,K], topk_logit [N,K]
+    bf16, or float32 with logits_f32)."""
+    import torch
+    for name, t in (("h", h), ("W", W)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError("%s must be a contiguous bfloat16 device tensor" % name)
+    if h.dim() != 2 or W.dim() != 2 or W.shape[1] != h.shape[1] or h.device != W.device:
+        raise ValueError("expected h[N,H] and W[V,H] on one device")
+    N, dev = h.shape[0], h.device
+    desc = make_desc(N, h.shape[1], W.shape[0], K, 1.0, chunk, DTYPE_F32 if logits_f32 else DTYPE_BF16)
+    need = topk_workspace_size(desc, chunk)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    if ws.numel() * ws.element_size() < need or not ws.is_contiguous():
+        raise ValueError("workspace of %d bytes needed" % need)
+    if topk_idx is None:
+        topk_idx = torch.empty((N, K), dtype=torch.int32, device=dev)
+    ldt = torch.float32 if logits_f32 else torch.bfloat16
+    if topk_logit is None:
+        topk_logit = torch.empty((N, K), dtype=ldt, device=dev)
+    for name, t, dt in (("topk_idx", topk_idx, torch.int32), ("topk_logit", topk_logit, ldt)):
+        if t.dtype != dt or tuple(t.shape) != (N, K) or not t.is_contiguous() or t.device != dev:
+            raise ValueError("%s must be a contiguous %s tensor of shape (%d, %d)" % (name, dt, N, K))
+    _call("fckl_topk", ctypes.byref(desc), h.data_ptr(), W.data_ptr(), topk_idx.data_ptr(), topk_logit.data_ptr(),
+          ws.data_ptr(), ctypes.c_size_t(ws.numel() * ws.element_size()), _stream_handle(stream))
+    return topk_idx, topk_logit
+
+
 __all__ = ["Desc", "Profile", "KERNELS", "FCKLError", "load", "plan", "workspace_size", "forward", "backward",
-           "forward_backward", "make_desc", "desc_for", "status_string", "version", "EXPORTS", "LIB_PATH"]
+           "forward_backward", "topk", "topk_workspace_size", "make_desc", "desc_for", "status_string", "version", "EXPORTS", "LIB_PATH"]

@@ -359,6 +359,59 @@ fckl_status fckl_forward_backward(const fckl_desc *desc, const void *h, const vo
     return loss_mean ? mean_of(desc, loss_tok, weights, loss_mean, stream) : FCKL_OK;
 }
 
+fckl_status fckl_topk_workspace_size(const fckl_desc *desc, int32_t chunk, size_t *ws_bytes_out)
+{
+    TopkLayout T;
+    fckl_status st = make_topk_layout(desc, chunk, &T);
+    if (st != FCKL_OK)
+        return st;
+    if (ws_bytes_out)
+        *ws_bytes_out = T.total;
+    return FCKL_OK;
+}
+
+fckl_status fckl_topk(const fckl_desc *desc, const void *h, const void *W, int32_t *topk_idx, void *topk_logit,
+                      void *ws, size_t ws_bytes, void *stream)
+{
+    TopkLayout T;
+    fckl_status st = make_topk_layout(desc, desc ? desc->chunk : 0, &T);
+    if (st != FCKL_OK)
+        return st;
+    if (!h || !W || !topk_idx || !topk_logit || !ws)
+        return FCKL_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || (reinterpret_cast<uintptr_t>(h) & 15u) != 0 ||
+        (reinterpret_cast<uintptr_t>(W) & 15u) != 0)
+        return FCKL_ERR_INVALID_ARG;
+    if (T.total > ws_bytes)
+        return FCKL_ERR_WORKSPACE;
+    uint32_t *flag = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(ws) + T.off_err);
+    if (launch_zero_flag(flag, stream))
+        return FCKL_ERR_HIP;
+    const bool f32 = desc->logit_dtype == FCKL_DTYPE_F32;
+    const size_t esz = f32 ? 4 : 2;
+    for (int64_t c0 = 0; c0 < desc->N; c0 += T.C) {
+        ChunkArgs a;
+        a.h = reinterpret_cast<const uint16_t *>(h) + (size_t)c0 * desc->H;
+        a.W = reinterpret_cast<const uint16_t *>(W);
+        a.rows = (int32_t)((desc->N - c0) < T.C ? (desc->N - c0) : T.C);
+        a.H = desc->H;
+        a.V = desc->V;
+        a.K = desc->K;
+        a.T = desc->T;
+        a.ws = reinterpret_cast<char *>(ws);
+        if (launch_topk_max(a, T, stream) || launch_topk_threshold(a, T, stream) || launch_topk_collect(a, T, stream) ||
+            launch_topk_select(a, T, topk_idx + (size_t)c0 * desc->K,
+                               reinterpret_cast<char *>(topk_logit) + (size_t)c0 * desc->K * esz, f32, stream))
+            return FCKL_ERR_HIP;
+    }
+    uint32_t host = 0;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(&host, flag, sizeof(host), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return FCKL_ERR_HIP;
+    return host ? FCKL_ERR_UNSUPPORTED : FCKL_OK;
+}
+
 const char *fckl_status_string(fckl_status s)
 {
     switch (s) {

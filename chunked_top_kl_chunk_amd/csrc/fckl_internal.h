@@ -17,6 +17,11 @@ constexpr int kTokenTile = 256;
 // for dH (higher operand reuse per loaded byte) and tie for dW.
 constexpr int kHiddenTile = 256;
 constexpr int kMaxK = 128;
+// Teacher top-K extraction: candidates kept per token (the logits at or above the K-th
+// largest of the token's 32-row sub-tile maxima), and the most sub-tile maxima per token
+// (V <= 2^21; their buffer is 4 bytes per maximum and token of a chunk).
+constexpr int kTopkCap = 2048;
+constexpr int kTopkMaxSub = 65536;
 constexpr int32_t kMaxChunk = 8192;
 constexpr size_t kDefaultBudget = size_t(12) << 30;  // 12 GiB of the 288 GB HBM3E
 
@@ -48,7 +53,19 @@ struct Layout {
     size_t total = 0;
 };
 
+// Workspace of the teacher top-K extraction (its own, much smaller than the loss's).
+struct TopkLayout {
+    int32_t C = 0, Cpad = 0, nVt = 0, nSub = 0;
+    size_t off_tmax = 0;    // f32   [nSub, Cpad]  maximum of z over each 256-row tile (or 32-row slice)
+    size_t off_thr = 0;     // f32   [Cpad]        K-th largest of a token's maxima
+    size_t off_count = 0;   // u32   [Cpad]        candidates found per token
+    size_t off_cand = 0;    // u64   [Cpad, kTopkCap] candidate keys
+    size_t off_err = 0;     // u32   [4]           overflow flag
+    size_t total = 0;
+};
+
 fckl_status check_desc(const fckl_desc *d);
+fckl_status make_topk_layout(const fckl_desc *d, int32_t chunk, TopkLayout *L);
 fckl_status make_layout(const fckl_desc *d, int32_t chunk, Layout *L);
 fckl_status plan_chunk(const fckl_desc *d, size_t budget, Layout *L);
 
@@ -97,5 +114,15 @@ int launch_dw(const ChunkArgs &a, float *dW, bool accumulate, void *stream);
 int launch_transpose_head(const ChunkArgs &a, void *stream);
 int launch_transpose_chunk(const ChunkArgs &a, void *stream);
 int launch_zero_flag(uint32_t *flag, void *stream);
+
+// Teacher top-K extraction of one chunk (a.L is unused; T is the top-K layout): the
+// 32-row sub-tile maxima of z, the per-token threshold, the candidates at or above it,
+// and the ordered selection (topk_logit written as f32 or bf16).  Candidate overflow
+// sets the error flag.
+int launch_topk_max(const ChunkArgs &a, const TopkLayout &T, void *stream);
+int launch_topk_threshold(const ChunkArgs &a, const TopkLayout &T, void *stream);
+int launch_topk_collect(const ChunkArgs &a, const TopkLayout &T, void *stream);
+int launch_topk_select(const ChunkArgs &a, const TopkLayout &T, int32_t *topk_idx, void *topk_logit, bool logit_f32,
+                       void *stream);
 
 }  // namespace fckl

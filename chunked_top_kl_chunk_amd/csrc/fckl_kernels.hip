@@ -1185,6 +1185,244 @@ __global__ __launch_bounds__(kSgThreads) void softmax_grad_kernel(SoftGradParams
     store_vocab_major<kSgTok, kSgThreads / 64>(smem, p.gT, (size_t)p.Cpad, m0, n0);
 }
 
+// ------------------------------------------------------------------ teacher top-K
+
+// The teacher's cache holds, per position, its top logits and their indices, extracted
+// once ("Preparing Offline Top-K Logits", getaibook.com).  Exact top-K of z = h W^T per
+// token in two passes of the logit GEMM:
+//   1. the maximum of z over each 256-row tile of the vocabulary per token, or over each
+//      32-row slice when there are fewer tiles than K;
+//   2. tau = the K-th largest of those maxima is at most the K-th largest logit (the
+//      maxima are K actual logits), so every logit >= tau is collected as a candidate
+//      (tau comes from a per-token min-heap of K entries);
+//   3. the candidates are sorted by (z descending, index ascending) and the first K kept.
+// z is bitwise the same in both passes (same tiles, same accumulation order), so the
+// logit that attains a maximum passes its own threshold.
+
+struct TopkParams {
+    const uint16_t *W;      // [V, H]
+    const uint16_t *h;      // [rows, H] chunk
+    int H, V, rows, Cpad, nVt, nNt;
+    int slices;             // maxima per 256-row tile: 1 or 8 (32-row slices)
+    float *tmax;            // [slices nVt, Cpad] maxima (pass 1)
+    const float *thr;       // [Cpad] thresholds (pass 2)
+    uint32_t *count;        // [Cpad] candidates per token (pass 2)
+    uint64_t *cand;         // [Cpad, kTopkCap] candidate keys (pass 2)
+};
+
+// Unsigned key whose ascending order is z descending, then index ascending: the high
+// word is the complement of an order-preserving image of z (-0 taken as +0), the low
+// word the index.
+__device__ __forceinline__ uint32_t topk_zkey(float z)
+{
+    uint32_t u = __float_as_uint(z + 0.0f);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ~u;
+}
+__device__ __forceinline__ float topk_zkey_value(uint32_t key)
+{
+    uint32_t u = ~key;
+    u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
+    return __uint_as_float(u);
+}
+
+template <bool COLLECT>
+__device__ __forceinline__ void topk_tile(const TopkParams &p, char *smem, int t)
+{
+    using G = LogitGemm;
+    int tm, tn;
+    map_tile(t, p.nVt, p.nNt, 4, tm, tn);
+    const int m0 = tm * G::BM, n0 = tn * G::BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / G::WN, wn = wave % G::WN;
+    float thr[G::NB];
+    if constexpr (COLLECT) {
+#pragma unroll
+        for (int j = 0; j < G::NB; ++j) {
+            const int tok = n0 + G::col_of(wn, j, lane);
+            thr[j] = tok < p.rows ? p.thr[tok] : __builtin_inff();
+        }
+    }
+    f32x16 acc[G::MB][G::NB];
+    G::run(smem, p.W, p.H, m0, p.V, p.H, p.h, p.H, n0, p.rows, p.H, 0, p.H, acc);
+    // element (i, r) of the lane sits at row row_of(wm, 0, 0, lane) + 32 i + 8 (r/4) + r%4
+    const int lim = p.V - m0 - G::row_of(wm, 0, 0, lane);
+    float tile_mx[G::NB];
+#pragma unroll
+    for (int j = 0; j < G::NB; ++j) {
+        const int tok = n0 + G::col_of(wn, j, lane);
+        tile_mx[j] = -__builtin_inff();
+#pragma unroll
+        for (int i = 0; i < G::MB; ++i) {
+            if constexpr (!COLLECT) {
+                // 32-row block i of the wave: 16 rows in this lane, 16 in lane ^ 32
+                float mx = -__builtin_inff();
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    mx = fmaxf(mx, (32 * i + 8 * (r >> 2) + (r & 3) < lim) ? acc[i][j][r] : -__builtin_inff());
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                tile_mx[j] = fmaxf(tile_mx[j], mx);
+                if (p.slices == 8 && lane < 32 && tok < p.rows)
+                    p.tmax[(size_t)(8 * tm + (G::WTM / 32) * wm + i) * p.Cpad + tok] = mx;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float z = acc[i][j][r];
+                    if (32 * i + 8 * (r >> 2) + (r & 3) < lim && z >= thr[j]) {
+                        const uint32_t slot = atomicAdd(p.count + tok, 1u);
+                        if (slot < (uint32_t)kTopkCap)
+                            p.cand[(size_t)tok * kTopkCap + slot] =
+                                ((uint64_t)topk_zkey(z) << 32) | (uint32_t)(m0 + G::row_of(wm, i, r, lane));
+                    }
+                }
+            }
+        }
+    }
+    if constexpr (!COLLECT) {
+        if (p.slices == 1) {
+            // the two waves holding a token's 256 rows merge their maxima through LDS
+            float *red = reinterpret_cast<float *>(smem);   // [WM][BN]
+#pragma unroll
+            for (int j = 0; j < G::NB; ++j)
+                if (lane < 32)
+                    red[wm * G::BN + G::col_of(wn, j, lane)] = tile_mx[j];
+            __syncthreads();
+            for (int nl = threadIdx.x; nl < G::BN; nl += G::NT)
+                if (n0 + nl < p.rows) {
+                    float m = red[nl];
+#pragma unroll
+                    for (int w2 = 1; w2 < G::WM; ++w2)
+                        m = fmaxf(m, red[w2 * G::BN + nl]);
+                    p.tmax[(size_t)tm * p.Cpad + n0 + nl] = m;
+                }
+        }
+    }
+}
+
+template <bool COLLECT>
+__global__ __launch_bounds__(LogitGemm::NT) void topk_logits_kernel(TopkParams p)
+{
+    __shared__ __attribute__((aligned(16))) char smem[LogitGemm::LDS_BYTES];
+    for (int t = blockIdx.x; t < p.nVt * p.nNt; t += gridDim.x) {
+        topk_tile<COLLECT>(p, smem, t);
+        __syncthreads();
+    }
+}
+
+// Ascending bitonic sort of s[0, P) (P a power of two) by one wave.
+template <class T>
+__device__ void wave_bitonic_sort(T *s, int P)
+{
+    const int lane = threadIdx.x & 63;
+    for (int k = 2; k <= P; k <<= 1)
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int q = lane; q < P / 2; q += 64) {
+                const int i = 2 * q - (q & (j - 1));    // the pair (i, i + j), bit j of i clear
+                const T a = s[i], b = s[i + j];
+                if ((a > b) == ((i & k) == 0)) {
+                    s[i] = b;
+                    s[i + j] = a;
+                }
+            }
+            __syncthreads();
+        }
+}
+
+// Restores the min-heap order below entry j of a heap of n floats whose entry e sits at
+// hp[e * 64] (one heap per lane, interleaved so that the lanes' accesses do not collide).
+__device__ __forceinline__ void heap_sift_down(float *hp, int j, int n)
+{
+    const float v = hp[j * 64];
+    for (;;) {
+        const int l = 2 * j + 1;
+        if (l >= n)
+            break;
+        const int m = (l + 1 < n && hp[(l + 1) * 64] < hp[l * 64]) ? l + 1 : l;
+        if (!(hp[m * 64] < v))
+            break;
+        hp[j * 64] = hp[m * 64];
+        j = m;
+    }
+    hp[j * 64] = v;
+}
+
+// One lane per token: tau = the K-th largest of the token's nSub sub-tile maxima (-inf
+// when there are fewer than K) as the root of a K-entry min-heap, and the token's
+// candidate count reset.  Consecutive lanes read consecutive tokens of each maxima row.
+__global__ __launch_bounds__(64) void topk_threshold_kernel(const float *tmax, int nSub, int Cpad, int rows, int K,
+                                                          float *thr, uint32_t *count)
+{
+    __shared__ float heap[kMaxK * 64];
+    const int lane = threadIdx.x, tok = blockIdx.x * 64 + lane;
+    if (tok >= rows)
+        return;
+    count[tok] = 0u;
+    if (K > nSub) {
+        thr[tok] = -__builtin_inff();
+        return;
+    }
+    float *hp = heap + lane;
+    for (int j = 0; j < K; ++j)
+        hp[j * 64] = tmax[(size_t)j * Cpad + tok];
+    for (int j = K / 2 - 1; j >= 0; --j)
+        heap_sift_down(hp, j, K);
+    constexpr int kBatch = 8;
+    int i = K;
+    for (; i + kBatch <= nSub; i += kBatch) {
+        float v[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q)
+            v[q] = tmax[(size_t)(i + q) * Cpad + tok];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q)
+            if (v[q] > hp[0]) {
+                hp[0] = v[q];
+                heap_sift_down(hp, 0, K);
+            }
+    }
+    for (; i < nSub; ++i) {
+        const float v = tmax[(size_t)i * Cpad + tok];
+        if (v > hp[0]) {
+            hp[0] = v;
+            heap_sift_down(hp, 0, K);
+        }
+    }
+    thr[tok] = hp[0];
+}
+
+// One wave per token: sort the candidates and write the first K (index, z).  More
+// candidates than kTopkCap (many logits tied at the threshold), or fewer than K,
+// raise the error flag.
+__global__ __launch_bounds__(64) void topk_select_kernel(const uint64_t *cand, const uint32_t *count, int K,
+                                                         int32_t *idx_out, void *logit_out, int logit_f32,
+                                                         uint32_t *err)
+{
+    __shared__ uint64_t s[kTopkCap];
+    const int tok = blockIdx.x, lane = threadIdx.x;
+    const uint32_t n = count[tok];
+    if (n > (uint32_t)kTopkCap || n < (uint32_t)K) {
+        if (lane == 0)
+            *err = 1u;
+        return;
+    }
+    int P = 1;
+    while (P < (int)n)
+        P <<= 1;
+    for (int i = lane; i < P; i += 64)
+        s[i] = i < (int)n ? cand[(size_t)tok * kTopkCap + i] : ~0ull;
+    __syncthreads();
+    wave_bitonic_sort(s, P);
+    for (int k = lane; k < K; k += 64) {
+        const uint64_t key = s[k];
+        const float z = topk_zkey_value((uint32_t)(key >> 32));
+        idx_out[(size_t)tok * K + k] = (int32_t)(uint32_t)key;
+        if (logit_f32)
+            reinterpret_cast<float *>(logit_out)[(size_t)tok * K + k] = z;
+        else
+            reinterpret_cast<uint16_t *>(logit_out)[(size_t)tok * K + k] = (uint16_t)pack_bf16x2(z, 0.0f);
+    }
+}
+
 // ------------------------------------------------------------------ dH = g . W
 
 struct DhParams {
@@ -1583,6 +1821,59 @@ int launch_transpose_chunk(const ChunkArgs &a, void *stream)
 int launch_zero_flag(uint32_t *flag, void *stream)
 {
     hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, S(stream), flag, 4);
+    return (int)hipGetLastError();
+}
+
+static TopkParams topk_params(const ChunkArgs &a, const TopkLayout &T)
+{
+    TopkParams p;
+    p.W = a.W;
+    p.h = a.h;
+    p.H = a.H;
+    p.V = a.V;
+    p.rows = a.rows;
+    p.Cpad = T.Cpad;
+    p.nVt = T.nVt;
+    p.nNt = (a.rows + LogitGemm::BN - 1) / LogitGemm::BN;
+    p.slices = T.nSub / T.nVt;
+    p.tmax = reinterpret_cast<float *>(a.ws + T.off_tmax);
+    p.thr = reinterpret_cast<const float *>(a.ws + T.off_thr);
+    p.count = reinterpret_cast<uint32_t *>(a.ws + T.off_count);
+    p.cand = reinterpret_cast<uint64_t *>(a.ws + T.off_cand);
+    return p;
+}
+
+int launch_topk_max(const ChunkArgs &a, const TopkLayout &T, void *stream)
+{
+    const TopkParams p = topk_params(a, T);
+    hipLaunchKernelGGL(topk_logits_kernel<false>, dim3(persistent_grid(p.nVt * p.nNt)), dim3(LogitGemm::NT), 0,
+                       S(stream), p);
+    return (int)hipGetLastError();
+}
+
+int launch_topk_threshold(const ChunkArgs &a, const TopkLayout &T, void *stream)
+{
+    hipLaunchKernelGGL(topk_threshold_kernel, dim3((a.rows + 63) / 64), dim3(64), 0, S(stream),
+                       reinterpret_cast<const float *>(a.ws + T.off_tmax), T.nSub, T.Cpad, a.rows, a.K,
+                       reinterpret_cast<float *>(a.ws + T.off_thr), reinterpret_cast<uint32_t *>(a.ws + T.off_count));
+    return (int)hipGetLastError();
+}
+
+int launch_topk_collect(const ChunkArgs &a, const TopkLayout &T, void *stream)
+{
+    const TopkParams p = topk_params(a, T);
+    hipLaunchKernelGGL(topk_logits_kernel<true>, dim3(persistent_grid(p.nVt * p.nNt)), dim3(LogitGemm::NT), 0,
+                       S(stream), p);
+    return (int)hipGetLastError();
+}
+
+int launch_topk_select(const ChunkArgs &a, const TopkLayout &T, int32_t *topk_idx, void *topk_logit, bool logit_f32,
+                       void *stream)
+{
+    hipLaunchKernelGGL(topk_select_kernel, dim3(a.rows), dim3(64), 0, S(stream),
+                       reinterpret_cast<const uint64_t *>(a.ws + T.off_cand),
+                       reinterpret_cast<const uint32_t *>(a.ws + T.off_count), a.K, topk_idx, topk_logit,
+                       logit_f32 ? 1 : 0, reinterpret_cast<uint32_t *>(a.ws + T.off_err));
     return (int)hipGetLastError();
 }
 

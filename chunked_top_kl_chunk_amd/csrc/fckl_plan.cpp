@@ -107,6 +107,41 @@ fckl_status make_layout(const fckl_desc *d, int32_t chunk, Layout *L)
     return FCKL_OK;
 }
 
+fckl_status make_topk_layout(const fckl_desc *d, int32_t chunk, TopkLayout *L)
+{
+    fckl_status st = check_desc(d);
+    if (st != FCKL_OK)
+        return st;
+    if (chunk < 0 || !L)
+        return FCKL_ERR_INVALID_ARG;
+    if (chunk == 0)
+        chunk = (int32_t)std::min<int64_t>(align_up((size_t)d->N, kTokenTile), kMaxChunk);
+    TopkLayout o;
+    o.C = chunk;
+    o.Cpad = (int32_t)align_up((size_t)chunk, kTokenTile);
+    o.nVt = (d->V + kVocabTile - 1) / kVocabTile;
+    // maxima per token: one per tile when there are at least K tiles, else one per
+    // 32-row slice (8 per tile)
+    o.nSub = o.nVt >= d->K ? o.nVt : o.nVt * (kVocabTile / 32);
+    if (o.nSub > kTopkMaxSub)
+        return FCKL_ERR_UNSUPPORTED;
+    const size_t Cp = (size_t)o.Cpad;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + bytes, 256);
+        return at;
+    };
+    o.off_tmax = take((size_t)o.nSub * Cp * 4);
+    o.off_thr = take(Cp * 4);
+    o.off_count = take(Cp * 4);
+    o.off_cand = take(Cp * (size_t)kTopkCap * 8);
+    o.off_err = take(16);
+    o.total = off;
+    *L = o;
+    return FCKL_OK;
+}
+
 fckl_status plan_chunk(const fckl_desc *d, size_t budget, Layout *L)
 {
     fckl_status st = check_desc(d);

@@ -218,6 +218,31 @@ fckl_status fckl_forward_backward(const fckl_desc *desc, const void *h, const vo
                                   float *loss_tok, float *lse, float *loss_mean,
                                   float *dH, float *dW, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Teacher-side top-K extraction: the cache the loss reads.  The teacher's top logits
+ * (100, or 10) and their vocabulary indices are extracted once per position and stored
+ * ("Preparing Offline Top-K Logits", getaibook.com; "Breaking the Bottleneck with
+ * Offline Caching and Chunked Loss", axbrief.com).  For each token i, the K entries of
+ * z[i,v] = sum_j h[i,j] W[v,j] with the largest z, in descending order of z; equal
+ * values are ordered by the smaller index first.  z is accumulated in fp32 from bf16
+ * inputs (the same GEMM tiles as the loss).  Two passes of the product: the maxima of z
+ * over 32-row slices of the vocabulary give a threshold at or below the K-th largest z,
+ * and the logits at or above it are sorted.
+ *   desc       N, H, V, K (K <= 128), chunk (0 = up to 8192 tokens); logit_dtype selects
+ *              the type of topk_logit; T, flags and profile are not used (T must be valid)
+ *   h          device, bf16 [N,H]      the teacher's final hidden states
+ *   W          device, bf16 [V,H]      the teacher's LM head
+ *   topk_idx   device, int32 [N,K]     out: indices, descending z
+ *   topk_logit device, bf16 or f32 [N,K] out: z at those indices (bf16: rounded to nearest even)
+ *   ws         device, fckl_topk_workspace_size bytes, 256-byte aligned
+ * Returns FCKL_ERR_UNSUPPORTED when V > 2097152, or when more than 2048 logits of one
+ * token lie at or above its threshold (massive ties, e.g. a zero head); the outputs are
+ * then undefined.  Checking that needs one host synchronisation at the end of the call.
+ */
+fckl_status fckl_topk_workspace_size(const fckl_desc *desc, int32_t chunk, size_t *ws_bytes_out);
+fckl_status fckl_topk(const fckl_desc *desc, const void *h, const void *W, int32_t *topk_idx,
+                      void *topk_logit, void *ws, size_t ws_bytes, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *fckl_status_string(fckl_status status);
 
