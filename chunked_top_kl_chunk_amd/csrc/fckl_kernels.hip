@@ -173,36 +173,42 @@ struct KTile {
         return CPR == 8 ? ((row & 7) ^ ((row >> 3) & 1)) : ((row >> 2) & 3);
     }
 
-    // Source state.  `base` (uniform) points at row row0, column k0 of the current
-    // k-slice; per piece, a lane keeps its 32-bit element offset from there and a
-    // check value: the piece's k offset, or a huge number when its row does not exist.
+    // Source state.  Piece i of a lane covers tile row r + i * RSTRIDE at 16-byte k-chunk
+    // kc, with r and kc the same for every piece: the slot of piece i is
+    // (i * NT/64 + wave) * 64 + lane, i.e. row (i * NT/64 + wave) * 64/CPR + lane/CPR and
+    // chunk lane % CPR, and the swizzle of a row depends only on row bits that i does not
+    // change.  So a lane keeps the element offset of its first piece, its k offset
+    // kc * 8 (the k-range check) and the rows left below the operand's end; `base`
+    // (uniform) points at row row0, column k0 of the current k-slice.
+    static constexpr int RSTRIDE = NT / CPR;
+    static_assert((NT / 64) % 2 == 0 || CPR == 4, "swizzle invariant across pieces");
     struct Src {
         const uint16_t *base;
-        uint32_t off[PER];
-        int kchk[PER];
+        uint32_t off0;          // element offset of piece 0 from base
+        uint32_t step;          // element offset between consecutive pieces (RSTRIDE rows)
+        int kc8;                // k offset of the lane's chunk within the slice
+        int rlim;               // rows_valid - row0 - (row of piece 0)
     };
     __device__ __forceinline__ static void init(Src &s, const uint16_t *base, int64_t ld, int row0, int rows_valid,
                                                 int k_begin)
     {
         const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
         s.base = base + (int64_t)row0 * ld + k_begin;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int pslot = (i * (NT / 64) + wave) * 64 + lane;
-            const int row = pslot / CPR, pc = pslot % CPR;
-            const int kc = pc ^ sw(row);
-            const bool ok = row0 + row < rows_valid;
-            s.off[i] = ok ? (uint32_t)(row * ld + kc * 8) : 0u;
-            s.kchk[i] = ok ? kc * 8 : (1 << 30);
-        }
+        const int pslot = wave * 64 + lane;
+        const int row = pslot / CPR, pc = pslot % CPR;
+        s.kc8 = (pc ^ sw(row)) * 8;
+        s.off0 = (uint32_t)(row * ld + s.kc8);
+        s.step = (uint32_t)(RSTRIDE * ld);
+        s.rlim = rows_valid - row0 - row;
     }
     // Piece i of the k-slice [k0, k0 + BKK) into `tile` (a piece past k_valid or past
     // the last row comes from the zero page).
     __device__ __forceinline__ static void issue_one(const Src &s, int i, int k0, int k_valid, char *tile)
     {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        const bool ok = k0 + s.kchk[i] < k_valid;
-        const void *src = ok ? static_cast<const void *>(s.base + s.off[i]) : static_cast<const void *>(kZeroPage);
+        const bool ok = RSTRIDE * i < s.rlim && k0 + s.kc8 < k_valid;
+        const void *src = ok ? static_cast<const void *>(s.base + s.off0 + (uint32_t)i * s.step)
+                             : static_cast<const void *>(kZeroPage);
         copy16_to_lds(src, tile + (i * (NT / 64) + wave) * 1024);
     }
     // Move the source to the next k-slice.
