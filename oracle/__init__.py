@@ -65,6 +65,8 @@ def _load() -> ctypes.CDLL:
         lib.fckl_oracle_weighted_backward.restype = ctypes.c_int
         lib.fckl_oracle_topk.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp]
         lib.fckl_oracle_topk.restype = ctypes.c_int
+        lib.fckl_oracle_full.argtypes = [i64, i64, i64, i64, f64, vp, vp, vp, vp, vp, f64, vp, vp, vp, vp, vp]
+        lib.fckl_oracle_full.restype = ctypes.c_int
         lib.fckl_oracle_num_threads.argtypes = []
         lib.fckl_oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -187,6 +189,30 @@ def topk(h, W, K: int):
     val = np.empty((N, K), np.float64)
     _check(_load().fckl_oracle_topk(N, H, V, int(K), _ptr(h), _ptr(W), _ptr(idx), _ptr(val)))
     return idx, val
+
+
+def full(hs, Ws, ht, Wt, T: float, w=None, grad_scale: float = 1.0, want_grads: bool = True):
+    """Online distillation against the full teacher distribution p = softmax(ht Wt^T / T).
+
+    Returns (loss[N], lse[N] of the student, weighted mean, dH[N,Hs] or None, dW[V,Hs] or None).
+    """
+    hs, Ws, ht, Wt = _f64(hs), _f64(Ws), _f64(ht), _f64(Wt)
+    N, Hs = hs.shape
+    V, Hs2 = Ws.shape
+    N2, Ht = ht.shape
+    if Hs2 != Hs or N2 != N or Wt.shape != (V, Ht):
+        raise ValueError("inconsistent shapes hs%s Ws%s ht%s Wt%s" % (hs.shape, Ws.shape, ht.shape, Wt.shape))
+    wv = None if w is None else _f64(w)
+    if wv is not None and wv.shape != (N,):
+        raise ValueError("weights must have shape (N,)")
+    loss = np.empty(N, np.float64)
+    lse = np.empty(N, np.float64)
+    mean = np.zeros(1, np.float64)
+    dH = np.empty((N, Hs), np.float64) if want_grads else None
+    dW = np.empty((V, Hs), np.float64) if want_grads else None
+    _check(_load().fckl_oracle_full(N, Hs, Ht, V, float(T), _ptr(hs), _ptr(Ws), _ptr(ht), _ptr(Wt), _ptr(wv),
+                                    float(grad_scale), _ptr(loss), _ptr(lse), _ptr(mean), _ptr(dH), _ptr(dW)))
+    return loss, lse, float(mean[0]), dH, dW
 
 
 def num_threads() -> int:

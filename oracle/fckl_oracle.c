@@ -451,6 +451,112 @@ int fckl_oracle_topk(int64_t N, int64_t H, int64_t V, int64_t K, const double *h
     return failed ? ORACLE_EMEM : ORACLE_OK;
 }
 
+/*
+ * Online distillation against the full teacher distribution (the variant the pages
+ * compare the cached top-K teacher with: the teacher's full vocabulary distribution,
+ * computed next to the student's, "The Distillation Bottleneck", getaibook.com; the
+ * teacher forward on the fly, "The 250GB VRAM Wall in Long-Context Distillation",
+ * axbrief.com).  The teacher's hidden states ht[N*Ht] and LM head Wt[V*Ht] are inputs:
+ *   p = softmax(zt / T) over the whole vocabulary, zt[v] = ht . Wt[v]
+ *   q = softmax(zs / T),                            zs[v] = hs . Ws[v]
+ *   loss[i] = T^2 * sum_v p[v] (log p[v] - log q[v])
+ * reduced as the weighted mean (w == NULL: all weights 1), and the gradient of
+ * grad_scale * mean with respect to the student:
+ *   g[i,v] = grad_scale * T * w[i] / sum_j w[j] * (q[v] - p[v]);  dH = g Ws,  dW = g^T hs.
+ * lse_out[i] = log sum_v exp(zs[v] / T).  Any of the outputs may be NULL.
+ */
+int fckl_oracle_full(int64_t N, int64_t Hs, int64_t Ht, int64_t V, double T,
+                     const double *hs, const double *Ws, const double *ht, const double *Wt,
+                     const double *w, double grad_scale,
+                     double *loss_out, double *lse_out, double *mean_out,
+                     double *dH_out, double *dW_out)
+{
+    if (N <= 0 || Hs <= 0 || Ht <= 0 || V <= 0 || !(T > 0.0) || isinf(T) || !hs || !Ws || !ht || !Wt)
+        return ORACLE_EARG;
+    double wsum = (double)N;
+    if (w && weight_sum(N, w, &wsum))
+        return ORACLE_EARG;
+    double *g = (double *)malloc(sizeof(double) * (size_t)N * (size_t)V);
+    double *loss = (double *)malloc(sizeof(double) * (size_t)N);
+    if (!g || !loss) {
+        free(g);
+        free(loss);
+        return ORACLE_EMEM;
+    }
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *zs = (double *)malloc(sizeof(double) * (size_t)V);
+        double *zt = (double *)malloc(sizeof(double) * (size_t)V);
+        int have = (zs && zt);
+        if (!have) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < N; ++i) {
+            if (!have)
+                continue;
+            student_logits(Ht, V, ht + i * Ht, Wt, zt);
+            student_logits(Hs, V, hs + i * Hs, Ws, zs);
+            const double lt = logsumexp_over_vocab(V, T, zt);
+            const double ls = logsumexp_over_vocab(V, T, zs);
+            const double scale = wsum > 0.0 ? grad_scale * T * (w ? w[i] : 1.0) / wsum : 0.0;
+            double kl = 0.0;
+            for (int64_t v = 0; v < V; ++v) {
+                const double log_p = zt[v] / T - lt, log_q = zs[v] / T - ls;
+                const double p = exp(log_p);
+                kl += p * (log_p - log_q);
+                g[i * V + v] = scale * (exp(log_q) - p);
+            }
+            loss[i] = T * T * kl;
+            if (loss_out)
+                loss_out[i] = loss[i];
+            if (lse_out)
+                lse_out[i] = ls;
+        }
+        free(zs);
+        free(zt);
+    }
+    if (!failed && mean_out) {
+        double s = 0.0;
+        for (int64_t i = 0; i < N; ++i)
+            s += (w ? w[i] : 1.0) * loss[i];
+        *mean_out = wsum > 0.0 ? s / wsum : 0.0;
+    }
+    if (!failed && dH_out) {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t i = 0; i < N; ++i) {
+            double *out = dH_out + i * Hs;
+            for (int64_t j = 0; j < Hs; ++j)
+                out[j] = 0.0;
+            for (int64_t v = 0; v < V; ++v) {
+                const double gv = g[i * V + v];
+                const double *wr = Ws + v * Hs;
+                for (int64_t j = 0; j < Hs; ++j)
+                    out[j] += gv * wr[j];
+            }
+        }
+    }
+    if (!failed && dW_out) {
+#pragma omp parallel for schedule(static)
+        for (int64_t v = 0; v < V; ++v) {
+            double *out = dW_out + v * Hs;
+            for (int64_t j = 0; j < Hs; ++j)
+                out[j] = 0.0;
+            for (int64_t i = 0; i < N; ++i) {
+                const double gv = g[i * V + v];
+                const double *hr = hs + i * Hs;
+                for (int64_t j = 0; j < Hs; ++j)
+                    out[j] += gv * hr[j];
+            }
+        }
+    }
+    free(g);
+    free(loss);
+    return failed ? ORACLE_EMEM : ORACLE_OK;
+}
+
 /* Number of OpenMP threads a parallel region of the oracle uses. */
 int fckl_oracle_num_threads(void)
 {

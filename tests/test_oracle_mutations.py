@@ -33,6 +33,9 @@ MUTANTS = {
                              "gr[v] = scale * psum * exp(z[v] - lse);"),
     "weighted_mean_over_count": ("*mean_out = wsum > 0.0 ? s / wsum : 0.0;",
                                  "*mean_out = wsum > 0.0 ? s / (double)N : 0.0;"),
+    "full_gradient_sign_flipped": ("g[i * V + v] = scale * (exp(log_q) - p);",
+                                   "g[i * V + v] = scale * (p - exp(log_q));"),
+    "full_reverse_kl": ("kl += p * (log_p - log_q);", "kl += exp(log_q) * (log_q - log_p);"),
     "topk_ties_to_larger_index": ("return a->z > b->z || (a->z == b->z && a->v < b->v);",
                                   "return a->z > b->z || (a->z == b->z && a->v > b->v);"),
     "topk_ascending": ("return a->z > b->z || (a->z == b->z && a->v < b->v);",

@@ -449,3 +449,51 @@ def test_topk_invariances():
     for badK in (0, 81):
         with pytest.raises(oracle.OracleError):
             oracle.topk(h, W, badK)
+
+
+# ---------------------------------------------------------------- online full-vocabulary teacher
+
+def full_problem(seed, N=6, Hs=10, Ht=14, V=40, T=1.5):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((N, Hs)), 0.4 * rng.standard_normal((V, Hs)),
+            rng.standard_normal((N, Ht)), 0.4 * rng.standard_normal((V, Ht)), T)
+
+
+@pytest.mark.parametrize("seed,gs", [(80, 1.0), (81, -2.0)])
+def test_full_teacher_is_the_cached_teacher_with_K_equal_V(seed, gs):
+    """The cached-teacher oracle with K = V, the teacher's own logits as the cache and
+    every vocabulary index, is the same loss: a second implementation."""
+    hs, Ws, ht, Wt, T = full_problem(seed)
+    N, V = hs.shape[0], Ws.shape[0]
+    zt = ht @ Wt.T
+    idx = np.tile(np.arange(V, dtype=np.int32), (N, 1))
+    loss, lse, mean, dH, dW = oracle.full(hs, Ws, ht, Wt, T, grad_scale=gs)
+    ref_loss, ref_lse = oracle.forward(hs, Ws, idx, zt, T)
+    ref_dH, ref_dW = oracle.backward(hs, Ws, idx, zt, T, grad_scale=gs)
+    np.testing.assert_allclose(loss, ref_loss, rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-13)
+    assert abs(mean - ref_loss.mean()) <= 1e-10 * abs(mean)
+    np.testing.assert_allclose(dH, ref_dH, rtol=1e-9, atol=1e-14)
+    np.testing.assert_allclose(dW, ref_dW, rtol=1e-9, atol=1e-14)
+
+
+def test_full_teacher_against_torch_and_identities():
+    hs, Ws, ht, Wt, T = full_problem(82)
+    w = np.random.default_rng(83).uniform(0.0, 2.0, size=hs.shape[0])
+    hst = torch.tensor(hs, requires_grad=True)
+    Wst = torch.tensor(Ws, requires_grad=True)
+    logp = torch.log_softmax(torch.tensor(ht @ Wt.T) / T, dim=1)
+    logq = torch.log_softmax(hst @ Wst.t() / T, dim=1)
+    per_tok = (T * T) * torch.nn.functional.kl_div(logq, logp, reduction="none", log_target=True).sum(1)
+    wt = torch.tensor(w)
+    mean_t = (wt * per_tok).sum() / wt.sum()
+    (0.7 * mean_t).backward()
+    loss, _, mean, dH, dW = oracle.full(hs, Ws, ht, Wt, T, w=w, grad_scale=0.7)
+    np.testing.assert_allclose(loss, per_tok.detach().numpy(), rtol=1e-10, atol=1e-13)
+    assert abs(mean - mean_t.item()) <= 1e-10 * abs(mean)
+    np.testing.assert_allclose(dH, hst.grad.numpy(), rtol=1e-9, atol=1e-14)
+    np.testing.assert_allclose(dW, Wst.grad.numpy(), rtol=1e-9, atol=1e-14)
+    # a teacher equal to the student: zero loss and zero gradient
+    l0, _, m0, dH0, dW0 = oracle.full(hs, Ws, hs, Ws, T)
+    assert np.abs(l0).max() <= 1e-13 and abs(m0) <= 1e-13
+    assert np.abs(dH0).max() <= 1e-14 and np.abs(dW0).max() <= 1e-14
