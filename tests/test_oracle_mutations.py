@@ -31,8 +31,8 @@ MUTANTS = {
                              "double gv = g[r * V + (V - 1 - v)];\n                const double *hr"),
     "dH_uses_softmax_only": ("gr[v] = scale * psum * exp(z[v] / T - lse);",
                              "gr[v] = scale * psum * exp(z[v] - lse);"),
-    "weighted_mean_over_count": ("*mean_out = wsum > 0.0 ? s / wsum : 0.0;",
-                                 "*mean_out = wsum > 0.0 ? s / (double)N : 0.0;"),
+    "weighted_mean_over_count": ("s += w[i] * loss[i];\n        *mean_out = wsum > 0.0 ? s / wsum : 0.0;",
+                                 "s += w[i] * loss[i];\n        *mean_out = wsum > 0.0 ? s / (double)N : 0.0;"),
     "full_gradient_sign_flipped": ("g[i * V + v] = scale * (exp(log_q) - p);",
                                    "g[i * V + v] = scale * (p - exp(log_q));"),
     "full_reverse_kl": ("kl += p * (log_p - log_q);", "kl += exp(log_q) * (log_q - log_p);"),
