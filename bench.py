@@ -16,6 +16,9 @@ library records around each launch on its own stream during the timed steps.
 chunk's logits once (6 N V H flop); it is reported beside the main line, which times
 the two passes of the method as defined (8 N V H flop).  `teacher_topk` times the
 teacher-side extraction of the top-K cache from the same hidden states (fckl_topk).
+`full_teacher` times the online variant against the teacher's whole distribution
+(fckl_full_forward_backward), with a teacher of the same shape (a perturbed copy of the
+student's hidden states and head): 2 N V Ht + 6 N V H flop per step.
 """
 from __future__ import annotations
 
@@ -81,6 +84,8 @@ def main():
                     help="skip timing fckl_forward_backward (the single-call path) after the main measurement")
     ap.add_argument("--no-topk", action="store_true",
                     help="skip timing the teacher-side top-K extraction (fckl_topk) of the same hidden states")
+    ap.add_argument("--no-full", action="store_true",
+                    help="skip the full-vocabulary teacher variant (fckl_full_forward_backward)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (reference dispatch for HBM byte counters)")
     args = ap.parse_args()
@@ -217,6 +222,37 @@ def main():
                                "flops_per_call": 4.0 * N * V * H,
                                "mfma_frac": round(4.0 * N * V * H / (ms_t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del tws, ti, tv
+
+    if not args.no_full:
+        # Online distillation against the full teacher distribution, teacher of the same
+        # shape: a perturbed copy of h and W (seeded), its logits formed chunk by chunk.
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(20260)
+        h_t = (h.float() + 0.3 * torch.randn(h.shape, generator=gen, device=dev)).to(torch.bfloat16)
+        W_t = (W.float() + 0.3 * W.float().std() * torch.randn(W.shape, generator=gen, device=dev)).to(torch.bfloat16)
+        fdesc = fckl.make_desc(N, H, V, 1, T)
+        fchunk, fws_bytes = fckl.full_plan(fdesc, H)
+        del ws
+        fws = torch.empty(fws_bytes, dtype=torch.uint8, device=dev)
+
+        def full(profile=None):
+            fckl.full_forward_backward(h, W, h_t, W_t, T=T, chunk=fchunk, ws=fws, loss_tok=loss, lse=lse,
+                                       loss_mean=mean, dH=dH, dW=dW, profile=profile)
+        full()
+        torch.cuda.synchronize()
+        nf = -(-N // fchunk)
+        msf, kf = timed_steps(fckl, full, args.steps, nf)
+        flops = 2.0 * N * V * H + 6.0 * N * V * H
+        log("full teacher: %.2f ms/step, %.0f tokens/s (chunk %d)" % (msf, N * 1e3 / msf, fchunk))
+        out["full_teacher"] = {
+            "value": round(N * 1e3 / msf, 1), "unit": "tokens/s", "ms_per_step": round(msf, 3),
+            "teacher_hidden": H, "chunk": fchunk, "workspace_gib": round(fws_bytes / GiB, 3),
+            "flops_per_step": flops, "mfma_frac": round(flops / (msf * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "kernels": {k: {"launches": v["launches"], "ms_per_step": round(v["ms"] / args.steps, 4)}
+                        for k, v in kf.items()},
+        }
+        del fws, h_t, W_t
+        ws = None
 
     if args.dense:
         # the fused path's workspace and outputs are released first: the dense loss is

@@ -35,11 +35,11 @@ FLAG_VALIDATE, FLAG_DW_ACCUMULATE = 1, 2
 # Every symbol include/fckl.h declares.
 EXPORTS = ("fckl_plan", "fckl_workspace_size", "fckl_forward", "fckl_backward", "fckl_forward_ex",
            "fckl_backward_ex", "fckl_forward_backward", "fckl_topk_workspace_size", "fckl_topk",
-           "fckl_status_string", "fckl_version")
+           "fckl_full_plan", "fckl_full_forward_backward", "fckl_status_string", "fckl_version")
 
 
 KERNELS = ("prepare", "fwd_logits", "combine", "mean", "bwd_logits", "dh", "dh_reduce", "dw", "transpose",
-           "softmax_grad", "weights")
+           "softmax_grad", "weights", "full_teacher", "full_student", "full_combine", "full_grad")
 
 
 class Profile(ctypes.Structure):
@@ -89,8 +89,12 @@ def load() -> ctypes.CDLL:
     lib.fckl_version.restype = ctypes.c_int32
     lib.fckl_topk_workspace_size.argtypes = [P(Desc), ctypes.c_int32, P(sz)]
     lib.fckl_topk.argtypes = [P(Desc), vp, vp, vp, vp, vp, sz, vp]
+    lib.fckl_full_plan.argtypes = [P(Desc), ctypes.c_int32, sz, P(ctypes.c_int32), P(sz)]
+    lib.fckl_full_forward_backward.argtypes = [P(Desc), ctypes.c_int32, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp,
+                                               vp, vp, vp, vp, sz, vp]
     for f in ("fckl_plan", "fckl_workspace_size", "fckl_forward", "fckl_backward", "fckl_forward_ex",
-              "fckl_backward_ex", "fckl_forward_backward", "fckl_topk_workspace_size", "fckl_topk"):
+              "fckl_backward_ex", "fckl_forward_backward", "fckl_topk_workspace_size", "fckl_topk",
+              "fckl_full_plan", "fckl_full_forward_backward"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -324,5 +328,50 @@ def topk(h, W, K: int, chunk: int = 0, logits_f32: bool = False, ws=None, topk_i
     return topk_idx, topk_logit
 
 
+def full_plan(desc: Desc, H_teacher: int, budget_bytes: int = 0) -> Tuple[int, int]:
+    """(tokens per chunk, workspace bytes) of the full-teacher variant (fckl_full_plan)."""
+    c, ws = ctypes.c_int32(0), ctypes.c_size_t(0)
+    _call("fckl_full_plan", ctypes.byref(desc), ctypes.c_int32(H_teacher), ctypes.c_size_t(budget_bytes),
+          ctypes.byref(c), ctypes.byref(ws))
+    return int(c.value), int(ws.value)
+
+
+def full_forward_backward(h, W, h_t, W_t, T: float = 1.0, grad_scale: float = 1.0, weights=None, chunk: int = 0,
+                          budget_bytes: int = 0, ws=None, loss_tok=None, lse=None, loss_mean=None, dH=None, dW=None,
+                          accumulate: bool = False, stream=None, profile: Optional[Profile] = None):
+    """Online distillation against the teacher's full distribution
+    (fckl_full_forward_backward): the student (h, W) and the teacher (h_t, W_t) share the
+    vocabulary.  Returns (loss_tok, lse, loss_mean, dH, dW)."""
+    import torch
+    for name, t in (("h", h), ("W", W), ("h_t", h_t), ("W_t", W_t)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError("%s must be a contiguous bfloat16 device tensor" % name)
+        if t.dim() != 2 or t.device != h.device:
+            raise ValueError("%s must be 2-D on the device of h" % name)
+    N, H = h.shape
+    V, Ht = W.shape[0], h_t.shape[1]
+    if W.shape[1] != H or h_t.shape[0] != N or tuple(W_t.shape) != (V, Ht):
+        raise ValueError("expected h[N,H], W[V,H], h_t[N,Ht], W_t[V,Ht]")
+    dev = h.device
+    flags = FLAG_DW_ACCUMULATE if accumulate else 0
+    desc = make_desc(N, H, V, 1, T, chunk, DTYPE_BF16, flags, profile)
+    desc.chunk, need = full_plan(desc, Ht, budget_bytes)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    if ws.numel() * ws.element_size() < need or not ws.is_contiguous():
+        raise ValueError("workspace of %d bytes needed" % need)
+    weights = _weights(weights, N, dev)
+    loss_tok = _out(loss_tok, (N,), dev, "loss_tok")
+    lse = _out(lse, (N,), dev, "lse")
+    loss_mean = _out(loss_mean, (1,), dev, "loss_mean")
+    dH = _out(dH, (N, H), dev, "dH")
+    dW = _out(dW, (V, H), dev, "dW")
+    _call("fckl_full_forward_backward", ctypes.byref(desc), ctypes.c_int32(Ht), h.data_ptr(), W.data_ptr(),
+          h_t.data_ptr(), W_t.data_ptr(), _ptr(weights), ctypes.c_float(grad_scale), loss_tok.data_ptr(),
+          lse.data_ptr(), loss_mean.data_ptr(), dH.data_ptr(), dW.data_ptr(), ws.data_ptr(),
+          ctypes.c_size_t(ws.numel() * ws.element_size()), _stream_handle(stream))
+    return loss_tok, lse, loss_mean, dH, dW
+
+
 __all__ = ["Desc", "Profile", "KERNELS", "FCKLError", "load", "plan", "workspace_size", "forward", "backward",
-           "forward_backward", "topk", "topk_workspace_size", "make_desc", "desc_for", "status_string", "version", "EXPORTS", "LIB_PATH"]
+           "forward_backward", "topk", "topk_workspace_size", "full_plan", "full_forward_backward", "make_desc", "desc_for", "status_string", "version", "EXPORTS", "LIB_PATH"]

@@ -35,8 +35,8 @@ ChunkArgs chunk_args(const fckl_desc *d, const void *h, const void *W, const int
     const size_t esz = d->logit_dtype == FCKL_DTYPE_F32 ? 4 : 2;
     a.h = reinterpret_cast<const uint16_t *>(h) + (size_t)c0 * d->H;
     a.W = reinterpret_cast<const uint16_t *>(W);
-    a.idx = idx + (size_t)c0 * d->K;
-    a.tl = reinterpret_cast<const char *>(tl) + (size_t)c0 * d->K * esz;
+    a.idx = idx ? idx + (size_t)c0 * d->K : nullptr;     // NULL in the full-teacher variant
+    a.tl = tl ? reinterpret_cast<const char *>(tl) + (size_t)c0 * d->K * esz : nullptr;
     a.logit_f32 = d->logit_dtype == FCKL_DTYPE_F32;
     a.rows = (int32_t)((d->N - c0) < L->C ? (d->N - c0) : L->C);
     a.H = d->H;
@@ -357,6 +357,110 @@ fckl_status fckl_forward_backward(const fckl_desc *desc, const void *h, const vo
             return st;
     }
     return loss_mean ? mean_of(desc, loss_tok, weights, loss_mean, stream) : FCKL_OK;
+}
+
+namespace {
+
+// The loss descriptor with the fields the full-teacher variant does not read made valid.
+fckl_desc full_desc(const fckl_desc *desc)
+{
+    fckl_desc d = *desc;
+    d.K = 1;
+    d.logit_dtype = FCKL_DTYPE_BF16;
+    d.flags &= ~(uint32_t)FCKL_FLAG_VALIDATE;
+    return d;
+}
+
+}  // namespace
+
+fckl_status fckl_full_plan(const fckl_desc *desc, int32_t H_teacher, size_t budget_bytes, int32_t *chunk_out,
+                           size_t *ws_bytes_out)
+{
+    if (!desc)
+        return FCKL_ERR_INVALID_ARG;
+    const fckl_desc d = full_desc(desc);
+    FullLayout F;
+    fckl_status st = plan_full_chunk(&d, H_teacher, budget_bytes, &F);
+    if (st != FCKL_OK)
+        return st;
+    if (chunk_out)
+        *chunk_out = F.base.C;
+    if (ws_bytes_out)
+        *ws_bytes_out = F.total;
+    return FCKL_OK;
+}
+
+fckl_status fckl_full_forward_backward(const fckl_desc *desc, int32_t H_teacher, const void *h, const void *W,
+                                       const void *h_t, const void *W_t, const float *weights, float grad_scale,
+                                       float *loss_tok, float *lse, float *loss_mean, float *dH, float *dW,
+                                       void *ws, size_t ws_bytes, void *stream)
+{
+    if (!desc)
+        return FCKL_ERR_INVALID_ARG;
+    const fckl_desc d = full_desc(desc);
+    fckl_status st = check_desc(&d);
+    if (st != FCKL_OK)
+        return st;
+    if (!h || !W || !h_t || !W_t || !ws || !loss_tok || !lse || !dH || !dW)
+        return FCKL_ERR_INVALID_ARG;
+    for (const void *ptr : {h, W, h_t, W_t})
+        if ((reinterpret_cast<uintptr_t>(ptr) & 15u) != 0)
+            return FCKL_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+        return FCKL_ERR_INVALID_ARG;
+    FullLayout F;
+    if ((st = plan_full_chunk(&d, H_teacher, ws_bytes, &F)) != FCKL_OK)
+        return st;
+    if (F.total > ws_bytes)
+        return FCKL_ERR_WORKSPACE;
+    const Layout &L = F.base;
+    float *wsum = nullptr;
+    if (weights && (st = weight_sum(&d, weights, ws, L, stream, &wsum)) != FCKL_OK)
+        return st;
+    {
+        ChunkArgs a = chunk_args(&d, h, W, nullptr, nullptr, ws, &L, 0);
+        Timed t(&d, FCKL_KERNEL_TRANSPOSE, 0, stream);
+        if (launch_transpose_head(a, stream))
+            return FCKL_ERR_HIP;
+    }
+    for (int64_t c0 = 0; c0 < d.N; c0 += L.C) {
+        ChunkArgs a = chunk_args(&d, h, W, nullptr, nullptr, ws, &L, c0);
+        const GradScale gs = chunk_scale(&d, grad_scale, weights, wsum, c0);
+        const uint16_t *ht_c = reinterpret_cast<const uint16_t *>(h_t) + (size_t)c0 * H_teacher;
+        {
+            Timed t(&d, FCKL_KERNEL_FULL_TEACHER, a.rows, stream);
+            if (launch_full_teacher(a, F, ht_c, reinterpret_cast<const uint16_t *>(W_t), stream))
+                return FCKL_ERR_HIP;
+        }
+        {
+            Timed t(&d, FCKL_KERNEL_FULL_COMBINE, a.rows, stream);
+            if (launch_full_combine_teacher(a, F, stream))
+                return FCKL_ERR_HIP;
+        }
+        {
+            Timed t(&d, FCKL_KERNEL_FULL_STUDENT, a.rows, stream);
+            if (launch_full_student(a, F, stream))
+                return FCKL_ERR_HIP;
+        }
+        {
+            Timed t(&d, FCKL_KERNEL_FULL_COMBINE, a.rows, stream);
+            if (launch_full_combine_student(a, F, loss_tok + c0, lse + c0, stream))
+                return FCKL_ERR_HIP;
+        }
+        {
+            Timed t(&d, FCKL_KERNEL_FULL_GRAD, a.rows, stream);
+            if (launch_full_grad(a, F, gs, stream))
+                return FCKL_ERR_HIP;
+        }
+        {
+            Timed t(&d, FCKL_KERNEL_TRANSPOSE, a.rows, stream);
+            if (launch_transpose_chunk(a, stream))
+                return FCKL_ERR_HIP;
+        }
+        if ((st = chunk_products(&d, a, c0, dH, dW, stream)) != FCKL_OK)
+            return st;
+    }
+    return loss_mean ? mean_of(&d, loss_tok, weights, loss_mean, stream) : FCKL_OK;
 }
 
 fckl_status fckl_topk_workspace_size(const fckl_desc *desc, int32_t chunk, size_t *ws_bytes_out)

@@ -64,8 +64,23 @@ struct TopkLayout {
     size_t total = 0;
 };
 
+// Workspace of the full-teacher variant: the loss layout (for the student) followed by
+// the teacher's fp32 logits of the chunk and the per-tile partials of both products.
+struct FullLayout {
+    Layout base;
+    int32_t Ht = 0;
+    size_t off_at = 0;      // f32   [Vpad, Cpad]  a_t = z_t log2(e) / T
+    size_t off_part_t = 0;  // f32x2 [nVt, Cpad]   teacher (max, sum) per tile
+    size_t off_px = 0;      // f32   [nVt, Cpad]   sum over the tile of p (a_t - a_s)
+    size_t off_lt2 = 0;     // f32   [Cpad]        teacher base-2 logsumexp
+    size_t off_ls2 = 0;     // f32   [Cpad]        student base-2 logsumexp
+    size_t total = 0;
+};
+
 fckl_status check_desc(const fckl_desc *d);
 fckl_status make_topk_layout(const fckl_desc *d, int32_t chunk, TopkLayout *L);
+fckl_status make_full_layout(const fckl_desc *d, int32_t Ht, int32_t chunk, FullLayout *L);
+fckl_status plan_full_chunk(const fckl_desc *d, int32_t Ht, size_t budget, FullLayout *L);
 fckl_status make_layout(const fckl_desc *d, int32_t chunk, Layout *L);
 fckl_status plan_chunk(const fckl_desc *d, size_t budget, Layout *L);
 
@@ -119,6 +134,14 @@ int launch_zero_flag(uint32_t *flag, void *stream);
 // 32-row sub-tile maxima of z, the per-token threshold, the candidates at or above it,
 // and the ordered selection (topk_logit written as f32 or bf16).  Candidate overflow
 // sets the error flag.
+// Full-teacher variant, per chunk (a.L is the student's loss layout inside F).
+int launch_full_teacher(const ChunkArgs &a, const FullLayout &F, const uint16_t *h_t, const uint16_t *W_t,
+                        void *stream);
+int launch_full_combine_teacher(const ChunkArgs &a, const FullLayout &F, void *stream);
+int launch_full_student(const ChunkArgs &a, const FullLayout &F, void *stream);
+int launch_full_combine_student(const ChunkArgs &a, const FullLayout &F, float *loss_tok, float *lse, void *stream);
+int launch_full_grad(const ChunkArgs &a, const FullLayout &F, const GradScale &gs, void *stream);
+
 int launch_topk_max(const ChunkArgs &a, const TopkLayout &T, void *stream);
 int launch_topk_threshold(const ChunkArgs &a, const TopkLayout &T, void *stream);
 int launch_topk_collect(const ChunkArgs &a, const TopkLayout &T, void *stream);

@@ -1191,6 +1191,307 @@ __global__ __launch_bounds__(kSgThreads) void softmax_grad_kernel(SoftGradParams
     store_vocab_major<kSgTok, kSgThreads / 64>(smem, p.gT, (size_t)p.Cpad, m0, n0);
 }
 
+// ------------------------------------------------------------------ full teacher distribution
+
+// Online distillation against the teacher's whole distribution ("The Distillation
+// Bottleneck", getaibook.com, the full-vocabulary teacher the cache replaces): with
+// a = z log2(e) / T, p = 2^(a_t - L_t), q = 2^(a_s - L_s) (L the base-2 logsumexp),
+//   loss = T^2 ln2 (sum_v p (a_t - a_s) - L_t + L_s),   g = c (q - p).
+// Per chunk: the teacher product keeps a_t in fp32 and its partials, the student product
+// forms sum p (a_t - a_s) per tile from those fp32 values while it keeps its own
+// exponentials (bf16) as the single-call path does, and a streaming kernel forms g.
+//
+// a_t is kept in the product's register order, not as a matrix: for logit tile (tm, tn),
+// wave, 32-column block j and lane, 16 float4 pieces, piece q holding rows
+// row_of(wm, q / 4, 4 (q % 4) + 0..3, lane) of column col_of(wn, j, lane).  Each piece is
+// one 1 KB access of the whole wave at an immediate offset from one base address, for
+// the teacher's store and for both readers.
+__device__ __forceinline__ size_t at_frag(int tm, int tn, int nNt, int wave, int j, int lane)
+{
+    return ((((size_t)tm * nNt + tn) * (LogitGemm::NT / 64) + wave) * LogitGemm::NB + j) * 4096 + 4 * lane;
+}
+
+struct FullTeacherParams {
+    const uint16_t *W, *h;  // the teacher's head [V, Ht] and chunk of hidden states
+    int H, V, rows, Cpad, nVt, nNt;
+    float scale2;           // log2(e) / T
+    float2 *part;           // [nVt, Cpad] (max, sum 2^(a - max)) of a_t per tile
+    float *at;              // Vpad * Cpad floats, a_t in fragment order (at_frag)
+};
+
+__device__ __forceinline__ void full_teacher_tile(const FullTeacherParams &p, char *smem, int t)
+{
+    using G = LogitGemm;
+    int tm, tn;
+    map_tile(t, p.nVt, p.nNt, 4, tm, tn);
+    const int m0 = tm * G::BM, n0 = tn * G::BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / G::WN, wn = wave % G::WN;
+    f32x16 acc[G::MB][G::NB];
+    G::run(smem, p.W, p.H, m0, p.V, p.H, p.h, p.H, n0, p.rows, p.H, 0, p.H, acc);
+    const int lim = p.V - m0 - G::row_of(wm, 0, 0, lane);
+    float *red = reinterpret_cast<float *>(smem);   // [WM][BN][2]
+#pragma unroll
+    for (int j = 0; j < G::NB; ++j) {
+        const int nl = G::col_of(wn, j, lane);
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int i = 0; i < G::MB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const bool in = 32 * i + 8 * (r >> 2) + (r & 3) < lim;
+                mx = fmaxf(mx, in ? acc[i][j][r] * p.scale2 : -__builtin_inff());
+            }
+        // padded rows and columns hold a = 0 (the product zero-fills them); readers mask them
+        float4 *dst = reinterpret_cast<float4 *>(p.at + at_frag(tm, tn, p.Cpad / G::BN, wave, j, lane));
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            dst[64 * q] = make_float4(acc[q >> 2][j][4 * (q & 3) + 0] * p.scale2, acc[q >> 2][j][4 * (q & 3) + 1] * p.scale2,
+                                      acc[q >> 2][j][4 * (q & 3) + 2] * p.scale2, acc[q >> 2][j][4 * (q & 3) + 3] * p.scale2);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float ms = (mx == -__builtin_inff()) ? 0.0f : mx;
+        float sum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < G::MB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                sum += (32 * i + 8 * (r >> 2) + (r & 3) < lim) ? fast_exp2(acc[i][j][r] * p.scale2 - ms) : 0.0f;
+        sum += __shfl_xor(sum, 32);
+        if (lane < 32) {
+            red[(wm * G::BN + nl) * 2 + 0] = mx;
+            red[(wm * G::BN + nl) * 2 + 1] = sum;
+        }
+    }
+    __syncthreads();
+    for (int nl = threadIdx.x; nl < G::BN; nl += G::NT)
+        if (n0 + nl < p.rows) {
+            float m = red[nl * 2 + 0], s = red[nl * 2 + 1];
+#pragma unroll
+            for (int w2 = 1; w2 < G::WM; ++w2)
+                lse_merge(m, s, red[(w2 * G::BN + nl) * 2 + 0], red[(w2 * G::BN + nl) * 2 + 1]);
+            p.part[(size_t)tm * p.Cpad + n0 + nl] = make_float2(m, s);
+        }
+}
+
+__global__ __launch_bounds__(LogitGemm::NT) void full_teacher_kernel(FullTeacherParams p)
+{
+    __shared__ __attribute__((aligned(16))) char smem[LogitGemm::LDS_BYTES];
+    for (int t = blockIdx.x; t < p.nVt * p.nNt; t += gridDim.x) {
+        full_teacher_tile(p, smem, t);
+        __syncthreads();
+    }
+}
+
+struct FullStudentParams {
+    const uint16_t *W, *h;  // the student's head [V, Hs] and chunk of hidden states
+    int H, V, rows, Cpad, Vpad, nVt, nNt;
+    float scale2;           // log2(e) / T
+    const float *at;        // a_t in fragment order (at_frag)
+    const float *lt2;       // [Cpad] L_t
+    float2 *part;           // [nVt, Cpad] (max, sum 2^(a - max)) of a_s per tile
+    float *px;              // [nVt, Cpad] sum over the tile of p (a_t - a_s)
+    uint16_t *ex;           // [Cpad, Vpad] bf16 2^(a_s - m), m the wave's 128-row maximum
+    float *mw;              // [2 nVt, Cpad] those maxima
+};
+
+__device__ __forceinline__ void full_student_tile(const FullStudentParams &p, char *smem, int t)
+{
+    using G = LogitGemm;
+    int tm, tn;
+    map_tile(t, p.nVt, p.nNt, 4, tm, tn);
+    const int m0 = tm * G::BM, n0 = tn * G::BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / G::WN, wn = wave % G::WN;
+    float lt[G::NB];
+#pragma unroll
+    for (int j = 0; j < G::NB; ++j) {
+        const int tok = n0 + G::col_of(wn, j, lane);
+        lt[j] = tok < p.rows ? p.lt2[tok] : 0.0f;
+    }
+    f32x16 acc[G::MB][G::NB];
+    G::run(smem, p.W, p.H, m0, p.V, p.H, p.h, p.H, n0, p.rows, p.H, 0, p.H, acc);
+    const int lim = p.V - m0 - G::row_of(wm, 0, 0, lane);
+    float *red = reinterpret_cast<float *>(smem);               // [WM][BN][2]
+    float *redx = red + 2 * G::WM * G::BN;                       // [WM][BN]
+#pragma unroll
+    for (int j = 0; j < G::NB; ++j) {
+        const int nl = G::col_of(wn, j, lane), tok = n0 + nl;
+        const bool tok_in = tok < p.rows;
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int i = 0; i < G::MB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                mx = fmaxf(mx, (32 * i + 8 * (r >> 2) + (r & 3) < lim) ? acc[i][j][r] * p.scale2 : -__builtin_inff());
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float ms = (mx == -__builtin_inff()) ? 0.0f : mx;
+        float sum = 0.0f, x = 0.0f;
+        const float4 *src = reinterpret_cast<const float4 *>(p.at + at_frag(tm, tn, p.Cpad / G::BN, wave, j, lane));
+#pragma unroll
+        for (int i = 0; i < G::MB; ++i) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 t4 = src[64 * (4 * i + q)];
+                const float at[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int r = 4 * q + c;
+                    const bool in = 32 * i + 8 * q + c < lim;
+                    const float as = acc[i][j][r] * p.scale2;
+                    const float e = in ? fast_exp2(as - ms) : 0.0f;
+                    sum += e;
+                    if (in && tok_in)
+                        x += fast_exp2(at[c] - lt[j]) * (at[c] - as);
+                    acc[i][j][r] = e;
+                }
+            }
+        }
+        sum += __shfl_xor(sum, 32);
+        x += __shfl_xor(x, 32);
+        if (lane < 32) {
+            red[(wm * G::BN + nl) * 2 + 0] = mx;
+            red[(wm * G::BN + nl) * 2 + 1] = sum;
+            redx[wm * G::BN + nl] = x;
+            p.mw[(size_t)(2 * tm + wm) * p.Cpad + tok] = ms;
+        }
+    }
+    __syncthreads();
+    for (int nl = threadIdx.x; nl < G::BN; nl += G::NT)
+        if (n0 + nl < p.rows) {
+            float m = red[nl * 2 + 0], s = red[nl * 2 + 1], x = redx[nl];
+#pragma unroll
+            for (int w2 = 1; w2 < G::WM; ++w2) {
+                lse_merge(m, s, red[(w2 * G::BN + nl) * 2 + 0], red[(w2 * G::BN + nl) * 2 + 1]);
+                x += redx[w2 * G::BN + nl];
+            }
+            p.part[(size_t)tm * p.Cpad + n0 + nl] = make_float2(m, s);
+            p.px[(size_t)tm * p.Cpad + n0 + nl] = x;
+        }
+    __syncthreads();    // the merge has read `red` before the staging overwrites it
+    store_token_major<G>(acc, smem, p.ex, (size_t)p.Vpad, m0, n0);
+}
+
+__global__ __launch_bounds__(LogitGemm::NT) void full_student_kernel(FullStudentParams p)
+{
+    __shared__ __attribute__((aligned(16))) char smem[kLogitLds];
+    for (int t = blockIdx.x; t < p.nVt * p.nNt; t += gridDim.x) {
+        full_student_tile(p, smem, t);
+        __syncthreads();
+    }
+}
+
+// 32 tokens x 8 slices of the vocabulary tiles per block: L = the base-2 logsumexp over
+// the tiles.  With px (student pass) also the loss T^2 ln2 (sum px - L_t + L_s), the sum
+// and the difference taken in fp64, and lse = L_s ln2.
+__global__ __launch_bounds__(256) void full_combine_kernel(const float2 *part, const float *px, int nVt, int Cpad,
+                                                           int rows, float T, const float *lt2, float *l2_out,
+                                                           float *loss_tok, float *lse)
+{
+    __shared__ float s_m[8][32], s_s[8][32];
+    __shared__ double s_x[8][32];
+    const int tl = threadIdx.x & 31, sp = threadIdx.x >> 5;
+    const int tok = blockIdx.x * 32 + tl;
+    float m = kNegInf, s = 0.0f;
+    double x = 0.0;
+    if (tok < rows)
+        for (int vt = sp; vt < nVt; vt += 8) {
+            const float2 q = part[(size_t)vt * Cpad + tok];
+            lse_merge(m, s, q.x, q.y);
+            if (px)
+                x += (double)px[(size_t)vt * Cpad + tok];
+        }
+    s_m[sp][tl] = m;
+    s_s[sp][tl] = s;
+    s_x[sp][tl] = x;
+    __syncthreads();
+    if (sp != 0 || tok >= rows)
+        return;
+#pragma unroll
+    for (int k = 1; k < 8; ++k) {
+        lse_merge(m, s, s_m[k][tl], s_s[k][tl]);
+        x += s_x[k][tl];
+    }
+    const float L = m + log2f(s);
+    if (l2_out)
+        l2_out[tok] = L;
+    if (px) {
+        loss_tok[tok] = (float)((double)T * T * (double)kLn2 * (x - (double)lt2[tok] + (double)L));
+        lse[tok] = L * kLn2;
+    }
+}
+
+struct FullGradParams {
+    uint16_t *ex;           // [Cpad, Vpad] the student's kept exponentials; overwritten with g
+    uint16_t *gT;           // [Vpad, Cpad] out
+    const float *at;        // a_t in fragment order (at_frag)
+    const float *mw;        // [2 nVt, Cpad]
+    const float *ls2, *lt2; // [Cpad] L_s, L_t
+    int rows, Cpad, Vpad, V;
+    float coef;             // grad_scale * T (/ N without weights)
+    const float *w;         // chunk's first token, or NULL
+    const float *inv_wsum;
+};
+
+// One block per (256-row vocabulary tile, 64 tokens), four waves, each taking the
+// fragments of one (128-row half, 32-token block) of a_t exactly as the logit product's
+// wave held them, so that each lane has one token.  The student's kept values are staged
+// [token][vocab] in LDS; each lane forms, for its 64 values,
+//   g = c (E 2^(m - L_s) - 2^(a_t - L_t)),
+// writes them back into the staged tile, whose rows (g) and columns (g^T) are then written.
+__global__ __launch_bounds__(256) void full_grad_kernel(FullGradParams p)
+{
+    using G = LogitGemm;
+    constexpr int kTok = 64;
+    __shared__ __attribute__((aligned(16))) char smem[kTok * kGStagePitch];
+    const int tm = blockIdx.x, n0 = blockIdx.y * kTok, m0 = tm * 256;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int wm = wv >> 1, j = wv & 1;
+    const int tn = n0 / G::BN, wn = (n0 % G::BN) / G::WTN;
+    const int nl = 32 * j + (lane & 31), tok = n0 + nl;
+    const bool tok_in = tok < p.rows;
+    const float4 *src = reinterpret_cast<const float4 *>(p.at + at_frag(tm, tn, p.Cpad / G::BN, wm * G::WN + wn, j, lane));
+    float4 a4[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+        a4[q] = src[64 * q];
+    const int ts = tok_in ? tok : 0;
+    const float cc = tok_in ? (p.w ? p.coef * p.w[ts] * *p.inv_wsum : p.coef) : 0.0f;
+    const float lt = p.lt2[ts];
+    const float sq = p.mw[(size_t)(2 * tm + wm) * p.Cpad + ts] - p.ls2[ts];
+    for (int c = threadIdx.x; c < kTok * 32; c += 256) {
+        const int rl = c >> 5, pc = c & 31, t = n0 + rl;
+        u32x4 e = {0u, 0u, 0u, 0u};
+        if (t < p.rows)
+            e = *reinterpret_cast<const u32x4 *>(p.ex + (size_t)t * p.Vpad + m0 + 8 * pc);
+        *reinterpret_cast<u32x4 *>(smem + rl * kGStagePitch + 16 * pc) = e;
+    }
+    __syncthreads();
+    const float fq = fast_exp2(sq);
+    const int vlim = p.V - m0 - G::row_of(wm, 0, 0, lane);    // rows at or past it are padding
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int rb = 32 * (q >> 2) + 8 * (q & 3);          // row of the piece's first value - row_of(wm, 0, 0, lane)
+        uint32_t *cell = reinterpret_cast<uint32_t *>(smem + nl * kGStagePitch + 2 * (G::row_of(wm, 0, 0, lane) + rb));
+        const uint32_t e01 = cell[0], e23 = cell[1];
+        const float e[4] = {__uint_as_float(e01 << 16), __uint_as_float(e01 & 0xffff0000u),
+                            __uint_as_float(e23 << 16), __uint_as_float(e23 & 0xffff0000u)};
+        const float a[4] = {a4[q].x, a4[q].y, a4[q].z, a4[q].w};
+        float g[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            g[c] = (rb + c < vlim) ? cc * (e[c] * fq - fast_exp2(a[c] - lt)) : 0.0f;
+        cell[0] = pack_bf16x2(g[0], g[1]);
+        cell[1] = pack_bf16x2(g[2], g[3]);
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < kTok * 32; c += 256) {
+        const int rl = c >> 5, pc = c & 31;
+        *reinterpret_cast<u32x4 *>(p.ex + (size_t)(n0 + rl) * p.Vpad + m0 + 8 * pc) =
+            *reinterpret_cast<const u32x4 *>(smem + rl * kGStagePitch + 16 * pc);
+    }
+    store_vocab_major<kTok, 4>(smem, p.gT, (size_t)p.Cpad, m0, n0);
+}
+
 // ------------------------------------------------------------------ teacher top-K
 
 // The teacher's cache holds, per position, its top logits and their indices, extracted
@@ -1827,6 +2128,92 @@ int launch_transpose_chunk(const ChunkArgs &a, void *stream)
 int launch_zero_flag(uint32_t *flag, void *stream)
 {
     hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, S(stream), flag, 4);
+    return (int)hipGetLastError();
+}
+
+int launch_full_teacher(const ChunkArgs &a, const FullLayout &F, const uint16_t *h_t, const uint16_t *W_t,
+                        void *stream)
+{
+    const Layout &L = F.base;
+    FullTeacherParams p;
+    p.W = W_t;
+    p.h = h_t;
+    p.H = F.Ht;
+    p.V = a.V;
+    p.rows = a.rows;
+    p.Cpad = L.Cpad;
+    p.nVt = L.nVt;
+    p.nNt = (a.rows + LogitGemm::BN - 1) / LogitGemm::BN;
+    p.scale2 = kLog2e / a.T;
+    p.part = reinterpret_cast<float2 *>(a.ws + F.off_part_t);
+    p.at = reinterpret_cast<float *>(a.ws + F.off_at);
+    hipLaunchKernelGGL(full_teacher_kernel, dim3(persistent_grid(p.nVt * p.nNt)), dim3(LogitGemm::NT), 0,
+                       S(stream), p);
+    return (int)hipGetLastError();
+}
+
+int launch_full_combine_teacher(const ChunkArgs &a, const FullLayout &F, void *stream)
+{
+    hipLaunchKernelGGL(full_combine_kernel, dim3((a.rows + 31) / 32), dim3(256), 0, S(stream),
+                       reinterpret_cast<const float2 *>(a.ws + F.off_part_t), (const float *)nullptr, F.base.nVt,
+                       F.base.Cpad, a.rows, a.T, (const float *)nullptr, reinterpret_cast<float *>(a.ws + F.off_lt2),
+                       (float *)nullptr, (float *)nullptr);
+    return (int)hipGetLastError();
+}
+
+int launch_full_student(const ChunkArgs &a, const FullLayout &F, void *stream)
+{
+    const Layout &L = F.base;
+    FullStudentParams p;
+    p.W = a.W;
+    p.h = a.h;
+    p.H = a.H;
+    p.V = a.V;
+    p.rows = a.rows;
+    p.Cpad = L.Cpad;
+    p.Vpad = L.Vpad;
+    p.nVt = L.nVt;
+    p.nNt = (a.rows + LogitGemm::BN - 1) / LogitGemm::BN;
+    p.scale2 = kLog2e / a.T;
+    p.at = reinterpret_cast<const float *>(a.ws + F.off_at);
+    p.lt2 = reinterpret_cast<const float *>(a.ws + F.off_lt2);
+    p.part = reinterpret_cast<float2 *>(a.ws + L.off_part);
+    p.px = reinterpret_cast<float *>(a.ws + F.off_px);
+    p.ex = reinterpret_cast<uint16_t *>(a.ws + L.off_g);
+    p.mw = reinterpret_cast<float *>(a.ws + L.off_mw);
+    hipLaunchKernelGGL(full_student_kernel, dim3(persistent_grid(p.nVt * p.nNt)), dim3(LogitGemm::NT), 0,
+                       S(stream), p);
+    return (int)hipGetLastError();
+}
+
+int launch_full_combine_student(const ChunkArgs &a, const FullLayout &F, float *loss_tok, float *lse, void *stream)
+{
+    hipLaunchKernelGGL(full_combine_kernel, dim3((a.rows + 31) / 32), dim3(256), 0, S(stream),
+                       reinterpret_cast<const float2 *>(a.ws + F.base.off_part),
+                       reinterpret_cast<const float *>(a.ws + F.off_px), F.base.nVt, F.base.Cpad, a.rows, a.T,
+                       reinterpret_cast<const float *>(a.ws + F.off_lt2), reinterpret_cast<float *>(a.ws + F.off_ls2),
+                       loss_tok, lse);
+    return (int)hipGetLastError();
+}
+
+int launch_full_grad(const ChunkArgs &a, const FullLayout &F, const GradScale &gs, void *stream)
+{
+    const Layout &L = F.base;
+    FullGradParams p;
+    p.ex = reinterpret_cast<uint16_t *>(a.ws + L.off_g);
+    p.gT = reinterpret_cast<uint16_t *>(a.ws + L.off_gT);
+    p.at = reinterpret_cast<const float *>(a.ws + F.off_at);
+    p.mw = reinterpret_cast<const float *>(a.ws + L.off_mw);
+    p.ls2 = reinterpret_cast<const float *>(a.ws + F.off_ls2);
+    p.lt2 = reinterpret_cast<const float *>(a.ws + F.off_lt2);
+    p.rows = a.rows;
+    p.Cpad = L.Cpad;
+    p.Vpad = L.Vpad;
+    p.V = a.V;
+    p.coef = gs.coef;
+    p.w = gs.w;
+    p.inv_wsum = gs.inv_wsum;
+    hipLaunchKernelGGL(full_grad_kernel, dim3(L.nVt, (a.rows + 63) / 64), dim3(256), 0, S(stream), p);
     return (int)hipGetLastError();
 }
 

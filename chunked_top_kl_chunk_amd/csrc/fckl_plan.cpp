@@ -142,6 +142,70 @@ fckl_status make_topk_layout(const fckl_desc *d, int32_t chunk, TopkLayout *L)
     return FCKL_OK;
 }
 
+fckl_status make_full_layout(const fckl_desc *d, int32_t Ht, int32_t chunk, FullLayout *L)
+{
+    if (Ht < 8)
+        return FCKL_ERR_INVALID_ARG;
+    if (Ht % 8 != 0 || Ht > 65536)
+        return FCKL_ERR_UNSUPPORTED;
+    FullLayout o;
+    fckl_status st = make_layout(d, chunk, &o.base);
+    if (st != FCKL_OK)
+        return st;
+    o.Ht = Ht;
+    const size_t Cp = (size_t)o.base.Cpad;
+    size_t off = o.base.total;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + bytes, 256);
+        return at;
+    };
+    o.off_at = take((size_t)o.base.Vpad * Cp * 4);
+    o.off_part_t = take((size_t)o.base.nVt * Cp * 8);
+    o.off_px = take((size_t)o.base.nVt * Cp * 4);
+    o.off_lt2 = take(Cp * 4);
+    o.off_ls2 = take(Cp * 4);
+    o.total = off;
+    *L = o;
+    return FCKL_OK;
+}
+
+fckl_status plan_full_chunk(const fckl_desc *d, int32_t Ht, size_t budget, FullLayout *L)
+{
+    fckl_status st = check_desc(d);
+    if (st != FCKL_OK)
+        return st;
+    if (d->chunk > 0)
+        return make_full_layout(d, Ht, d->chunk, L);
+    if (budget == 0)
+        budget = kDefaultBudget;
+    const int32_t npad = (int32_t)std::min<int64_t>(align_up((size_t)d->N, kTokenTile), kMaxChunk);
+    int32_t best = 0;
+    for (int32_t c = npad; c >= kTokenTile; c -= kTokenTile) {
+        FullLayout t;
+        if ((st = make_full_layout(d, Ht, c, &t)) != FCKL_OK)
+            return st;
+        if (t.total <= budget) {
+            best = c;
+            break;
+        }
+    }
+    if (best == 0)
+        return FCKL_ERR_WORKSPACE;
+    // the fewest even chunks that fit (the workspace is not monotone in the chunk)
+    for (int64_t nchunks = (d->N + best - 1) / best;; ++nchunks) {
+        const int32_t c = (int32_t)align_up((size_t)((d->N + nchunks - 1) / nchunks), kTokenTile);
+        FullLayout even;
+        if (c <= best && make_full_layout(d, Ht, c, &even) == FCKL_OK && even.total <= budget) {
+            *L = even;
+            return FCKL_OK;
+        }
+        if (c <= kTokenTile)
+            break;
+    }
+    return make_full_layout(d, Ht, best, L);
+}
+
 fckl_status plan_chunk(const fckl_desc *d, size_t budget, Layout *L)
 {
     fckl_status st = check_desc(d);

@@ -86,7 +86,11 @@ enum {
     FCKL_KERNEL_TRANSPOSE = 8,     /* W^T once per backward call, h^T once per chunk */
     FCKL_KERNEL_SOFTMAX_GRAD = 9,  /* fckl_forward_backward: g from the kept exponentials */
     FCKL_KERNEL_WEIGHTS = 10,      /* sum of the per-token weights */
-    FCKL_KERNEL_COUNT = 11
+    FCKL_KERNEL_FULL_TEACHER = 11, /* fckl_full_*: teacher logit GEMM, keeps its logits */
+    FCKL_KERNEL_FULL_STUDENT = 12, /* fckl_full_*: student logit GEMM + cross-entropy epilogue */
+    FCKL_KERNEL_FULL_COMBINE = 13, /* fckl_full_*: per-token logsumexp (teacher, then student + loss) */
+    FCKL_KERNEL_FULL_GRAD = 14,    /* fckl_full_*: g = c (q - p) */
+    FCKL_KERNEL_COUNT = 15
 };
 
 /*
@@ -242,6 +246,42 @@ fckl_status fckl_forward_backward(const fckl_desc *desc, const void *h, const vo
 fckl_status fckl_topk_workspace_size(const fckl_desc *desc, int32_t chunk, size_t *ws_bytes_out);
 fckl_status fckl_topk(const fckl_desc *desc, const void *h, const void *W, int32_t *topk_idx,
                       void *topk_logit, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Online distillation against the teacher's whole distribution: the setting the cached
+ * top-K teacher replaces, where the teacher's full-vocabulary distribution is computed
+ * beside the student's ("The Distillation Bottleneck", getaibook.com; the teacher run on
+ * the fly, "The 250GB VRAM Wall in Long-Context Distillation", axbrief.com).  The teacher's
+ * final hidden states and LM head are inputs; the teacher's logits are formed chunk by
+ * chunk like the student's and never exist for all N tokens.  With
+ *   p = softmax(h_t W_t^T / T), q = softmax(h W^T / T) over the whole vocabulary,
+ *   loss_tok[i] = T^2 sum_v p[i,v] (log p[i,v] - log q[i,v]),
+ *   lse[i] = log sum_v exp(z[i,v] / T) of the student,
+ *   loss_mean = sum_i w_i loss_tok[i] / sum_i w_i (weights NULL: the plain mean),
+ *   dH, dW = the gradients of grad_scale * loss_mean with respect to h and W, through
+ *   g[i,v] = grad_scale T w_i / sum_j w_j (q[i,v] - p[i,v]) (weights NULL: w_i / sum = 1/N).
+ * The teacher receives no gradient.  Per chunk the teacher product keeps its logits in
+ * fp32 (4 V bytes per token of workspace) and the student product keeps 2^(z/T log2 e - m)
+ * in bf16, as fckl_forward_backward does, so the logits of each model are formed once:
+ * 2 N V Ht + 6 N V H flop.
+ *   desc       N, H (the student's), V, T, chunk, flags (FCKL_FLAG_DW_ACCUMULATE), profile;
+ *              K and logit_dtype are not read; FCKL_FLAG_VALIDATE has no effect
+ *   H_teacher  the teacher's hidden size (a multiple of 8, at most 65536)
+ *   h, W       device, bf16 [N,H], [V,H]            the student
+ *   h_t, W_t   device, bf16 [N,H_teacher], [V,H_teacher]  the teacher (same vocabulary)
+ *   weights    device, f32 [N] or NULL              per-token weights (>= 0, not all 0)
+ *   loss_tok, lse  device, f32 [N]  out;  loss_mean device, f32 [1] out or NULL
+ *   dH         device, f32 [N,H] out;  dW device, f32 [V,H] out (or accumulated)
+ *   ws         device, 256-byte aligned; fckl_full_plan gives the size
+ * fckl_full_plan chooses the chunk as fckl_plan does, for this workspace (budget 0 = 12 GiB).
+ */
+fckl_status fckl_full_plan(const fckl_desc *desc, int32_t H_teacher, size_t budget_bytes,
+                           int32_t *chunk_out, size_t *ws_bytes_out);
+fckl_status fckl_full_forward_backward(const fckl_desc *desc, int32_t H_teacher, const void *h,
+                                       const void *W, const void *h_t, const void *W_t,
+                                       const float *weights, float grad_scale, float *loss_tok,
+                                       float *lse, float *loss_mean, float *dH, float *dW, void *ws,
+                                       size_t ws_bytes, void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *fckl_status_string(fckl_status status);

@@ -192,6 +192,51 @@ def test_weighted_and_single_call_entry_points_reject_before_any_hip_call():
     assert st == fckl.ERR_INVALID_ARG
 
 
+def test_full_teacher_plan_and_argument_checks():
+    """fckl_full_plan: its workspace holds the teacher's fp32 logits of a chunk on top of the
+    loss workspace, never depends on N, fits the budget; bad sizes are refused before any
+    HIP call."""
+    lib = fckl.load()
+    d = fckl.make_desc(C3["N"], C3["H"], C3["V"], 1, 1.0)
+    chunk, ws = fckl.full_plan(d, 2880)
+    assert ws <= DEFAULT_BUDGET and chunk % 256 == 0
+    base = fckl.workspace_size(fckl.make_desc(C3["N"], C3["H"], C3["V"], 1, 1.0), chunk)
+    assert ws >= base + 4 * chunk * C3["V"]
+    sizes = {fckl.full_plan(fckl.make_desc(N, 2880, 201088, 1, 1.0, 4096), 2880)[1] for N in (4096, 2 ** 31 - 1)}
+    assert len(sizes) == 1
+    # K and logit_dtype are not read
+    d_any = fckl.make_desc(C3["N"], C3["H"], C3["V"], 0, 1.0, 0, 7)
+    assert fckl.full_plan(d_any, 2880) == (chunk, ws)
+    for Ht, status in ((12, fckl.ERR_UNSUPPORTED), (0, fckl.ERR_INVALID_ARG), (-8, fckl.ERR_INVALID_ARG),
+                       (65544, fckl.ERR_UNSUPPORTED)):
+        with pytest.raises(fckl.FCKLError) as e:
+            fckl.full_plan(d, Ht)
+        assert e.value.status == status, Ht
+    with pytest.raises(fckl.FCKLError) as e:
+        fckl.full_plan(d, 2880, budget_bytes=1 << 20)
+    assert e.value.status == fckl.ERR_WORKSPACE
+    small = fckl.make_desc(512, 256, 4096, 1, 1.0, chunk=256)
+    _, need = fckl.full_plan(small, 384)
+    P = 1 << 40
+    ins = [_fake(P)] * 4
+    outs = [_fake(P)] * 5
+    size = ctypes.c_size_t
+    for missing in range(9):
+        args = ins + outs
+        if missing == 6:        # loss_mean may be NULL
+            continue
+        args[missing] = None
+        st = lib.fckl_full_forward_backward(ctypes.byref(small), 384, *args[:4], None, ctypes.c_float(1.0), *args[4:],
+                                            _fake(P), size(need), None)
+        assert st == fckl.ERR_INVALID_ARG, missing
+    st = lib.fckl_full_forward_backward(ctypes.byref(small), 384, *ins, None, ctypes.c_float(1.0), *outs, _fake(P),
+                                        size(need - 256), None)
+    assert st == fckl.ERR_WORKSPACE
+    st = lib.fckl_full_forward_backward(ctypes.byref(small), 384, *ins[:3], _fake(P + 8), None, ctypes.c_float(1.0),
+                                        *outs, _fake(P), size(need), None)
+    assert st == fckl.ERR_INVALID_ARG
+
+
 def test_module_validates_arguments_without_a_gpu():
     import torch
     from chunked_top_kl_chunk_amd.loss import FusedChunkedKLLoss
