@@ -17,8 +17,9 @@ chunk's logits once (6 N V H flop); it is reported beside the main line, which t
 the two passes of the method as defined (8 N V H flop).  `teacher_topk` times the
 teacher-side extraction of the top-K cache from the same hidden states (fckl_topk).
 `full_teacher` times the online variant against the teacher's whole distribution
-(fckl_full_forward_backward), with a teacher of the same shape (a perturbed copy of the
-student's hidden states and head): 2 N V Ht + 6 N V H flop per step.
+(fckl_full_forward_backward), with a teacher of the same shape (a seeded perturbed copy
+of the student's hidden states and head, synth.full_teacher): 2 N V Ht + 6 N V H flop
+per step.
 """
 from __future__ import annotations
 
@@ -225,11 +226,11 @@ def main():
 
     if not args.no_full:
         # Online distillation against the full teacher distribution, teacher of the same
-        # shape: a perturbed copy of h and W (seeded), its logits formed chunk by chunk.
-        gen = torch.Generator(device=dev)
-        gen.manual_seed(20260)
-        h_t = (h.float() + 0.3 * torch.randn(h.shape, generator=gen, device=dev)).to(torch.bfloat16)
-        W_t = (W.float() + 0.3 * W.float().std() * torch.randn(W.shape, generator=gen, device=dev)).to(torch.bfloat16)
+        # shape: a seeded perturbed copy of h and W, its logits formed chunk by chunk.
+        tch = synth.full_teacher(wl, x)
+        h_t = torch.from_numpy(tch.h_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        W_t = torch.from_numpy(tch.W_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        del tch
         fdesc = fckl.make_desc(N, H, V, 1, T)
         fchunk, fws_bytes = fckl.full_plan(fdesc, H)
         del ws

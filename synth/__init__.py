@@ -17,8 +17,13 @@ stood in for by tensors of the same shapes and value distributions:
 * values are drawn in float32 and rounded to bf16 (round to nearest even) where the
   workload is bf16, so the oracle and the GPU path see bit-identical inputs.
 
+For the online variant against the teacher's whole distribution, the teacher's final
+hidden states and LM head are perturbed copies of the student's (a related model of
+the same shape): h_t = h + N(0, 0.3^2), W_t = W + N(0, (0.3 * 0.02)^2), rounded to bf16.
+
 Seeds: ``seed = 1000 * config_number + stream`` with stream h:0, W:1, W'-noise:2,
-idx:3, teacher logits:4, scaled-row pick:5, parity row sample:6.
+idx:3, teacher logits:4, scaled-row pick:5, parity row sample:6, teacher h noise:7,
+teacher W noise:8.
 """
 from __future__ import annotations
 
@@ -27,7 +32,8 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-S_H, S_W, S_WNOISE, S_IDX, S_TL, S_ROWS, S_SAMPLE = 0, 1, 2, 3, 4, 5, 6
+S_H, S_W, S_WNOISE, S_IDX, S_TL, S_ROWS, S_SAMPLE, S_HT, S_WT = 0, 1, 2, 3, 4, 5, 6, 7, 8
+TEACHER_NOISE = 0.3
 
 
 @dataclass(frozen=True)
@@ -232,6 +238,25 @@ def make_inputs(wl: Workload, device=None) -> Inputs:
     if wl.dtype == "fp32":
         return Inputs(wl, hb, Wb, idx, tlb, h_bits, W_bits, tl_bits, h_raw=h, W_raw=W, tl_raw=tl)
     return Inputs(wl, hb, Wb, idx, tlb, h_bits, W_bits, tl_bits)
+
+
+@dataclass
+class Teacher:
+    """A full teacher model's final hidden states [N, H] and LM head [V, H]: bf16 values
+    as float32 and their bit patterns."""
+    h: np.ndarray
+    W: np.ndarray
+    h_bits: np.ndarray
+    W_bits: np.ndarray
+
+
+def full_teacher(wl: Workload, x: Inputs) -> Teacher:
+    """The teacher of the online variant: the student's bf16 h and W plus seeded noise."""
+    ht = x.h + normal(wl.seed(S_HT), x.h.shape, TEACHER_NOISE)
+    Wt = x.W + normal(wl.seed(S_WT), x.W.shape, TEACHER_NOISE * 0.02)
+    hb, Wb = bf16_bits(ht), bf16_bits(Wt)
+    del ht, Wt
+    return Teacher(bf16_to_f32(hb), bf16_to_f32(Wb), hb, Wb)
 
 
 def sample_rows(wl: Workload, n: int, must_include=None) -> np.ndarray:

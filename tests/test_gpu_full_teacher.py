@@ -51,8 +51,11 @@ CASES = [
     (81, 517, 136, 200, 1000, 2.0, 256, True, 0.0),    # three chunks, ragged, Ht != Hs
     (82, 130, 2880, 2880, 777, 0.7, 0, False, 0.3),    # the 20B model's hidden size, a close teacher
     (83, 600, 512, 512, 5000, 1.5, 512, True, 0.5),    # two chunks, weighted, close teacher
+    (87, 1, 8, 16, 100, 1.0, 0, False, 0.0),           # one token, the smallest hidden sizes, V < one tile
+    (88, 257, 64, 64, 257, 3.0, 0, True, 0.2),         # one row into the second vocabulary tile
+    (89, 64, 96, 40, 600, 0.25, 0, False, 0.0),        # low temperature: sharp distributions
 ]
-IDS = ["ragged-V", "chunks-Ht", "H2880-close", "weighted-close"]
+IDS = ["ragged-V", "chunks-Ht", "H2880-close", "weighted-close", "N1-H8", "V257", "T0.25"]
 
 
 @pytest.mark.parametrize("case", CASES, ids=IDS)

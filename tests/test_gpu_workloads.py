@@ -19,7 +19,7 @@ import torch
 import chunked_top_kl_chunk_amd as fckl
 import oracle
 import synth
-from gpu_util import GRAD_TOL, LOSS_RTOL, LSE_ATOL, check_grad, check_loss, device, rel_max, say, upload
+from gpu_util import GRAD_TOL, LSE_ATOL, check_grad, check_loss, device, say, upload
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
@@ -126,6 +126,58 @@ def test_single_call_at_full_size():
     assert e_dH <= GRAD_TOL and e_dW <= GRAD_TOL
     assert sum_rows <= 1e-3 * scale_rows
     assert abs(ip_w - ip_h) <= 2e-2 * max(abs(ip_w), abs(ip_h))
+
+
+@pytest.mark.timeout(900)
+def test_full_teacher_at_full_size():
+    """fckl_full_forward_backward on the 32K-token shape, teacher of the same shape (a
+    perturbed copy of the student), in the launch configuration the benchmark uses:
+    size-independent identities at full size, sampled tokens against the oracle, and
+    dW over the full vocabulary x hidden size on a token subset."""
+    wl = synth.WORKLOADS["c3"]
+    say("case: full teacher, full workload", wl.name)
+    x = synth.make_inputs(wl, device=device())
+    tch = synth.full_teacher(wl, x)
+    dev = device()
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+    h, W, ht, Wt = bf(x.h_bits), bf(x.W_bits), bf(tch.h_bits), bf(tch.W_bits)
+    chunk, ws_bytes = fckl.full_plan(fckl.make_desc(wl.N, wl.H, wl.V, 1, wl.T), wl.H)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    loss, lse, mean, dH, dW = fckl.full_forward_backward(h, W, ht, Wt, T=wl.T, chunk=chunk, ws=ws)
+    torch.cuda.synchronize()
+    sum_rows = dW.double().sum(0).abs().max().item()
+    scale_rows = dW.double().abs().sum(0).max().item()
+    ip_w = (dW.double() * W.double()).sum().item()
+    ip_h = (dH.double() * h.double()).sum().item()
+    loss_n, lse_n = loss.cpu().numpy(), lse.cpu().numpy()
+    assert np.isfinite(loss_n).all()
+    assert (loss_n >= -1e-5 * np.abs(loss_n).max()).all()
+    assert abs(float(mean.item()) - loss_n.astype(np.float64).mean()) <= 1e-5 * abs(float(mean.item()))
+    assert sum_rows <= 1e-3 * scale_rows, (sum_rows, scale_rows)
+    assert abs(ip_w - ip_h) <= 2e-2 * max(abs(ip_w), abs(ip_h)), (ip_w, ip_h)
+    rows = synth.sample_rows(wl, 32)
+    rt = torch.from_numpy(rows).to(dev)
+    dH_rows = dH[rt].cpu().numpy()
+    del dH, dW, ws
+    torch.cuda.empty_cache()
+    # the oracle on the sampled tokens alone (its gradient is normalised by their count)
+    r_loss, r_lse, _, r_dH, r_dW = oracle.full(x.h[rows], x.W, tch.h[rows], tch.W, wl.T)
+    e_loss = check_loss(loss_n[rows], r_loss, "full teacher")
+    e_lse = float(np.abs(lse_n[rows] - r_lse).max())
+    assert e_lse <= LSE_ATOL, "lse abs err %.3e" % e_lse
+    e_dH = check_grad(dH_rows, r_dH * (rows.size / wl.N), "full teacher dH rows")
+    # the same tokens as their own batch: dW over the full V x H
+    _, _, _, dH_s, dW_s = fckl.full_forward_backward(h[rt].contiguous(), W, ht[rt].contiguous(), Wt, T=wl.T,
+                                                     chunk=chunk)
+    torch.cuda.synchronize()
+    e_dHs = check_grad(dH_s.cpu().numpy(), r_dH, "full teacher subset dH")
+    e_dWs = check_grad(dW_s.cpu().numpy(), r_dW, "full teacher subset dW")
+    say("full teacher at full size: chunk %d, mean KL %.4f; sampled %d rows: loss %.2e lse %.2e dH %.2e; "
+        "subset dH %.2e dW %.2e; sum_v dW %.1e of %.1e; <dW,W> %.6e <dH,h> %.6e"
+        % (chunk, float(mean.item()), rows.size, e_loss, e_lse, e_dH, e_dHs, e_dWs, sum_rows, scale_rows,
+           ip_w, ip_h))
 
 
 def test_peak_memory_has_no_tokens_times_vocab_term():
