@@ -250,3 +250,30 @@ def test_module_validates_arguments_without_a_gpu():
         FusedChunkedKLLoss()(h, W, idx, tl)
     with pytest.raises(ValueError):
         fckl.forward_backward(h, W, idx, tl)
+
+
+def test_missing_library_fails_loudly():
+    """Without libfckl.so every entry point raises: there is no CPU or eager fallback."""
+    saved_lib, saved_path = fckl._lib, fckl.LIB_PATH
+    try:
+        fckl._lib = None
+        fckl.LIB_PATH = os.path.join(ROOT, "no-such-dir", "libfckl.so")
+        d = fckl.make_desc(64, 64, 256, 4, 1.0)
+        calls = [lambda: fckl.plan(d), lambda: fckl.workspace_size(d, 256), lambda: fckl.full_plan(d, 64),
+                 lambda: fckl.topk_workspace_size(d), lambda: fckl.version(), lambda: fckl.load()]
+        for call in calls:
+            with pytest.raises(ImportError):
+                call()
+    finally:
+        fckl._lib, fckl.LIB_PATH = saved_lib, saved_path
+
+
+def test_product_code_does_not_reach_the_oracle():
+    """The oracle is test infrastructure: nothing in the package or the C ABI names it."""
+    pkg = os.path.join(ROOT, "chunked_top_kl_chunk_amd")
+    files = [os.path.join(dp, f) for dp, _, fs in os.walk(pkg) for f in fs
+             if f.endswith((".py", ".cpp", ".hip", ".h"))] + [HEADER]
+    assert len(files) >= 6
+    for path in files:
+        text = open(path).read()
+        assert not re.search(r"\boracle\b|fckl_oracle", text), path
