@@ -220,113 +220,22 @@ struct KTile {
     }
 };
 
-// Operand tile whose row (m or n) dimension is contiguous: BKK k-rows x COLS columns.
-// The MFMA operand (8 consecutive k of one column per lane) is gathered with two
-// ds_read_b64_tr_b16: in each group of 16 lanes, lane l receives element l%4 of the
-// 8-byte pieces addressed by lanes l/4, 4 + l/4, 8 + l/4 and 12 + l/4, so lanes
-// addressing k-rows kb..kb+3 at columns c..c+15 hand each lane 4 k-values of one
-// column.  One LDS cycle serves 32 lanes (256 bytes): four k-rows x four 16-byte
-// chunks; the chunk index is XOR-swizzled by a function of k so that the four rows
-// land in four distinct 64-byte bank groups.
-template <int COLS, int BKK, int NT>
-struct MNTile {
-    static constexpr int CPR = COLS / 8;
-    static constexpr int CHUNKS = BKK * CPR;
-    static_assert(CHUNKS % NT == 0, "whole wave instructions");
-    static constexpr int PER = CHUNKS / NT;
-    static constexpr int BYTES = CHUNKS * 16;
-
-    static_assert((CPR * 16) % 256 == 0 || (CPR * 16) % 256 == 128, "row pitch a multiple of 128 bytes");
-    static_assert(CPR % 8 == 0, "XOR swizzle stays inside the row");
-    // Rows whose pitch is a multiple of 256 bytes: XOR by 4*(k%4).  Rows of an odd
-    // multiple of 128 bytes alternate between the two halves of the 256-byte bank
-    // window, so XOR by 4*((k/2)%2) suffices.
-    __device__ __forceinline__ static int sw(int k)
-    {
-        return (CPR * 16) % 256 == 0 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
-    }
-
-    // Source state.  `base` (uniform) points at k-row k0 of the current slice, column
-    // col0; per piece, a lane keeps its 32-bit element offset from there and a check
-    // value: the piece's k-row in the slice, or a huge number when its columns do not
-    // exist.
-    struct Src {
-        const uint16_t *base;
-        uint32_t off[PER];
-        int kchk[PER];
-    };
-    __device__ __forceinline__ static void init(Src &s, const uint16_t *base, int64_t ld, int col0, int cols_valid,
-                                                int k_begin)
-    {
-        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-        s.base = base + (int64_t)k_begin * ld + col0;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int pslot = (i * (NT / 64) + wave) * 64 + lane;
-            const int k = pslot / CPR, pc = pslot % CPR;
-            const int c = (pc ^ sw(k)) * 8;
-            const bool ok = col0 + c < cols_valid;
-            s.off[i] = ok ? (uint32_t)(k * ld + c) : 0u;
-            s.kchk[i] = ok ? k : (1 << 30);
-        }
-    }
-    // Piece i of k-rows [k0, k0 + BKK) into `tile`.
-    __device__ __forceinline__ static void issue_one(const Src &s, int i, int k0, int k_valid, char *tile)
-    {
-        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        const bool ok = k0 + s.kchk[i] < k_valid;
-        const void *src = ok ? static_cast<const void *>(s.base + s.off[i]) : static_cast<const void *>(kZeroPage);
-        copy16_to_lds(src, tile + (i * (NT / 64) + wave) * 1024);
-    }
-    // Move the source to the next k-slice.
-    __device__ __forceinline__ static void advance(Src &s, int64_t ld) { s.base += (int64_t)BKK * ld; }
-    // Operand of one lane for the 32-column block starting at `col`, k-step ks (16 k).
-    __device__ __forceinline__ static bf16x8 frag(const char *tile, int col, int ks)
-    {
-        const int lane = threadIdx.x & 63;
-        const int s = lane & 15;
-        const int c = col + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
-        const int kb = ks * 16 + 8 * (lane >> 5) + (s >> 2);
-        i16x4 v[2];
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int k = kb + 4 * r;
-            const char *a = tile + (k * CPR + ((c >> 3) ^ sw(k))) * 16 + ((c >> 2) & 1) * 8;
-            v[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(a));
-        }
-        i16x4 lo = v[0], hi = v[1];
-        typedef short i16x8 __attribute__((ext_vector_type(8)));
-        i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        return __builtin_bit_cast(bf16x8, w);
-    }
-};
-
-template <bool KMAJ, int ROWS, int BKK, int NT>
-struct TileOf {
-    using type = KTile<ROWS, BKK, NT>;
-};
-template <int ROWS, int BKK, int NT>
-struct TileOf<false, ROWS, BKK, NT> {
-    using type = MNTile<ROWS, BKK, NT>;
-};
-
 // C[m, n] = sum_k A(m, k) * B(n, k) for one BM x BN tile, operands streamed
 // global -> LDS by the DMA path with S stages in flight (no staging registers).
-// Accumulator layout as in Gemm.  A k-major: A(m,k) = A[m*lda + k]; otherwise
-// A(m,k) = A[k*lda + m]; the same for B.
+// Both operands k-major: A(m,k) = A[m*lda + k], B(n,k) = B[n*ldb + k].
 struct NoHook {
     __device__ __forceinline__ void operator()() const {}
 };
 
-template <int BM_, int BN_, int WM_, int WN_, bool AK, bool BKM, int BKK, int S>
+template <int BM_, int BN_, int WM_, int WN_, int BKK, int S>
 struct GemmD {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BKK;
     static constexpr int NT = WM * WN * 64;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int MB = WTM / 32, NB = WTN / 32;
     static_assert(MB * 32 == WTM && NB * 32 == WTN, "wave tile");
-    using AT = typename TileOf<AK, BM, BKK, NT>::type;
-    using BT = typename TileOf<BKM, BN, BKK, NT>::type;
+    using AT = KTile<BM, BKK, NT>;
+    using BT = KTile<BN, BKK, NT>;
     static constexpr int STAGE = AT::BYTES + BT::BYTES;
     static constexpr int LDS_BYTES = S * STAGE;
     static constexpr int L = AT::PER + BT::PER;     // DMA loads per thread per k-step
@@ -345,19 +254,11 @@ struct GemmD {
     __device__ __forceinline__ static void load_frags(const char *stage, int ks, int wm, int wn, int lane, Frags &f)
     {
 #pragma unroll
-        for (int i = 0; i < MB; ++i) {
-            if constexpr (AK)
-                f.a[i] = AT::frag(stage, wm * WTM + i * 32 + (lane & 31), ks * 2 + (lane >> 5));
-            else
-                f.a[i] = AT::frag(stage, wm * WTM + i * 32, ks);
-        }
+        for (int i = 0; i < MB; ++i)
+            f.a[i] = AT::frag(stage, wm * WTM + i * 32 + (lane & 31), ks * 2 + (lane >> 5));
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            if constexpr (BKM)
-                f.b[j] = BT::frag(stage + AT::BYTES, wn * WTN + j * 32 + (lane & 31), ks * 2 + (lane >> 5));
-            else
-                f.b[j] = BT::frag(stage + AT::BYTES, wn * WTN + j * 32, ks);
-        }
+        for (int j = 0; j < NB; ++j)
+            f.b[j] = BT::frag(stage + AT::BYTES, wn * WTN + j * 32 + (lane & 31), ks * 2 + (lane >> 5));
     }
 
     __device__ __forceinline__ static void mma(const Frags &f, f32x16 (&acc)[MB][NB])
@@ -369,8 +270,8 @@ struct GemmD {
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
     }
 
-    // DS-read instructions per fragment set (a transposed fragment takes two reads).
-    static constexpr int DS_PER_SUB = (AK ? MB : 2 * MB) + (BKM ? NB : 2 * NB);
+    // DS-read instructions per fragment set (one ds_read_b128 per fragment).
+    static constexpr int DS_PER_SUB = MB + NB;
     static constexpr int SUB = BKK / 16;
     // The L loads of one k-step are spread over the first ISSUE_SUBS substeps of the
     // step before, P per substep.
@@ -495,7 +396,7 @@ struct GemmD {
 };
 
 // The logit GEMM: rows = vocabulary (W), columns = tokens (h), k = hidden.
-using LogitGemm = GemmD<256, 256, 2, 4, true, true, 64, 2>;
+using LogitGemm = GemmD<256, 256, 2, 4, 64, 2>;
 static_assert(LogitGemm::BM == kVocabTile, "entry counts are kept per 256-row vocabulary tile");
 static_assert(kTokenTile % LogitGemm::BN == 0, "chunk padding covers whole token tiles");
 constexpr int kGStagePitch = 256 * 2 + 16;   // bytes per token row of the staged bf16 g tile
@@ -1839,8 +1740,8 @@ __global__ __launch_bounds__(G::NT) void dw_kernel(DwParams p)
     }
 }
 
-using DGemm = GemmD<256, kHiddenTile, 2, 4, true, true, 64, 2>;   // dH: tokens x hidden, k = vocabulary
-using WGemm = GemmD<256, kHiddenTile, 2, 4, true, true, 64, 2>;   // dW: vocabulary x hidden, k = tokens
+using DGemm = GemmD<256, kHiddenTile, 2, 4, 64, 2>;   // dH: tokens x hidden, k = vocabulary
+using WGemm = GemmD<256, kHiddenTile, 2, 4, 64, 2>;   // dW: vocabulary x hidden, k = tokens
 
 // dst[c][r] = src[r][c] for r < rows, c < cols; dst[c][r] = 0 for rows <= r < rpad.
 // 64 x 64 tiles through LDS so that both sides are read and written along rows.
