@@ -269,7 +269,8 @@ fckl_status fckl_topk(const fckl_desc *desc, const void *h, const void *W, int32
  *   H_teacher  the teacher's hidden size (a multiple of 8, at most 65536)
  *   h, W       device, bf16 [N,H], [V,H]            the student
  *   h_t, W_t   device, bf16 [N,H_teacher], [V,H_teacher]  the teacher (same vocabulary)
- *   weights    device, f32 [N] or NULL              per-token weights (>= 0, not all 0)
+ *   weights    device, f32 [N] or NULL              per-token weights: finite and >= 0 (not
+ *              checked); all 0 gives loss_mean = 0 and zero gradients
  *   loss_tok, lse  device, f32 [N]  out;  loss_mean device, f32 [1] out or NULL
  *   dH         device, f32 [N,H] out;  dW device, f32 [V,H] out (or accumulated)
  *   ws         device, 256-byte aligned; fckl_full_plan gives the size
