@@ -151,6 +151,20 @@ def main():
     ms_step, kernels = timed_steps(fckl, step, args.steps, nchunks)
     tokens_per_s = N * 1e3 / ms_step
     log("timed %d steps: %.2f ms/step, %.0f tokens/s" % (args.steps, ms_step, tokens_per_s))
+    # the two passes on their own (after the timed steps, so they do not enter `value`)
+    reps = max(1, min(args.steps, 5))
+    pass_ms = {}
+    for name, call in (("forward", lambda: fckl.forward(h, W, idx, tl, T=T, chunk=chunk, ws=ws, loss_tok=loss,
+                                                        lse=lse, loss_mean=mean)),
+                       ("backward", lambda: fckl.backward(h, W, idx, tl, lse, T=T, chunk=chunk, ws=ws, dH=dH,
+                                                          dW=dW))):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            call()
+        torch.cuda.synchronize()
+        pass_ms[name] = (time.perf_counter() - t0) * 1e3 / reps
+    log("forward %.2f ms, backward %.2f ms" % (pass_ms["forward"], pass_ms["backward"]))
     gemms = ("fwd_logits", "bwd_logits", "dh", "dw")
     for name, d in kernels.items():
         d["avg_ms"] = d["ms"] / d["launches"]
@@ -178,6 +192,7 @@ def main():
                    "chunks": nchunks},
         "roofline": roofline,
         "mfma_frac_step": round(step_tflops / PEAK_BF16_TFLOPS, 4),
+        "forward_ms": round(pass_ms["forward"], 3), "backward_ms": round(pass_ms["backward"], 3),
         "step_tflops": round(step_tflops, 1),
         "peak_gib": round(peak_bytes / GiB, 3),
         "workspace_gib": round(ws_bytes / GiB, 3),

@@ -59,11 +59,13 @@ CASES = [
     (6, 512, 512, 3000, 10, 4.0, 0, {"scaled_frac": 0.01, "tl_sigma": 1.0}),
     (7, 700, 1024, 5000, 100, 1.0, 512, {"z_sigma": 4.0}),
     (8, 130, 3072, 513, 16, 1.0, 0, {}),
+    (9, 200, 64, 100, 100, 1.0, 0, {}),                                   # K = V, V < one tile
+    (10, 300, 128, 2000, 10, 0.25, 0, {"z_sigma": 20.0, "tl_sigma": 10.0}),  # z/T spread ~80: sharp softmaxes
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=["ragged", "one-token", "K128", "K1", "H2880", "scaled-rows",
-                                             "K100", "H3072"])
+                                             "K100", "H3072", "K-equals-V", "sharp"])
 def test_parity_shapes(case):
     seed, N, H, V, K, T, chunk, extra = case
     say("case:", case)
