@@ -30,7 +30,7 @@ LIB_PATH = os.path.join(_PKG, "libfckl.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_INDEX, ERR_HIP = range(6)
 DTYPE_BF16, DTYPE_F32 = 0, 1
-FLAG_VALIDATE, FLAG_DW_ACCUMULATE = 1, 2
+FLAG_VALIDATE, FLAG_DW_ACCUMULATE, FLAG_TOPK_FULL_FIRST_PASS = 1, 2, 4
 
 # Every symbol include/fckl.h declares.
 EXPORTS = ("fckl_plan", "fckl_workspace_size", "fckl_forward", "fckl_backward", "fckl_forward_ex",
@@ -298,10 +298,10 @@ def topk_workspace_size(desc: Desc, chunk: int = 0) -> int:
 
 
 def topk(h, W, K: int, chunk: int = 0, logits_f32: bool = False, ws=None, topk_idx=None, topk_logit=None,
-         stream=None):
+         stream=None, full_first_pass: bool = False):
     """Teacher-side extraction (fckl_topk): per token the K largest z = h W^T, descending,
     equal values by the smaller index.  Returns (topk_idx int32 [N,K], topk_logit [N,K]
-    bf16, or float32 with logits_f32)."""
+    bf16, or float32 with logits_f32).  full_first_pass: FCKL_FLAG_TOPK_FULL_FIRST_PASS."""
     import torch
     for name, t in (("h", h), ("W", W)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
@@ -309,7 +309,8 @@ def topk(h, W, K: int, chunk: int = 0, logits_f32: bool = False, ws=None, topk_i
     if h.dim() != 2 or W.dim() != 2 or W.shape[1] != h.shape[1] or h.device != W.device:
         raise ValueError("expected h[N,H] and W[V,H] on one device")
     N, dev = h.shape[0], h.device
-    desc = make_desc(N, h.shape[1], W.shape[0], K, 1.0, chunk, DTYPE_F32 if logits_f32 else DTYPE_BF16)
+    desc = make_desc(N, h.shape[1], W.shape[0], K, 1.0, chunk, DTYPE_F32 if logits_f32 else DTYPE_BF16,
+                     FLAG_TOPK_FULL_FIRST_PASS if full_first_pass else 0)
     need = topk_workspace_size(desc, chunk)
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)

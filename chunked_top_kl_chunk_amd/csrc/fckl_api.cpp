@@ -489,6 +489,7 @@ fckl_status fckl_topk(const fckl_desc *desc, const void *h, const void *W, int32
     if (T.total > ws_bytes)
         return FCKL_ERR_WORKSPACE;
     uint32_t *flag = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(ws) + T.off_err);
+    uint32_t *retry = flag + 1;
     if (launch_zero_flag(flag, stream))
         return FCKL_ERR_HIP;
     const bool f32 = desc->logit_dtype == FCKL_DTYPE_F32;
@@ -503,9 +504,21 @@ fckl_status fckl_topk(const fckl_desc *desc, const void *h, const void *W, int32
         a.K = desc->K;
         a.T = desc->T;
         a.ws = reinterpret_cast<char *>(ws);
-        if (launch_topk_max(a, T, stream) || launch_topk_threshold(a, T, stream) || launch_topk_collect(a, T, stream) ||
-            launch_topk_select(a, T, topk_idx + (size_t)c0 * desc->K,
-                               reinterpret_cast<char *>(topk_logit) + (size_t)c0 * desc->K * esz, f32, stream))
+        int32_t *idx_c = topk_idx + (size_t)c0 * desc->K;
+        void *logit_c = reinterpret_cast<char *>(topk_logit) + (size_t)c0 * desc->K * esz;
+        if (T.nSubPart > 0) {
+            // first pass over a quarter of the vocabulary; the chunk's retry flag is raised
+            // when a token then has more candidates than fit, and the guarded sequence
+            // below redoes the chunk with a first pass over every tile
+            if (launch_topk_max(a, T, true, nullptr, stream) ||
+                launch_topk_threshold(a, T, true, nullptr, retry, stream) || launch_topk_collect(a, T, nullptr, stream) ||
+                launch_topk_select(a, T, idx_c, logit_c, f32, nullptr, retry, stream))
+                return FCKL_ERR_HIP;
+        }
+        const uint32_t *guard = T.nSubPart > 0 ? retry : nullptr;
+        if (launch_topk_max(a, T, false, guard, stream) ||
+            launch_topk_threshold(a, T, false, guard, nullptr, stream) || launch_topk_collect(a, T, guard, stream) ||
+            launch_topk_select(a, T, idx_c, logit_c, f32, guard, nullptr, stream))
             return FCKL_ERR_HIP;
     }
     uint32_t host = 0;

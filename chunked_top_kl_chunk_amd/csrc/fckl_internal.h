@@ -21,6 +21,7 @@ constexpr int kMaxK = 128;
 // largest of the token's 32-row sub-tile maxima), and the most sub-tile maxima per token
 // (V <= 2^21; their buffer is 4 bytes per maximum and token of a chunk).
 constexpr int kTopkCap = 2048;
+constexpr int kTopkStride = 4;      // the partial first pass visits every 4th vocabulary tile
 constexpr int kTopkMaxSub = 65536;
 constexpr int32_t kMaxChunk = 8192;
 constexpr size_t kDefaultBudget = size_t(12) << 30;  // 12 GiB of the 288 GB HBM3E
@@ -55,12 +56,15 @@ struct Layout {
 
 // Workspace of the teacher top-K extraction (its own, much smaller than the loss's).
 struct TopkLayout {
-    int32_t C = 0, Cpad = 0, nVt = 0, nSub = 0;
-    size_t off_tmax = 0;    // f32   [nSub, Cpad]  maximum of z over each 256-row tile (or 32-row slice)
+    int32_t C = 0, Cpad = 0, nVt = 0;
+    int32_t nSubFull = 0;   // maxima per token of a first pass over every tile (per tile, or per 32-row slice)
+    int32_t nSubPart = 0;   // maxima per token of a first pass over every kTopkStride-th tile (64-row
+                            // slices); 0 = that pass is not used
+    size_t off_tmax = 0;    // f32   [max(nSubFull, nSubPart), Cpad]  slice maxima
     size_t off_thr = 0;     // f32   [Cpad]        K-th largest of a token's maxima
     size_t off_count = 0;   // u32   [Cpad]        candidates found per token
     size_t off_cand = 0;    // u64   [Cpad, kTopkCap] candidate keys
-    size_t off_err = 0;     // u32   [4]           overflow flag
+    size_t off_err = 0;     // u32   [4]           [0] error flag, [1] the chunk's retry flag
     size_t total = 0;
 };
 
@@ -142,10 +146,13 @@ int launch_full_student(const ChunkArgs &a, const FullLayout &F, void *stream);
 int launch_full_combine_student(const ChunkArgs &a, const FullLayout &F, float *loss_tok, float *lse, void *stream);
 int launch_full_grad(const ChunkArgs &a, const FullLayout &F, const GradScale &gs, void *stream);
 
-int launch_topk_max(const ChunkArgs &a, const TopkLayout &T, void *stream);
-int launch_topk_threshold(const ChunkArgs &a, const TopkLayout &T, void *stream);
-int launch_topk_collect(const ChunkArgs &a, const TopkLayout &T, void *stream);
+// Teacher top-K, per chunk.  `partial`: the first pass over every kTopkStride-th tile;
+// `guard` (may be NULL): the kernel returns at once unless *guard != 0.
+int launch_topk_max(const ChunkArgs &a, const TopkLayout &T, bool partial, const uint32_t *guard, void *stream);
+int launch_topk_threshold(const ChunkArgs &a, const TopkLayout &T, bool partial, const uint32_t *guard,
+                          uint32_t *retry_reset, void *stream);
+int launch_topk_collect(const ChunkArgs &a, const TopkLayout &T, const uint32_t *guard, void *stream);
 int launch_topk_select(const ChunkArgs &a, const TopkLayout &T, int32_t *topk_idx, void *topk_logit, bool logit_f32,
-                       void *stream);
+                       const uint32_t *guard, uint32_t *retry, void *stream);
 
 }  // namespace fckl

@@ -1398,21 +1398,30 @@ __global__ __launch_bounds__(256) void full_grad_kernel(FullGradParams p)
 // The teacher's cache holds, per position, its top logits and their indices, extracted
 // once ("Preparing Offline Top-K Logits", getaibook.com).  Exact top-K of z = h W^T per
 // token in two passes of the logit GEMM:
-//   1. the maximum of z over each 256-row tile of the vocabulary per token, or over each
-//      32-row slice when there are fewer tiles than K;
+//   1. maxima of z per token over disjoint row slices of the vocabulary;
 //   2. tau = the K-th largest of those maxima is at most the K-th largest logit (the
-//      maxima are K actual logits), so every logit >= tau is collected as a candidate
-//      (tau comes from a per-token min-heap of K entries);
+//      maxima are K actual logits of distinct rows), so every logit >= tau is collected
+//      as a candidate (tau comes from a per-token min-heap of K entries);
 //   3. the candidates are sorted by (z descending, index ascending) and the first K kept.
-// z is bitwise the same in both passes (same tiles, same accumulation order), so the
-// logit that attains a maximum passes its own threshold.
+// Any set of at least K disjoint slices gives a valid tau, so the first pass only needs
+// part of the vocabulary: every 4th 256-row tile, with one maximum per 64-row slice,
+// costs a quarter of the product and leaves a few times K candidates.  When a token of
+// the chunk then has more than kTopkCap candidates (its large logits all outside that
+// quarter), the chunk is redone with a first pass over every tile (one maximum per
+// tile, or per 32-row slice when there are fewer tiles than K); the redo kernels are
+// launched regardless and return at once unless the chunk's retry flag is set, so no
+// host synchronisation is needed.  z is bitwise the same in every pass (same tiles,
+// same accumulation order), so the logit that attains a maximum passes its own threshold.
 
 struct TopkParams {
     const uint16_t *W;      // [V, H]
     const uint16_t *h;      // [rows, H] chunk
     int H, V, rows, Cpad, nVt, nNt;
-    int slices;             // maxima per 256-row tile: 1 or 8 (32-row slices)
-    float *tmax;            // [slices nVt, Cpad] maxima (pass 1)
+    int stride;             // pass 1 visits vocabulary tiles 0, stride, 2 stride, ... (pass 2: 1)
+    int nTm;                // vocabulary tiles visited: ceil(nVt / stride)
+    int slices;             // maxima per visited tile: 1, 4 (64-row slices) or 8 (32-row slices)
+    const uint32_t *guard;  // NULL, or run only when *guard != 0
+    float *tmax;            // [slices nTm, Cpad] maxima (pass 1)
     const float *thr;       // [Cpad] thresholds (pass 2)
     uint32_t *count;        // [Cpad] candidates per token (pass 2)
     uint64_t *cand;         // [Cpad, kTopkCap] candidate keys (pass 2)
@@ -1438,8 +1447,9 @@ template <bool COLLECT>
 __device__ __forceinline__ void topk_tile(const TopkParams &p, char *smem, int t)
 {
     using G = LogitGemm;
-    int tm, tn;
-    map_tile(t, p.nVt, p.nNt, 4, tm, tn);
+    int ts, tn;
+    map_tile(t, p.nTm, p.nNt, 4, ts, tn);
+    const int tm = ts * p.stride;
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / G::WN, wn = wave % G::WN;
@@ -1460,6 +1470,7 @@ __device__ __forceinline__ void topk_tile(const TopkParams &p, char *smem, int t
     for (int j = 0; j < G::NB; ++j) {
         const int tok = n0 + G::col_of(wn, j, lane);
         tile_mx[j] = -__builtin_inff();
+        float pair_mx = -__builtin_inff();
 #pragma unroll
         for (int i = 0; i < G::MB; ++i) {
             if constexpr (!COLLECT) {
@@ -1470,8 +1481,13 @@ __device__ __forceinline__ void topk_tile(const TopkParams &p, char *smem, int t
                     mx = fmaxf(mx, (32 * i + 8 * (r >> 2) + (r & 3) < lim) ? acc[i][j][r] : -__builtin_inff());
                 mx = fmaxf(mx, __shfl_xor(mx, 32));
                 tile_mx[j] = fmaxf(tile_mx[j], mx);
+                pair_mx = fmaxf(pair_mx, mx);
                 if (p.slices == 8 && lane < 32 && tok < p.rows)
-                    p.tmax[(size_t)(8 * tm + (G::WTM / 32) * wm + i) * p.Cpad + tok] = mx;
+                    p.tmax[(size_t)(8 * ts + (G::WTM / 32) * wm + i) * p.Cpad + tok] = mx;
+                if (p.slices == 4 && (i & 1) && lane < 32 && tok < p.rows)
+                    p.tmax[(size_t)(4 * ts + (G::WTM / 64) * wm + (i >> 1)) * p.Cpad + tok] = pair_mx;
+                if (i & 1)
+                    pair_mx = -__builtin_inff();
             } else {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -1501,7 +1517,7 @@ __device__ __forceinline__ void topk_tile(const TopkParams &p, char *smem, int t
 #pragma unroll
                     for (int w2 = 1; w2 < G::WM; ++w2)
                         m = fmaxf(m, red[w2 * G::BN + nl]);
-                    p.tmax[(size_t)tm * p.Cpad + n0 + nl] = m;
+                    p.tmax[(size_t)ts * p.Cpad + n0 + nl] = m;
                 }
         }
     }
@@ -1511,7 +1527,9 @@ template <bool COLLECT>
 __global__ __launch_bounds__(LogitGemm::NT) void topk_logits_kernel(TopkParams p)
 {
     __shared__ __attribute__((aligned(16))) char smem[LogitGemm::LDS_BYTES];
-    for (int t = blockIdx.x; t < p.nVt * p.nNt; t += gridDim.x) {
+    if (p.guard && *p.guard == 0u)
+        return;
+    for (int t = blockIdx.x; t < p.nTm * p.nNt; t += gridDim.x) {
         topk_tile<COLLECT>(p, smem, t);
         __syncthreads();
     }
@@ -1554,14 +1572,20 @@ __device__ __forceinline__ void heap_sift_down(float *hp, int j, int n)
     hp[j * 64] = v;
 }
 
-// One lane per token: tau = the K-th largest of the token's nSub sub-tile maxima (-inf
+// One lane per token: tau = the K-th largest of the token's nSub slice maxima (-inf
 // when there are fewer than K) as the root of a K-entry min-heap, and the token's
 // candidate count reset.  Consecutive lanes read consecutive tokens of each maxima row.
+// With `guard`, runs only when *guard != 0; `retry_reset` (may be NULL) is cleared.
 __global__ __launch_bounds__(64) void topk_threshold_kernel(const float *tmax, int nSub, int Cpad, int rows, int K,
-                                                          float *thr, uint32_t *count)
+                                                          float *thr, uint32_t *count, const uint32_t *guard,
+                                                          uint32_t *retry_reset)
 {
     __shared__ float heap[kMaxK * 64];
+    if (guard && *guard == 0u)
+        return;
     const int lane = threadIdx.x, tok = blockIdx.x * 64 + lane;
+    if (retry_reset && tok == 0)
+        *retry_reset = 0u;
     if (tok >= rows)
         return;
     count[tok] = 0u;
@@ -1598,19 +1622,22 @@ __global__ __launch_bounds__(64) void topk_threshold_kernel(const float *tmax, i
     thr[tok] = hp[0];
 }
 
-// One wave per token: sort the candidates and write the first K (index, z).  More
-// candidates than kTopkCap (many logits tied at the threshold), or fewer than K,
-// raise the error flag.
+// One wave per token: sort the candidates and write the first K (index, z).  Fewer
+// candidates than K raise the error flag; more than kTopkCap raise `retry` when it is
+// given (a first pass over part of the vocabulary: the chunk is redone), else the error
+// flag (many logits tied at the threshold).  With `guard`, runs only when *guard != 0.
 __global__ __launch_bounds__(64) void topk_select_kernel(const uint64_t *cand, const uint32_t *count, int K,
                                                          int32_t *idx_out, void *logit_out, int logit_f32,
-                                                         uint32_t *err)
+                                                         uint32_t *err, const uint32_t *guard, uint32_t *retry)
 {
     __shared__ uint64_t s[kTopkCap];
+    if (guard && *guard == 0u)
+        return;
     const int tok = blockIdx.x, lane = threadIdx.x;
     const uint32_t n = count[tok];
     if (n > (uint32_t)kTopkCap || n < (uint32_t)K) {
         if (lane == 0)
-            *err = 1u;
+            *((retry && n >= (uint32_t)K) ? retry : err) = 1u;
         return;
     }
     int P = 1;
@@ -2120,7 +2147,7 @@ int launch_full_grad(const ChunkArgs &a, const FullLayout &F, const GradScale &g
     return (int)hipGetLastError();
 }
 
-static TopkParams topk_params(const ChunkArgs &a, const TopkLayout &T)
+static TopkParams topk_params(const ChunkArgs &a, const TopkLayout &T, const uint32_t *guard)
 {
     TopkParams p;
     p.W = a.W;
@@ -2131,7 +2158,10 @@ static TopkParams topk_params(const ChunkArgs &a, const TopkLayout &T)
     p.Cpad = T.Cpad;
     p.nVt = T.nVt;
     p.nNt = (a.rows + LogitGemm::BN - 1) / LogitGemm::BN;
-    p.slices = T.nSub / T.nVt;
+    p.stride = 1;
+    p.nTm = T.nVt;
+    p.slices = 1;
+    p.guard = guard;
     p.tmax = reinterpret_cast<float *>(a.ws + T.off_tmax);
     p.thr = reinterpret_cast<const float *>(a.ws + T.off_thr);
     p.count = reinterpret_cast<uint32_t *>(a.ws + T.off_count);
@@ -2139,37 +2169,46 @@ static TopkParams topk_params(const ChunkArgs &a, const TopkLayout &T)
     return p;
 }
 
-int launch_topk_max(const ChunkArgs &a, const TopkLayout &T, void *stream)
+int launch_topk_max(const ChunkArgs &a, const TopkLayout &T, bool partial, const uint32_t *guard, void *stream)
 {
-    const TopkParams p = topk_params(a, T);
-    hipLaunchKernelGGL(topk_logits_kernel<false>, dim3(persistent_grid(p.nVt * p.nNt)), dim3(LogitGemm::NT), 0,
+    TopkParams p = topk_params(a, T, guard);
+    if (partial) {
+        p.stride = kTopkStride;
+        p.nTm = (T.nVt + kTopkStride - 1) / kTopkStride;
+        p.slices = kVocabTile / 64;
+    } else {
+        p.slices = T.nSubFull / T.nVt;
+    }
+    hipLaunchKernelGGL(topk_logits_kernel<false>, dim3(persistent_grid(p.nTm * p.nNt)), dim3(LogitGemm::NT), 0,
                        S(stream), p);
     return (int)hipGetLastError();
 }
 
-int launch_topk_threshold(const ChunkArgs &a, const TopkLayout &T, void *stream)
+int launch_topk_threshold(const ChunkArgs &a, const TopkLayout &T, bool partial, const uint32_t *guard,
+                          uint32_t *retry_reset, void *stream)
 {
     hipLaunchKernelGGL(topk_threshold_kernel, dim3((a.rows + 63) / 64), dim3(64), 0, S(stream),
-                       reinterpret_cast<const float *>(a.ws + T.off_tmax), T.nSub, T.Cpad, a.rows, a.K,
-                       reinterpret_cast<float *>(a.ws + T.off_thr), reinterpret_cast<uint32_t *>(a.ws + T.off_count));
+                       reinterpret_cast<const float *>(a.ws + T.off_tmax), partial ? T.nSubPart : T.nSubFull, T.Cpad,
+                       a.rows, a.K, reinterpret_cast<float *>(a.ws + T.off_thr),
+                       reinterpret_cast<uint32_t *>(a.ws + T.off_count), guard, retry_reset);
     return (int)hipGetLastError();
 }
 
-int launch_topk_collect(const ChunkArgs &a, const TopkLayout &T, void *stream)
+int launch_topk_collect(const ChunkArgs &a, const TopkLayout &T, const uint32_t *guard, void *stream)
 {
-    const TopkParams p = topk_params(a, T);
-    hipLaunchKernelGGL(topk_logits_kernel<true>, dim3(persistent_grid(p.nVt * p.nNt)), dim3(LogitGemm::NT), 0,
+    const TopkParams p = topk_params(a, T, guard);
+    hipLaunchKernelGGL(topk_logits_kernel<true>, dim3(persistent_grid(p.nTm * p.nNt)), dim3(LogitGemm::NT), 0,
                        S(stream), p);
     return (int)hipGetLastError();
 }
 
 int launch_topk_select(const ChunkArgs &a, const TopkLayout &T, int32_t *topk_idx, void *topk_logit, bool logit_f32,
-                       void *stream)
+                       const uint32_t *guard, uint32_t *retry, void *stream)
 {
     hipLaunchKernelGGL(topk_select_kernel, dim3(a.rows), dim3(64), 0, S(stream),
                        reinterpret_cast<const uint64_t *>(a.ws + T.off_cand),
                        reinterpret_cast<const uint32_t *>(a.ws + T.off_count), a.K, topk_idx, topk_logit,
-                       logit_f32 ? 1 : 0, reinterpret_cast<uint32_t *>(a.ws + T.off_err));
+                       logit_f32 ? 1 : 0, reinterpret_cast<uint32_t *>(a.ws + T.off_err), guard, retry);
     return (int)hipGetLastError();
 }
 

@@ -28,7 +28,7 @@ fckl_status check_desc(const fckl_desc *d)
         return FCKL_ERR_INVALID_ARG;
     if (d->logit_dtype != FCKL_DTYPE_BF16 && d->logit_dtype != FCKL_DTYPE_F32)
         return FCKL_ERR_INVALID_ARG;
-    if (d->flags & ~(uint32_t)(FCKL_FLAG_VALIDATE | FCKL_FLAG_DW_ACCUMULATE))
+    if (d->flags & ~(uint32_t)(FCKL_FLAG_VALIDATE | FCKL_FLAG_DW_ACCUMULATE | FCKL_FLAG_TOPK_FULL_FIRST_PASS))
         return FCKL_ERR_INVALID_ARG;
     if (d->H % 8 != 0)
         return FCKL_ERR_UNSUPPORTED;
@@ -120,11 +120,15 @@ fckl_status make_topk_layout(const fckl_desc *d, int32_t chunk, TopkLayout *L)
     o.C = chunk;
     o.Cpad = (int32_t)align_up((size_t)chunk, kTokenTile);
     o.nVt = (d->V + kVocabTile - 1) / kVocabTile;
-    // maxima per token: one per tile when there are at least K tiles, else one per
-    // 32-row slice (8 per tile)
-    o.nSub = o.nVt >= d->K ? o.nVt : o.nVt * (kVocabTile / 32);
-    if (o.nSub > kTopkMaxSub)
+    // maxima per token of a first pass over every tile: one per tile when there are at
+    // least K tiles, else one per 32-row slice (8 per tile)
+    o.nSubFull = o.nVt >= d->K ? o.nVt : o.nVt * (kVocabTile / 32);
+    if (o.nSubFull > kTopkMaxSub)
         return FCKL_ERR_UNSUPPORTED;
+    // a first pass over every kTopkStride-th tile (one maximum per 64-row slice) when it
+    // still gives at least 4 K maxima, unless the caller asks for the full first pass
+    const int32_t part = (o.nVt + kTopkStride - 1) / kTopkStride * (kVocabTile / 64);
+    o.nSubPart = (part >= 4 * d->K && !(d->flags & FCKL_FLAG_TOPK_FULL_FIRST_PASS)) ? part : 0;
     const size_t Cp = (size_t)o.Cpad;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -132,7 +136,7 @@ fckl_status make_topk_layout(const fckl_desc *d, int32_t chunk, TopkLayout *L)
         off = align_up(off + bytes, 256);
         return at;
     };
-    o.off_tmax = take((size_t)o.nSub * Cp * 4);
+    o.off_tmax = take((size_t)std::max(o.nSubFull, o.nSubPart) * Cp * 4);
     o.off_thr = take(Cp * 4);
     o.off_count = take(Cp * 4);
     o.off_cand = take(Cp * (size_t)kTopkCap * 8);

@@ -70,7 +70,8 @@ enum { FCKL_DTYPE_BF16 = 0, FCKL_DTYPE_F32 = 1 };
 /* Flags (bitwise or). */
 enum {
     FCKL_FLAG_VALIDATE = 1u,       /* check indices on the GPU and report FCKL_ERR_INDEX (syncs the stream) */
-    FCKL_FLAG_DW_ACCUMULATE = 2u   /* backward adds into dW instead of overwriting it */
+    FCKL_FLAG_DW_ACCUMULATE = 2u,  /* backward adds into dW instead of overwriting it */
+    FCKL_FLAG_TOPK_FULL_FIRST_PASS = 4u /* fckl_topk: first pass over the whole vocabulary (see there) */
 };
 
 /* Kernels of the path, for fckl_profile.kernel_mask (bit 1u << id). */
@@ -230,10 +231,16 @@ fckl_status fckl_forward_backward(const fckl_desc *desc, const void *h, const vo
  * z[i,v] = sum_j h[i,j] W[v,j] with the largest z, in descending order of z; equal
  * values are ordered by the smaller index first.  z is accumulated in fp32 from bf16
  * inputs (the same GEMM tiles as the loss).  Two passes of the product: the maxima of z
- * over 32-row slices of the vocabulary give a threshold at or below the K-th largest z,
- * and the logits at or above it are sorted.
+ * over K or more disjoint row slices of the vocabulary give a threshold at or below the
+ * K-th largest z, and the logits at or above it are sorted.  The first pass covers
+ * every 4th 256-row tile (64-row slices) when that gives at least 4 K maxima, so it
+ * costs a quarter of the product; a chunk in which some token then has more than 2048
+ * candidates is redone on the GPU with a first pass over every tile (no host round
+ * trip).  FCKL_FLAG_TOPK_FULL_FIRST_PASS always takes the first pass over every tile.
+ * The result does not depend on which first pass ran.
  *   desc       N, H, V, K (K <= 128), chunk (0 = up to 8192 tokens); logit_dtype selects
- *              the type of topk_logit; T, flags and profile are not used (T must be valid)
+ *              the type of topk_logit; flags: FCKL_FLAG_TOPK_FULL_FIRST_PASS or 0; T and
+ *              profile are not used (T must be valid)
  *   h          device, bf16 [N,H]      the teacher's final hidden states
  *   W          device, bf16 [V,H]      the teacher's LM head
  *   topk_idx   device, int32 [N,K]     out: indices, descending z

@@ -147,3 +147,64 @@ def test_topk_at_the_32k_shape_against_torch():
     assert same >= 0.97
     few = rows[:16]
     check_topk(x.h[few], x.W, wl.K, gi.cpu().numpy()[few], gz.cpu().numpy()[few].astype(np.float64), "32K shape")
+
+
+PARTIAL_CASES = [
+    # seed, N, H, V, K: shapes where the first pass covers every 4th tile
+    (76, 300, 128, 20000, 10),
+    (77, 257, 64, 120000, 100),
+]
+
+
+@pytest.mark.parametrize("case", PARTIAL_CASES, ids=["K10-V20000", "K100-V120000"])
+def test_partial_first_pass_matches_full_and_oracle(case):
+    """The first pass over a quarter of the vocabulary and the one over all of it give
+    the same result, the oracle's."""
+    seed, N, H, V, K = case
+    say("case: partial first pass", case)
+    rng = np.random.default_rng(seed)
+    h = synth.round_bf16(rng.standard_normal((N, H)).astype(np.float32))
+    W = synth.round_bf16((rng.standard_normal((V, H)) * (2.0 / np.sqrt(H))).astype(np.float32))
+    th, tW, _, _ = arrays(h, W, np.zeros((N, 1), np.int32), np.zeros((N, 1), np.float32))
+    gi, gz = fckl.topk(th, tW, K, logits_f32=True)
+    fi, fz = fckl.topk(th, tW, K, logits_f32=True, full_first_pass=True)
+    torch.cuda.synchronize()
+    assert torch.equal(gi, fi) and torch.equal(gz, fz)
+    check_topk(h, W, K, gi.cpu().numpy(), gz.cpu().numpy().astype(np.float64), "partial%d" % seed)
+
+
+def test_partial_first_pass_falls_back_when_candidates_overflow():
+    """2400 large logits per token, all in tiles the partial first pass skips: its
+    threshold comes from ordinary logits and leaves more than 2048 candidates, so every
+    chunk is redone with a first pass over every tile -- with the oracle's result."""
+    N, H, V, K = 64, 64, 150000, 100
+    rng = np.random.default_rng(78)
+    h = rng.standard_normal((N, H)).astype(np.float32)
+    h[:, 0] = 3.0
+    W = (rng.standard_normal((V, H)) * 0.02).astype(np.float32)
+    W[:, 0] = 0.0
+    tiles = np.arange((V + 255) // 256)
+    skipped = np.concatenate([np.arange(t * 256, min(V, t * 256 + 256)) for t in tiles if t % 4 != 0])
+    high = rng.choice(skipped, size=2400, replace=False)
+    W[high, 0] = (5.0 + 0.5 * rng.standard_normal(high.size)) / 3.0
+    h, W = synth.round_bf16(h), synth.round_bf16(W)
+    # the precondition, in fp64: the partial first pass overflows, the full one does not
+    z = h.astype(np.float64) @ W.astype(np.float64).T
+    visited = np.concatenate([np.arange(t * 256, min(V, t * 256 + 256)) for t in tiles if t % 4 == 0])
+    zs = z[:, visited]
+    pad = (-zs.shape[1]) % 64
+    zs = np.concatenate([zs, np.full((N, pad), -np.inf)], axis=1)
+    tau_part = -np.sort(-zs.reshape(N, -1, 64).max(axis=2), axis=1)[:, K - 1]
+    n_part = (z >= tau_part[:, None]).sum(axis=1)
+    zt = np.concatenate([z, np.full((N, (-V) % 256), -np.inf)], axis=1)
+    tau_full = -np.sort(-zt.reshape(N, -1, 256).max(axis=2), axis=1)[:, K - 1]
+    n_full = (z >= tau_full[:, None]).sum(axis=1)
+    say("candidates per token: partial first pass %d..%d, full first pass %d..%d"
+        % (n_part.min(), n_part.max(), n_full.min(), n_full.max()))
+    assert n_part.min() > 2048 + 100 and n_full.max() < 2048 - 100
+    th, tW, _, _ = arrays(h, W, np.zeros((N, 1), np.int32), np.zeros((N, 1), np.float32))
+    gi, gz = fckl.topk(th, tW, K, logits_f32=True)
+    fi, fz = fckl.topk(th, tW, K, logits_f32=True, full_first_pass=True)
+    torch.cuda.synchronize()
+    assert torch.equal(gi, fi) and torch.equal(gz, fz)
+    check_topk(h, W, K, gi.cpu().numpy(), gz.cpu().numpy().astype(np.float64), "fallback")
