@@ -22,6 +22,7 @@ constexpr int kMaxK = 128;
 // (V <= 2^21; their buffer is 4 bytes per maximum and token of a chunk).
 constexpr int kTopkCap = 2048;
 constexpr int kTopkStride = 4;      // the partial first pass visits every 4th vocabulary tile
+constexpr int kTopkSortSub = 2048;  // slice maxima per token up to which the threshold is found by a sort
 constexpr int kTopkMaxSub = 65536;
 constexpr int32_t kMaxChunk = 8192;
 constexpr size_t kDefaultBudget = size_t(12) << 30;  // 12 GiB of the 288 GB HBM3E

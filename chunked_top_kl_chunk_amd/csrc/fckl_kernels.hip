@@ -613,7 +613,6 @@ __device__ __forceinline__ void store_vocab_major(const char *smem, uint16_t *ds
     constexpr int kBlocks = (256 / 16) * kTokBlocks;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int grp = lane >> 4, gl = lane & 15;
-#pragma unroll 2
     for (int b = wave; b < kBlocks; b += NWAVES) {
         const int vb = (b / kTokBlocks) * 16, tb = (b % kTokBlocks) * 32 + grp * 8;
         const char *src = smem + (tb + (gl >> 2)) * kGStagePitch + (vb + 4 * (gl & 3)) * 2;
@@ -1622,6 +1621,39 @@ __global__ __launch_bounds__(64) void topk_threshold_kernel(const float *tmax, i
     thr[tok] = hp[0];
 }
 
+// One wave per token: tau = the K-th largest of the token's nSub slice maxima by an
+// ascending bitonic sort of them in LDS (nSub <= kTopkSortSub), and the token's
+// candidate count reset; with many tokens this keeps every compute unit busy where the
+// heap kernel above has one lane per token.  `guard` and `retry_reset` as there.
+__global__ __launch_bounds__(64) void topk_threshold_sort_kernel(const float *tmax, int nSub, int Cpad, int K,
+                                                               float *thr, uint32_t *count, const uint32_t *guard,
+                                                               uint32_t *retry_reset)
+{
+    __shared__ float s[kTopkSortSub];
+    if (guard && *guard == 0u)
+        return;
+    const int tok = blockIdx.x, lane = threadIdx.x;
+    if (lane == 0) {
+        count[tok] = 0u;
+        if (retry_reset && tok == 0)
+            *retry_reset = 0u;
+    }
+    if (K > nSub) {
+        if (lane == 0)
+            thr[tok] = -__builtin_inff();
+        return;
+    }
+    int P = 64;
+    while (P < nSub)
+        P <<= 1;
+    for (int i = lane; i < P; i += 64)
+        s[i] = i < nSub ? tmax[(size_t)i * Cpad + tok] : -__builtin_inff();
+    __syncthreads();
+    wave_bitonic_sort(s, P);
+    if (lane == 0)
+        thr[tok] = s[P - K];
+}
+
 // One wave per token: sort the candidates and write the first K (index, z).  Fewer
 // candidates than K raise the error flag; more than kTopkCap raise `retry` when it is
 // given (a first pass over part of the vocabulary: the chunk is redone), else the error
@@ -2187,10 +2219,16 @@ int launch_topk_max(const ChunkArgs &a, const TopkLayout &T, bool partial, const
 int launch_topk_threshold(const ChunkArgs &a, const TopkLayout &T, bool partial, const uint32_t *guard,
                           uint32_t *retry_reset, void *stream)
 {
-    hipLaunchKernelGGL(topk_threshold_kernel, dim3((a.rows + 63) / 64), dim3(64), 0, S(stream),
-                       reinterpret_cast<const float *>(a.ws + T.off_tmax), partial ? T.nSubPart : T.nSubFull, T.Cpad,
-                       a.rows, a.K, reinterpret_cast<float *>(a.ws + T.off_thr),
-                       reinterpret_cast<uint32_t *>(a.ws + T.off_count), guard, retry_reset);
+    const int nSub = partial ? T.nSubPart : T.nSubFull;
+    const float *tmax = reinterpret_cast<const float *>(a.ws + T.off_tmax);
+    float *thr = reinterpret_cast<float *>(a.ws + T.off_thr);
+    uint32_t *count = reinterpret_cast<uint32_t *>(a.ws + T.off_count);
+    if (nSub <= kTopkSortSub)
+        hipLaunchKernelGGL(topk_threshold_sort_kernel, dim3(a.rows), dim3(64), 0, S(stream), tmax, nSub, T.Cpad, a.K,
+                           thr, count, guard, retry_reset);
+    else
+        hipLaunchKernelGGL(topk_threshold_kernel, dim3((a.rows + 63) / 64), dim3(64), 0, S(stream), tmax, nSub,
+                           T.Cpad, a.rows, a.K, thr, count, guard, retry_reset);
     return (int)hipGetLastError();
 }
 
