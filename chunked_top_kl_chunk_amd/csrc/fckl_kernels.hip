@@ -84,8 +84,12 @@ __device__ __forceinline__ float wave_sum(float v)
 __device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2)
 {
     float M = fmaxf(m, m2);
-    if (M == kNegInf)
+    if (M == kNegInf) {
+        // both empty (sums 0), or values that were all NaN (fmaxf skipped them, their
+        // sum is NaN): keep the NaN so that it reaches the lse
+        s += s2;
         return;
+    }
     s = s * fast_exp2(m - M) + s2 * fast_exp2(m2 - M);
     m = M;
 }

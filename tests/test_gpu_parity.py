@@ -145,3 +145,32 @@ def test_dw_accumulate_and_validate():
                 else:
                     fckl.backward(dh, dW_, bad, dt, lse, T=1.0, validate=True)
             assert e.value.status == fckl.ERR_INDEX
+
+
+def test_nan_in_one_row_stays_in_that_token():
+    """No scrubbing: a NaN in one hidden row gives that token a NaN loss, lse and dH row
+    and makes the mean and dW NaN; every other token's loss, lse and dH row equal the
+    clean run's bit for bit (each column of the logit tiles is its own token)."""
+    N, H, V, K, T = 300, 128, 1500, 8, 1.0
+    h, W, idx, tl = synthetic(95, N, H, V, K, T)
+    clean = arrays(h, W, idx, tl)
+    hn = h.copy()
+    hn[137, 5] = np.nan
+    dirty = arrays(hn, W, idx, tl)
+    outs = []
+    for t in (clean, dirty):
+        loss, lse, mean = fckl.forward(*t, T=T, chunk=256)
+        dH, dW = fckl.backward(*t, lse, T=T, chunk=256)
+        single = fckl.forward_backward(*t, T=T, chunk=256)
+        outs.append((loss, lse, mean, dH, dW) + tuple(single))
+    torch.cuda.synchronize()
+    c, d = [[x.cpu().numpy() for x in o] for o in outs]
+    keep = np.arange(N) != 137
+    for base in (0, 5):     # the two passes, then the single call
+        loss_c, lse_c, mean_c, dH_c, dW_c = c[base:base + 5]
+        loss_d, lse_d, mean_d, dH_d, dW_d = d[base:base + 5]
+        assert np.isnan(loss_d[137]) and np.isnan(lse_d[137]) and np.isnan(dH_d[137]).all()
+        assert np.isnan(mean_d[0]) and np.isnan(dW_d).all()
+        assert np.array_equal(loss_d[keep], loss_c[keep]) and np.array_equal(lse_d[keep], lse_c[keep])
+        assert np.array_equal(dH_d[keep], dH_c[keep])
+        assert np.isfinite(mean_c[0]) and np.isfinite(dW_c).all()
