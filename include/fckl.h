@@ -246,9 +246,11 @@ fckl_status fckl_forward_backward(const fckl_desc *desc, const void *h, const vo
  *   topk_idx   device, int32 [N,K]     out: indices, descending z
  *   topk_logit device, bf16 or f32 [N,K] out: z at those indices (bf16: rounded to nearest even)
  *   ws         device, fckl_topk_workspace_size bytes, 256-byte aligned
- * Returns FCKL_ERR_UNSUPPORTED when V > 2097152, or when more than 2048 logits of one
- * token lie at or above its threshold (massive ties, e.g. a zero head); the outputs are
- * then undefined.  Checking that needs one host synchronisation at the end of the call.
+ * Returns FCKL_ERR_UNSUPPORTED when V > 2097152, when more than 2048 logits of one
+ * token lie at or above its threshold even after a first pass over every tile (massive
+ * ties, e.g. a zero head), or when a token has fewer than K comparable logits (a NaN
+ * in its hidden row makes them all NaN); the outputs are then undefined.  Checking that
+ * needs one host synchronisation at the end of the call.
  */
 fckl_status fckl_topk_workspace_size(const fckl_desc *desc, int32_t chunk, size_t *ws_bytes_out);
 fckl_status fckl_topk(const fckl_desc *desc, const void *h, const void *W, int32_t *topk_idx,
