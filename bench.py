@@ -17,6 +17,8 @@ chunk's logits once (6 N V H flop); it is reported beside the main line, which t
 the two passes of the method as defined (8 N V H flop).  `teacher_topk` times the
 teacher-side extraction of the top-K cache from the same hidden states (fckl_topk), and
 the same call with its first pass over the whole vocabulary.
+`autograd_module` times FusedChunkedKLLoss as a training loop calls it (forward, then
+loss.backward()), with the two passes and with single_call=True.
 `full_teacher` times the online variant against the teacher's whole distribution
 (fckl_full_forward_backward), with a teacher of the same shape (a seeded perturbed copy
 of the student's hidden states and head, synth.full_teacher): 2 N V Ht + 6 N V H flop
@@ -86,6 +88,8 @@ def main():
                     help="skip timing fckl_forward_backward (the single-call path) after the main measurement")
     ap.add_argument("--no-topk", action="store_true",
                     help="skip timing the teacher-side top-K extraction (fckl_topk) of the same hidden states")
+    ap.add_argument("--no-module", action="store_true",
+                    help="skip the torch autograd module leg (FusedChunkedKLLoss, both modes)")
     ap.add_argument("--no-full", action="store_true",
                     help="skip the full-vocabulary teacher variant (fckl_full_forward_backward)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -219,6 +223,35 @@ def main():
             "kernels": {k: {"launches": v["launches"], "ms_per_step": round(v["ms"] / args.steps, 4)}
                         for k, v in k1.items()},
         }
+
+    if not args.no_module:
+        # The torch autograd module, as a training loop calls it (loss = module(...);
+        # loss.backward(), gradients cast to the bf16 leaves by autograd): the two passes,
+        # and single_call=True (gradients formed in the forward call, scaled in backward).
+        from chunked_top_kl_chunk_amd.loss import FusedChunkedKLLoss
+        hl = h.detach().clone().requires_grad_(True)
+        Wl = W.detach().clone().requires_grad_(True)
+        mod_ms = {}
+        for single in (False, True):
+            mod = FusedChunkedKLLoss(temperature=T, chunk=chunk, single_call=single)
+
+            def module_step():
+                hl.grad = None
+                Wl.grad = None
+                mod(hl, Wl, idx, tl).backward()
+            module_step()
+            torch.cuda.synchronize()
+            reps = max(1, min(args.steps, 3))
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                module_step()
+            torch.cuda.synchronize()
+            mod_ms[single] = (time.perf_counter() - t0) * 1e3 / reps
+        log("autograd module: %.2f ms per step, single_call %.2f ms" % (mod_ms[False], mod_ms[True]))
+        out["autograd_module"] = {"ms_per_step": round(mod_ms[False], 3), "tokens_per_s": round(N * 1e3 / mod_ms[False], 1),
+                                  "single_call_ms_per_step": round(mod_ms[True], 3),
+                                  "single_call_tokens_per_s": round(N * 1e3 / mod_ms[True], 1)}
+        del hl, Wl
 
     if not args.no_topk:
         # Teacher-side extraction of the cache the loss reads: top-K of h W^T in two

@@ -35,7 +35,7 @@ FLAG_VALIDATE, FLAG_DW_ACCUMULATE, FLAG_TOPK_FULL_FIRST_PASS = 1, 2, 4
 # Every symbol include/fckl.h declares.
 EXPORTS = ("fckl_plan", "fckl_workspace_size", "fckl_forward", "fckl_backward", "fckl_forward_ex",
            "fckl_backward_ex", "fckl_forward_backward", "fckl_topk_workspace_size", "fckl_topk",
-           "fckl_full_plan", "fckl_full_forward_backward", "fckl_status_string", "fckl_version")
+           "fckl_full_plan", "fckl_full_forward_backward", "fckl_scale", "fckl_status_string", "fckl_version")
 
 
 KERNELS = ("prepare", "fwd_logits", "combine", "mean", "bwd_logits", "dh", "dh_reduce", "dw", "transpose",
@@ -92,9 +92,10 @@ def load() -> ctypes.CDLL:
     lib.fckl_full_plan.argtypes = [P(Desc), ctypes.c_int32, sz, P(ctypes.c_int32), P(sz)]
     lib.fckl_full_forward_backward.argtypes = [P(Desc), ctypes.c_int32, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp,
                                                vp, vp, vp, vp, sz, vp]
+    lib.fckl_scale.argtypes = [vp, ctypes.c_int64, vp, vp]
     for f in ("fckl_plan", "fckl_workspace_size", "fckl_forward", "fckl_backward", "fckl_forward_ex",
               "fckl_backward_ex", "fckl_forward_backward", "fckl_topk_workspace_size", "fckl_topk",
-              "fckl_full_plan", "fckl_full_forward_backward"):
+              "fckl_full_plan", "fckl_full_forward_backward", "fckl_scale"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -374,5 +375,18 @@ def full_forward_backward(h, W, h_t, W_t, T: float = 1.0, grad_scale: float = 1.
     return loss_tok, lse, loss_mean, dH, dW
 
 
+def scale_(x, scale, stream=None):
+    """x *= scale[0] in place on the device (fckl_scale); x contiguous float32, scale a
+    float32 device tensor of one element.  Returns x."""
+    import torch
+    for name, t in (("x", x), ("scale", scale)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous() or t.dtype != torch.float32:
+            raise ValueError("%s must be a contiguous float32 device tensor" % name)
+    if scale.numel() != 1 or scale.device != x.device:
+        raise ValueError("scale must hold one element on the device of x")
+    _call("fckl_scale", x.data_ptr(), ctypes.c_int64(x.numel()), scale.data_ptr(), _stream_handle(stream))
+    return x
+
+
 __all__ = ["Desc", "Profile", "KERNELS", "FCKLError", "load", "plan", "workspace_size", "forward", "backward",
-           "forward_backward", "topk", "topk_workspace_size", "full_plan", "full_forward_backward", "make_desc", "desc_for", "status_string", "version", "EXPORTS", "LIB_PATH"]
+           "forward_backward", "topk", "topk_workspace_size", "full_plan", "full_forward_backward", "scale_", "make_desc", "desc_for", "status_string", "version", "EXPORTS", "LIB_PATH"]

@@ -529,6 +529,15 @@ fckl_status fckl_topk(const fckl_desc *desc, const void *h, const void *W, int32
     return host ? FCKL_ERR_UNSUPPORTED : FCKL_OK;
 }
 
+fckl_status fckl_scale(float *x, int64_t n, const float *scale, void *stream)
+{
+    if (!x || !scale || n < 0 || (reinterpret_cast<uintptr_t>(x) & 15u) != 0)
+        return FCKL_ERR_INVALID_ARG;
+    if (n == 0)
+        return FCKL_OK;
+    return launch_scale(x, n, scale, stream) ? FCKL_ERR_HIP : FCKL_OK;
+}
+
 const char *fckl_status_string(fckl_status s)
 {
     switch (s) {

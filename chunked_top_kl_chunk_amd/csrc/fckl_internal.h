@@ -134,6 +134,7 @@ int launch_dw(const ChunkArgs &a, float *dW, bool accumulate, void *stream);
 int launch_transpose_head(const ChunkArgs &a, void *stream);
 int launch_transpose_chunk(const ChunkArgs &a, void *stream);
 int launch_zero_flag(uint32_t *flag, void *stream);
+int launch_scale(float *x, int64_t n, const float *scale, void *stream);
 
 // Teacher top-K extraction of one chunk (a.L is unused; T is the top-K layout): the
 // 32-row sub-tile maxima of z, the per-token threshold, the candidates at or above it,

@@ -31,6 +31,8 @@
 // The two logit kernels are persistent (one work-group per compute unit looping over
 // tiles), which removes the per-work-group dispatch gap between tiles.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 #include <type_traits>
@@ -1825,6 +1827,24 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t *src, int
     }
 }
 
+// x[i] *= *scale, four floats per thread (x 16-byte aligned), a grid-stride loop.
+__global__ __launch_bounds__(256) void scale_kernel(float *x, int64_t n, const float *scale)
+{
+    const float c = *scale;
+    const int64_t n4 = n / 4;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+        float4 v = reinterpret_cast<float4 *>(x)[i];
+        v.x *= c;
+        v.y *= c;
+        v.z *= c;
+        v.w *= c;
+        reinterpret_cast<float4 *>(x)[i] = v;
+    }
+    if (blockIdx.x == 0 && threadIdx.x < (unsigned)(n - 4 * n4))
+        x[4 * n4 + threadIdx.x] *= c;
+}
+
 __global__ void zero_u32_kernel(uint32_t *p, int n)
 {
     if ((int)threadIdx.x < n)
@@ -2088,6 +2108,14 @@ int launch_transpose_chunk(const ChunkArgs &a, void *stream)
     dim3 grid((L.Cpad + 63) / 64, (a.H + 63) / 64);
     hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, S(stream), a.h, (int64_t)a.H, a.rows, a.H, hT,
                        (int64_t)L.Cpad, L.Cpad);
+    return (int)hipGetLastError();
+}
+
+int launch_scale(float *x, int64_t n, const float *scale, void *stream)
+{
+    const int64_t n4 = n / 4;
+    const int64_t blocks = std::min<int64_t>(std::max<int64_t>((n4 + 255) / 256, 1), 8192);
+    hipLaunchKernelGGL(scale_kernel, dim3((unsigned)blocks), dim3(256), 0, S(stream), x, n, scale);
     return (int)hipGetLastError();
 }
 

@@ -15,6 +15,12 @@ The library computes dH and dW in float32; autograd hands them to h and W in tho
 tensors' dtype (bf16), as it does for any gradient.  A caller that keeps an fp32
 master copy of W can call ``chunked_top_kl_chunk_amd.backward`` with
 ``accumulate=True`` on that buffer instead.
+
+With ``single_call=True`` the forward pass runs ``fckl_forward_backward`` (each chunk's
+logits formed once, 6 N V H flop instead of 8) with an upstream gradient of 1 and keeps
+dH and dW (float32, N H + V H values) until the backward pass, which scales them in
+place by the upstream gradient with ``fckl_scale`` on the device.  The gradients are
+those of the two-pass path up to the bf16 rounding of the kept exponentials.
 """
 from __future__ import annotations
 
@@ -24,6 +30,8 @@ import torch
 
 from . import backward as _backward
 from . import forward as _forward
+from . import forward_backward as _forward_backward
+from . import scale_ as _scale_
 
 
 class FusedChunkedKLFunction(torch.autograd.Function):
@@ -49,6 +57,29 @@ class FusedChunkedKLFunction(torch.autograd.Function):
                 None, None, None, None, None)
 
 
+class FusedChunkedKLSingleCallFunction(torch.autograd.Function):
+    """The same loss with both passes in the forward call; backward only scales."""
+
+    @staticmethod
+    def forward(ctx, h, W, topk_idx, topk_logit, weights, T: float, chunk: int):
+        _, _, mean, dH, dW = _forward_backward(h.detach(), W.detach(), topk_idx, topk_logit, T=T, grad_scale=1.0,
+                                               weights=weights, chunk=chunk)
+        ctx.dH, ctx.dW = dH, dW
+        return mean.reshape(())
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        dH, dW = ctx.dH, ctx.dW
+        ctx.dH = ctx.dW = None
+        g = grad_out.detach().to(torch.float32).reshape(1).contiguous()
+        if ctx.needs_input_grad[0]:
+            _scale_(dH, g)
+        if ctx.needs_input_grad[1]:
+            _scale_(dW, g)
+        return (dH if ctx.needs_input_grad[0] else None, dW if ctx.needs_input_grad[1] else None,
+                None, None, None, None, None)
+
+
 class FusedChunkedKLLoss(torch.nn.Module):
     """Fused chunked KL distillation loss against a cached top-K teacher.
 
@@ -59,19 +90,24 @@ class FusedChunkedKLLoss(torch.nn.Module):
         ignore_index: topk_idx rows whose first entry equals this value are masked
             (their other entries are then not read as indices; they must still be in
             [0, V) or be replaced by the caller).  None = no such convention.
+        single_call: form the gradients in the forward call (fckl_forward_backward)
+            and only scale them in the backward call; for a loss whose backward
+            follows its forward once (the usual training step).
 
     forward(hidden [.., H] bf16, lm_head_weight [V, H] bf16, topk_idx [.., K] int32,
             topk_logit [.., K] bf16/f32, mask [..] bool (True = keep) or None,
             weights [..] float or None) -> scalar loss (float32).
     """
 
-    def __init__(self, temperature: float = 1.0, chunk: int = 0, ignore_index: Optional[int] = None):
+    def __init__(self, temperature: float = 1.0, chunk: int = 0, ignore_index: Optional[int] = None,
+                 single_call: bool = False):
         super().__init__()
         if not temperature > 0:
             raise ValueError("temperature must be > 0")
         self.temperature = float(temperature)
         self.chunk = int(chunk)
         self.ignore_index = ignore_index
+        self.single_call = bool(single_call)
 
     def forward(self, hidden, lm_head_weight, topk_idx, topk_logit, mask=None, weights=None):
         H = hidden.shape[-1]
@@ -92,9 +128,10 @@ class FusedChunkedKLLoss(torch.nn.Module):
                 w = keep.to(torch.float32) if w is None else w * keep.to(torch.float32)
                 # ignored rows get a valid placeholder index row; their weight is 0
                 idx = torch.where(keep[:, None], idx, torch.arange(K, device=idx.device, dtype=idx.dtype)[None, :])
-        return FusedChunkedKLFunction.apply(h.contiguous(), lm_head_weight.contiguous(), idx.contiguous(),
-                                            tl.contiguous(), None if w is None else w.contiguous(),
-                                            self.temperature, self.chunk)
+        wants_grad = torch.is_grad_enabled() and (hidden.requires_grad or lm_head_weight.requires_grad)
+        fn = FusedChunkedKLSingleCallFunction if self.single_call and wants_grad else FusedChunkedKLFunction
+        return fn.apply(h.contiguous(), lm_head_weight.contiguous(), idx.contiguous(), tl.contiguous(),
+                        None if w is None else w.contiguous(), self.temperature, self.chunk)
 
 
-__all__ = ["FusedChunkedKLFunction", "FusedChunkedKLLoss"]
+__all__ = ["FusedChunkedKLFunction", "FusedChunkedKLSingleCallFunction", "FusedChunkedKLLoss"]

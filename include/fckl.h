@@ -293,6 +293,20 @@ fckl_status fckl_full_forward_backward(const fckl_desc *desc, int32_t H_teacher,
                                        float *lse, float *loss_mean, float *dH, float *dW, void *ws,
                                        size_t ws_bytes, void *stream);
 
+/*
+ * x[i] *= *scale for i in [0, n): the chain rule for an upstream gradient that arrives
+ * after the gradients were formed.  The torch module ("Configuring Fused Chunked KL
+ * Loss", getaibook.com: the fused loss replaces the stock loss in the training loop)
+ * runs fckl_forward_backward in its forward pass with grad_scale = 1 and, in its
+ * backward pass, scales dH and dW by the upstream gradient where it already lives, on
+ * the device, without a host read-back.
+ *   x      device, f32 [n], in place (16-byte aligned)
+ *   n      >= 0
+ *   scale  device, f32 [1]
+ * Returns FCKL_ERR_INVALID_ARG for NULL pointers, n < 0 or a misaligned x.
+ */
+fckl_status fckl_scale(float *x, int64_t n, const float *scale, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *fckl_status_string(fckl_status status);
 

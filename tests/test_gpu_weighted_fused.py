@@ -168,3 +168,47 @@ def test_autograd_module_ignore_index():
     ref_dH, ref_dW = oracle.backward(h[keep], W, idx[keep], tl[keep], T)
     check_grad(hb.grad.float().cpu().numpy()[keep], ref_dH, "ignore_index dH")
     check_grad(Wb.grad.float().cpu().numpy(), ref_dW, "ignore_index dW")
+
+
+def test_scale_in_place():
+    dev = device()
+    for n in (1, 3, 1003, 1 << 20):
+        x = torch.randn(n, device=dev)
+        s = torch.tensor([-2.5], device=dev)
+        ref = x * -2.5
+        fckl.scale_(x, s)
+        torch.cuda.synchronize()
+        assert torch.equal(x, ref), n
+
+
+def test_autograd_module_single_call():
+    """FusedChunkedKLLoss(single_call=True): both passes in the forward call, the backward
+    only scales by the upstream gradient; loss equal to the two-pass module, gradients
+    within the bf16 rounding of the kept exponentials, both against the oracle."""
+    N, H, V, K, T = 2 * 300, 256, 3000, 16, 2.0
+    h, W, idx, tl = synthetic(51, N, H, V, K, T)
+    t = arrays(h, W, idx, tl)
+    keep = np.ones(N, dtype=bool)
+    keep[280:300] = False
+    mask = torch.from_numpy(keep).to(device()).reshape(2, 300)
+    grads = {}
+    for single in (False, True):
+        hb = t[0].clone().reshape(2, 300, H).requires_grad_(True)
+        Wb = t[1].clone().requires_grad_(True)
+        mod = FusedChunkedKLLoss(temperature=T, chunk=256, single_call=single)
+        loss = mod(hb, Wb, t[2].reshape(2, 300, K), t[3].reshape(2, 300, K), mask=mask)
+        (3.0 * loss).backward()
+        torch.cuda.synchronize()
+        grads[single] = (float(loss.detach()), hb.grad.float().reshape(N, H).cpu().numpy(),
+                         Wb.grad.float().cpu().numpy())
+    assert grads[True][0] == grads[False][0]
+    w = keep.astype(np.float64)
+    ref_dH, ref_dW = oracle.weighted_backward(h, W, idx, tl, T, w, grad_scale=3.0)
+    check_grad(grads[True][1], ref_dH, "single-call module dH")
+    check_grad(grads[True][2], ref_dW, "single-call module dW")
+    assert rel_max(grads[True][1], grads[False][1]) <= 2e-2 and rel_max(grads[True][2], grads[False][2]) <= 2e-2
+    # no gradient wanted: the module takes the forward-only path
+    with torch.no_grad():
+        l2 = FusedChunkedKLLoss(temperature=T, chunk=256, single_call=True)(
+            t[0].reshape(2, 300, H), t[1], t[2].reshape(2, 300, K), t[3].reshape(2, 300, K), mask=mask)
+    assert float(l2) == grads[True][0]

@@ -252,6 +252,16 @@ def test_module_validates_arguments_without_a_gpu():
         fckl.forward_backward(h, W, idx, tl)
 
 
+def test_scale_rejects_bad_arguments_before_any_hip_call():
+    lib = fckl.load()
+    P = 1 << 40
+    assert lib.fckl_scale(None, 10, _fake(P), None) == fckl.ERR_INVALID_ARG
+    assert lib.fckl_scale(_fake(P), 10, None, None) == fckl.ERR_INVALID_ARG
+    assert lib.fckl_scale(_fake(P), -1, _fake(P), None) == fckl.ERR_INVALID_ARG
+    assert lib.fckl_scale(_fake(P + 4), 10, _fake(P), None) == fckl.ERR_INVALID_ARG
+    assert lib.fckl_scale(_fake(P), 0, _fake(P), None) == fckl.OK      # nothing to do: no launch
+
+
 def test_missing_library_fails_loudly():
     """Without libfckl.so every entry point raises: there is no CPU or eager fallback."""
     saved_lib, saved_path = fckl._lib, fckl.LIB_PATH
