@@ -31,6 +31,7 @@ import torch
 from . import backward as _backward
 from . import forward as _forward
 from . import forward_backward as _forward_backward
+from . import full_forward_backward as _full_forward_backward
 from . import scale_ as _scale_
 
 
@@ -134,4 +135,65 @@ class FusedChunkedKLLoss(torch.nn.Module):
                         None if w is None else w.contiguous(), self.temperature, self.chunk)
 
 
-__all__ = ["FusedChunkedKLFunction", "FusedChunkedKLSingleCallFunction", "FusedChunkedKLLoss"]
+class FullTeacherKLFunction(torch.autograd.Function):
+    """KL against the teacher's whole distribution; gradients formed in the forward call."""
+
+    @staticmethod
+    def forward(ctx, h, W, h_t, W_t, weights, T: float, chunk: int, want_grad: bool):
+        _, _, mean, dH, dW = _full_forward_backward(h.detach(), W.detach(), h_t.detach(), W_t.detach(), T=T,
+                                                    grad_scale=1.0, weights=weights, chunk=chunk)
+        ctx.dH, ctx.dW = (dH, dW) if want_grad else (None, None)
+        return mean.reshape(())
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        dH, dW = ctx.dH, ctx.dW
+        ctx.dH = ctx.dW = None
+        g = grad_out.detach().to(torch.float32).reshape(1).contiguous()
+        if ctx.needs_input_grad[0]:
+            _scale_(dH, g)
+        if ctx.needs_input_grad[1]:
+            _scale_(dW, g)
+        return (dH if ctx.needs_input_grad[0] else None, dW if ctx.needs_input_grad[1] else None,
+                None, None, None, None, None, None)
+
+
+class FullTeacherKLLoss(torch.nn.Module):
+    """Online distillation against the teacher's whole distribution (the setting the
+    cached top-K teacher replaces, "The Distillation Bottleneck", getaibook.com):
+    loss = weighted mean over tokens of T^2 KL(softmax(h_t W_t^T / T) || softmax(h W^T / T)).
+    The teacher's final hidden states and LM head are inputs and get no gradient; the
+    forward call runs fckl_full_forward_backward and keeps dH and dW, which the backward
+    call scales by the upstream gradient on the device (fckl_scale).
+
+    forward(hidden [.., H] bf16, lm_head_weight [V, H] bf16, teacher_hidden [.., Ht] bf16,
+            teacher_lm_head_weight [V, Ht] bf16, mask [..] bool or None, weights [..] or None)
+            -> scalar loss (float32).
+    """
+
+    def __init__(self, temperature: float = 1.0, chunk: int = 0):
+        super().__init__()
+        if not temperature > 0:
+            raise ValueError("temperature must be > 0")
+        self.temperature = float(temperature)
+        self.chunk = int(chunk)
+
+    def forward(self, hidden, lm_head_weight, teacher_hidden, teacher_lm_head_weight, mask=None, weights=None):
+        H, Ht = hidden.shape[-1], teacher_hidden.shape[-1]
+        h = hidden.reshape(-1, H)
+        ht = teacher_hidden.reshape(-1, Ht)
+        N = h.shape[0]
+        w = None
+        if weights is not None:
+            w = weights.reshape(N).to(torch.float32)
+        if mask is not None:
+            m = mask.reshape(N).to(torch.float32)
+            w = m if w is None else w * m
+        want_grad = torch.is_grad_enabled() and (hidden.requires_grad or lm_head_weight.requires_grad)
+        return FullTeacherKLFunction.apply(h.contiguous(), lm_head_weight.contiguous(), ht.contiguous(),
+                                           teacher_lm_head_weight.contiguous(), None if w is None else w.contiguous(),
+                                           self.temperature, self.chunk, want_grad)
+
+
+__all__ = ["FusedChunkedKLFunction", "FusedChunkedKLSingleCallFunction", "FusedChunkedKLLoss",
+           "FullTeacherKLFunction", "FullTeacherKLLoss"]

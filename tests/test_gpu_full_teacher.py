@@ -127,3 +127,30 @@ def test_accumulate_and_the_full_plan():
     for x, what in ((a, "two chunks"), (b, "one chunk")):
         check_grad(x[3].cpu().numpy(), r[3], what + " dH")
         check_grad(x[4].cpu().numpy(), r[4], what + " dW")
+
+
+def test_full_teacher_module():
+    """FullTeacherKLLoss through autograd, with a padding mask and an upstream scale,
+    against the oracle; the teacher gets no gradient."""
+    from chunked_top_kl_chunk_amd.loss import FullTeacherKLLoss
+    N, Hs, Ht, V, T = 2 * 200, 128, 192, 2500, 1.5
+    h, W, ht, Wt = models(96, N, Hs, Ht, V)
+    dh, dW_, dht, dWt = to_dev(h, W, ht, Wt)
+    keep = np.ones(N, dtype=bool)
+    keep[180:200] = False
+    hb = dh.clone().reshape(2, 200, Hs).requires_grad_(True)
+    Wb = dW_.clone().requires_grad_(True)
+    htb = dht.reshape(2, 200, Ht)
+    mask = torch.from_numpy(keep).to(device()).reshape(2, 200)
+    loss = FullTeacherKLLoss(temperature=T, chunk=256)(hb, Wb, htb, dWt, mask=mask)
+    (-2.0 * loss).backward()
+    torch.cuda.synchronize()
+    w = keep.astype(np.float64)
+    _, _, r_mean, r_dH, r_dW = oracle.full(h, W, ht, Wt, T, w=w, grad_scale=-2.0)
+    assert abs(float(loss.detach()) - r_mean) <= 1e-3 * abs(r_mean)
+    check_grad(hb.grad.float().reshape(N, Hs).cpu().numpy(), r_dH, "full module dH")
+    check_grad(Wb.grad.float().cpu().numpy(), r_dW, "full module dW")
+    assert float(hb.grad.reshape(N, Hs)[~torch.from_numpy(keep)].abs().max()) == 0.0
+    with torch.no_grad():
+        l2 = FullTeacherKLLoss(temperature=T, chunk=256)(hb, Wb, htb, dWt, mask=mask)
+    assert float(l2) == float(loss.detach())
