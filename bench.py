@@ -96,7 +96,7 @@ def main():
                     help="run one plain 1 GiB device copy first (reference dispatch for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+        print("bench.py measures one GPU: the library has no multi-GPU path (--gpus %d requested)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 
