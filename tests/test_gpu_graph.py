@@ -1,4 +1,4 @@
-"""The loss calls inside a captured HIP graph.
+"""The loss calls inside a captured HIP graph, and on concurrent streams.
 
 The library allocates nothing, records no memset and (without FCKL_FLAG_VALIDATE) never
 synchronises, so a training or serving loop can capture a whole step -- the two passes,
@@ -105,3 +105,38 @@ def test_single_call_and_full_teacher_in_graphs():
         with torch.cuda.graph(g):
             fn()
         check_replays(g, o, ref, what)
+
+
+def test_two_streams_at_once_give_the_sequential_results():
+    """No global state: two problems on two streams, each with its own workspace, run
+    concurrently and give exactly what they give alone."""
+    dev = device()
+    probs = []
+    for seed, (N, H, V, K, T) in ((97, (700, 256, 4100, 10, 1.0)), (98, (500, 128, 3000, 20, 2.0))):
+        t = arrays(*synthetic(seed, N, H, V, K, T))
+        desc = fckl.desc_for(*t, T, 256)
+        ws = torch.empty(fckl.workspace_size(desc, 256), dtype=torch.uint8, device=dev)
+        probs.append((t, T, ws))
+
+    def run_one(p, stream):
+        t, T, ws = p
+        loss, lse, mean = fckl.forward(*t, T=T, chunk=256, ws=ws, stream=stream)
+        dH, dW = fckl.backward(*t, lse, T=T, chunk=256, ws=ws, stream=stream)
+        return [loss, lse, mean, dH, dW]
+
+    alone = []
+    for p in probs:
+        alone.append(run_one(p, None))
+        torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    together = []
+    for p, s in zip(probs, streams):
+        with torch.cuda.stream(s):
+            together.append(run_one(p, s))
+    torch.cuda.synchronize()
+    for a, b in zip(alone, together):
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+    say("two streams at once: outputs equal the sequential ones")
