@@ -88,6 +88,8 @@ def main():
                     help="skip timing fckl_forward_backward (the single-call path) after the main measurement")
     ap.add_argument("--no-topk", action="store_true",
                     help="skip timing the teacher-side top-K extraction (fckl_topk) of the same hidden states")
+    ap.add_argument("--sweep", default="",
+                    help="comma-separated chunk sizes: also time the step and its peak memory at each")
     ap.add_argument("--no-module", action="store_true",
                     help="skip the torch autograd module leg (FusedChunkedKLLoss, both modes)")
     ap.add_argument("--no-full", action="store_true",
@@ -223,6 +225,37 @@ def main():
             "kernels": {k: {"launches": v["launches"], "ms_per_step": round(v["ms"] / args.steps, 4)}
                         for k, v in k1.items()},
         }
+
+    if args.sweep:
+        # The chunk scheduler's trade-off: the same step at other chunk sizes, each with
+        # its own workspace, peak memory measured from the inputs and outputs alone.
+        del ws
+        ws = None
+        sweep = []
+        for c in [int(x) for x in args.sweep.split(",") if x]:
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            torch.cuda.reset_peak_memory_stats()
+            cws_bytes = fckl.workspace_size(fckl.desc_for(h, W, idx, tl, T, c), c)
+            cws = torch.empty(cws_bytes, dtype=torch.uint8, device=dev)
+
+            def sweep_step(profile=None):
+                fckl.forward(h, W, idx, tl, T=T, chunk=c, ws=cws, loss_tok=loss, lse=lse, loss_mean=mean)
+                fckl.backward(h, W, idx, tl, lse, T=T, chunk=c, ws=cws, dH=dH, dW=dW)
+            sweep_step()
+            torch.cuda.synchronize()
+            reps = max(1, min(args.steps, 3))
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                sweep_step()
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) * 1e3 / reps
+            peak = torch.cuda.max_memory_allocated()
+            log("chunk %d: %.2f ms per step, peak %.2f GiB, workspace %.2f GiB" % (c, ms, peak / GiB, cws_bytes / GiB))
+            sweep.append({"chunk": c, "ms_per_step": round(ms, 3), "tokens_per_s": round(N * 1e3 / ms, 1),
+                          "peak_gib": round(peak / GiB, 3), "workspace_gib": round(cws_bytes / GiB, 3)})
+            del cws
+        out["chunk_sweep"] = sweep
 
     if not args.no_module:
         # The torch autograd module, as a training loop calls it (loss = module(...);
