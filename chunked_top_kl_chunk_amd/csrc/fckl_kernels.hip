@@ -1814,21 +1814,38 @@ using DGemm = GemmD<256, kHiddenTile, 2, 4, 64, 2>;   // dH: tokens x hidden, k 
 using WGemm = GemmD<256, kHiddenTile, 2, 4, 64, 2>;   // dW: vocabulary x hidden, k = tokens
 
 // dst[c][r] = src[r][c] for r < rows, c < cols; dst[c][r] = 0 for rows <= r < rpad.
-// 64 x 64 tiles through LDS so that both sides are read and written along rows.
+// 64 x 64 tiles through LDS, 16-byte pieces on both sides: each thread loads two
+// 8-element row pieces and stores two 8-element column pieces.  cols is a multiple of
+// 8 (H), rpad a multiple of 64, both leading dimensions multiples of 8.  The LDS row
+// pitch of 72 elements (144 bytes) keeps the pieces 16-byte aligned and puts the eight
+// rows an output piece gathers in distinct banks.
 __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t *src, int64_t ld_src, int rows, int cols,
                                                         uint16_t *dst, int64_t ld_dst, int rpad)
 {
-    __shared__ uint16_t t[64][66];
+    constexpr int kPitch = 72;
+    __shared__ __attribute__((aligned(16))) uint16_t t[64 * kPitch];
     const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-        const int r = e >> 6, c = e & 63;
-        t[r][c] = (r0 + r < rows && c0 + c < cols) ? src[(int64_t)(r0 + r) * ld_src + c0 + c] : (uint16_t)0;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int e = threadIdx.x + 256 * q;
+        const int r = e >> 3, c8 = (e & 7) * 8;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (r0 + r < rows && c0 + c8 < cols)
+            v = *reinterpret_cast<const u32x4 *>(src + (int64_t)(r0 + r) * ld_src + c0 + c8);
+        *reinterpret_cast<u32x4 *>(t + r * kPitch + c8) = v;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-        const int c = e >> 6, r = e & 63;
-        if (c0 + c < cols && r0 + r < rpad)
-            dst[(int64_t)(c0 + c) * ld_dst + r0 + r] = t[r][c];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int e = threadIdx.x + 256 * q;
+        const int c = e >> 3, r8 = (e & 7) * 8;
+        if (c0 + c < cols && r0 + r8 < rpad) {
+            u32x4 v;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                v[w] = (uint32_t)t[(r8 + 2 * w) * kPitch + c] | ((uint32_t)t[(r8 + 2 * w + 1) * kPitch + c] << 16);
+            *reinterpret_cast<u32x4 *>(dst + (int64_t)(c0 + c) * ld_dst + r0 + r8) = v;
+        }
     }
 }
 
