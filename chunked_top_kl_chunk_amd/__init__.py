@@ -34,7 +34,7 @@ FLAG_VALIDATE, FLAG_DW_ACCUMULATE, FLAG_TOPK_FULL_FIRST_PASS = 1, 2, 4
 
 # Every symbol include/fckl.h declares.
 EXPORTS = ("fckl_plan", "fckl_workspace_size", "fckl_forward", "fckl_backward", "fckl_forward_ex",
-           "fckl_backward_ex", "fckl_forward_backward", "fckl_topk_workspace_size", "fckl_topk",
+           "fckl_backward_ex", "fckl_forward_backward", "fckl_topk_workspace_size", "fckl_topk", "fckl_topk_async",
            "fckl_full_plan", "fckl_full_forward_backward", "fckl_scale", "fckl_status_string", "fckl_version")
 
 
@@ -89,13 +89,14 @@ def load() -> ctypes.CDLL:
     lib.fckl_version.restype = ctypes.c_int32
     lib.fckl_topk_workspace_size.argtypes = [P(Desc), ctypes.c_int32, P(sz)]
     lib.fckl_topk.argtypes = [P(Desc), vp, vp, vp, vp, vp, sz, vp]
+    lib.fckl_topk_async.argtypes = [P(Desc), vp, vp, vp, vp, vp, sz, vp, vp]
     lib.fckl_full_plan.argtypes = [P(Desc), ctypes.c_int32, sz, P(ctypes.c_int32), P(sz)]
     lib.fckl_full_forward_backward.argtypes = [P(Desc), ctypes.c_int32, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp,
                                                vp, vp, vp, vp, sz, vp]
     lib.fckl_scale.argtypes = [vp, ctypes.c_int64, vp, vp]
     for f in ("fckl_plan", "fckl_workspace_size", "fckl_forward", "fckl_backward", "fckl_forward_ex",
               "fckl_backward_ex", "fckl_forward_backward", "fckl_topk_workspace_size", "fckl_topk",
-              "fckl_full_plan", "fckl_full_forward_backward", "fckl_scale"):
+              "fckl_topk_async", "fckl_full_plan", "fckl_full_forward_backward", "fckl_scale"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -299,10 +300,12 @@ def topk_workspace_size(desc: Desc, chunk: int = 0) -> int:
 
 
 def topk(h, W, K: int, chunk: int = 0, logits_f32: bool = False, ws=None, topk_idx=None, topk_logit=None,
-         stream=None, full_first_pass: bool = False):
+         stream=None, full_first_pass: bool = False, status=None):
     """Teacher-side extraction (fckl_topk): per token the K largest z = h W^T, descending,
     equal values by the smaller index.  Returns (topk_idx int32 [N,K], topk_logit [N,K]
-    bf16, or float32 with logits_f32).  full_first_pass: FCKL_FLAG_TOPK_FULL_FIRST_PASS."""
+    bf16, or float32 with logits_f32).  full_first_pass: FCKL_FLAG_TOPK_FULL_FIRST_PASS.
+    status: a one-element int32 device tensor selects fckl_topk_async (no host
+    synchronisation; the call's status is written there on the stream)."""
     import torch
     for name, t in (("h", h), ("W", W)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
@@ -325,8 +328,17 @@ def topk(h, W, K: int, chunk: int = 0, logits_f32: bool = False, ws=None, topk_i
     for name, t, dt in (("topk_idx", topk_idx, torch.int32), ("topk_logit", topk_logit, ldt)):
         if t.dtype != dt or tuple(t.shape) != (N, K) or not t.is_contiguous() or t.device != dev:
             raise ValueError("%s must be a contiguous %s tensor of shape (%d, %d)" % (name, dt, N, K))
-    _call("fckl_topk", ctypes.byref(desc), h.data_ptr(), W.data_ptr(), topk_idx.data_ptr(), topk_logit.data_ptr(),
-          ws.data_ptr(), ctypes.c_size_t(ws.numel() * ws.element_size()), _stream_handle(stream))
+    if status is not None:
+        if (not isinstance(status, torch.Tensor) or status.dtype != torch.int32 or status.numel() != 1
+                or status.device != dev):
+            raise ValueError("status must be a one-element int32 tensor on the device of h")
+        _call("fckl_topk_async", ctypes.byref(desc), h.data_ptr(), W.data_ptr(), topk_idx.data_ptr(),
+              topk_logit.data_ptr(), ws.data_ptr(), ctypes.c_size_t(ws.numel() * ws.element_size()),
+              status.data_ptr(), _stream_handle(stream))
+    else:
+        _call("fckl_topk", ctypes.byref(desc), h.data_ptr(), W.data_ptr(), topk_idx.data_ptr(),
+              topk_logit.data_ptr(), ws.data_ptr(), ctypes.c_size_t(ws.numel() * ws.element_size()),
+              _stream_handle(stream))
     return topk_idx, topk_logit
 
 

@@ -474,14 +474,14 @@ fckl_status fckl_topk_workspace_size(const fckl_desc *desc, int32_t chunk, size_
     return FCKL_OK;
 }
 
-fckl_status fckl_topk(const fckl_desc *desc, const void *h, const void *W, int32_t *topk_idx, void *topk_logit,
-                      void *ws, size_t ws_bytes, void *stream)
+fckl_status fckl_topk_async(const fckl_desc *desc, const void *h, const void *W, int32_t *topk_idx,
+                            void *topk_logit, void *ws, size_t ws_bytes, uint32_t *status, void *stream)
 {
     TopkLayout T;
     fckl_status st = make_topk_layout(desc, desc ? desc->chunk : 0, &T);
     if (st != FCKL_OK)
         return st;
-    if (!h || !W || !topk_idx || !topk_logit || !ws)
+    if (!h || !W || !topk_idx || !topk_logit || !ws || !status)
         return FCKL_ERR_INVALID_ARG;
     if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || (reinterpret_cast<uintptr_t>(h) & 15u) != 0 ||
         (reinterpret_cast<uintptr_t>(W) & 15u) != 0)
@@ -521,12 +521,28 @@ fckl_status fckl_topk(const fckl_desc *desc, const void *h, const void *W, int32
             launch_topk_select(a, T, idx_c, logit_c, f32, guard, nullptr, stream))
             return FCKL_ERR_HIP;
     }
+    return launch_topk_status(flag, status, (uint32_t)FCKL_ERR_UNSUPPORTED, stream) ? FCKL_ERR_HIP : FCKL_OK;
+}
+
+fckl_status fckl_topk(const fckl_desc *desc, const void *h, const void *W, int32_t *topk_idx, void *topk_logit,
+                      void *ws, size_t ws_bytes, void *stream)
+{
+    TopkLayout T;
+    fckl_status st = make_topk_layout(desc, desc ? desc->chunk : 0, &T);
+    if (st != FCKL_OK)
+        return st;
+    if (!ws || T.total > ws_bytes)
+        return ws ? FCKL_ERR_WORKSPACE : FCKL_ERR_INVALID_ARG;
+    // the status word goes to the workspace's error slot (word 2), read back once
+    uint32_t *status = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(ws) + T.off_err) + 2;
+    if ((st = fckl_topk_async(desc, h, W, topk_idx, topk_logit, ws, ws_bytes, status, stream)) != FCKL_OK)
+        return st;
     uint32_t host = 0;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (hipMemcpyAsync(&host, flag, sizeof(host), hipMemcpyDeviceToHost, s) != hipSuccess ||
+    if (hipMemcpyAsync(&host, status, sizeof(host), hipMemcpyDeviceToHost, s) != hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess)
         return FCKL_ERR_HIP;
-    return host ? FCKL_ERR_UNSUPPORTED : FCKL_OK;
+    return (fckl_status)host;
 }
 
 fckl_status fckl_scale(float *x, int64_t n, const float *scale, void *stream)

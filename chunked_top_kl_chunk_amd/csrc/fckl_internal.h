@@ -135,6 +135,8 @@ int launch_transpose_head(const ChunkArgs &a, void *stream);
 int launch_transpose_chunk(const ChunkArgs &a, void *stream);
 int launch_zero_flag(uint32_t *flag, void *stream);
 int launch_scale(float *x, int64_t n, const float *scale, void *stream);
+// *status = *flag ? code : 0 (one thread).
+int launch_topk_status(const uint32_t *flag, uint32_t *status, uint32_t code, void *stream);
 
 // Teacher top-K extraction of one chunk (a.L is unused; T is the top-K layout): the
 // 32-row sub-tile maxima of z, the per-token threshold, the candidates at or above it,

@@ -1867,6 +1867,12 @@ __global__ __launch_bounds__(256) void scale_kernel(float *x, int64_t n, const f
         x[4 * n4 + threadIdx.x] *= c;
 }
 
+__global__ void topk_status_kernel(const uint32_t *flag, uint32_t *status, uint32_t code)
+{
+    if (threadIdx.x == 0)
+        *status = *flag ? code : 0u;
+}
+
 __global__ void zero_u32_kernel(uint32_t *p, int n)
 {
     if ((int)threadIdx.x < n)
@@ -2138,6 +2144,12 @@ int launch_scale(float *x, int64_t n, const float *scale, void *stream)
     const int64_t n4 = n / 4;
     const int64_t blocks = std::min<int64_t>(std::max<int64_t>((n4 + 255) / 256, 1), 8192);
     hipLaunchKernelGGL(scale_kernel, dim3((unsigned)blocks), dim3(256), 0, S(stream), x, n, scale);
+    return (int)hipGetLastError();
+}
+
+int launch_topk_status(const uint32_t *flag, uint32_t *status, uint32_t code, void *stream)
+{
+    hipLaunchKernelGGL(topk_status_kernel, dim3(1), dim3(64), 0, S(stream), flag, status, code);
     return (int)hipGetLastError();
 }
 

@@ -257,6 +257,18 @@ fckl_status fckl_topk(const fckl_desc *desc, const void *h, const void *W, int32
                       void *topk_logit, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * fckl_topk without the host synchronisation: the status the call would return for the
+ * data (FCKL_OK, or FCKL_ERR_UNSUPPORTED for a candidate overflow or NaN logits) is
+ * written on the stream to `status` (device, one uint32), which the caller reads when
+ * it chooses.  The call records only kernel launches, so it can be captured in a HIP
+ * graph.  Argument errors are still returned before any HIP call; `status` must not be
+ * NULL.
+ */
+fckl_status fckl_topk_async(const fckl_desc *desc, const void *h, const void *W, int32_t *topk_idx,
+                            void *topk_logit, void *ws, size_t ws_bytes, uint32_t *status,
+                            void *stream);
+
+/*
  * Online distillation against the teacher's whole distribution: the setting the cached
  * top-K teacher replaces, where the teacher's full-vocabulary distribution is computed
  * beside the student's ("The Distillation Bottleneck", getaibook.com; the teacher run on

@@ -208,3 +208,46 @@ def test_partial_first_pass_falls_back_when_candidates_overflow():
     torch.cuda.synchronize()
     assert torch.equal(gi, fi) and torch.equal(gz, fz)
     check_topk(h, W, K, gi.cpu().numpy(), gz.cpu().numpy().astype(np.float64), "fallback")
+
+
+def test_topk_async_in_a_graph_and_its_status():
+    """fckl_topk_async: the same result as fckl_topk with its status on the device, no
+    host synchronisation, so a captured graph can replay it; a zero head over a large
+    vocabulary reports FCKL_ERR_UNSUPPORTED through the status word."""
+    rng = np.random.default_rng(79)
+    N, H, V, K = 300, 128, 20000, 10
+    h = synth.round_bf16(rng.standard_normal((N, H)).astype(np.float32))
+    W = synth.round_bf16((rng.standard_normal((V, H)) * 0.2).astype(np.float32))
+    th, tW, _, _ = arrays(h, W, np.zeros((N, 1), np.int32), np.zeros((N, 1), np.float32))
+    dev = device()
+    ri, rz = fckl.topk(th, tW, K, logits_f32=True)
+    desc = fckl.make_desc(N, H, V, K, 1.0, 0, fckl.DTYPE_F32)
+    ws = torch.empty(fckl.topk_workspace_size(desc), dtype=torch.uint8, device=dev)
+    gi = torch.empty(N, K, dtype=torch.int32, device=dev)
+    gz = torch.empty(N, K, dtype=torch.float32, device=dev)
+    status = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    fckl.topk(th, tW, K, logits_f32=True, ws=ws, topk_idx=gi, topk_logit=gz, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == fckl.OK and torch.equal(gi, ri) and torch.equal(gz, rz)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fckl.topk(th, tW, K, logits_f32=True, ws=ws, topk_idx=gi, topk_logit=gz, status=status)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fckl.topk(th, tW, K, logits_f32=True, ws=ws, topk_idx=gi, topk_logit=gz, status=status)
+    for _ in range(3):
+        gi.fill_(-7)
+        gz.fill_(float("nan"))
+        status.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(status.item()) == fckl.OK and torch.equal(gi, ri) and torch.equal(gz, rz)
+    zero = torch.zeros(5000, H, dtype=torch.bfloat16, device=dev)
+    fckl.topk(th, zero, 16, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == fckl.ERR_UNSUPPORTED
+    say("topk_async: equal to fckl_topk, 3 graph replays equal, overflow reported as status %d" % int(status.item()))

@@ -252,6 +252,19 @@ def test_module_validates_arguments_without_a_gpu():
         fckl.forward_backward(h, W, idx, tl)
 
 
+def test_topk_async_requires_a_status_word():
+    lib = fckl.load()
+    d = fckl.make_desc(512, 256, 4096, 10, 1.0)
+    need = fckl.topk_workspace_size(d)
+    P = 1 << 40
+    st = lib.fckl_topk_async(ctypes.byref(d), _fake(P), _fake(P), _fake(P), _fake(P), _fake(P), ctypes.c_size_t(need),
+                             None, None)
+    assert st == fckl.ERR_INVALID_ARG
+    st = lib.fckl_topk_async(ctypes.byref(d), _fake(P), _fake(P), _fake(P), _fake(P), _fake(P),
+                             ctypes.c_size_t(need - 1), _fake(P), None)
+    assert st == fckl.ERR_WORKSPACE
+
+
 def test_scale_rejects_bad_arguments_before_any_hip_call():
     lib = fckl.load()
     P = 1 << 40
