@@ -21,6 +21,10 @@ logits formed once, 6 N V H flop instead of 8) with an upstream gradient of 1 an
 dH and dW (float32, N H + V H values) until the backward pass, which scales them in
 place by the upstream gradient with ``fckl_scale`` on the device.  The gradients are
 those of the two-pass path up to the bf16 rounding of the kept exponentials.
+
+``FullTeacherKLLoss`` is the same kind of module for online distillation against the
+teacher's whole distribution (``fckl_full_forward_backward``): it takes the teacher's
+final hidden states and LM head instead of a cache.
 """
 from __future__ import annotations
 
