@@ -212,3 +212,24 @@ def test_autograd_module_single_call():
         l2 = FusedChunkedKLLoss(temperature=T, chunk=256, single_call=True)(
             t[0].reshape(2, 300, H), t[1], t[2].reshape(2, 300, K), t[3].reshape(2, 300, K), mask=mask)
     assert float(l2) == grads[True][0]
+
+
+def test_single_call_validate():
+    """FCKL_FLAG_VALIDATE on the single call: valid indices give the unvalidated results
+    bit for bit; an index out of range or repeated within a token is reported."""
+    h, W, idx, tl = synthetic(52, 400, 128, 1200, 8, 1.0)
+    t = arrays(h, W, idx, tl)
+    a = fckl.forward_backward(*t, T=1.0, validate=True)
+    b = fckl.forward_backward(*t, T=1.0)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    for bad_value in (1200, -5, None):
+        bad = t[2].clone()
+        if bad_value is None:
+            bad[9, 4] = bad[9, 0]
+        else:
+            bad[3, 6] = bad_value
+        with pytest.raises(fckl.FCKLError) as e:
+            fckl.forward_backward(t[0], t[1], bad, t[3], T=1.0, validate=True)
+        assert e.value.status == fckl.ERR_INDEX
