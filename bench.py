@@ -155,7 +155,8 @@ def main():
         log("warmup step %d done" % i)
     peak_bytes = torch.cuda.max_memory_allocated()
 
-    ms_step, kernels = timed_steps(fckl, step, args.steps, nchunks)
+    clock = {}
+    ms_step, kernels = timed_steps(fckl, step, args.steps, nchunks, clock)
     tokens_per_s = N * 1e3 / ms_step
     log("timed %d steps: %.2f ms/step, %.0f tokens/s" % (args.steps, ms_step, tokens_per_s))
     # the two passes on their own (after the timed steps, so they do not enter `value`)
@@ -189,6 +190,12 @@ def main():
                 "traffic": measured_traffic(wl.name, chunk, dom),
                 "avg_launch_ms": round(kd["avg_ms"], 4),
                 "flops_per_launch": flops_per_launch}
+    if clock.get("mhz"):
+        # the same rate against the dense bf16 peak at the shader clock measured during the
+        # timed steps (the published 2.5 PFLOP/s assumes 2400 MHz)
+        roofline["sustained_clock_mhz"] = round(clock["mhz"], 1)
+        roofline["peak_at_sustained_clock"] = round(PEAK_BF16_TFLOPS * clock["mhz"] / 2400.0, 1)
+        roofline["frac_at_sustained_clock"] = round(achieved / roofline["peak_at_sustained_clock"], 4)
     step_tflops = 8.0 * N * V * H / (ms_step * 1e-3) / 1e12
 
     out = {
@@ -357,7 +364,56 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def timed_steps(fckl, step, steps, nchunks):
+class ClockSampler:
+    """Samples the GPU's current shader clock (the amdgpu driver's pp_dpm_sclk, its
+    "S:" line or the level marked "*") every 50 ms on a background thread while the
+    timed steps run.  mean_mhz() is None where the file is not readable."""
+
+    def __init__(self, period_s=0.05):
+        import glob
+        import threading
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = paths[0] if paths else None
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        import re
+        try:
+            text = open(self.path).read()
+        except OSError:
+            return None
+        for line in text.splitlines():
+            if "*" in line:
+                m = re.search(r"(\d+)\s*Mhz", line, re.I)
+                if m:
+                    return int(m.group(1))
+        return None
+
+    def _run(self):
+        while not self._stop.wait(self.period):
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+
+    def __enter__(self):
+        if self.path:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self.path:
+            self._stop.set()
+            self._thread.join()
+
+    def mean_mhz(self):
+        busy = [v for v in self.samples if v >= 500]     # samples taken while the GPU worked
+        return sum(busy) / len(busy) if busy else None
+
+
+def timed_steps(fckl, step, steps, nchunks, clock=None):
     """Time `steps` calls of step(profile) between two device syncs; the library records
     HIP events around each of its kernel launches on its stream.  Returns (ms per step,
     per-kernel {launches, ms, tokens})."""
@@ -370,11 +426,18 @@ def timed_steps(fckl, step, steps, nchunks):
     work = (ctypes.c_int32 * cap)()
     prof = fckl.Profile((1 << len(fckl.KERNELS)) - 1, cap, 0, events, kid, work)
     torch.cuda.synchronize()
+    sampler = ClockSampler() if clock is not None else None
+    if sampler:
+        sampler.__enter__()
     t_start = time.perf_counter()
     for _ in range(steps):
         step(prof)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
+    if sampler:
+        sampler.__exit__(None, None, None)
+        clock["mhz"] = sampler.mean_mhz()
+        clock["samples"] = len(sampler.samples)
     kernels = {}
     for i in range(prof.count):
         name = fckl.KERNELS[kid[i]]
