@@ -27,6 +27,17 @@ constexpr int kTopkMaxSub = 65536;
 constexpr int32_t kMaxChunk = 8192;
 constexpr size_t kDefaultBudget = size_t(12) << 30;  // 12 GiB of the 288 GB HBM3E
 
+// Kernel limits.  The GEMM operand loaders keep each lane's offset inside a 256-row
+// tile in 32 bits (up to 255 rows of the operand's pitch), and the pitch of g and W^T is
+// Vpad, that of g^T and h^T the padded chunk: both at most kMaxPitch elements.  A
+// non-persistent GEMM launches one 512-thread work-group per 256 x 256 output tile, and
+// HIP counts a grid dimension in 32-bit work-items: at most kMaxTiles tiles.  The dH
+// split reduce runs one thread per 4 elements of a chunk's dH: at most kMaxChunkElems
+// elements.
+constexpr int64_t kMaxPitch = int64_t(1) << 24;
+constexpr int64_t kMaxTiles = (int64_t(1) << 23) - 1;
+constexpr int64_t kMaxChunkElems = int64_t(1) << 33;
+
 // Where each per-chunk buffer lives inside the caller's workspace.  Every buffer is
 // sized by the chunk, never by N.
 struct Layout {

@@ -15,6 +15,7 @@
 namespace fckl {
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+static int64_t tiles(int64_t n, int64_t t) { return (n + t - 1) / t; }
 
 fckl_status check_desc(const fckl_desc *d)
 {
@@ -32,9 +33,19 @@ fckl_status check_desc(const fckl_desc *d)
         return FCKL_ERR_INVALID_ARG;
     if (d->H % 8 != 0)
         return FCKL_ERR_UNSUPPORTED;
-    if (d->K > kMaxK || d->H > 65536 || d->V > (1 << 30))
+    if (d->K > kMaxK || d->H > 65536 || d->V > kMaxPitch)
+        return FCKL_ERR_UNSUPPORTED;
+    if (tiles(d->V, kVocabTile) * tiles(d->H, kHiddenTile) > kMaxTiles)
         return FCKL_ERR_UNSUPPORTED;
     return FCKL_OK;
+}
+
+// The token dimension of a chunk of Cpad tokens (padded) within the kernels' limits
+// (see kMaxPitch and kMaxTiles).
+static bool chunk_supported(int64_t Cpad, int32_t H)
+{
+    return Cpad <= kMaxPitch && tiles(Cpad, kTokenTile) * tiles(H, kHiddenTile) <= kMaxTiles &&
+           Cpad * (int64_t)H <= kMaxChunkElems;
 }
 
 // Number of vocabulary splits of the dH product (its reduction runs over V).  Each
@@ -73,6 +84,8 @@ fckl_status make_layout(const fckl_desc *d, int32_t chunk, Layout *L)
         return st;
     if (chunk < 1 || !L)
         return FCKL_ERR_INVALID_ARG;
+    if (!chunk_supported((int64_t)align_up((size_t)chunk, kTokenTile), d->H))
+        return FCKL_ERR_UNSUPPORTED;
     Layout o;
     o.C = chunk;
     o.Cpad = (int32_t)align_up((size_t)chunk, kTokenTile);
@@ -116,6 +129,8 @@ fckl_status make_topk_layout(const fckl_desc *d, int32_t chunk, TopkLayout *L)
         return FCKL_ERR_INVALID_ARG;
     if (chunk == 0)
         chunk = (int32_t)std::min<int64_t>(align_up((size_t)d->N, kTokenTile), kMaxChunk);
+    if (!chunk_supported((int64_t)align_up((size_t)chunk, kTokenTile), d->H))
+        return FCKL_ERR_UNSUPPORTED;
     TopkLayout o;
     o.C = chunk;
     o.Cpad = (int32_t)align_up((size_t)chunk, kTokenTile);

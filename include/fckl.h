@@ -40,7 +40,11 @@
  *   - Errors are returned as status codes; nothing throws across the ABI.  Argument
  *     errors are detected before any HIP call and leave every output untouched.
  *   - Limits of this version: 1 <= K <= 128, K <= V, H % 8 == 0, H <= 65536,
- *     V <= 2^30, N <= 2^31 - 1, T finite and > 0.  Cached indices must be distinct
+ *     V <= 2^24 with ceil(V/256) * ceil(H/256) < 2^23, N <= 2^31 - 1, T finite and
+ *     > 0; a chunk of C tokens (C rounded up to a multiple of 256) needs C <= 2^24,
+ *     ceil(C/256) * ceil(H/256) < 2^23 and C * H <= 2^33 (the scheduler's chunks, at
+ *     most 8192 tokens, always do).  Outside these limits the calls return
+ *     FCKL_ERR_UNSUPPORTED.  Cached indices must be distinct
  *     within a token and lie in [0, V); with FCKL_FLAG_VALIDATE the call checks them
  *     and returns FCKL_ERR_INDEX, otherwise results for such inputs are undefined
  *     (no out-of-bounds memory access is made either way).

@@ -49,7 +49,7 @@ int main()
 {
     const int64_t Ns[] = {1, 255, 256, 257, 32768, 262144, 2147483647LL};
     const int32_t Hs[] = {8, 136, 2880, 3072, 65536};
-    const int32_t Vs[] = {1, 100, 257, 4100, 128256, 201088, 1 << 21};
+    const int32_t Vs[] = {1, 100, 257, 4100, 128256, 201088, 1 << 21, 1 << 24, (1 << 24) + 1};
     const int32_t Ks[] = {1, 10, 100, 128};
     const size_t budgets[] = {0, size_t(1) << 20, size_t(3) << 30, size_t(12) << 30, size_t(64) << 30};
     int planned = 0, rejected = 0;
@@ -64,11 +64,13 @@ int main()
                     d.K = K;
                     d.T = 1.0f;
                     d.logit_dtype = FCKL_DTYPE_BF16;
+                    const int64_t vocab_tiles = ((int64_t)V + 255) / 256 * (((int64_t)H + 255) / 256);
                     if (check_desc(&d) != FCKL_OK) {
-                        CHECK(K > V);
+                        CHECK(K > V || V > kMaxPitch || vocab_tiles > kMaxTiles);
                         ++rejected;
                         continue;
                     }
+                    CHECK(V <= kMaxPitch && vocab_tiles <= kMaxTiles);
                     for (size_t budget : budgets) {
                         Layout L;
                         if (plan_chunk(&d, budget, &L) == FCKL_OK) {
@@ -90,9 +92,14 @@ int main()
                             CHECK(F.off_at >= F.base.total);
                         }
                     }
-                    for (int32_t chunk : {1, 256, 1000, 8192}) {
+                    for (int32_t chunk : {1, 256, 1000, 8192, 1 << 20, (1 << 24) + 1}) {
                         Layout L;
-                        if (make_layout(&d, chunk, &L) == FCKL_OK)
+                        const int64_t Cpad = ((int64_t)chunk + 255) / 256 * 256;
+                        const bool fits = Cpad <= kMaxPitch && Cpad / 256 * (((int64_t)H + 255) / 256) <= kMaxTiles &&
+                                          Cpad * H <= kMaxChunkElems;
+                        const fckl_status ls = make_layout(&d, chunk, &L);
+                        CHECK(fits ? ls == FCKL_OK : ls == FCKL_ERR_UNSUPPORTED);
+                        if (ls == FCKL_OK)
                             check_layout(d, L);
                         for (uint32_t flags : {0u, (uint32_t)FCKL_FLAG_TOPK_FULL_FIRST_PASS}) {
                             fckl_desc dt = d;

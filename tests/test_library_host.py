@@ -94,6 +94,11 @@ def test_plan_explicit_chunk_and_small_budget():
     (dict(flags=64), fckl.ERR_INVALID_ARG),
     (dict(H=260), fckl.ERR_UNSUPPORTED),
     (dict(K=129), fckl.ERR_UNSUPPORTED),
+    # past the kernels' 32-bit tile offsets (pitch 2^24) and grid sizes (2^23 tiles of 256 x 256)
+    (dict(V=2 ** 24 + 1), fckl.ERR_UNSUPPORTED),
+    (dict(V=2 ** 23, H=65536), fckl.ERR_UNSUPPORTED),
+    (dict(N=2 ** 25, chunk=2 ** 24 + 1), fckl.ERR_UNSUPPORTED),
+    (dict(N=2 ** 21, H=65536, chunk=2 ** 20), fckl.ERR_UNSUPPORTED),
 ])
 def test_invalid_descriptions_rejected(bad, status):
     args = dict(N=512, H=256, V=4096, K=10, T=1.0)
@@ -102,6 +107,17 @@ def test_invalid_descriptions_rejected(bad, status):
     with pytest.raises(fckl.FCKLError) as e:
         fckl.plan(d, 0)
     assert e.value.status == status
+
+
+def test_limits_at_their_edges_are_planned():
+    """The largest supported vocabulary and chunk sizes still plan (given the memory)."""
+    budget = 1 << 44          # sizes only: W^T alone is 1.1 TB in the second case
+    for args in (dict(N=512, H=256, V=2 ** 24, K=10),                  # 65536 x 1 tiles
+                 dict(N=512, H=65536, V=(2 ** 23 - 1) // 256 * 256, K=10),  # 32767 x 256 tiles
+                 dict(N=2 ** 20, H=8192, V=4096, K=10, chunk=2 ** 20)):     # C * H = 2^33
+        d = fckl.make_desc(T=1.0, **args)
+        chunk, ws = fckl.plan(d, budget)
+        assert chunk >= 256 and ws > 0
 
 
 def _fake(addr):
