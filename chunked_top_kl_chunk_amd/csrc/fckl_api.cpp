@@ -9,6 +9,9 @@ using namespace fckl;
 
 namespace {
 
+// h, W (and the teacher's h_t, W_t) are read, and dH written, in 16-byte pieces.
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 fckl_status common_checks(const fckl_desc *d, const void *h, const void *W, const int32_t *idx, const void *tl,
                           void *ws, size_t ws_bytes, Layout *L)
 {
@@ -199,7 +202,7 @@ fckl_status backward_impl(const fckl_desc *desc, const void *h, const void *W, c
     fckl_status st = common_checks(desc, h, W, topk_idx, topk_logit, ws, ws_bytes, &L);
     if (st != FCKL_OK)
         return st;
-    if (!lse || !dH || !dW)
+    if (!lse || !dH || !dW || !aligned16(dH))
         return FCKL_ERR_INVALID_ARG;
     if (desc->flags & FCKL_FLAG_VALIDATE) {
         st = validate_indices(desc, h, W, topk_idx, topk_logit, ws, L, stream);
@@ -309,7 +312,7 @@ fckl_status fckl_forward_backward(const fckl_desc *desc, const void *h, const vo
     fckl_status st = common_checks(desc, h, W, topk_idx, topk_logit, ws, ws_bytes, &L);
     if (st != FCKL_OK)
         return st;
-    if (!loss_tok || !lse || !dH || !dW)
+    if (!loss_tok || !lse || !dH || !dW || !aligned16(dH))
         return FCKL_ERR_INVALID_ARG;
     if (desc->flags & FCKL_FLAG_VALIDATE) {
         st = validate_indices(desc, h, W, topk_idx, topk_logit, ws, L, stream);
@@ -403,8 +406,8 @@ fckl_status fckl_full_forward_backward(const fckl_desc *desc, int32_t H_teacher,
         return st;
     if (!h || !W || !h_t || !W_t || !ws || !loss_tok || !lse || !dH || !dW)
         return FCKL_ERR_INVALID_ARG;
-    for (const void *ptr : {h, W, h_t, W_t})
-        if ((reinterpret_cast<uintptr_t>(ptr) & 15u) != 0)
+    for (const void *ptr : {h, W, h_t, W_t, (const void *)dH})
+        if (!aligned16(ptr))
             return FCKL_ERR_INVALID_ARG;
     if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
         return FCKL_ERR_INVALID_ARG;

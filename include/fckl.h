@@ -61,7 +61,7 @@ extern "C" {
 
 typedef enum fckl_status {
     FCKL_OK = 0,
-    FCKL_ERR_INVALID_ARG = 1,   /* null pointer, bad size, T <= 0, unsupported shape */
+    FCKL_ERR_INVALID_ARG = 1,   /* null or misaligned pointer, bad size, T <= 0 */
     FCKL_ERR_UNSUPPORTED = 2,   /* a valid request outside this version's limits */
     FCKL_ERR_WORKSPACE = 3,     /* workspace too small for the chosen chunk */
     FCKL_ERR_INDEX = 4,         /* FCKL_FLAG_VALIDATE found an index out of range or repeated */
@@ -155,8 +155,8 @@ fckl_status fckl_workspace_size(const fckl_desc *desc, int32_t chunk, size_t *ws
 
 /*
  * Forward pass: per-token loss, saved lse, and the mean loss.
- *   h          device, bf16 [N,H]      student hidden states
- *   W          device, bf16 [V,H]      student LM head
+ *   h          device, bf16 [N,H]      student hidden states (16-byte aligned)
+ *   W          device, bf16 [V,H]      student LM head (16-byte aligned)
  *   topk_idx   device, int32 [N,K]     teacher's cached vocabulary indices
  *   topk_logit device, bf16 or f32 [N,K] (desc->logit_dtype) teacher's cached logits
  *   loss_tok   device, f32 [N]         out: loss[i]
@@ -177,7 +177,7 @@ fckl_status fckl_forward(const fckl_desc *desc, const void *h, const void *W,
  * gradient g (bf16, in the workspace) feeds the dH and dW products.
  *   lse        device, f32 [N]         the lse written by fckl_forward for these inputs
  *   grad_scale                         upstream gradient of loss_mean (1 for a plain loss)
- *   dH         device, f32 [N,H]       out: overwritten
+ *   dH         device, f32 [N,H]       out: overwritten (16-byte aligned)
  *   dW         device, f32 [V,H]       out: overwritten, or added to with FCKL_FLAG_DW_ACCUMULATE;
  *                                      accumulated in fp32 across chunks in chunk order
  * Other arguments as in fckl_forward.  Deterministic.
@@ -294,6 +294,7 @@ fckl_status fckl_topk_async(const fckl_desc *desc, const void *h, const void *W,
  *   H_teacher  the teacher's hidden size (a multiple of 8, at most 65536)
  *   h, W       device, bf16 [N,H], [V,H]            the student
  *   h_t, W_t   device, bf16 [N,H_teacher], [V,H_teacher]  the teacher (same vocabulary)
+ *              (h, W, h_t, W_t and dH 16-byte aligned)
  *   weights    device, f32 [N] or NULL              per-token weights: finite and >= 0 (not
  *              checked); all 0 gives loss_mean = 0 and zero gradients
  *   loss_tok, lse  device, f32 [N]  out;  loss_mean device, f32 [1] out or NULL

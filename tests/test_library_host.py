@@ -124,6 +124,21 @@ def _fake(addr):
     return ctypes.c_void_p(addr)
 
 
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+# The tests below pass fake device addresses that every case must refuse before any HIP
+# call.  On a machine with a GPU they are skipped, so that a check that regressed could
+# never launch a kernel on those addresses.
+fake_addresses = pytest.mark.skipif(_gpu_visible(), reason="host-only check with fake device addresses")
+
+
+@fake_addresses
 def test_entry_points_reject_before_any_hip_call():
     """Null or misaligned pointers and a short workspace are refused up front.
 
@@ -170,6 +185,7 @@ def test_binding_refuses_host_tensors():
         fckl.forward(h, W, idx, tl)
 
 
+@fake_addresses
 def test_weighted_and_single_call_entry_points_reject_before_any_hip_call():
     """The weighted passes and the single-call path check their arguments up front too."""
     lib = fckl.load()
@@ -208,6 +224,41 @@ def test_weighted_and_single_call_entry_points_reject_before_any_hip_call():
     assert st == fckl.ERR_INVALID_ARG
 
 
+@fake_addresses
+def test_misaligned_pointers_are_refused():
+    """h, W (and the teacher's h_t, W_t) are read and dH is written in 16-byte pieces: a
+    pointer off that alignment is refused before any HIP call."""
+    lib = fckl.load()
+    d = fckl.make_desc(512, 256, 4096, 10, 1.0, chunk=128)
+    need = ctypes.c_size_t(fckl.workspace_size(d, 128))
+    P, odd = 1 << 40, (1 << 40) + 4
+    f = _fake
+    st = lib.fckl_forward(ctypes.byref(d), f(P + 8), f(P), f(P), f(P), f(P), f(P), None, f(P), need, None)
+    assert st == fckl.ERR_INVALID_ARG
+    st = lib.fckl_forward(ctypes.byref(d), f(P), f(P + 8), f(P), f(P), f(P), f(P), None, f(P), need, None)
+    assert st == fckl.ERR_INVALID_ARG
+    st = lib.fckl_backward(ctypes.byref(d), f(P), f(P), f(P), f(P), f(P), ctypes.c_float(1.0), f(odd), f(P), f(P),
+                           need, None)
+    assert st == fckl.ERR_INVALID_ARG
+    st = lib.fckl_backward_ex(ctypes.byref(d), f(P), f(P), f(P), f(P), None, f(P), ctypes.c_float(1.0), None,
+                              f(odd), f(P), f(P), need, None)
+    assert st == fckl.ERR_INVALID_ARG
+    st = lib.fckl_forward_backward(ctypes.byref(d), f(P), f(P), f(P), f(P), None, ctypes.c_float(1.0), f(P), f(P),
+                                   None, f(odd), f(P), f(P), need, None)
+    assert st == fckl.ERR_INVALID_ARG
+    # dW is written element by element: any 4-byte alignment is fine (the same call with an
+    # aligned dH would only fail later, on the fake addresses, so it is not made here)
+    small = fckl.make_desc(512, 256, 4096, 1, 1.0, chunk=256)
+    _, fneed = fckl.full_plan(small, 384)
+    for i_bad in (2, 3, 7):     # h_t, W_t, dH (after loss_tok, lse, loss_mean)
+        args = [f(P)] * 4 + [f(P)] * 5
+        args[i_bad] = f(odd)
+        st = lib.fckl_full_forward_backward(ctypes.byref(small), 384, *args[:4], None, ctypes.c_float(1.0),
+                                            *args[4:], f(P), ctypes.c_size_t(fneed), None)
+        assert st == fckl.ERR_INVALID_ARG, i_bad
+
+
+@fake_addresses
 def test_full_teacher_plan_and_argument_checks():
     """fckl_full_plan: its workspace holds the teacher's fp32 logits of a chunk on top of the
     loss workspace, never depends on N, fits the budget; bad sizes are refused before any
@@ -268,6 +319,7 @@ def test_module_validates_arguments_without_a_gpu():
         fckl.forward_backward(h, W, idx, tl)
 
 
+@fake_addresses
 def test_topk_async_requires_a_status_word():
     lib = fckl.load()
     d = fckl.make_desc(512, 256, 4096, 10, 1.0)
@@ -281,6 +333,7 @@ def test_topk_async_requires_a_status_word():
     assert st == fckl.ERR_WORKSPACE
 
 
+@fake_addresses
 def test_scale_rejects_bad_arguments_before_any_hip_call():
     lib = fckl.load()
     P = 1 << 40
