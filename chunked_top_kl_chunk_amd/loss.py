@@ -102,6 +102,10 @@ class FusedChunkedKLLoss(torch.nn.Module):
     forward(hidden [.., H] bf16, lm_head_weight [V, H] bf16, topk_idx [.., K] int32,
             topk_logit [.., K] bf16/f32, mask [..] bool (True = keep) or None,
             weights [..] float or None) -> scalar loss (float32).
+
+    At least one token is needed: an empty batch raises FCKLError (ERR_INVALID_ARG), as
+    the library refuses N = 0.  A batch whose tokens are all masked gives a loss of 0
+    and zero gradients.
     """
 
     def __init__(self, temperature: float = 1.0, chunk: int = 0, ignore_index: Optional[int] = None,
@@ -118,9 +122,9 @@ class FusedChunkedKLLoss(torch.nn.Module):
         H = hidden.shape[-1]
         K = topk_idx.shape[-1]
         h = hidden.reshape(-1, H)
-        idx = topk_idx.reshape(-1, K)
-        tl = topk_logit.reshape(-1, K)
         N = h.shape[0]
+        idx = topk_idx.reshape(N, K)
+        tl = topk_logit.reshape(N, K)
         w = None
         if weights is not None:
             w = weights.reshape(N).to(torch.float32)

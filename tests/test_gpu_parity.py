@@ -174,3 +174,25 @@ def test_nan_in_one_row_stays_in_that_token():
         assert np.array_equal(loss_d[keep], loss_c[keep]) and np.array_equal(lse_d[keep], lse_c[keep])
         assert np.array_equal(dH_d[keep], dH_c[keep])
         assert np.isfinite(mean_c[0]) and np.isfinite(dW_c).all()
+
+
+def test_empty_inputs_are_refused():
+    """N = 0 (an empty batch) and K = 0 (no cached entry) are argument errors, reported
+    before any kernel is launched; the autograd module passes the error on."""
+    from chunked_top_kl_chunk_amd.loss import FusedChunkedKLLoss
+    dev = device()
+    W = torch.zeros(300, 64, dtype=torch.bfloat16, device=dev)
+    for N, K in ((0, 5), (4, 0)):
+        h = torch.zeros(N, 64, dtype=torch.bfloat16, device=dev)
+        idx = torch.zeros(N, K, dtype=torch.int32, device=dev)
+        tl = torch.zeros(N, K, dtype=torch.bfloat16, device=dev)
+        with pytest.raises(fckl.FCKLError) as e:
+            fckl.forward(h, W, idx, tl)
+        assert e.value.status == fckl.ERR_INVALID_ARG, (N, K)
+        with pytest.raises(fckl.FCKLError) as e:
+            fckl.forward_backward(h, W, idx, tl)
+        assert e.value.status == fckl.ERR_INVALID_ARG, (N, K)
+        with pytest.raises(fckl.FCKLError):
+            FusedChunkedKLLoss()(h.requires_grad_(True), W, idx, tl)
+    torch.cuda.synchronize()
+    say("empty batch and empty cache rows: refused with ERR_INVALID_ARG")
