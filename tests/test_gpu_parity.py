@@ -61,11 +61,14 @@ CASES = [
     (8, 130, 3072, 513, 16, 1.0, 0, {}),
     (9, 200, 64, 100, 100, 1.0, 0, {}),                                   # K = V, V < one tile
     (10, 300, 128, 2000, 10, 0.25, 0, {"z_sigma": 20.0, "tl_sigma": 10.0}),  # z/T spread ~80: sharp softmaxes
+    (12, 300, 8, 600, 5, 1.0, 256, {}),                                    # smallest H: one partial k-step
+    (13, 333, 264, 1500, 12, 1.0, 0, {}),                                  # a hidden tail of 8 columns
+    (14, 400, 256, 3000, 20, 50.0, 0, {"z_sigma": 8.0, "tl_sigma": 8.0}),  # high T: near-uniform p and q
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=["ragged", "one-token", "K128", "K1", "H2880", "scaled-rows",
-                                             "K100", "H3072", "K-equals-V", "sharp"])
+                                             "K100", "H3072", "K-equals-V", "sharp", "H8", "H264", "T50"])
 def test_parity_shapes(case):
     seed, N, H, V, K, T, chunk, extra = case
     say("case:", case)
