@@ -199,3 +199,20 @@ def test_empty_inputs_are_refused():
             FusedChunkedKLLoss()(h.requires_grad_(True), W, idx, tl)
     torch.cuda.synchronize()
     say("empty batch and empty cache rows: refused with ERR_INVALID_ARG")
+
+
+def test_single_vocabulary_entry_gives_zero():
+    """V = K = 1: teacher and student both put all their mass on the one entry, so every
+    loss is 0 and so are dH and dW, up to the rounding of lse (stored in natural-log
+    units and converted back to base 2 by the backward pass)."""
+    N, H, T = 300, 64, 1.3
+    h, W, idx, tl = synthetic(130, N, H, 1, 1, T)
+    g = run(*arrays(h, W, idx, tl), T=T, chunk=256)
+    z = h.astype(np.float64) @ W.astype(np.float64).T          # [N, 1]
+    assert np.abs(g["lse"] - z[:, 0] / T).max() <= LSE_ATOL
+    assert float(np.abs(g["loss"]).max()) <= 1e-5 and abs(float(g["mean"][0])) <= 1e-5
+    # against the gradient scale T/N of one entry of probability 1
+    assert float(np.abs(g["dH"]).max()) <= 1e-5 * (T / N) * float(np.abs(W).max())
+    assert float(np.abs(g["dW"]).max()) <= 1e-5 * (T / N) * float(np.abs(h).sum(axis=0).max())
+    say("V = K = 1: max|loss| %.1e, max|dH| %.1e, max|dW| %.1e"
+        % (float(np.abs(g["loss"]).max()), float(np.abs(g["dH"]).max()), float(np.abs(g["dW"]).max())))
