@@ -1816,14 +1816,22 @@ using WGemm = GemmD<256, kHiddenTile, 2, 4, 64, 2>;   // dW: vocabulary x hidden
 // dst[c][r] = src[r][c] for r < rows, c < cols; dst[c][r] = 0 for rows <= r < rpad.
 // 64 x 64 tiles through LDS, 16-byte pieces on both sides: each thread loads two
 // 8-element row pieces and stores two 8-element column pieces.  cols is a multiple of
-// 8 (H), rpad a multiple of 64, both leading dimensions multiples of 8.  The LDS row
-// pitch of 72 elements (144 bytes) keeps the pieces 16-byte aligned and puts the eight
-// rows an output piece gathers in distinct banks.
+// 8 (H), rpad a multiple of 64, both leading dimensions multiples of 8.
+// LDS: 128-byte rows, with the 16-byte chunk of element (r, c) XORed with (r / 8) % 8.
+// A wave's element reads take one column c per group of 8 lanes at rows r8 + j with
+// r8 = 0, 8, .., 56: in one row the 8 rows would share their bank offsets (a 128-byte
+// pitch puts every other row at the same bank; padding cannot help while rows stay
+// 16-byte aligned), and the swizzle moves them to 8 distinct chunks instead, so the
+// wave's 64 reads hit 32 distinct dwords in 32 distinct banks.
+__device__ __forceinline__ int transpose_lds_index(int r, int c)
+{
+    return r * 64 + ((((c >> 3) ^ (r >> 3)) & 7) << 3) + (c & 7);
+}
+
 __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t *src, int64_t ld_src, int rows, int cols,
                                                         uint16_t *dst, int64_t ld_dst, int rpad)
 {
-    constexpr int kPitch = 72;
-    __shared__ __attribute__((aligned(16))) uint16_t t[64 * kPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t t[64 * 64];
     const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -1832,7 +1840,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t *src, int
         u32x4 v = {0u, 0u, 0u, 0u};
         if (r0 + r < rows && c0 + c8 < cols)
             v = *reinterpret_cast<const u32x4 *>(src + (int64_t)(r0 + r) * ld_src + c0 + c8);
-        *reinterpret_cast<u32x4 *>(t + r * kPitch + c8) = v;
+        *reinterpret_cast<u32x4 *>(t + transpose_lds_index(r, c8)) = v;
     }
     __syncthreads();
 #pragma unroll
@@ -1843,7 +1851,8 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t *src, int
             u32x4 v;
 #pragma unroll
             for (int w = 0; w < 4; ++w)
-                v[w] = (uint32_t)t[(r8 + 2 * w) * kPitch + c] | ((uint32_t)t[(r8 + 2 * w + 1) * kPitch + c] << 16);
+                v[w] = (uint32_t)t[transpose_lds_index(r8 + 2 * w, c)] |
+                       ((uint32_t)t[transpose_lds_index(r8 + 2 * w + 1, c)] << 16);
             *reinterpret_cast<u32x4 *>(dst + (int64_t)(c0 + c) * ld_dst + r0 + r8) = v;
         }
     }
