@@ -216,3 +216,27 @@ def test_single_vocabulary_entry_gives_zero():
     assert float(np.abs(g["dW"]).max()) <= 1e-5 * (T / N) * float(np.abs(h).sum(axis=0).max())
     say("V = K = 1: max|loss| %.1e, max|dH| %.1e, max|dW| %.1e"
         % (float(np.abs(g["loss"]).max()), float(np.abs(g["dH"]).max()), float(np.abs(g["dW"]).max())))
+
+
+@pytest.mark.parametrize("case", [
+    # seed, N, H, V, K, T: the largest hidden size, and the largest vocabulary (its g and
+    # W^T pitch of 2^24 takes the products' 32-bit operand offsets to their limit)
+    (140, 40, 65536, 300, 8, 1.0),
+    (141, 8, 8, 2 ** 24, 128, 1.0),
+], ids=["H65536", "V2^24"])
+def test_largest_supported_shapes(case):
+    seed, N, H, V, K, T = case
+    say("case: largest shapes", case)
+    h, W, idx, tl = synthetic(seed, N, H, V, K, T)
+    t = arrays(h, W, idx, tl)
+    dev = device()
+    desc = fckl.desc_for(*t, T, 256)
+    ws = torch.empty(fckl.workspace_size(desc, 256), dtype=torch.uint8, device=dev)
+    loss, lse, mean = fckl.forward(*t, T=T, chunk=256, ws=ws)
+    dH, dW = fckl.backward(*t, lse, T=T, chunk=256, ws=ws)
+    torch.cuda.synchronize()
+    g = {"loss": loss.cpu().numpy(), "lse": lse.cpu().numpy(), "mean": mean.cpu().numpy(),
+         "dH": dH.cpu().numpy(), "dW": dW.cpu().numpy()}
+    del ws, dH, dW
+    torch.cuda.empty_cache()
+    compare_all(g, h, W, idx, tl, T, what="largest%d" % seed)
