@@ -219,21 +219,25 @@ def test_single_vocabulary_entry_gives_zero():
 
 
 @pytest.mark.parametrize("case", [
-    # seed, N, H, V, K, T: the largest hidden size, and the largest vocabulary (its g and
-    # W^T pitch of 2^24 takes the products' 32-bit operand offsets to their limit)
-    (140, 40, 65536, 300, 8, 1.0),
-    (141, 8, 8, 2 ** 24, 128, 1.0),
-], ids=["H65536", "V2^24"])
+    # seed, N, H, V, K, T, chunk: the largest hidden size; the largest vocabulary (its g
+    # and W^T pitch of 2^24 takes the products' 32-bit operand offsets to their limit);
+    # 2M tokens in 256 chunks of the scheduler's 8192 (dW accumulated across all of them,
+    # the mean a fixed-order sum over 2M tokens)
+    (140, 40, 65536, 300, 8, 1.0, 256),
+    (141, 8, 8, 2 ** 24, 128, 1.0, 256),
+    (142, 2 ** 21, 8, 300, 4, 1.0, 0),
+], ids=["H65536", "V2^24", "N2^21"])
 def test_largest_supported_shapes(case):
-    seed, N, H, V, K, T = case
+    seed, N, H, V, K, T, chunk = case
     say("case: largest shapes", case)
     h, W, idx, tl = synthetic(seed, N, H, V, K, T)
     t = arrays(h, W, idx, tl)
     dev = device()
-    desc = fckl.desc_for(*t, T, 256)
-    ws = torch.empty(fckl.workspace_size(desc, 256), dtype=torch.uint8, device=dev)
-    loss, lse, mean = fckl.forward(*t, T=T, chunk=256, ws=ws)
-    dH, dW = fckl.backward(*t, lse, T=T, chunk=256, ws=ws)
+    desc = fckl.desc_for(*t, T, chunk)
+    chunk = chunk or fckl.plan(desc)[0]
+    ws = torch.empty(fckl.workspace_size(desc, chunk), dtype=torch.uint8, device=dev)
+    loss, lse, mean = fckl.forward(*t, T=T, chunk=chunk, ws=ws)
+    dH, dW = fckl.backward(*t, lse, T=T, chunk=chunk, ws=ws)
     torch.cuda.synchronize()
     g = {"loss": loss.cpu().numpy(), "lse": lse.cpu().numpy(), "mean": mean.cpu().numpy(),
          "dH": dH.cpu().numpy(), "dW": dW.cpu().numpy()}
