@@ -1,9 +1,12 @@
 // A C++ consumer of the C ABI alone (include/fckl.h and the HIP runtime; no Python, no
 // torch): plans a workspace, allocates every buffer with hipMalloc, runs the two passes,
-// the single call and the teacher top-K on seeded inputs, and checks what holds for any
-// input -- finite non-negative losses, the mean, the sum rule sum_v dW[v] = 0, the
-// identity <dW, W> = <dH, h>, bitwise repeatability, the single call against the two
-// passes, top-K ordering and values -- plus the argument errors.  Exit status 0 on success.
+// the single call, the weighted passes, fckl_scale, the full-vocabulary teacher and the
+// teacher top-K (both calls) on seeded inputs, and checks what holds for any input --
+// finite non-negative losses, the mean, the sum rule sum_v dW[v] = 0, the identity
+// <dW, W> = <dH, h>, bitwise repeatability, the single call against the two passes,
+// unit weights against no weights, zero weights against zero dH rows, a teacher equal to
+// the student against zero loss, top-K ordering and values -- plus the argument errors.
+// Exit status 0 on success.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -209,6 +212,117 @@ int main()
         }
     }
 
+    // the weighted passes: weights of 1 give the plain passes' results (up to the order of
+    // the fp64 sums); a weight of 0 leaves that token's dH row at exactly 0
+    std::vector<float> w1(N, 1.0f), w01(N, 1.0f);
+    for (int64_t i = 0; i < N; i += 5)
+        w01[i] = 0.0f;
+    float *dw1 = dev_alloc<float>(N), *dw01 = dev_alloc<float>(N), *two = dev_alloc<float>(1);
+    uint32_t *status = dev_alloc<uint32_t>(1);
+    if (!dw1 || !dw01 || !two || !status)
+        return 2;
+    const float two_h = 2.0f;
+    HIP_OK(hipMemcpy(dw1, w1.data(), N * 4, hipMemcpyHostToDevice));
+    HIP_OK(hipMemcpy(dw01, w01.data(), N * 4, hipMemcpyHostToDevice));
+    HIP_OK(hipMemcpy(two, &two_h, 4, hipMemcpyHostToDevice));
+    CHECK(fckl_forward_ex(&d, dh, dW_in, didx, dtl, dw1, loss, lse, mean, ws, ws_bytes, s) == FCKL_OK);
+    CHECK(fckl_backward_ex(&d, dh, dW_in, didx, dtl, dw1, lse, 1.0f, nullptr, dH, dW, ws, ws_bytes, s) == FCKL_OK);
+    fetch(l2, m2, gh2, gw2);
+    CHECK(l1 == l2 && std::fabs(m2[0] - m1[0]) <= 1e-6 * std::fabs(m1[0]));
+    double e1 = 0.0;
+    for (size_t q = 0; q < gw1.size(); ++q)
+        e1 = std::fmax(e1, std::fabs(gw1[q] - gw2[q]));
+    CHECK(e1 <= 1e-2 * mw);     // w / sum w against 1 / N can move a bf16 rounding of g
+    CHECK(fckl_forward_ex(&d, dh, dW_in, didx, dtl, dw01, loss, lse, mean, ws, ws_bytes, s) == FCKL_OK);
+    CHECK(fckl_backward_ex(&d, dh, dW_in, didx, dtl, dw01, lse, 1.0f, nullptr, dH, dW, ws, ws_bytes, s) == FCKL_OK);
+    fetch(l2, m2, gh2, gw2);
+    double wl = 0.0, ws_ = 0.0;
+    for (int64_t i = 0; i < N; ++i) {
+        wl += (double)w01[i] * l1[i];
+        ws_ += w01[i];
+    }
+    CHECK(std::fabs(m2[0] - wl / ws_) <= 1e-5 * std::fabs(m2[0]));
+    for (int64_t i = 0; i < N; i += 5)
+        for (int j = 0; j < H; ++j)
+            CHECK(gh2[i * H + j] == 0.0f);
+
+    // fckl_scale: dH of the plain pass doubled in place on the device, exactly
+    run_two_pass();
+    CHECK(fckl_scale(dH, (int64_t)N * H, two, s) == FCKL_OK);
+    fetch(l2, m2, gh2, gw2);
+    for (size_t q = 0; q < gh1.size(); ++q)
+        CHECK(gh2[q] == 2.0f * gh1[q]);
+
+    // the online teacher over the whole vocabulary: teacher = student gives zero loss;
+    // another teacher (a rescaled head) gives finite losses >= 0, the sum rule and the
+    // <dW, W> = <dH, h> identity
+    {
+        std::vector<uint16_t> Wt(W.size());
+        for (size_t q = 0; q < W.size(); ++q)
+            Wt[q] = to_bf16((float)(1.5 * from_bf16(W[q])));
+        uint16_t *dWt = dev_alloc<uint16_t>(Wt.size());
+        int32_t fchunk = 0;
+        size_t fws_bytes = 0;
+        CHECK(fckl_full_plan(&d, H, 0, &fchunk, &fws_bytes) == FCKL_OK && fchunk > 0);
+        void *fws = dev_alloc<char>(fws_bytes);
+        if (!dWt || !fws)
+            return 2;
+        HIP_OK(hipMemcpy(dWt, Wt.data(), Wt.size() * 2, hipMemcpyHostToDevice));
+        CHECK(fckl_full_forward_backward(&d, H, dh, dW_in, dh, dW_in, nullptr, 1.0f, loss, lse, mean, dH, dW, fws,
+                                         fws_bytes, s) == FCKL_OK);
+        fetch(l2, m2, gh2, gw2);
+        for (float x : l2)
+            CHECK(std::fabs(x) <= 1e-4);
+        CHECK(fckl_full_forward_backward(&d, H, dh, dW_in, dh, dWt, nullptr, 1.0f, loss, lse, mean, dH, dW, fws,
+                                         fws_bytes, s) == FCKL_OK);
+        fetch(l2, m2, gh2, gw2);
+        double fmax = 0.0;
+        for (float x : l2) {
+            CHECK(std::isfinite(x));
+            fmax = std::fmax(fmax, std::fabs(x));
+        }
+        CHECK(fmax > 1e-3);
+        for (float x : l2)
+            CHECK(x >= -1e-5 * fmax);
+        for (int j = 0; j < H; ++j) {
+            double sr = 0.0, ar = 0.0;
+            for (int v = 0; v < V; ++v) {
+                sr += gw2[(size_t)v * H + j];
+                ar += std::fabs(gw2[(size_t)v * H + j]);
+            }
+            CHECK(std::fabs(sr) <= 1e-3 * ar);
+        }
+        double fpw = 0.0, fph = 0.0;
+        for (size_t q = 0; q < W.size(); ++q)
+            fpw += gw2[q] * from_bf16(W[q]);
+        for (size_t q = 0; q < h.size(); ++q)
+            fph += gh2[q] * from_bf16(h[q]);
+        CHECK(std::fabs(fpw - fph) <= 2e-2 * std::fmax(std::fabs(fpw), std::fabs(fph)));
+        HIP_OK(hipFree(dWt));
+        HIP_OK(hipFree(fws));
+    }
+
+    // fckl_topk_async: the same cache as fckl_topk, bit for bit, and status FCKL_OK on the device
+    {
+        const uint32_t junk = 0xFFFFFFFFu;
+        HIP_OK(hipMemcpy(status, &junk, 4, hipMemcpyHostToDevice));
+        int32_t *ti2 = dev_alloc<int32_t>((size_t)N * K);
+        uint16_t *tv2 = dev_alloc<uint16_t>((size_t)N * K);
+        if (!ti2 || !tv2)
+            return 2;
+        CHECK(fckl_topk_async(&d, dh, dW_in, ti2, tv2, tws, tws_bytes, status, s) == FCKL_OK);
+        HIP_OK(hipStreamSynchronize(s));
+        uint32_t st = 0;
+        std::vector<int32_t> hi2((size_t)N * K);
+        std::vector<uint16_t> hv2((size_t)N * K);
+        HIP_OK(hipMemcpy(&st, status, 4, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(hi2.data(), ti2, hi2.size() * 4, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(hv2.data(), tv2, hv2.size() * 2, hipMemcpyDeviceToHost));
+        CHECK(st == (uint32_t)FCKL_OK && hi2 == hi && hv2 == hv);
+        HIP_OK(hipFree(ti2));
+        HIP_OK(hipFree(tv2));
+    }
+
     // argument errors come back as status codes, before any work
     CHECK(fckl_forward(&d, nullptr, dW_in, didx, dtl, loss, lse, mean, ws, ws_bytes, s) == FCKL_ERR_INVALID_ARG);
     CHECK(fckl_forward(&d, dh, dW_in, didx, dtl, loss, lse, mean, ws, 1024, s) == FCKL_ERR_WORKSPACE);
@@ -219,7 +333,8 @@ int main()
 
     HIP_OK(hipStreamDestroy(s));
     for (void *p : {(void *)dh, (void *)dW_in, (void *)dtl, (void *)didx, (void *)loss, (void *)lse, (void *)mean,
-                    (void *)dH, (void *)dW, ws, tws, (void *)ti, (void *)tv})
+                    (void *)dH, (void *)dW, ws, tws, (void *)ti, (void *)tv, (void *)dw1, (void *)dw01, (void *)two,
+                    (void *)status})
         HIP_OK(hipFree(p));
     if (failures) {
         std::fprintf(stderr, "%d checks failed\n", failures);
