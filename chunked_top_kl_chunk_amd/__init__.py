@@ -34,8 +34,9 @@ FLAG_VALIDATE, FLAG_DW_ACCUMULATE, FLAG_TOPK_FULL_FIRST_PASS = 1, 2, 4
 
 # Every symbol include/fckl.h declares.
 EXPORTS = ("fckl_plan", "fckl_workspace_size", "fckl_forward", "fckl_backward", "fckl_forward_ex",
-           "fckl_backward_ex", "fckl_forward_backward", "fckl_topk_workspace_size", "fckl_topk", "fckl_topk_async",
-           "fckl_full_plan", "fckl_full_forward_backward", "fckl_scale", "fckl_status_string", "fckl_version")
+           "fckl_backward_ex", "fckl_single_plan", "fckl_forward_backward", "fckl_topk_workspace_size", "fckl_topk",
+           "fckl_topk_async", "fckl_full_plan", "fckl_full_forward_backward", "fckl_scale", "fckl_status_string",
+           "fckl_version")
 
 
 KERNELS = ("prepare", "fwd_logits", "combine", "mean", "bwd_logits", "dh", "dh_reduce", "dw", "transpose",
@@ -76,6 +77,7 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     P, vp, sz = ctypes.POINTER, ctypes.c_void_p, ctypes.c_size_t
     lib.fckl_plan.argtypes = [P(Desc), sz, P(ctypes.c_int32), P(sz)]
+    lib.fckl_single_plan.argtypes = [P(Desc), sz, P(ctypes.c_int32), P(sz)]
     lib.fckl_workspace_size.argtypes = [P(Desc), ctypes.c_int32, P(sz)]
     lib.fckl_forward.argtypes = [P(Desc), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.fckl_backward.argtypes = [P(Desc), vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
@@ -94,8 +96,8 @@ def load() -> ctypes.CDLL:
     lib.fckl_full_forward_backward.argtypes = [P(Desc), ctypes.c_int32, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp,
                                                vp, vp, vp, vp, sz, vp]
     lib.fckl_scale.argtypes = [vp, ctypes.c_int64, vp, vp]
-    for f in ("fckl_plan", "fckl_workspace_size", "fckl_forward", "fckl_backward", "fckl_forward_ex",
-              "fckl_backward_ex", "fckl_forward_backward", "fckl_topk_workspace_size", "fckl_topk",
+    for f in ("fckl_plan", "fckl_single_plan", "fckl_workspace_size", "fckl_forward", "fckl_backward",
+              "fckl_forward_ex", "fckl_backward_ex", "fckl_forward_backward", "fckl_topk_workspace_size", "fckl_topk",
               "fckl_topk_async", "fckl_full_plan", "fckl_full_forward_backward", "fckl_scale"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
@@ -124,10 +126,37 @@ def _call(name: str, *args) -> None:
         raise FCKLError(st, name)
 
 
-def plan(desc: Desc, budget_bytes: int = 0) -> Tuple[int, int]:
-    """(tokens per chunk, workspace bytes) chosen by the library's chunk scheduler."""
+def device_budget(device=None) -> int:
+    """Default workspace budget for the chunk scheduler: a quarter of the device memory
+    that is free right now (torch.cuda.mem_get_info), so that the loss leaves most of
+    the card to the rest of the step.  On an idle MI355X that admits the scheduler's
+    largest chunk; on a nearly full one it shrinks the chunk instead of failing."""
+    import torch
+    free, _ = torch.cuda.mem_get_info(device)
+    return max(int(free) // 4, 1)
+
+
+def plan(desc: Desc, budget_bytes: Optional[int] = None, device=None) -> Tuple[int, int]:
+    """(tokens per chunk, workspace bytes) chosen by the library's chunk scheduler for
+    fckl_forward / fckl_backward.  budget_bytes None: device_budget(device); 0: the
+    library's own default (12 GiB)."""
+    load()      # a missing library fails first, before any device query
+    if budget_bytes is None:
+        budget_bytes = device_budget(device)
     c, ws = ctypes.c_int32(0), ctypes.c_size_t(0)
     _call("fckl_plan", ctypes.byref(desc), ctypes.c_size_t(budget_bytes), ctypes.byref(c), ctypes.byref(ws))
+    return int(c.value), int(ws.value)
+
+
+def single_plan(desc: Desc, budget_bytes: Optional[int] = None, device=None) -> Tuple[int, int]:
+    """The same for fckl_forward_backward, whose workspace also holds the kept
+    exponentials of the chunk (fckl_single_plan).  With desc.chunk > 0 that chunk is
+    kept and its workspace size returned."""
+    load()      # a missing library fails first, before any device query
+    if budget_bytes is None:
+        budget_bytes = device_budget(device)
+    c, ws = ctypes.c_int32(0), ctypes.c_size_t(0)
+    _call("fckl_single_plan", ctypes.byref(desc), ctypes.c_size_t(budget_bytes), ctypes.byref(c), ctypes.byref(ws))
     return int(c.value), int(ws.value)
 
 
@@ -184,11 +213,12 @@ def _out(t, shape, device, name):
     return t
 
 
-def _workspace(desc: Desc, ws, device):
+def _workspace(desc: Desc, ws, device, single: bool = False):
     import torch
-    if desc.chunk == 0:
-        chunk, need = plan(desc)
-        desc.chunk = chunk
+    if single:
+        desc.chunk, need = single_plan(desc, None, device)
+    elif desc.chunk == 0:
+        desc.chunk, need = plan(desc, None, device)
     else:
         need = workspace_size(desc, desc.chunk)
     if ws is None:
@@ -278,7 +308,7 @@ def forward_backward(h, W, topk_idx, topk_logit, T: float = 1.0, grad_scale: flo
     dev = h.device
     flags = (FLAG_VALIDATE if validate else 0) | (FLAG_DW_ACCUMULATE if accumulate else 0)
     desc = desc_for(h, W, topk_idx, topk_logit, T, chunk, flags, profile)
-    ws = _workspace(desc, ws, dev)
+    ws = _workspace(desc, ws, dev, single=True)
     N = h.shape[0]
     weights = _weights(weights, N, dev)
     loss_tok = _out(loss_tok, (N,), dev, "loss_tok")
@@ -369,7 +399,7 @@ def full_forward_backward(h, W, h_t, W_t, T: float = 1.0, grad_scale: float = 1.
     dev = h.device
     flags = FLAG_DW_ACCUMULATE if accumulate else 0
     desc = make_desc(N, H, V, 1, T, chunk, DTYPE_BF16, flags, profile)
-    desc.chunk, need = full_plan(desc, Ht, budget_bytes)
+    desc.chunk, need = full_plan(desc, Ht, budget_bytes if budget_bytes else device_budget(dev))
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     if ws.numel() * ws.element_size() < need or not ws.is_contiguous():
@@ -400,5 +430,6 @@ def scale_(x, scale, stream=None):
     return x
 
 
-__all__ = ["Desc", "Profile", "KERNELS", "FCKLError", "load", "plan", "workspace_size", "forward", "backward",
+__all__ = ["Desc", "Profile", "KERNELS", "FCKLError", "load", "plan", "single_plan", "device_budget",
+           "workspace_size", "forward", "backward",
            "forward_backward", "topk", "topk_workspace_size", "full_plan", "full_forward_backward", "scale_", "make_desc", "desc_for", "status_string", "version", "EXPORTS", "LIB_PATH"]

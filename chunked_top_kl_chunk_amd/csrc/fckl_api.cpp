@@ -13,7 +13,7 @@ namespace {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 fckl_status common_checks(const fckl_desc *d, const void *h, const void *W, const int32_t *idx, const void *tl,
-                          void *ws, size_t ws_bytes, Layout *L)
+                          void *ws, size_t ws_bytes, Layout *L, bool keep = false)
 {
     fckl_status st = check_desc(d);
     if (st != FCKL_OK)
@@ -23,7 +23,7 @@ fckl_status common_checks(const fckl_desc *d, const void *h, const void *W, cons
     if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || (reinterpret_cast<uintptr_t>(h) & 15u) != 0 ||
         (reinterpret_cast<uintptr_t>(W) & 15u) != 0)
         return FCKL_ERR_INVALID_ARG;
-    st = plan_chunk(d, ws_bytes, L);
+    st = plan_chunk(d, ws_bytes, L, keep);
     if (st != FCKL_OK)
         return st;
     if (L->total > ws_bytes)
@@ -261,6 +261,19 @@ fckl_status fckl_plan(const fckl_desc *desc, size_t budget_bytes, int32_t *chunk
     return FCKL_OK;
 }
 
+fckl_status fckl_single_plan(const fckl_desc *desc, size_t budget_bytes, int32_t *chunk_out, size_t *ws_bytes_out)
+{
+    Layout L;
+    fckl_status st = plan_chunk(desc, budget_bytes, &L, true);
+    if (st != FCKL_OK)
+        return st;
+    if (chunk_out)
+        *chunk_out = L.C;
+    if (ws_bytes_out)
+        *ws_bytes_out = L.total;
+    return FCKL_OK;
+}
+
 fckl_status fckl_workspace_size(const fckl_desc *desc, int32_t chunk, size_t *ws_bytes_out)
 {
     Layout L;
@@ -309,7 +322,7 @@ fckl_status fckl_forward_backward(const fckl_desc *desc, const void *h, const vo
                                   size_t ws_bytes, void *stream)
 {
     Layout L;
-    fckl_status st = common_checks(desc, h, W, topk_idx, topk_logit, ws, ws_bytes, &L);
+    fckl_status st = common_checks(desc, h, W, topk_idx, topk_logit, ws, ws_bytes, &L, true);
     if (st != FCKL_OK)
         return st;
     if (!loss_tok || !lse || !dH || !dW || !aligned16(dH))
@@ -576,6 +589,6 @@ const char *fckl_status_string(fckl_status s)
     return "unknown status";
 }
 
-int32_t fckl_version(void) { return 200; }
+int32_t fckl_version(void) { return 300; }
 
 }  // extern "C"

@@ -28,8 +28,9 @@ constexpr int32_t kMaxChunk = 8192;
 constexpr size_t kDefaultBudget = size_t(12) << 30;  // 12 GiB of the 288 GB HBM3E
 
 // Kernel limits.  The GEMM operand loaders keep each lane's offset inside a 256-row
-// tile in 32 bits (up to 255 rows of the operand's pitch), and the pitch of g and W^T is
-// Vpad, that of g^T and h^T the padded chunk: both at most kMaxPitch elements.  A
+// tile in 32 bits (up to 255 rows of the operand's pitch; the transposed g^T operand of
+// dH spans 64 rows of a k-step), and the pitch of W^T is Vpad, that of g^T and h^T the
+// padded chunk: both at most kMaxPitch elements.  A
 // non-persistent GEMM launches one 512-thread work-group per 256 x 256 output tile, and
 // HIP counts a grid dimension in 32-bit work-items: at most kMaxTiles tiles.  The dH
 // split reduce runs one thread per 4 elements of a chunk's dH: at most kMaxChunkElems
@@ -39,8 +40,10 @@ constexpr int64_t kMaxTiles = (int64_t(1) << 23) - 1;
 constexpr int64_t kMaxChunkElems = int64_t(1) << 33;
 
 // Where each per-chunk buffer lives inside the caller's workspace.  Every buffer is
-// sized by the chunk, never by N.
+// sized by the chunk, never by N.  `keep` layouts (the single call and the full-teacher
+// variant, whose forward product keeps its exponentials) add off_mw and off_ex.
 struct Layout {
+    bool keep = false;
     int32_t C = 0;          // tokens per chunk
     int32_t Cpad = 0;       // C rounded up to kTokenTile
     int32_t nVt = 0;        // vocabulary tiles: ceil(V / kVocabTile)
@@ -55,10 +58,11 @@ struct Layout {
     size_t off_cnt = 0;     // u8    [Cpad, cnt_stride] entries below each vocabulary tile start
     size_t off_part = 0;    // f32x2 [nVt, Cpad] per-tile (max, sum exp) of z/T, base 2
     size_t off_mw = 0;      // f32   [2 nVt, Cpad] max of z/T (base 2) per 128-row half tile,
-                            //       kept by the single-call path with the exponentials
+                            //       kept with the exponentials (keep layouts only)
     size_t off_wsum = 0;    // f32   [2]         sum of the token weights and its inverse
-    size_t off_g = 0;       // bf16  [Cpad, Vpad] chunk gradient w.r.t. the logits
-    size_t off_gT = 0;      // bf16  [Vpad, Cpad] the same, transposed (dW operand)
+    size_t off_ex = 0;      // bf16  [Cpad, Vpad] kept 2^(z/T log2 e - m) (keep layouts only)
+    size_t off_gT = 0;      // bf16  [Vpad, Cpad] chunk gradient w.r.t. the logits, vocabulary-major
+                            //       (the operand of both the dH and the dW product)
     size_t off_hT = 0;      // bf16  [H, Cpad]    chunk hidden states, transposed (dW operand)
     size_t off_WT = 0;      // bf16  [H, Vpad]    LM head, transposed (dH operand)
     size_t off_dhp = 0;     // f32   [dh_splits, Cpad, H] split partial sums of dH
@@ -97,8 +101,8 @@ fckl_status check_desc(const fckl_desc *d);
 fckl_status make_topk_layout(const fckl_desc *d, int32_t chunk, TopkLayout *L);
 fckl_status make_full_layout(const fckl_desc *d, int32_t Ht, int32_t chunk, FullLayout *L);
 fckl_status plan_full_chunk(const fckl_desc *d, int32_t Ht, size_t budget, FullLayout *L);
-fckl_status make_layout(const fckl_desc *d, int32_t chunk, Layout *L);
-fckl_status plan_chunk(const fckl_desc *d, size_t budget, Layout *L);
+fckl_status make_layout(const fckl_desc *d, int32_t chunk, Layout *L, bool keep = false);
+fckl_status plan_chunk(const fckl_desc *d, size_t budget, Layout *L, bool keep = false);
 
 // ------------------------------------------------------------------ launchers
 // All return hipSuccess (0) or the launch error; they never synchronise.
@@ -129,8 +133,8 @@ struct GradScale {
 // `gs` != NULL: the teacher probabilities and their sum are stored multiplied by the
 // token's gradient scale (the backward pass uses them only in that form).
 int launch_prepare(const ChunkArgs &a, bool validate, void *stream, const GradScale *gs = nullptr);
-// keep_exp: also write 2^(z/T log2 e - m) in bf16 over the chunk's gradient buffer and
-// the half-tile maxima m (single-call path).
+// keep_exp: also write 2^(z/T log2 e - m) in bf16 to the kept-exponential buffer and
+// the half-tile maxima m (single-call path; a keep layout).
 int launch_forward_logits(const ChunkArgs &a, void *stream, bool keep_exp = false);
 int launch_combine(const ChunkArgs &a, float *loss_tok, float *lse, void *stream);
 int launch_mean(const float *loss_tok, int64_t N, float *loss_mean, void *stream);

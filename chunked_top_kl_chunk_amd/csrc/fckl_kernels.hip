@@ -15,16 +15,18 @@
 //   backward_logits  the same MFMA tiles recompute z (the extra projection in the
 //                    backward pass that the chunked loss pays for, axbrief.com);
 //                    the epilogue forms g = c((sum p) softmax(z/T) - scatter(p, idx)),
-//                    rounds it to bf16 and writes the chunk's g twice: [C, V] for the
-//                    dH product and [V, C] for the dW product
-//   dh               dH_chunk = g . W   (split over the vocabulary, fixed-order reduce)
+//                    rounds it to bf16 and writes the chunk's g once, vocabulary-major
+//                    g^T [V, C], the operand of both products below
+//   dh               dH_chunk^T = W^T . g^T over the vocabulary (g^T read through
+//                    transposing LDS reads; split over the vocabulary, fixed-order reduce)
 //   dw               dW += g^T . h_chunk (fp32 read-modify-write, chunk after chunk)
 //   transpose        W -> W^T once per backward call, h_chunk -> h_chunk^T per chunk
 //
 // GEMM core: 256 x 256 tiles, 512 threads = 8 wave64s, each wave owns a 128 x 64 block
-// of v_mfma_f32_32x32x16_bf16 accumulators.  Every operand
-// is read k-major (contiguous along the reduction), which is why the backward products
-// use W^T, h_chunk^T and the second layout of g.  Each lane's 16-byte piece goes from
+// of v_mfma_f32_32x32x16_bf16 accumulators.  Operands are read k-major (contiguous
+// along the reduction), which is why the backward products use W^T and h_chunk^T; the
+// one exception is g^T in the dH product, whose fragments come from gfx950's transposing
+// LDS reads.  Each lane's 16-byte piece goes from
 // global memory straight into LDS (global_load_lds_dwordx4, no register staging); two
 // LDS stages of 64-deep k-steps, one barrier per step, and an XOR swizzle of the
 // 16-byte chunks that keeps the MFMA operand reads free of bank conflicts.
@@ -226,6 +228,72 @@ struct KTile {
     }
 };
 
+// Operand tile whose n dimension is contiguous in memory, B(n, k) = src[k * ld + n]:
+// BKK rows of k, each COLS elements of n, copied as they lie (16-byte pieces of n).
+// The MFMA wants 8 consecutive k per lane, so the fragment is read with two gfx950
+// transposing reads (ds_read_b64_tr_b16): in a group of 16 lanes, lane l addresses
+// the 4 elements of row k + l/4 at columns n + 4 (l % 4), and every lane receives the
+// 4 rows k .. k+3 of column n + l.  Half a wave (two groups) reads 4 rows x 4
+// consecutive 16-byte chunks; the chunk index is XOR-swizzled by 4 (row % 4) so those
+// 16 chunks fall on 16 different bank groups.
+template <int COLS, int BKK, int NT>
+struct KTileT {
+    static constexpr int CPR = COLS / 8;         // 16-byte chunks per k-row
+    static constexpr int RB = COLS * 2;          // bytes per k-row
+    static constexpr int CHUNKS = BKK * CPR;
+    static_assert(CHUNKS % NT == 0, "whole wave instructions");
+    static_assert(CPR % 16 == 0, "rows of at least 16 chunks");
+    static constexpr int PER = CHUNKS / NT;
+    static constexpr int BYTES = CHUNKS * 16;
+    static constexpr int RSTRIDE = NT / CPR;     // k-rows between a lane's pieces
+    static_assert(RSTRIDE % 4 == 0, "swizzle invariant across pieces");
+    __device__ __forceinline__ static int sw(int krow) { return (krow & 3) << 2; }
+
+    struct Src {
+        const uint16_t *base;   // row k of the current slice, column n0
+        uint32_t off0;          // element offset of piece 0 from base
+        uint32_t step;          // element offset between pieces (RSTRIDE rows)
+        int krow0;              // k-row of piece 0 within the slice
+        bool nok;               // the lane's 8 columns start inside the operand
+    };
+    __device__ __forceinline__ static void init(Src &s, const uint16_t *base, int64_t ld, int n0, int n_valid,
+                                                int k_begin)
+    {
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        s.base = base + (int64_t)k_begin * ld + n0;
+        const int slot = wave * 64 + lane;
+        s.krow0 = slot / CPR;
+        const int gc = (slot % CPR) ^ sw(s.krow0);
+        s.off0 = (uint32_t)(s.krow0 * ld + 8 * gc);
+        s.step = (uint32_t)(RSTRIDE * ld);
+        s.nok = n0 + 8 * gc < n_valid;
+    }
+    __device__ __forceinline__ static void issue_one(const Src &s, int i, int k0, int k_valid, char *tile)
+    {
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const bool ok = s.nok && k0 + s.krow0 + RSTRIDE * i < k_valid;
+        const void *src = ok ? static_cast<const void *>(s.base + s.off0 + (uint32_t)i * s.step)
+                             : static_cast<const void *>(kZeroPage);
+        copy16_to_lds(src, tile + (i * (NT / 64) + wave) * 1024);
+    }
+    __device__ __forceinline__ static void advance(Src &s, int64_t ld) { s.base += (int64_t)BKK * ld; }
+    // The MFMA operand of one lane for the 32 columns starting at nb and the 16 k-rows
+    // starting at 16 ks: column nb + lane % 32, rows 16 ks + 8 (lane / 32) + 0..7.
+    __device__ __forceinline__ static bf16x8 frag(const char *tile, int nb, int ks, int lane)
+    {
+        const int gl = lane & 15, grp = lane >> 4;
+        const int n = nb + 16 * (grp & 1) + 4 * (gl & 3);
+        const int k = ks * 16 + 8 * (grp >> 1) + (gl >> 2);
+        const char *a = tile + k * RB + (((n >> 3) ^ sw(k)) << 4) + (n & 7) * 2;
+        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a + 4 * RB));
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(bf16x8, v);
+    }
+};
+
 // C[m, n] = sum_k A(m, k) * B(n, k) for one BM x BN tile, operands streamed
 // global -> LDS by the DMA path with S stages in flight (no staging registers).
 // Both operands k-major: A(m,k) = A[m*lda + k], B(n,k) = B[n*ldb + k].
@@ -233,7 +301,7 @@ struct NoHook {
     __device__ __forceinline__ void operator()() const {}
 };
 
-template <int BM_, int BN_, int WM_, int WN_, int BKK, int S>
+template <int BM_, int BN_, int WM_, int WN_, int BKK, int S, bool SPREAD = false, bool BTR = false>
 struct GemmD {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BKK;
     static constexpr int NT = WM * WN * 64;
@@ -241,7 +309,7 @@ struct GemmD {
     static constexpr int MB = WTM / 32, NB = WTN / 32;
     static_assert(MB * 32 == WTM && NB * 32 == WTN, "wave tile");
     using AT = KTile<BM, BKK, NT>;
-    using BT = KTile<BN, BKK, NT>;
+    using BT = std::conditional_t<BTR, KTileT<BN, BKK, NT>, KTile<BN, BKK, NT>>;
     static constexpr int STAGE = AT::BYTES + BT::BYTES;
     static constexpr int LDS_BYTES = S * STAGE;
     static constexpr int L = AT::PER + BT::PER;     // DMA loads per thread per k-step
@@ -251,29 +319,53 @@ struct GemmD {
     {
         return wm * WTM + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
     }
-    __device__ __forceinline__ static int col_of(int wn, int nb, int lane) { return wn * WTN + nb * 32 + (lane & 31); }
+    // SPREAD: the 32-column fragment blocks of the waves interleave (block nb of wave wn
+    // is block nb * WN + wn) and wm varies fastest over the waves, whose SIMD is wave % 4.
+    // A tile whose last columns are past the operand's end then leaves its live column
+    // blocks spread over all four SIMDs, and run<.., true> skips the dead blocks' MFMAs.
+    __device__ __forceinline__ static int col_of(int wn, int nb, int lane)
+    {
+        return SPREAD ? (nb * WN + wn) * 32 + (lane & 31) : wn * WTN + nb * 32 + (lane & 31);
+    }
+    __device__ __forceinline__ static int wm_of(int wave) { return SPREAD ? wave % WM : wave / WN; }
+    __device__ __forceinline__ static int wn_of(int wave) { return SPREAD ? wave / WM : wave % WN; }
 
     struct Frags {
         bf16x8 a[MB], b[NB];
     };
 
-    __device__ __forceinline__ static void load_frags(const char *stage, int ks, int wm, int wn, int lane, Frags &f)
+    // ilive / jlive: bit i (j) set when fragment row block i (column block j) of the wave
+    // holds live rows (columns); only looked at when TAIL.
+    template <bool TAIL = false>
+    __device__ __forceinline__ static void load_frags(const char *stage, int ks, int wm, int wn, int lane, Frags &f,
+                                                      uint32_t ilive = ~0u, uint32_t jlive = ~0u)
     {
 #pragma unroll
         for (int i = 0; i < MB; ++i)
-            f.a[i] = AT::frag(stage, wm * WTM + i * 32 + (lane & 31), ks * 2 + (lane >> 5));
+            if (!TAIL || ((ilive >> i) & 1u))
+                f.a[i] = AT::frag(stage, wm * WTM + i * 32 + (lane & 31), ks * 2 + (lane >> 5));
 #pragma unroll
         for (int j = 0; j < NB; ++j)
-            f.b[j] = BT::frag(stage + AT::BYTES, wn * WTN + j * 32 + (lane & 31), ks * 2 + (lane >> 5));
+            if (!TAIL || ((jlive >> j) & 1u)) {
+                if constexpr (BTR)
+                    f.b[j] = BT::frag(stage + AT::BYTES, col_of(wn, j, 0), ks, lane);
+                else
+                    f.b[j] = BT::frag(stage + AT::BYTES, col_of(wn, j, lane), ks * 2 + (lane >> 5));
+            }
     }
 
-    __device__ __forceinline__ static void mma(const Frags &f, f32x16 (&acc)[MB][NB])
+    template <bool TAIL = false>
+    __device__ __forceinline__ static void mma(const Frags &f, f32x16 (&acc)[MB][NB], uint32_t ilive = ~0u,
+                                               uint32_t jlive = ~0u)
     {
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
+        for (int j = 0; j < NB; ++j)
+            if (!TAIL || ((jlive >> j) & 1u)) {
 #pragma unroll
-            for (int j = 0; j < NB; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+                for (int i = 0; i < MB; ++i)
+                    if (!TAIL || ((ilive >> i) & 1u))
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+            }
     }
 
     // DS-read instructions per fragment set (one ds_read_b128 per fragment).
@@ -313,13 +405,31 @@ struct GemmD {
     // which keeps the wait counts uniform.  `hook` runs once, right after the first
     // stage has landed: loads it issues are older than every k-step load, so the first
     // step's wait covers them.
-    template <class Hook = NoHook>
+    // TAIL: the tile's rows or columns end inside it (m_valid < m0 + BM or n_valid <
+    // n0 + BN); fragment blocks wholly past them are neither read nor multiplied (their
+    // accumulators stay 0).
+    template <class Hook = NoHook, bool TAIL = false>
     __device__ static void run(char *smem, const uint16_t *A, int64_t lda, int m0, int m_valid, int ka_valid,
                                const uint16_t *B, int64_t ldb, int n0, int n_valid, int kb_valid, int k_begin,
                                int k_end, f32x16 (&acc)[MB][NB], const Hook &hook = Hook())
     {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-        const int wm = wave / WN, wn = wave % WN;
+        const int wm = wm_of(wave), wn = wn_of(wave);
+        uint32_t ilive = ~0u, jlive = ~0u;
+        if constexpr (TAIL) {
+            const int live_cols = n_valid - n0, live_rows = m_valid - m0;
+            ilive = jlive = 0u;
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+                if (wm * WTM + i * 32 < live_rows)
+                    ilive |= 1u << i;
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                if (col_of(wn, j, 0) < live_cols)
+                    jlive |= 1u << j;
+            ilive = __builtin_amdgcn_readfirstlane(ilive);
+            jlive = __builtin_amdgcn_readfirstlane(jlive);
+        }
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -363,7 +473,7 @@ struct GemmD {
         __builtin_amdgcn_s_barrier();
         hook();
         Frags f, fn;
-        load_frags(smem, 0, wm, wn, lane, f);
+        load_frags<TAIL>(smem, 0, wm, wn, lane, f, ilive, jlive);
         auto step = [&](int kb, auto last_c) {
             constexpr bool last = decltype(last_c)::value;
             const char *cur = smem + (kb % S) * STAGE;
@@ -375,26 +485,91 @@ struct GemmD {
                 if constexpr (lo < hi)
                     issue(next, std::integral_constant<int, lo>{}, std::integral_constant<int, hi>{});
                 if constexpr (ss + 1 < SUB) {
-                    load_frags(cur, ss + 1, wm, wn, lane, fn);
-                    mma(f, acc);
-                    interleave<DS_PER_SUB, hi - lo>();
+                    load_frags<TAIL>(cur, ss + 1, wm, wn, lane, fn, ilive, jlive);
+                    mma<TAIL>(f, acc, ilive, jlive);
+                    if constexpr (!TAIL)
+                        interleave<DS_PER_SUB, hi - lo>();
                     f = fn;
                 } else if constexpr (!last) {
                     wait_vmcnt<(S - 2) * L>();
                     wait_lgkmcnt0();
                     __builtin_amdgcn_s_barrier();
-                    load_frags(smem + ((kb + 1) % S) * STAGE, 0, wm, wn, lane, fn);
-                    mma(f, acc);
-                    interleave<DS_PER_SUB, 0>();
+                    load_frags<TAIL>(smem + ((kb + 1) % S) * STAGE, 0, wm, wn, lane, fn, ilive, jlive);
+                    mma<TAIL>(f, acc, ilive, jlive);
+                    if constexpr (!TAIL)
+                        interleave<DS_PER_SUB, 0>();
                     f = fn;
                 } else {
-                    mma(f, acc);
+                    mma<TAIL>(f, acc, ilive, jlive);
                 }
             });
         };
-        for (int kb = 0; kb + 1 < nk; ++kb)
-            step(kb, std::false_type{});
-        step(nk - 1, std::true_type{});
+        if constexpr (!BTR) {
+            for (int kb = 0; kb + 1 < nk; ++kb)
+                step(kb, std::false_type{});
+            step(nk - 1, std::true_type{});
+        } else {
+            // Transposing reads of B.  They may not overlap a global -> LDS copy in flight
+            // (the compiler waits for every copy before such a read), so all B fragments
+            // of a k-step are read right after its barrier, when no copy is in flight, and
+            // the next step's copies are issued after them.
+            bf16x8 bq[SUB][NB];
+            auto load_b = [&](const char *stage) {
+                static_for<SUB>([&](auto kc) {
+#pragma unroll
+                    for (int j = 0; j < NB; ++j)
+                        if (!TAIL || ((jlive >> j) & 1u))
+                            bq[decltype(kc)::value][j] = BT::frag(stage + AT::BYTES, col_of(wn, j, 0), decltype(kc)::value, lane);
+                });
+            };
+            auto load_a = [&](const char *stage, int ks, Frags &g) {
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+                    if (!TAIL || ((ilive >> i) & 1u))
+                        g.a[i] = AT::frag(stage, wm * WTM + i * 32 + (lane & 31), ks * 2 + (lane >> 5));
+            };
+            load_b(smem);
+            auto stepT = [&](int kb, auto last_c) {
+                constexpr bool last = decltype(last_c)::value;
+                const char *cur = smem + (kb % S) * STAGE;
+                const int next = kb + S - 1;
+                static_for<SUB>([&](auto ssc) {
+                    constexpr int ss = decltype(ssc)::value;
+                    constexpr int lo = ss * P < L ? ss * P : L;
+                    constexpr int hi = (ss + 1) * P < L ? (ss + 1) * P : L;
+                    if constexpr (lo < hi)
+                        issue(next, std::integral_constant<int, lo>{}, std::integral_constant<int, hi>{});
+#pragma unroll
+                    for (int j = 0; j < NB; ++j)
+                        f.b[j] = bq[ss][j];
+                    if constexpr (ss + 1 < SUB) {
+                        load_a(cur, ss + 1, fn);
+                        mma<TAIL>(f, acc, ilive, jlive);
+                        if constexpr (!TAIL)
+                            interleave<MB, hi - lo>();
+#pragma unroll
+                        for (int i = 0; i < MB; ++i)
+                            f.a[i] = fn.a[i];
+                    } else if constexpr (!last) {
+                        wait_vmcnt<(S - 2) * L>();
+                        wait_lgkmcnt0();
+                        __builtin_amdgcn_s_barrier();
+                        const char *nst = smem + ((kb + 1) % S) * STAGE;
+                        load_b(nst);
+                        load_a(nst, 0, fn);
+                        mma<TAIL>(f, acc, ilive, jlive);
+#pragma unroll
+                        for (int i = 0; i < MB; ++i)
+                            f.a[i] = fn.a[i];
+                    } else {
+                        mma<TAIL>(f, acc, ilive, jlive);
+                    }
+                });
+            };
+            for (int kb = 0; kb + 1 < nk; ++kb)
+                stepT(kb, std::false_type{});
+            stepT(nk - 1, std::true_type{});
+        }
         // every wave is done reading LDS (and no load is in flight) before the caller reuses it
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -639,11 +814,33 @@ __device__ __forceinline__ void store_vocab_major(const char *smem, uint16_t *ds
 // 16-byte stores.  The staged tile stays in LDS for the caller; LDS must be free on
 // entry (every wave past its last read of the previous contents).
 template <class G>
+__device__ __forceinline__ void stage_token_major(const f32x16 (&acc)[G::MB][G::NB], char *smem)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = G::wm_of(wave), wn = G::wn_of(wave);
+#pragma unroll
+    for (int j = 0; j < G::NB; ++j) {
+        const int nl = G::col_of(wn, j, lane);
+#pragma unroll
+        for (int i = 0; i < G::MB; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int ml = G::row_of(wm, i, 4 * q, lane);
+                u32x2 pk;
+                pk[0] = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
+                pk[1] = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                *reinterpret_cast<u32x2 *>(smem + nl * kGStagePitch + ml * 2) = pk;
+            }
+    }
+    __syncthreads();
+}
+
+template <class G>
 __device__ __forceinline__ void store_token_major(const f32x16 (&acc)[G::MB][G::NB], char *smem, uint16_t *dst,
                                                   size_t pitch, int m0, int n0)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave / G::WN, wn = wave % G::WN;
+    const int wm = G::wm_of(wave), wn = G::wn_of(wave);
 #pragma unroll
     for (int j = 0; j < G::NB; ++j) {
         const int nl = G::col_of(wn, j, lane);
@@ -700,7 +897,7 @@ __device__ __forceinline__ void forward_tile(const FwdParams &p, char *smem, int
     map_tile(t, p.nVt, p.nNt, 4, tm, tn);
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave / G::WN, wn = wave % G::WN;
+    const int wm = G::wm_of(wave), wn = G::wn_of(wave);
     char *pre = smem + kLogitLds;
     EntryPrefetch pf;
     pf.init(p.cnt, p.cnt_stride, tm, n0, p.rows, p.K, p.idx_s, nullptr);
@@ -931,7 +1128,6 @@ struct BwdParams {
     const int32_t *idx_s;
     const float *p_s, *psum;    // stored times each token's gradient scale
     const uint8_t *cnt;
-    uint16_t *g;            // [Cpad, Vpad] bf16
     uint16_t *gT;           // [Vpad, Cpad] bf16
 };
 
@@ -942,7 +1138,7 @@ __device__ __forceinline__ void backward_tile(const BwdParams &p, char *smem, in
     map_tile(t, p.nVt, p.nNt, 4, tm, tn);
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave / G::WN, wn = wave % G::WN;
+    const int wm = G::wm_of(wave), wn = G::wn_of(wave);
     char *pre = smem + kLogitLds;
     EntryPrefetch pf;
     pf.init(p.cnt, p.cnt_stride, tm, n0, p.rows, p.K, p.idx_s, p.p_s);
@@ -1004,9 +1200,9 @@ __device__ __forceinline__ void backward_tile(const BwdParams &p, char *smem, in
             }
         }
     }
-    // Both layouts of the bf16 tile: [token][vocab] for the dH product, [vocab][token] for
-    // the dW product.  (The main loop ended with a barrier, so the operand buffers are free.)
-    store_token_major<G>(acc, smem, p.g, (size_t)p.Vpad, m0, n0);
+    // The bf16 tile, [vocab][token], the operand of both the dH and the dW product.  (The
+    // main loop ended with a barrier, so the operand buffers are free.)
+    stage_token_major<G>(acc, smem);
     store_vocab_major<G::BN, G::NT / 64>(smem, p.gT, (size_t)p.Cpad, m0, n0);
 }
 
@@ -1022,7 +1218,7 @@ __global__ __launch_bounds__(LogitGemm::NT) void backward_logits_kernel(BwdParam
 // ------------------------------------------------------------------ single-call gradient
 
 struct SoftGradParams {
-    uint16_t *ex;           // [Cpad, Vpad] bf16: the kept 2^(z/T log2 e - m); overwritten with g
+    const uint16_t *ex;     // [Cpad, Vpad] bf16: the kept 2^(z/T log2 e - m)
     uint16_t *gT;           // [Vpad, Cpad] bf16 out
     const float *mw;        // [2 nVt, Cpad] the half-tile maxima m (base 2)
     const float *lse;       // chunk's first token (natural log, z/T units)
@@ -1040,10 +1236,10 @@ struct SoftGradParams {
 constexpr int kSgTok = 128;       // tokens per block of the gradient kernel
 constexpr int kSgThreads = 512;   // its threads: 32 per token row, kSgThreads / 32 rows at a time
 
-// One block per (256-row vocabulary tile, 64 tokens).  With c the token's gradient scale:
+// One block per (256-row vocabulary tile, kSgTok tokens).  With c the token's gradient scale:
 //   g = c ((sum p) 2^(z/T log2 e - lse log2 e) - scatter(p, idx))
 //     = c ((sum p) E 2^(m - lse log2 e) - scatter(p, idx)),   E the kept value,
-// rounded to bf16, written over E ([token][vocab]) and, through LDS, as g^T.
+// rounded to bf16, staged [token][vocab] in LDS and written as g^T.
 __global__ __launch_bounds__(kSgThreads) void softmax_grad_kernel(SoftGradParams p)
 {
     __shared__ __attribute__((aligned(16))) char smem[kSgTok * kGStagePitch];
@@ -1053,8 +1249,7 @@ __global__ __launch_bounds__(kSgThreads) void softmax_grad_kernel(SoftGradParams
     const int c = threadIdx.x & 31;     // 16-byte piece of the tile row
     const int half = c >> 4;            // its 128-row half of the vocabulary tile
     const int r0 = threadIdx.x >> 5;
-    // Every load first: the pieces are rewritten in place below, and loads placed after
-    // those stores would each wait for them.  Rows past the chunk read row 0.
+    // Every load first, so that they are in flight together.  Rows past the chunk read row 0.
     u32x4 e[kRows];
     float f[kRows], gsc[kRows];
     int ks[kRows], ke[kRows];
@@ -1095,7 +1290,6 @@ __global__ __launch_bounds__(kSgThreads) void softmax_grad_kernel(SoftGradParams
             for (int q = 0; q < 4; ++q)
                 out[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
         }
-        *reinterpret_cast<u32x4 *>(p.ex + (size_t)tok * p.Vpad + m0 + 8 * c) = out;
         *reinterpret_cast<u32x4 *>(smem + rl * kGStagePitch + 16 * c) = out;
     }
     __syncthreads();
@@ -1137,7 +1331,7 @@ __device__ __forceinline__ void full_teacher_tile(const FullTeacherParams &p, ch
     map_tile(t, p.nVt, p.nNt, 4, tm, tn);
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave / G::WN, wn = wave % G::WN;
+    const int wm = G::wm_of(wave), wn = G::wn_of(wave);
     f32x16 acc[G::MB][G::NB];
     G::run(smem, p.W, p.H, m0, p.V, p.H, p.h, p.H, n0, p.rows, p.H, 0, p.H, acc);
     const int lim = p.V - m0 - G::row_of(wm, 0, 0, lane);
@@ -1212,7 +1406,7 @@ __device__ __forceinline__ void full_student_tile(const FullStudentParams &p, ch
     map_tile(t, p.nVt, p.nNt, 4, tm, tn);
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave / G::WN, wn = wave % G::WN;
+    const int wm = G::wm_of(wave), wn = G::wn_of(wave);
     float lt[G::NB];
 #pragma unroll
     for (int j = 0; j < G::NB; ++j) {
@@ -1332,7 +1526,7 @@ __global__ __launch_bounds__(256) void full_combine_kernel(const float2 *part, c
 }
 
 struct FullGradParams {
-    uint16_t *ex;           // [Cpad, Vpad] the student's kept exponentials; overwritten with g
+    const uint16_t *ex;     // [Cpad, Vpad] the student's kept exponentials
     uint16_t *gT;           // [Vpad, Cpad] out
     const float *at;        // a_t in fragment order (at_frag)
     const float *mw;        // [2 nVt, Cpad]
@@ -1348,7 +1542,7 @@ struct FullGradParams {
 // wave held them, so that each lane has one token.  The student's kept values are staged
 // [token][vocab] in LDS; each lane forms, for its 64 values,
 //   g = c (E 2^(m - L_s) - 2^(a_t - L_t)),
-// writes them back into the staged tile, whose rows (g) and columns (g^T) are then written.
+// writes them back into the staged tile, whose columns are then written as g^T.
 __global__ __launch_bounds__(256) void full_grad_kernel(FullGradParams p)
 {
     using G = LogitGemm;
@@ -1395,11 +1589,6 @@ __global__ __launch_bounds__(256) void full_grad_kernel(FullGradParams p)
         cell[1] = pack_bf16x2(g[2], g[3]);
     }
     __syncthreads();
-    for (int c = threadIdx.x; c < kTok * 32; c += 256) {
-        const int rl = c >> 5, pc = c & 31;
-        *reinterpret_cast<u32x4 *>(p.ex + (size_t)(n0 + rl) * p.Vpad + m0 + 8 * pc) =
-            *reinterpret_cast<const u32x4 *>(smem + rl * kGStagePitch + 16 * pc);
-    }
     store_vocab_major<kTok, 4>(smem, p.gT, (size_t)p.Cpad, m0, n0);
 }
 
@@ -1462,7 +1651,7 @@ __device__ __forceinline__ void topk_tile(const TopkParams &p, char *smem, int t
     const int tm = ts * p.stride;
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave / G::WN, wn = wave % G::WN;
+    const int wm = G::wm_of(wave), wn = G::wn_of(wave);
     float thr[G::NB];
     if constexpr (COLLECT) {
 #pragma unroll
@@ -1704,7 +1893,7 @@ __global__ __launch_bounds__(64) void topk_select_kernel(const uint64_t *cand, c
 // ------------------------------------------------------------------ dH = g . W
 
 struct DhParams {
-    const uint16_t *g;      // [Cpad, Vpad]
+    const uint16_t *gT;     // [Vpad, Cpad]
     const uint16_t *WT;     // [H, Vpad]
     int H, V, Vpad, rows, Cpad, nMt, nNt, ksplit;
     float *part;            // [splits, Cpad, H]
@@ -1715,27 +1904,35 @@ __global__ __launch_bounds__(G::NT) void dh_kernel(DhParams p)
 {
     __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
     int tm, tn;
-    map_tile(blockIdx.x, p.nMt, p.nNt, 1, tm, tn);
-    const int m0 = tm * G::BM, n0 = tn * G::BN;
+    // one token tile with all its hidden tiles at a time
+    map_tile(blockIdx.x, p.nMt, p.nNt, p.nMt, tm, tn);
+    const int m0 = tm * G::BM, n0 = tn * G::BN;     // m: hidden, n: tokens
     const int k_begin = blockIdx.y * p.ksplit;
     const int k_end = min(p.V, k_begin + p.ksplit);
     f32x16 acc[G::MB][G::NB];
-    // A(m = token, k = vocab) = g[m][k]; B(n = hidden, k = vocab) = WT[n][k].
-    G::run(smem, p.g, p.Vpad, m0, p.rows, k_end, p.WT, p.Vpad, n0, p.H, k_end, k_begin, k_end, acc);
+    // dH^T tile: A(m = hidden, k = vocab) = WT[m][k]; B(n = token, k = vocab) = gT[k][n].
+    if (m0 + G::BM <= p.H)
+        G::run(smem, p.WT, p.Vpad, m0, p.H, k_end, p.gT, p.Cpad, n0, p.rows, k_end, k_begin, k_end, acc);
+    else
+        G::template run<NoHook, true>(smem, p.WT, p.Vpad, m0, p.H, k_end, p.gT, p.Cpad, n0, p.rows, k_end, k_begin,
+                                      k_end, acc);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave / G::WN, wn = wave % G::WN;
+    const int wm = G::wm_of(wave), wn = G::wn_of(wave);
     float *out = p.part + (size_t)blockIdx.y * p.Cpad * p.H;
+    // each lane holds 4 consecutive hidden entries of one token per (i, j, q)
 #pragma unroll
     for (int j = 0; j < G::NB; ++j) {
-        const int col = n0 + G::col_of(wn, j, lane);
-        if (col < p.H) {
+        const int t = n0 + G::col_of(wn, j, lane);
+        if (t < p.rows) {
 #pragma unroll
             for (int i = 0; i < G::MB; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + G::row_of(wm, i, r, lane);
-                    if (row < p.rows)
-                        out[(size_t)row * p.H + col] = acc[i][j][r];
+                for (int q = 0; q < 4; ++q) {
+                    const int hh = m0 + G::row_of(wm, i, 4 * q, lane);
+                    if (hh < p.H)
+                        *reinterpret_cast<float4 *>(out + (size_t)t * p.H + hh) =
+                            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                        acc[i][j][4 * q + 3]);
                 }
         }
     }
@@ -1779,9 +1976,13 @@ __global__ __launch_bounds__(G::NT) void dw_kernel(DwParams p)
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     f32x16 acc[G::MB][G::NB];
     // A(m = vocab, k = token) = gT[m][k]; B(n = hidden, k = token) = hT[n][k].
-    G::run(smem, p.gT, p.Cpad, m0, p.Vpad, p.rows, p.hT, p.Cpad, n0, p.H, p.rows, 0, p.rows, acc);
+    if (n0 + G::BN <= p.H)
+        G::run(smem, p.gT, p.Cpad, m0, p.Vpad, p.rows, p.hT, p.Cpad, n0, p.H, p.rows, 0, p.rows, acc);
+    else
+        G::template run<NoHook, true>(smem, p.gT, p.Cpad, m0, p.Vpad, p.rows, p.hT, p.Cpad, n0, p.H, p.rows, 0,
+                                      p.rows, acc);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave / G::WN, wn = wave % G::WN;
+    const int wm = G::wm_of(wave), wn = G::wn_of(wave);
     // Each lane owns one hidden column of 16 * MB rows per fragment column.  When
     // accumulating, all old values of a fragment column are read before any is written,
     // so the reads are in flight together instead of each waiting behind the store
@@ -1810,8 +2011,8 @@ __global__ __launch_bounds__(G::NT) void dw_kernel(DwParams p)
     }
 }
 
-using DGemm = GemmD<256, kHiddenTile, 2, 4, 64, 2>;   // dH: tokens x hidden, k = vocabulary
-using WGemm = GemmD<256, kHiddenTile, 2, 4, 64, 2>;   // dW: vocabulary x hidden, k = tokens
+using DGemm = GemmD<kHiddenTile, 256, 2, 4, 64, 2, false, true>;   // dH^T: hidden x tokens, k = vocabulary
+using WGemm = GemmD<256, kHiddenTile, 2, 4, 64, 2, true>;   // dW: vocabulary x hidden, k = tokens
 
 // dst[c][r] = src[r][c] for r < rows, c < cols; dst[c][r] = 0 for rows <= r < rpad.
 // 64 x 64 tiles through LDS, 16-byte pieces on both sides: each thread loads two
@@ -1895,21 +2096,16 @@ __global__ void zero_u32_kernel(uint32_t *p, int n)
 static inline hipStream_t S(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
 // Work-groups of a persistent logit kernel: one per compute unit of the current device
-// (rounded up to a multiple of the 8 XCDs), never more than there are tiles.
+// (rounded up to a multiple of the 8 XCDs), never more than there are tiles.  The count
+// is asked of the runtime on every launch (it answers from the device properties it
+// holds), so the library keeps no state of its own.
 static int persistent_grid(int tiles)
 {
-    static int cus[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        dev = -1;
-    int n = dev >= 0 ? cus[dev] : 0;
-    if (n <= 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess || n <= 0)
-            n = 256;
-        n = (n + 7) / 8 * 8;
-        if (dev >= 0)
-            cus[dev] = n;
-    }
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    n = (n + 7) / 8 * 8;
     return tiles < n ? tiles : n;
 }
 
@@ -1962,7 +2158,7 @@ int launch_forward_logits(const ChunkArgs &a, void *stream, bool keep_exp)
     p.cnt = reinterpret_cast<const uint8_t *>(a.ws + L.off_cnt);
     p.zk = reinterpret_cast<float *>(a.ws + L.off_zk);
     p.part = reinterpret_cast<float2 *>(a.ws + L.off_part);
-    p.ex = reinterpret_cast<uint16_t *>(a.ws + L.off_g);
+    p.ex = reinterpret_cast<uint16_t *>(a.ws + L.off_ex);
     p.mw = reinterpret_cast<float *>(a.ws + L.off_mw);
     p.Vpad = L.Vpad;
     const dim3 grid(persistent_grid(p.nVt * p.nNt));
@@ -2015,7 +2211,7 @@ int launch_softmax_grad(const ChunkArgs &a, const float *lse, const GradScale &g
 {
     const Layout &L = *a.L;
     SoftGradParams p;
-    p.ex = reinterpret_cast<uint16_t *>(a.ws + L.off_g);
+    p.ex = reinterpret_cast<const uint16_t *>(a.ws + L.off_ex);
     p.gT = reinterpret_cast<uint16_t *>(a.ws + L.off_gT);
     p.mw = reinterpret_cast<const float *>(a.ws + L.off_mw);
     p.lse = lse;
@@ -2058,7 +2254,6 @@ int launch_backward_logits(const ChunkArgs &a, const float *lse, void *stream)
     p.p_s = reinterpret_cast<const float *>(a.ws + L.off_p);
     p.psum = reinterpret_cast<const float *>(a.ws + L.off_psum);
     p.cnt = reinterpret_cast<const uint8_t *>(a.ws + L.off_cnt);
-    p.g = reinterpret_cast<uint16_t *>(a.ws + L.off_g);
     p.gT = reinterpret_cast<uint16_t *>(a.ws + L.off_gT);
     hipLaunchKernelGGL(backward_logits_kernel, dim3(persistent_grid(p.nVt * p.nNt)), dim3(LogitGemm::NT), 0, S(stream), p);
     return (int)hipGetLastError();
@@ -2077,15 +2272,15 @@ int launch_dh(const ChunkArgs &a, void *stream)
 {
     const Layout &L = *a.L;
     DhParams p;
-    p.g = reinterpret_cast<const uint16_t *>(a.ws + L.off_g);
+    p.gT = reinterpret_cast<const uint16_t *>(a.ws + L.off_gT);
     p.WT = reinterpret_cast<const uint16_t *>(a.ws + L.off_WT);
     p.H = a.H;
     p.V = a.V;
     p.Vpad = L.Vpad;
     p.rows = a.rows;
     p.Cpad = L.Cpad;
-    p.nMt = (a.rows + 255) / 256;
-    p.nNt = (a.H + kHiddenTile - 1) / kHiddenTile;
+    p.nMt = (a.H + kHiddenTile - 1) / kHiddenTile;
+    p.nNt = (a.rows + 255) / 256;
     int used = 0;
     dh_splits(a, p.ksplit, used);
     p.part = reinterpret_cast<float *>(a.ws + L.off_dhp);
@@ -2216,7 +2411,7 @@ int launch_full_student(const ChunkArgs &a, const FullLayout &F, void *stream)
     p.lt2 = reinterpret_cast<const float *>(a.ws + F.off_lt2);
     p.part = reinterpret_cast<float2 *>(a.ws + L.off_part);
     p.px = reinterpret_cast<float *>(a.ws + F.off_px);
-    p.ex = reinterpret_cast<uint16_t *>(a.ws + L.off_g);
+    p.ex = reinterpret_cast<uint16_t *>(a.ws + L.off_ex);
     p.mw = reinterpret_cast<float *>(a.ws + L.off_mw);
     hipLaunchKernelGGL(full_student_kernel, dim3(persistent_grid(p.nVt * p.nNt)), dim3(LogitGemm::NT), 0,
                        S(stream), p);
@@ -2237,7 +2432,7 @@ int launch_full_grad(const ChunkArgs &a, const FullLayout &F, const GradScale &g
 {
     const Layout &L = F.base;
     FullGradParams p;
-    p.ex = reinterpret_cast<uint16_t *>(a.ws + L.off_g);
+    p.ex = reinterpret_cast<const uint16_t *>(a.ws + L.off_ex);
     p.gT = reinterpret_cast<uint16_t *>(a.ws + L.off_gT);
     p.at = reinterpret_cast<const float *>(a.ws + F.off_at);
     p.mw = reinterpret_cast<const float *>(a.ws + L.off_mw);

@@ -84,7 +84,7 @@ enum {
     FCKL_KERNEL_FWD_LOGITS = 1,    /* forward logit GEMM + online logsumexp / pick epilogue */
     FCKL_KERNEL_COMBINE = 2,       /* per-token logsumexp over tiles and KL */
     FCKL_KERNEL_MEAN = 3,          /* mean of the per-token loss */
-    FCKL_KERNEL_BWD_LOGITS = 4,    /* recompute GEMM + gradient epilogue, writes g */
+    FCKL_KERNEL_BWD_LOGITS = 4,    /* recompute GEMM + gradient epilogue, writes g^T */
     FCKL_KERNEL_DH = 5,            /* dH = g W (vocabulary splits) */
     FCKL_KERNEL_DH_REDUCE = 6,     /* fixed-order sum of the dH splits */
     FCKL_KERNEL_DW = 7,            /* dW += g^T h */
@@ -174,7 +174,8 @@ fckl_status fckl_forward(const fckl_desc *desc, const void *h, const void *W,
 /*
  * Backward pass: gradients of grad_scale * loss_mean with respect to h and W.  Each
  * chunk's logits are recomputed with the same tiles as the forward pass; the chunk's
- * gradient g (bf16, in the workspace) feeds the dH and dW products.
+ * gradient g (bf16, written once, vocabulary-major, in the workspace) feeds the dH and
+ * dW products.
  *   lse        device, f32 [N]         the lse written by fckl_forward for these inputs
  *   grad_scale                         upstream gradient of loss_mean (1 for a plain loss)
  *   dH         device, f32 [N,H]       out: overwritten (16-byte aligned)
@@ -219,8 +220,13 @@ fckl_status fckl_backward_ex(const fckl_desc *desc, const void *h, const void *W
  * of a 256-row vocabulary tile, and once the chunk's lse is known a streaming kernel
  * turns those values into g.  That is 6 N V H flop instead of 8.  g differs from the
  * two-call path by the bf16 rounding of the kept values, which has the same relative size
- * as the rounding of g itself.  Workspace: the same size as for the two-call path.
+ * as the rounding of g itself.  Workspace: the kept values take 2 V bytes per token of the
+ * chunk more than the two-call path needs; fckl_single_plan gives the size (and, with
+ * desc->chunk = 0, the chunk as fckl_plan chooses it for that layout), and the call uses
+ * the chunk fckl_single_plan(desc, ws_bytes) reports.
  */
+fckl_status fckl_single_plan(const fckl_desc *desc, size_t budget_bytes, int32_t *chunk_out,
+                             size_t *ws_bytes_out);
 fckl_status fckl_forward_backward(const fckl_desc *desc, const void *h, const void *W,
                                   const int32_t *topk_idx, const void *topk_logit,
                                   const float *weights, float grad_scale,

@@ -103,9 +103,12 @@ int main()
     d.K = K;
     d.T = T;
     d.logit_dtype = FCKL_DTYPE_BF16;
-    int32_t chunk = 0;
-    size_t ws_bytes = 0;
+    int32_t chunk = 0, chunk1 = 0;
+    size_t ws_bytes = 0, ws1_bytes = 0;
     CHECK(fckl_plan(&d, 0, &chunk, &ws_bytes) == FCKL_OK && chunk > 0 && ws_bytes > 0);
+    // the single call keeps the chunk's exponentials as well: a larger workspace
+    CHECK(fckl_single_plan(&d, 0, &chunk1, &ws1_bytes) == FCKL_OK && chunk1 == chunk && ws1_bytes > ws_bytes);
+    ws_bytes = ws1_bytes;
 
     uint16_t *dh = dev_alloc<uint16_t>(h.size()), *dW_in = dev_alloc<uint16_t>(W.size());
     uint16_t *dtl = dev_alloc<uint16_t>(tl.size());

@@ -36,13 +36,21 @@ static void check_layout(const fckl_desc &d, const Layout &L)
     const size_t Cp = (size_t)L.Cpad, K = (size_t)d.K;
     CHECK(L.Cpad % kTokenTile == 0 && L.Cpad >= L.C && L.Vpad % kVocabTile == 0 && L.Vpad >= d.V);
     CHECK(L.dh_splits >= 1);
-    check_regions({{L.off_idx, Cp * K * 4}, {L.off_p, Cp * K * 4}, {L.off_zk, Cp * K * 4}, {L.off_psum, Cp * 4},
-                   {L.off_negent, Cp * 4}, {L.off_cnt, Cp * (size_t)L.cnt_stride}, {L.off_part, (size_t)L.nVt * Cp * 8},
-                   {L.off_mw, 2 * (size_t)L.nVt * Cp * 4}, {L.off_wsum, 8}, {L.off_g, Cp * (size_t)L.Vpad * 2},
-                   {L.off_gT, (size_t)L.Vpad * Cp * 2}, {L.off_hT, (size_t)d.H * Cp * 2},
-                   {L.off_WT, (size_t)d.H * (size_t)L.Vpad * 2},
-                   {L.off_dhp, (size_t)L.dh_splits * Cp * (size_t)d.H * 4}, {L.off_err, 16}},
-                  L.total);
+    std::vector<std::pair<size_t, size_t>> regions = {
+        {L.off_idx, Cp * K * 4}, {L.off_p, Cp * K * 4}, {L.off_zk, Cp * K * 4}, {L.off_psum, Cp * 4},
+        {L.off_negent, Cp * 4}, {L.off_cnt, Cp * (size_t)L.cnt_stride}, {L.off_part, (size_t)L.nVt * Cp * 8}};
+    // the kept exponentials and their maxima exist only in a keep layout
+    if (L.keep)
+        regions.push_back({L.off_mw, 2 * (size_t)L.nVt * Cp * 4});
+    regions.push_back({L.off_wsum, 8});
+    if (L.keep)
+        regions.push_back({L.off_ex, Cp * (size_t)L.Vpad * 2});
+    for (const auto &r : std::vector<std::pair<size_t, size_t>>{
+             {L.off_gT, (size_t)L.Vpad * Cp * 2}, {L.off_hT, (size_t)d.H * Cp * 2},
+             {L.off_WT, (size_t)d.H * (size_t)L.Vpad * 2},
+             {L.off_dhp, (size_t)L.dh_splits * Cp * (size_t)d.H * 4}, {L.off_err, 16}})
+        regions.push_back(r);
+    check_regions(regions, L.total);
 }
 
 int main()
@@ -72,16 +80,20 @@ int main()
                     }
                     CHECK(V <= kMaxPitch && vocab_tiles <= kMaxTiles);
                     for (size_t budget : budgets) {
-                        Layout L;
-                        if (plan_chunk(&d, budget, &L) == FCKL_OK) {
-                            ++planned;
-                            CHECK(L.total <= (budget ? budget : (size_t(12) << 30)));
-                            CHECK(L.C >= 1 && L.C <= kMaxChunk);
-                            check_layout(d, L);
+                        for (bool keep : {false, true}) {
+                            Layout L;
+                            if (plan_chunk(&d, budget, &L, keep) == FCKL_OK) {
+                                ++planned;
+                                CHECK(L.keep == keep);
+                                CHECK(L.total <= (budget ? budget : (size_t(12) << 30)));
+                                CHECK(L.C >= 1 && L.C <= kMaxChunk);
+                                check_layout(d, L);
+                            }
                         }
                         FullLayout F;
                         if (plan_full_chunk(&d, H, budget, &F) == FCKL_OK) {
                             CHECK(F.total <= (budget ? budget : (size_t(12) << 30)));
+                            CHECK(F.base.keep);
                             check_layout(d, F.base);
                             const size_t Cp = (size_t)F.base.Cpad;
                             check_regions({{F.off_at, (size_t)F.base.Vpad * Cp * 4},
@@ -97,10 +109,12 @@ int main()
                         const int64_t Cpad = ((int64_t)chunk + 255) / 256 * 256;
                         const bool fits = Cpad <= kMaxPitch && Cpad / 256 * (((int64_t)H + 255) / 256) <= kMaxTiles &&
                                           Cpad * H <= kMaxChunkElems;
-                        const fckl_status ls = make_layout(&d, chunk, &L);
-                        CHECK(fits ? ls == FCKL_OK : ls == FCKL_ERR_UNSUPPORTED);
-                        if (ls == FCKL_OK)
-                            check_layout(d, L);
+                        for (bool keep : {false, true}) {
+                            const fckl_status ls = make_layout(&d, chunk, &L, keep);
+                            CHECK(fits ? ls == FCKL_OK : ls == FCKL_ERR_UNSUPPORTED);
+                            if (ls == FCKL_OK)
+                                check_layout(d, L);
+                        }
                         for (uint32_t flags : {0u, (uint32_t)FCKL_FLAG_TOPK_FULL_FIRST_PASS}) {
                             fckl_desc dt = d;
                             dt.flags = flags;

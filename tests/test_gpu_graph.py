@@ -70,7 +70,7 @@ def test_single_call_and_full_teacher_in_graphs():
     dev = device()
     w = torch.from_numpy(np.random.default_rng(92).uniform(0.0, 2.0, N).astype(np.float32)).to(dev)
     desc = fckl.desc_for(dh, dW_, di, dt, T, 256)
-    ws = torch.empty(fckl.workspace_size(desc, 256), dtype=torch.uint8, device=dev)
+    ws = torch.empty(fckl.single_plan(desc)[1], dtype=torch.uint8, device=dev)
     outs = [torch.empty(N, device=dev), torch.empty(N, device=dev), torch.empty(1, device=dev),
             torch.empty(N, H, device=dev), torch.empty(V, H, device=dev)]
 

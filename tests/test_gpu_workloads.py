@@ -108,8 +108,9 @@ def test_single_call_at_full_size():
     x = synth.make_inputs(wl, device=device())
     h, W, idx, tl = upload(x, device())
     desc = fckl.desc_for(h, W, idx, tl, wl.T)
-    chunk, ws_bytes = fckl.plan(desc)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device())
+    chunk, _ = fckl.plan(desc)
+    desc.chunk = chunk
+    ws = torch.empty(fckl.single_plan(desc)[1], dtype=torch.uint8, device=device())
     loss1, lse1, mean1, dH1, dW1 = fckl.forward_backward(h, W, idx, tl, T=wl.T, chunk=chunk, ws=ws)
     loss2, lse2, mean2 = fckl.forward(h, W, idx, tl, T=wl.T, chunk=chunk, ws=ws)
     assert torch.equal(loss1, loss2) and torch.equal(lse1, lse2) and torch.equal(mean1, mean2)

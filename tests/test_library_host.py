@@ -62,10 +62,16 @@ def test_workspace_grows_with_chunk():
     d = fckl.make_desc(**C3)
     w = [fckl.workspace_size(d, c) for c in (256, 1024, 4096, 8192, 16384)]
     assert all(a < b for a, b in zip(w, w[1:]))
-    # dominated by the bf16 chunk gradient in two layouts (4*C*V bytes) and the
-    # transposed LM head (2*V*H bytes)
+    # dominated by the bf16 chunk gradient, kept once (2*C*V bytes), and the transposed
+    # LM head (2*V*H bytes)
     C, V, H = 4096, 201088, 2880
-    assert 4 * C * V + 2 * V * H < w[2] < 6 * C * V + 2 * V * H
+    assert 2 * C * V + 2 * V * H < w[2] < 3 * C * V + 2 * V * H
+    # the single call also keeps the chunk's exponentials (2*C*V bytes) and their
+    # half-tile maxima (8*C*ceil(V/256) bytes)
+    d.chunk = C
+    chunk, single = fckl.single_plan(d, 0)
+    assert chunk == C
+    assert single == w[2] + 2 * C * ((V + 255) // 256 * 256) + 8 * C * ((V + 255) // 256)
 
 
 def test_plan_explicit_chunk_and_small_budget():
@@ -206,7 +212,9 @@ def test_weighted_and_single_call_entry_points_reject_before_any_hip_call():
     st = lib.fckl_backward_ex(ctypes.byref(d), *ok, _fake(P), _fake(P), ctypes.c_float(1.0), None, _fake(P),
                               _fake(P), _fake(P + 8), size(need), None)
     assert st == fckl.ERR_INVALID_ARG
-    # fckl_forward_backward: every output is required
+    # fckl_forward_backward: every output is required; its workspace (fckl_single_plan)
+    # also holds the kept exponentials
+    need = fckl.single_plan(d, 0)[1]
     args = [_fake(P)] * 5
     for missing in range(5):
         outs = list(args)
@@ -244,7 +252,7 @@ def test_misaligned_pointers_are_refused():
                               f(odd), f(P), f(P), need, None)
     assert st == fckl.ERR_INVALID_ARG
     st = lib.fckl_forward_backward(ctypes.byref(d), f(P), f(P), f(P), f(P), None, ctypes.c_float(1.0), f(P), f(P),
-                                   None, f(odd), f(P), f(P), need, None)
+                                   None, f(odd), f(P), f(P), ctypes.c_size_t(fckl.single_plan(d, 0)[1]), None)
     assert st == fckl.ERR_INVALID_ARG
     # dW is written element by element: any 4-byte alignment is fine (the same call with an
     # aligned dH would only fail later, on the fake addresses, so it is not made here)
@@ -351,7 +359,8 @@ def test_missing_library_fails_loudly():
         fckl._lib = None
         fckl.LIB_PATH = os.path.join(ROOT, "no-such-dir", "libfckl.so")
         d = fckl.make_desc(64, 64, 256, 4, 1.0)
-        calls = [lambda: fckl.plan(d), lambda: fckl.workspace_size(d, 256), lambda: fckl.full_plan(d, 64),
+        calls = [lambda: fckl.plan(d), lambda: fckl.single_plan(d), lambda: fckl.workspace_size(d, 256),
+                 lambda: fckl.full_plan(d, 64),
                  lambda: fckl.topk_workspace_size(d), lambda: fckl.version(), lambda: fckl.load()]
         for call in calls:
             with pytest.raises(ImportError):
