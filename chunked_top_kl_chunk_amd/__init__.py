@@ -34,7 +34,7 @@ FLAG_VALIDATE, FLAG_DW_ACCUMULATE, FLAG_TOPK_FULL_FIRST_PASS = 1, 2, 4
 
 # Every symbol include/fckl.h declares.
 EXPORTS = ("fckl_plan", "fckl_workspace_size", "fckl_forward", "fckl_backward", "fckl_forward_ex",
-           "fckl_backward_ex", "fckl_single_plan", "fckl_forward_backward", "fckl_topk_workspace_size", "fckl_topk",
+           "fckl_backward_ex", "fckl_forward_noalloc", "fckl_single_plan", "fckl_forward_backward", "fckl_topk_workspace_size", "fckl_topk",
            "fckl_topk_async", "fckl_full_plan", "fckl_full_forward_backward", "fckl_scale", "fckl_status_string",
            "fckl_version")
 
@@ -82,6 +82,7 @@ def load() -> ctypes.CDLL:
     lib.fckl_forward.argtypes = [P(Desc), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.fckl_backward.argtypes = [P(Desc), vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.fckl_forward_ex.argtypes = [P(Desc), vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.fckl_forward_noalloc.argtypes = [P(Desc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.fckl_backward_ex.argtypes = [P(Desc), vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
     lib.fckl_forward_backward.argtypes = [P(Desc), vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp,
                                           sz, vp]
@@ -97,7 +98,7 @@ def load() -> ctypes.CDLL:
                                                vp, vp, vp, vp, sz, vp]
     lib.fckl_scale.argtypes = [vp, ctypes.c_int64, vp, vp]
     for f in ("fckl_plan", "fckl_single_plan", "fckl_workspace_size", "fckl_forward", "fckl_backward",
-              "fckl_forward_ex", "fckl_backward_ex", "fckl_forward_backward", "fckl_topk_workspace_size", "fckl_topk",
+              "fckl_forward_ex", "fckl_forward_noalloc", "fckl_backward_ex", "fckl_forward_backward", "fckl_topk_workspace_size", "fckl_topk",
               "fckl_topk_async", "fckl_full_plan", "fckl_full_forward_backward", "fckl_scale"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
@@ -267,6 +268,25 @@ def forward(h, W, topk_idx, topk_logit, T: float = 1.0, chunk: int = 0, ws=None,
     return loss_tok, lse, loss_mean
 
 
+def forward_noalloc(h, W, topk_idx, topk_logit, loss_tok, lse, loss_mean=None, T: float = 1.0, chunk: int = 0,
+                    weights=None, validate: bool = False, stream=None):
+    """The forward pass without a workspace (fckl_forward_noalloc): the chunk's buffers are
+    the library's own device array.  The outputs must be given (nothing is allocated
+    here either).  Returns (loss_tok, lse, loss_mean)."""
+    _check_inputs(h, W, topk_idx, topk_logit)
+    dev, N = h.device, h.shape[0]
+    desc = desc_for(h, W, topk_idx, topk_logit, T, chunk, FLAG_VALIDATE if validate else 0)
+    weights = _weights(weights, N, dev)
+    loss_tok = _out(loss_tok, (N,), dev, "loss_tok")
+    lse = _out(lse, (N,), dev, "lse")
+    if loss_mean is not None:
+        loss_mean = _out(loss_mean, (1,), dev, "loss_mean")
+    _call("fckl_forward_noalloc", ctypes.byref(desc), h.data_ptr(), W.data_ptr(), topk_idx.data_ptr(),
+          topk_logit.data_ptr(), _ptr(weights), loss_tok.data_ptr(), lse.data_ptr(), _ptr(loss_mean),
+          _stream_handle(stream))
+    return loss_tok, lse, loss_mean
+
+
 def backward(h, W, topk_idx, topk_logit, lse, T: float = 1.0, grad_scale: float = 1.0, chunk: int = 0, ws=None,
              dH=None, dW=None, accumulate: bool = False, validate: bool = False, stream=None,
              profile: Optional[Profile] = None, weights=None, grad_scale_dev=None):
@@ -431,5 +451,5 @@ def scale_(x, scale, stream=None):
 
 
 __all__ = ["Desc", "Profile", "KERNELS", "FCKLError", "load", "plan", "single_plan", "device_budget",
-           "workspace_size", "forward", "backward",
+           "workspace_size", "forward", "forward_noalloc", "backward",
            "forward_backward", "topk", "topk_workspace_size", "full_plan", "full_forward_backward", "scale_", "make_desc", "desc_for", "status_string", "version", "EXPORTS", "LIB_PATH"]

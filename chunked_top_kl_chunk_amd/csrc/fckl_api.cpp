@@ -13,7 +13,7 @@ namespace {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 fckl_status common_checks(const fckl_desc *d, const void *h, const void *W, const int32_t *idx, const void *tl,
-                          void *ws, size_t ws_bytes, Layout *L, bool keep = false)
+                          void *ws, size_t ws_bytes, Layout *L, LayoutKind kind = LayoutKind::TwoPass)
 {
     fckl_status st = check_desc(d);
     if (st != FCKL_OK)
@@ -23,7 +23,7 @@ fckl_status common_checks(const fckl_desc *d, const void *h, const void *W, cons
     if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || (reinterpret_cast<uintptr_t>(h) & 15u) != 0 ||
         (reinterpret_cast<uintptr_t>(W) & 15u) != 0)
         return FCKL_ERR_INVALID_ARG;
-    st = plan_chunk(d, ws_bytes, L, keep);
+    st = plan_chunk(d, ws_bytes, L, kind);
     if (st != FCKL_OK)
         return st;
     if (L->total > ws_bytes)
@@ -134,16 +134,12 @@ fckl_status mean_of(const fckl_desc *desc, const float *loss_tok, const float *w
     return rc ? FCKL_ERR_HIP : FCKL_OK;
 }
 
-fckl_status forward_impl(const fckl_desc *desc, const void *h, const void *W, const int32_t *topk_idx,
-                         const void *topk_logit, const float *weights, float *loss_tok, float *lse,
-                         float *loss_mean, void *ws, size_t ws_bytes, void *stream)
+// The forward chunk loop on a workspace whose layout L has been planned and checked.
+fckl_status forward_chunks(const fckl_desc *desc, const void *h, const void *W, const int32_t *topk_idx,
+                           const void *topk_logit, const float *weights, float *loss_tok, float *lse,
+                           float *loss_mean, void *ws, const Layout &L, void *stream)
 {
-    Layout L;
-    fckl_status st = common_checks(desc, h, W, topk_idx, topk_logit, ws, ws_bytes, &L);
-    if (st != FCKL_OK)
-        return st;
-    if (!loss_tok || !lse)
-        return FCKL_ERR_INVALID_ARG;
+    fckl_status st;
     if (desc->flags & FCKL_FLAG_VALIDATE) {
         st = validate_indices(desc, h, W, topk_idx, topk_logit, ws, L, stream);
         if (st != FCKL_OK)
@@ -168,6 +164,19 @@ fckl_status forward_impl(const fckl_desc *desc, const void *h, const void *W, co
         }
     }
     return loss_mean ? mean_of(desc, loss_tok, weights, loss_mean, stream) : FCKL_OK;
+}
+
+fckl_status forward_impl(const fckl_desc *desc, const void *h, const void *W, const int32_t *topk_idx,
+                         const void *topk_logit, const float *weights, float *loss_tok, float *lse,
+                         float *loss_mean, void *ws, size_t ws_bytes, void *stream)
+{
+    Layout L;
+    fckl_status st = common_checks(desc, h, W, topk_idx, topk_logit, ws, ws_bytes, &L);
+    if (st != FCKL_OK)
+        return st;
+    if (!loss_tok || !lse)
+        return FCKL_ERR_INVALID_ARG;
+    return forward_chunks(desc, h, W, topk_idx, topk_logit, weights, loss_tok, lse, loss_mean, ws, L, stream);
 }
 
 // dH, dH reduce and dW of one chunk whose g (both layouts) and h^T are in the workspace.
@@ -264,7 +273,7 @@ fckl_status fckl_plan(const fckl_desc *desc, size_t budget_bytes, int32_t *chunk
 fckl_status fckl_single_plan(const fckl_desc *desc, size_t budget_bytes, int32_t *chunk_out, size_t *ws_bytes_out)
 {
     Layout L;
-    fckl_status st = plan_chunk(desc, budget_bytes, &L, true);
+    fckl_status st = plan_chunk(desc, budget_bytes, &L, LayoutKind::Keep);
     if (st != FCKL_OK)
         return st;
     if (chunk_out)
@@ -299,6 +308,29 @@ fckl_status fckl_forward_ex(const fckl_desc *desc, const void *h, const void *W,
     return forward_impl(desc, h, W, topk_idx, topk_logit, weights, loss_tok, lse, loss_mean, ws, ws_bytes, stream);
 }
 
+fckl_status fckl_forward_noalloc(const fckl_desc *desc, const void *h, const void *W, const int32_t *topk_idx,
+                                 const void *topk_logit, const float *weights, float *loss_tok, float *lse,
+                                 float *loss_mean, void *stream)
+{
+    fckl_status st = check_desc(desc);
+    if (st != FCKL_OK)
+        return st;
+    if (!h || !W || !topk_idx || !topk_logit || !loss_tok || !lse || !aligned16(h) || !aligned16(W))
+        return FCKL_ERR_INVALID_ARG;
+    // the forward buffers of a chunk in the library's device array: the largest chunk
+    // that fits (or desc->chunk, refused when it does not fit)
+    Layout L;
+    st = plan_chunk(desc, kScratchBytes, &L, LayoutKind::ForwardOnly);
+    if (st != FCKL_OK)
+        return st;
+    if (L.total > kScratchBytes)
+        return FCKL_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (scratch_address(&ws) != 0)
+        return FCKL_ERR_HIP;
+    return forward_chunks(desc, h, W, topk_idx, topk_logit, weights, loss_tok, lse, loss_mean, ws, L, stream);
+}
+
 fckl_status fckl_backward(const fckl_desc *desc, const void *h, const void *W, const int32_t *topk_idx,
                           const void *topk_logit, const float *lse, float grad_scale, float *dH, float *dW,
                           void *ws, size_t ws_bytes, void *stream)
@@ -322,7 +354,7 @@ fckl_status fckl_forward_backward(const fckl_desc *desc, const void *h, const vo
                                   size_t ws_bytes, void *stream)
 {
     Layout L;
-    fckl_status st = common_checks(desc, h, W, topk_idx, topk_logit, ws, ws_bytes, &L, true);
+    fckl_status st = common_checks(desc, h, W, topk_idx, topk_logit, ws, ws_bytes, &L, LayoutKind::Keep);
     if (st != FCKL_OK)
         return st;
     if (!loss_tok || !lse || !dH || !dW || !aligned16(dH))

@@ -39,11 +39,16 @@ constexpr int64_t kMaxPitch = int64_t(1) << 24;
 constexpr int64_t kMaxTiles = (int64_t(1) << 23) - 1;
 constexpr int64_t kMaxChunkElems = int64_t(1) << 33;
 
+// Which calls a workspace layout serves: the two passes, the single call and the
+// full-teacher variant (whose forward product keeps its exponentials: off_mw and off_ex
+// added), or the forward pass alone (the buffers of the forward pass only, up to off_part,
+// with off_err; the others are left at 0).
+enum class LayoutKind { TwoPass, Keep, ForwardOnly };
+
 // Where each per-chunk buffer lives inside the caller's workspace.  Every buffer is
-// sized by the chunk, never by N.  `keep` layouts (the single call and the full-teacher
-// variant, whose forward product keeps its exponentials) add off_mw and off_ex.
+// sized by the chunk, never by N.
 struct Layout {
-    bool keep = false;
+    LayoutKind kind = LayoutKind::TwoPass;
     int32_t C = 0;          // tokens per chunk
     int32_t Cpad = 0;       // C rounded up to kTokenTile
     int32_t nVt = 0;        // vocabulary tiles: ceil(V / kVocabTile)
@@ -101,8 +106,14 @@ fckl_status check_desc(const fckl_desc *d);
 fckl_status make_topk_layout(const fckl_desc *d, int32_t chunk, TopkLayout *L);
 fckl_status make_full_layout(const fckl_desc *d, int32_t Ht, int32_t chunk, FullLayout *L);
 fckl_status plan_full_chunk(const fckl_desc *d, int32_t Ht, size_t budget, FullLayout *L);
-fckl_status make_layout(const fckl_desc *d, int32_t chunk, Layout *L, bool keep = false);
-fckl_status plan_chunk(const fckl_desc *d, size_t budget, Layout *L, bool keep = false);
+fckl_status make_layout(const fckl_desc *d, int32_t chunk, Layout *L, LayoutKind kind = LayoutKind::TwoPass);
+fckl_status plan_chunk(const fckl_desc *d, size_t budget, Layout *L, LayoutKind kind = LayoutKind::TwoPass);
+
+// The allocation-free forward pass (fckl_forward_noalloc) runs in a device array of the
+// library instead of a caller's workspace: its size, and the lookup of its address on the
+// current device (once per device; a HIP status).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+int scratch_address(void **ptr);
 
 // ------------------------------------------------------------------ launchers
 // All return hipSuccess (0) or the launch error; they never synchronise.

@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <stdint.h>
 
 #include <type_traits>
@@ -2090,6 +2091,40 @@ __global__ void zero_u32_kernel(uint32_t *p, int n)
 }
 
 }  // namespace
+
+// ------------------------------------------------------------------ allocation-free workspace
+
+// The workspace of fckl_forward_noalloc: a device array of the library, so that the call
+// needs no memory from its caller (each device the library runs on holds it until the
+// process ends).  In host code `scratch` is only a stand-in for the symbol; its device
+// address on the current device comes from hipGetSymbolAddress, looked up once per
+// device and kept below.  Calls that overlap on one device share the array and race.
+static __device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::once_flag g_scratch_once[kMaxDevices];
+static void *g_scratch_ptr[kMaxDevices];
+static hipError_t g_scratch_err[kMaxDevices];
+
+int scratch_address(void **ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return (int)e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return (int)hipErrorInvalidDevice;
+    // with `dev` current (this thread's device), once per device
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = p;
+    });
+    if (g_scratch_err[dev] != hipSuccess)
+        return (int)g_scratch_err[dev];
+    *ptr = g_scratch_ptr[dev];
+    return 0;
+}
 
 // ------------------------------------------------------------------ launchers
 

@@ -77,7 +77,7 @@ static int32_t dh_split_count(int32_t Cpad, int32_t H, int32_t Vpad)
     return (int32_t)best;
 }
 
-fckl_status make_layout(const fckl_desc *d, int32_t chunk, Layout *L, bool keep)
+fckl_status make_layout(const fckl_desc *d, int32_t chunk, Layout *L, LayoutKind kind)
 {
     fckl_status st = check_desc(d);
     if (st != FCKL_OK)
@@ -87,7 +87,8 @@ fckl_status make_layout(const fckl_desc *d, int32_t chunk, Layout *L, bool keep)
     if (!chunk_supported((int64_t)align_up((size_t)chunk, kTokenTile), d->H))
         return FCKL_ERR_UNSUPPORTED;
     Layout o;
-    o.keep = keep;
+    o.kind = kind;
+    const bool keep = kind == LayoutKind::Keep, fwd_only = kind == LayoutKind::ForwardOnly;
     o.C = chunk;
     o.Cpad = (int32_t)align_up((size_t)chunk, kTokenTile);
     o.nVt = (d->V + kVocabTile - 1) / kVocabTile;
@@ -108,6 +109,13 @@ fckl_status make_layout(const fckl_desc *d, int32_t chunk, Layout *L, bool keep)
     o.off_negent = take(Cp * 4);
     o.off_cnt = take(Cp * (size_t)o.cnt_stride);
     o.off_part = take((size_t)o.nVt * Cp * 8);
+    if (fwd_only) {
+        o.dh_splits = 0;
+        o.off_err = take(16);
+        o.total = off;
+        *L = o;
+        return FCKL_OK;
+    }
     o.off_mw = keep ? take((size_t)o.nVt * 2 * Cp * 4) : 0;
     o.off_wsum = take(16);
     o.off_ex = keep ? take(Cp * (size_t)o.Vpad * 2) : 0;
@@ -169,7 +177,7 @@ fckl_status make_full_layout(const fckl_desc *d, int32_t Ht, int32_t chunk, Full
     if (Ht % 8 != 0 || Ht > 65536)
         return FCKL_ERR_UNSUPPORTED;
     FullLayout o;
-    fckl_status st = make_layout(d, chunk, &o.base, true);
+    fckl_status st = make_layout(d, chunk, &o.base, LayoutKind::Keep);
     if (st != FCKL_OK)
         return st;
     o.Ht = Ht;
@@ -226,13 +234,13 @@ fckl_status plan_full_chunk(const fckl_desc *d, int32_t Ht, size_t budget, FullL
     return make_full_layout(d, Ht, best, L);
 }
 
-fckl_status plan_chunk(const fckl_desc *d, size_t budget, Layout *L, bool keep)
+fckl_status plan_chunk(const fckl_desc *d, size_t budget, Layout *L, LayoutKind kind)
 {
     fckl_status st = check_desc(d);
     if (st != FCKL_OK)
         return st;
     if (d->chunk > 0)
-        return make_layout(d, d->chunk, L, keep);
+        return make_layout(d, d->chunk, L, kind);
     if (budget == 0)
         budget = kDefaultBudget;
     const int32_t npad = (int32_t)std::min<int64_t>(align_up((size_t)d->N, kTokenTile), kMaxChunk);
@@ -240,7 +248,7 @@ fckl_status plan_chunk(const fckl_desc *d, size_t budget, Layout *L, bool keep)
     int32_t best = 0;
     for (int32_t c = npad; c >= kTokenTile; c -= kTokenTile) {
         Layout t;
-        if (make_layout(d, c, &t, keep) == FCKL_OK && t.total <= budget) {
+        if (make_layout(d, c, &t, kind) == FCKL_OK && t.total <= budget) {
             best = c;
             break;
         }
@@ -253,14 +261,14 @@ fckl_status plan_chunk(const fckl_desc *d, size_t budget, Layout *L, bool keep)
     for (int64_t nchunks = (d->N + best - 1) / best;; ++nchunks) {
         const int32_t c = (int32_t)align_up((size_t)((d->N + nchunks - 1) / nchunks), kTokenTile);
         Layout even;
-        if (c <= best && make_layout(d, c, &even, keep) == FCKL_OK && even.total <= budget) {
+        if (c <= best && make_layout(d, c, &even, kind) == FCKL_OK && even.total <= budget) {
             *L = even;
             return FCKL_OK;
         }
         if (c <= kTokenTile)
             break;
     }
-    return make_layout(d, best, L, keep);
+    return make_layout(d, best, L, kind);
 }
 
 }  // namespace fckl

@@ -34,6 +34,8 @@
  *     memory of the current HIP device; the library reads and writes them only from
  *     kernels launched on `stream`.  The caller owns every buffer, including the
  *     workspace; the library allocates no device memory and keeps no global state.
+ *   - fckl_forward_noalloc is the exception: it keeps one device array per device (see
+ *     there).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls are
  *     asynchronous: outputs are valid once the stream has reached the call.  The only
  *     host synchronisation is the index check requested by FCKL_FLAG_VALIDATE.
@@ -210,6 +212,26 @@ fckl_status fckl_backward_ex(const fckl_desc *desc, const void *h, const void *W
                              const int32_t *topk_idx, const void *topk_logit, const float *weights,
                              const float *lse, float grad_scale, const float *grad_scale_dev,
                              float *dH, float *dW, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * fckl_forward_ex without a caller workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The chunk's buffers live in a device array of the library instead (64 MiB
+ * per device, held from the first call on that device until the process ends; the first
+ * call on a device looks up its address once).  The call allocates nothing; the caller
+ * still passes the inputs and outputs, as for fckl_forward_ex (weights may be NULL).
+ * The chunk is desc->chunk, or, when it is 0, the largest chunk (up to 8192 tokens,
+ * evened out over N) whose forward buffers fit the array: about 4 V + 12 K bytes per
+ * token of the chunk (7936 tokens at V = 201088, K = 100).
+ * Returns FCKL_ERR_WORKSPACE, before any HIP call, when desc->chunk's buffers do not fit
+ * the array or even a 256-token chunk does not (V above about 7.3 million).  Every call on
+ * a device uses that device's one array, which keeps the last call's contents: calls that
+ * overlap on one device (two streams, two host threads) race and must be serialised by
+ * the caller.  Results are those of fckl_forward_ex run with the same chunk, bit for bit.
+ */
+fckl_status fckl_forward_noalloc(const fckl_desc *desc, const void *h, const void *W,
+                                 const int32_t *topk_idx, const void *topk_logit, const float *weights,
+                                 float *loss_tok, float *lse, float *loss_mean, void *stream);
 
 /*
  * Forward and backward in one call, for a loss that is the last operation of the step,

@@ -35,15 +35,21 @@ static void check_layout(const fckl_desc &d, const Layout &L)
 {
     const size_t Cp = (size_t)L.Cpad, K = (size_t)d.K;
     CHECK(L.Cpad % kTokenTile == 0 && L.Cpad >= L.C && L.Vpad % kVocabTile == 0 && L.Vpad >= d.V);
-    CHECK(L.dh_splits >= 1);
+    CHECK(L.kind == LayoutKind::ForwardOnly ? L.dh_splits == 0 : L.dh_splits >= 1);
     std::vector<std::pair<size_t, size_t>> regions = {
         {L.off_idx, Cp * K * 4}, {L.off_p, Cp * K * 4}, {L.off_zk, Cp * K * 4}, {L.off_psum, Cp * 4},
         {L.off_negent, Cp * 4}, {L.off_cnt, Cp * (size_t)L.cnt_stride}, {L.off_part, (size_t)L.nVt * Cp * 8}};
     // the kept exponentials and their maxima exist only in a keep layout
-    if (L.keep)
+    if (L.kind == LayoutKind::ForwardOnly) {
+        regions.push_back({L.off_err, 16});
+        check_regions(regions, L.total);
+        return;
+    }
+    const bool keep = L.kind == LayoutKind::Keep;
+    if (keep)
         regions.push_back({L.off_mw, 2 * (size_t)L.nVt * Cp * 4});
     regions.push_back({L.off_wsum, 8});
-    if (L.keep)
+    if (keep)
         regions.push_back({L.off_ex, Cp * (size_t)L.Vpad * 2});
     for (const auto &r : std::vector<std::pair<size_t, size_t>>{
              {L.off_gT, (size_t)L.Vpad * Cp * 2}, {L.off_hT, (size_t)d.H * Cp * 2},
@@ -80,11 +86,11 @@ int main()
                     }
                     CHECK(V <= kMaxPitch && vocab_tiles <= kMaxTiles);
                     for (size_t budget : budgets) {
-                        for (bool keep : {false, true}) {
+                        for (LayoutKind kind : {LayoutKind::TwoPass, LayoutKind::Keep, LayoutKind::ForwardOnly}) {
                             Layout L;
-                            if (plan_chunk(&d, budget, &L, keep) == FCKL_OK) {
+                            if (plan_chunk(&d, budget, &L, kind) == FCKL_OK) {
                                 ++planned;
-                                CHECK(L.keep == keep);
+                                CHECK(L.kind == kind);
                                 CHECK(L.total <= (budget ? budget : (size_t(12) << 30)));
                                 CHECK(L.C >= 1 && L.C <= kMaxChunk);
                                 check_layout(d, L);
@@ -93,7 +99,7 @@ int main()
                         FullLayout F;
                         if (plan_full_chunk(&d, H, budget, &F) == FCKL_OK) {
                             CHECK(F.total <= (budget ? budget : (size_t(12) << 30)));
-                            CHECK(F.base.keep);
+                            CHECK(F.base.kind == LayoutKind::Keep);
                             check_layout(d, F.base);
                             const size_t Cp = (size_t)F.base.Cpad;
                             check_regions({{F.off_at, (size_t)F.base.Vpad * Cp * 4},
@@ -109,8 +115,8 @@ int main()
                         const int64_t Cpad = ((int64_t)chunk + 255) / 256 * 256;
                         const bool fits = Cpad <= kMaxPitch && Cpad / 256 * (((int64_t)H + 255) / 256) <= kMaxTiles &&
                                           Cpad * H <= kMaxChunkElems;
-                        for (bool keep : {false, true}) {
-                            const fckl_status ls = make_layout(&d, chunk, &L, keep);
+                        for (LayoutKind kind : {LayoutKind::TwoPass, LayoutKind::Keep, LayoutKind::ForwardOnly}) {
+                            const fckl_status ls = make_layout(&d, chunk, &L, kind);
                             CHECK(fits ? ls == FCKL_OK : ls == FCKL_ERR_UNSUPPORTED);
                             if (ls == FCKL_OK)
                                 check_layout(d, L);

@@ -233,6 +233,31 @@ def test_weighted_and_single_call_entry_points_reject_before_any_hip_call():
 
 
 @fake_addresses
+def test_noalloc_forward_rejects_before_any_hip_call():
+    """fckl_forward_noalloc checks its arguments, and that the chunk's forward buffers fit
+    the library's 64 MiB device array, before any HIP call (the addresses here are fake)."""
+    lib = fckl.load()
+    P = 1 << 40
+    f = _fake
+    d = fckl.make_desc(512, 256, 4096, 10, 1.0)
+    ok = [f(P)] * 4
+    for missing in (0, 1, 2, 3, 5, 6):     # h, W, idx, tl, loss_tok, lse (weights and loss_mean may be NULL)
+        args = ok + [None, f(P), f(P), None]
+        args[missing] = None
+        assert lib.fckl_forward_noalloc(ctypes.byref(d), *args, None) == fckl.ERR_INVALID_ARG, missing
+    assert lib.fckl_forward_noalloc(ctypes.byref(d), f(P + 8), *ok[1:], None, f(P), f(P), None,
+                                    None) == fckl.ERR_INVALID_ARG
+    bad = fckl.make_desc(512, 256, 4096, 10, 0.0)
+    assert lib.fckl_forward_noalloc(ctypes.byref(bad), *ok, None, f(P), f(P), None, None) == fckl.ERR_INVALID_ARG
+    # ~68 MB of forward buffers at 8192 tokens of a 201088-entry vocabulary: over the array
+    big = fckl.make_desc(32768, 2880, 201088, 100, 1.0, chunk=8192)
+    assert lib.fckl_forward_noalloc(ctypes.byref(big), *ok, None, f(P), f(P), None, None) == fckl.ERR_WORKSPACE
+    # a vocabulary whose 256-token chunk alone does not fit
+    huge = fckl.make_desc(1000, 64, 1 << 24, 10, 1.0)
+    assert lib.fckl_forward_noalloc(ctypes.byref(huge), *ok, None, f(P), f(P), None, None) == fckl.ERR_WORKSPACE
+
+
+@fake_addresses
 def test_misaligned_pointers_are_refused():
     """h, W (and the teacher's h_t, W_t) are read and dH is written in 16-byte pieces: a
     pointer off that alignment is refused before any HIP call."""
