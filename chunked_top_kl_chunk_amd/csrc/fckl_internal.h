@@ -78,7 +78,8 @@ struct Layout {
 // Workspace of the teacher top-K extraction (its own, much smaller than the loss's).
 struct TopkLayout {
     int32_t C = 0, Cpad = 0, nVt = 0;
-    int32_t nSubFull = 0;   // maxima per token of a first pass over every tile (per tile, or per 32-row slice)
+    int32_t nSubFull = 0;   // maxima per token of a first pass over every tile (per tile, or per 32- or
+                            // 16-row slice)
     int32_t nSubPart = 0;   // maxima per token of a first pass over every kTopkStride-th tile (64-row
                             // slices); 0 = that pass is not used
     size_t off_tmax = 0;    // f32   [max(nSubFull, nSubPart), Cpad]  slice maxima

@@ -727,9 +727,12 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepParams p)
     ne = wave_sum(ne);
     if (p.scaled && live) {
         const float gsc = (p.gw ? p.gcoef * p.gw[t] * *p.ginv : p.gcoef) * (p.gmul ? *p.gmul : 1.0f);
-        pr[0] *= gsc;
-        pr[1] *= gsc;
-        ps *= gsc;
+        // A token whose scale is 0 (a masked token) contributes nothing to the gradient,
+        // whatever its cached logits hold: padding rows often carry -inf or NaN there,
+        // and 0 times the NaN they give would reach every row of dW.
+        pr[0] = gsc != 0.0f ? pr[0] * gsc : 0.0f;
+        pr[1] = gsc != 0.0f ? pr[1] * gsc : 0.0f;
+        ps = gsc != 0.0f ? ps * gsc : 0.0f;
     }
     __syncthreads();
     bool bad = false;
@@ -1077,12 +1080,15 @@ __global__ __launch_bounds__(1024) void mean_kernel(const float *x, int64_t n, f
 }
 
 // Weighted mean sum_i w_i x_i / sum_i w_i (0 when the weights sum to 0), fixed order, fp64.
+// Tokens of weight 0 are left out of the numerator, so a masked token whose loss is not
+// finite (cached logits of -inf or NaN) does not reach the mean.
 __global__ __launch_bounds__(1024) void weighted_mean_kernel(const float *x, const float *w, int64_t n, float *out)
 {
     __shared__ double s[1024], sw[1024];
     double a = 0.0, b = 0.0;
     for (int64_t i = threadIdx.x; i < n; i += 1024) {
-        a += (double)w[i] * (double)x[i];
+        if (w[i] != 0.0f)
+            a += (double)w[i] * (double)x[i];
         b += (double)w[i];
     }
     s[threadIdx.x] = a;
@@ -1269,7 +1275,7 @@ __global__ __launch_bounds__(kSgThreads) void softmax_grad_kernel(SoftGradParams
     for (int i = 0; i < kRows; ++i) {
         const int rl = r0 + kStride * i, tok = n0 + rl;
         u32x4 out = {0u, 0u, 0u, 0u};
-        if (tok < p.rows) {
+        if (tok < p.rows && gsc[i] != 0.0f) {    // a masked token (scale 0) gets g = 0
             const float fs = gsc[i] * f[i];
             float v[8];
 #pragma unroll
@@ -1585,7 +1591,7 @@ __global__ __launch_bounds__(256) void full_grad_kernel(FullGradParams p)
         float g[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-            g[c] = (rb + c < vlim) ? cc * (e[c] * fq - fast_exp2(a[c] - lt)) : 0.0f;
+            g[c] = (rb + c < vlim && cc != 0.0f) ? cc * (e[c] * fq - fast_exp2(a[c] - lt)) : 0.0f;
         cell[0] = pack_bf16x2(g[0], g[1]);
         cell[1] = pack_bf16x2(g[2], g[3]);
     }
@@ -1619,7 +1625,8 @@ struct TopkParams {
     int H, V, rows, Cpad, nVt, nNt;
     int stride;             // pass 1 visits vocabulary tiles 0, stride, 2 stride, ... (pass 2: 1)
     int nTm;                // vocabulary tiles visited: ceil(nVt / stride)
-    int slices;             // maxima per visited tile: 1, 4 (64-row slices) or 8 (32-row slices)
+    int slices;             // maxima per visited tile: 1, 4 (64-row slices), 8 (32-row slices) or 16
+                            // (16-row slices: the rows one lane holds of a 32-row block)
     const uint32_t *guard;  // NULL, or run only when *guard != 0
     float *tmax;            // [slices nTm, Cpad] maxima (pass 1)
     const float *thr;       // [Cpad] thresholds (pass 2)
@@ -1679,6 +1686,8 @@ __device__ __forceinline__ void topk_tile(const TopkParams &p, char *smem, int t
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     mx = fmaxf(mx, (32 * i + 8 * (r >> 2) + (r & 3) < lim) ? acc[i][j][r] : -__builtin_inff());
+                if (p.slices == 16 && tok < p.rows)
+                    p.tmax[(size_t)(16 * ts + 2 * (G::WTM / 32) * wm + 2 * i + (lane >> 5)) * p.Cpad + tok] = mx;
                 mx = fmaxf(mx, __shfl_xor(mx, 32));
                 tile_mx[j] = fmaxf(tile_mx[j], mx);
                 pair_mx = fmaxf(pair_mx, mx);

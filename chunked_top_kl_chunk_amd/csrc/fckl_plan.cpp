@@ -145,8 +145,12 @@ fckl_status make_topk_layout(const fckl_desc *d, int32_t chunk, TopkLayout *L)
     o.Cpad = (int32_t)align_up((size_t)chunk, kTokenTile);
     o.nVt = (d->V + kVocabTile - 1) / kVocabTile;
     // maxima per token of a first pass over every tile: one per tile when there are at
-    // least K tiles, else one per 32-row slice (8 per tile)
-    o.nSubFull = o.nVt >= d->K ? o.nVt : o.nVt * (kVocabTile / 32);
+    // least K tiles, else one per 32-row slice (8 per tile), else one per 16-row slice (16
+    // per tile).  With fewer than K maxima even then (V <= 2048 for K <= 128) every logit
+    // is a candidate, at most V <= kTopkCap of them.
+    o.nSubFull = o.nVt >= d->K ? o.nVt
+                 : o.nVt * (kVocabTile / 32) >= d->K ? o.nVt * (kVocabTile / 32)
+                                                     : o.nVt * (kVocabTile / 16);
     if (o.nSubFull > kTopkMaxSub)
         return FCKL_ERR_UNSUPPORTED;
     // a first pass over every kTopkStride-th tile (one maximum per 64-row slice) when it

@@ -133,10 +133,13 @@ class FusedChunkedKLLoss(torch.nn.Module):
             w = m if w is None else w * m
         if self.ignore_index is not None:
             keep = idx[:, 0] != self.ignore_index
-            if not bool(keep.all()):
-                w = keep.to(torch.float32) if w is None else w * keep.to(torch.float32)
-                # ignored rows get a valid placeholder index row; their weight is 0
-                idx = torch.where(keep[:, None], idx, torch.arange(K, device=idx.device, dtype=idx.dtype)[None, :])
+            w = keep.to(torch.float32) if w is None else w * keep.to(torch.float32)
+            # ignored rows get a valid placeholder index row; their weight is 0
+            idx = torch.where(keep[:, None], idx, torch.arange(K, device=idx.device, dtype=idx.dtype)[None, :])
+        if w is not None:
+            # masked and ignored rows get finite placeholder logits too (padding rows often
+            # hold -inf or NaN there); with weight 0 they reach neither the mean nor a gradient
+            tl = torch.where((w != 0)[:, None], tl, torch.zeros((), dtype=tl.dtype, device=tl.device))
         wants_grad = torch.is_grad_enabled() and (hidden.requires_grad or lm_head_weight.requires_grad)
         fn = FusedChunkedKLSingleCallFunction if self.single_call and wants_grad else FusedChunkedKLFunction
         return fn.apply(h.contiguous(), lm_head_weight.contiguous(), idx.contiguous(), tl.contiguous(),

@@ -58,11 +58,14 @@ CASES = [
     (70, 300, 256, 4100, 100, 0),
     (71, 517, 136, 1000, 10, 256),
     (72, 130, 2880, 777, 128, 0),
-    (73, 64, 512, 300, 100, 0),          # fewer 32-row slices than K: every logit is a candidate
+    (73, 64, 512, 300, 100, 0),          # fewer 16-row slices than K: every logit is a candidate
+    (74, 200, 256, 3000, 100, 0),        # fewer 32-row slices than K, 2048 < V: 16-row slices
+    (75, 96, 128, 3840, 128, 0),         # the same at the largest K
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=["K100", "K10-ragged", "K128-H2880", "small-V"])
+@pytest.mark.parametrize("case", CASES, ids=["K100", "K10-ragged", "K128-H2880", "small-V", "V3000-16-row-slices",
+                                           "V3840-K128"])
 def test_topk_matches_oracle(case):
     seed, N, H, V, K, chunk = case
     say("case: top-K", case)

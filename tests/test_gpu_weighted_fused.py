@@ -233,3 +233,52 @@ def test_single_call_validate():
         with pytest.raises(fckl.FCKLError) as e:
             fckl.forward_backward(t[0], t[1], bad, t[3], T=1.0, validate=True)
         assert e.value.status == fckl.ERR_INDEX
+
+
+def test_masked_rows_with_non_finite_cached_logits():
+    """Padding rows often carry -inf or NaN as cached logits.  With weight 0 such a row
+    reaches neither the weighted mean nor any gradient: the two calls, the single call
+    and the autograd module give the oracle's results for the same batch with those
+    rows' logits finite (their weight is 0 either way); the kept rows' loss and every
+    lse match it too."""
+    N, H, V, K, T = 600, 160, 3000, 12, 1.2
+    say("case: masked rows with non-finite cached logits", N, H, V, K, T)
+    h, W, idx, tl = synthetic(51, N, H, V, K, T)
+    w = weights_for(52, N, zero_frac=0.0)
+    bad = np.random.default_rng(53).permutation(N)[:60]
+    w[bad] = 0.0
+    tl_bad = tl.copy()
+    tl_bad[bad[:20]] = -np.inf
+    tl_bad[bad[20:35]] = np.nan
+    tl_bad[bad[35:50], : K // 2] = np.nan
+    tl_bad[bad[50:]] = np.inf
+    dh, dW_, di, dt = arrays(h, W, idx, tl_bad)
+    wt = torch.from_numpy(w).to(device())
+    kept = w != 0.0
+    ref_loss, ref_lse = oracle.forward(h, W, idx, tl, T)
+    ref_mean = oracle.weighted_mean(h, W, idx, tl, T, w)
+    ref_dH, ref_dW = oracle.weighted_backward(h, W, idx, tl, T, w, grad_scale=1.0)
+
+    def check(loss, lse, mean, dH, dWg, what):
+        torch.cuda.synchronize()
+        loss, lse, mean, dH, dWg = (v.detach().cpu().numpy() for v in (loss, lse, mean, dH, dWg))
+        check_loss(loss[kept], ref_loss[kept], what)
+        assert float(np.abs(lse - ref_lse).max()) <= LSE_ATOL, what + " lse"
+        assert np.isfinite(mean).all(), what + " mean not finite"
+        e_mean = abs(float(mean.reshape(-1)[0]) - ref_mean) / abs(ref_mean)
+        assert e_mean <= 1e-3, "%s weighted mean rel err %.3e" % (what, e_mean)
+        check_grad(dH, ref_dH, what + " dH")
+        check_grad(dWg, ref_dW, what + " dW")
+        assert np.abs(dH[~kept]).max() == 0.0, what + ": masked tokens got a gradient"
+
+    loss, lse, mean = fckl.forward(dh, dW_, di, dt, T=T, chunk=256, weights=wt)
+    dH, dWg = fckl.backward(dh, dW_, di, dt, lse, T=T, chunk=256, weights=wt)
+    check(loss, lse, mean, dH, dWg, "two calls")
+    check(*fckl.forward_backward(dh, dW_, di, dt, T=T, weights=wt, chunk=256), "single call")
+    for single in (False, True):
+        hl = dh.float().requires_grad_(True)
+        Wl = dW_.float().requires_grad_(True)
+        mod = FusedChunkedKLLoss(temperature=T, chunk=256, single_call=single)
+        out = mod(hl.to(torch.bfloat16), Wl.to(torch.bfloat16), di, dt, weights=wt)
+        out.backward()
+        check(loss, lse, out.detach().reshape(1), hl.grad, Wl.grad, "module single_call=%s" % single)
