@@ -23,6 +23,12 @@ loss.backward()), with the two passes and with single_call=True.
 (fckl_full_forward_backward), with a teacher of the same shape (a seeded perturbed copy
 of the student's hidden states and head, synth.full_teacher): 2 N V Ht + 6 N V H flop
 per step.
+`w_stream` gives, for each product that streams the LM head, its algorithmic W bytes per
+launch (V H bf16, read once per launch) over the live launch time.  `memory_slope` runs
+one step at N = 32K .. 256K tokens with the step's chunk and fits peak = a + b N: b is the
+per-token cost of the inputs and outputs, with no N x V term.  `dense_baseline` is the
+same loss with the N x V logits materialised in eager torch (peak memory and step time),
+run last with only the inputs resident.
 """
 from __future__ import annotations
 
@@ -83,13 +89,17 @@ def main():
     ap.add_argument("--tokens", type=int, default=0, help="override N (for quick runs)")
     ap.add_argument("--chunk", type=int, default=0, help="tokens per chunk (0 = library scheduler)")
     ap.add_argument("--cpu-tokens", type=int, default=256, help="oracle sample size for cpu_baseline (0 = skip)")
-    ap.add_argument("--dense", action="store_true", help="also measure peak memory of a dense torch KL baseline")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense torch KL baseline (N x V logits materialised: peak memory and step time)")
+    ap.add_argument("--no-slope", action="store_true",
+                    help="skip the peak-memory fit over N = 32K .. 256K tokens")
     ap.add_argument("--no-single-call", action="store_true",
                     help="skip timing fckl_forward_backward (the single-call path) after the main measurement")
     ap.add_argument("--no-topk", action="store_true",
                     help="skip timing the teacher-side top-K extraction (fckl_topk) of the same hidden states")
-    ap.add_argument("--sweep", default="",
-                    help="comma-separated chunk sizes: also time the step and its peak memory at each")
+    ap.add_argument("--sweep", default="4096",
+                    help="comma-separated chunk sizes: also time the step and its peak memory at each (default "
+                         "4096, the chunk at which the 32K-token step peaks under 7 GiB; '' = none)")
     ap.add_argument("--no-module", action="store_true",
                     help="skip the torch autograd module leg (FusedChunkedKLLoss, both modes)")
     ap.add_argument("--no-full", action="store_true",
@@ -174,6 +184,16 @@ def main():
         pass_ms[name] = (time.perf_counter() - t0) * 1e3 / reps
     log("forward %.2f ms, backward %.2f ms" % (pass_ms["forward"], pass_ms["backward"]))
     gemms = ("fwd_logits", "bwd_logits", "dh", "dw")
+    # the products that stream the LM head read its V H bf16 values once per launch
+    w_bytes = 2.0 * V * H
+    w_stream = {"bytes_per_launch": w_bytes,
+                "note": "algorithmic W bytes (W, W, W^T) over the live mean launch time; the L2-miss bytes "
+                        "per launch (FETCH_SIZE / TCC_EA0_RDREQ_DRAM count requests to the memory side, which the "
+                        "256 MB MALL serves in part, so an upper bound on HBM bytes: no counter on this GPU "
+                        "separates MALL hits from HBM reads) are in profiles/hbm_bytes_<workload>.md"}
+    for name in ("fwd_logits", "bwd_logits", "dh"):
+        d = kernels[name]
+        w_stream[name + "_gb_per_s"] = round(w_bytes / (d["ms"] / d["launches"] * 1e-3) / 1e9, 1)
     for name, d in kernels.items():
         d["avg_ms"] = d["ms"] / d["launches"]
         d["ms_per_step"] = d["ms"] / args.steps
@@ -210,6 +230,7 @@ def main():
         "step_tflops": round(step_tflops, 1),
         "peak_gib": round(peak_bytes / GiB, 3),
         "workspace_gib": round(ws_bytes / GiB, 3),
+        "w_stream": w_stream,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
     }
@@ -218,16 +239,24 @@ def main():
         # The same step as one fckl_forward_backward call: each chunk's logits are formed
         # once (6 N V H flop instead of 8).  Reported beside the main line, which times
         # the two passes the method defines.
+        # its workspace also holds the chunk's kept exponentials (fckl_single_plan)
+        sdesc = fckl.desc_for(h, W, idx, tl, T, chunk)
+        sws_bytes = fckl.single_plan(sdesc)[1]
+        del ws
+        sws = torch.empty(sws_bytes, dtype=torch.uint8, device=dev)
+
         def single(profile=None):
-            fckl.forward_backward(h, W, idx, tl, T=T, chunk=chunk, ws=ws, loss_tok=loss, lse=lse, loss_mean=mean,
+            fckl.forward_backward(h, W, idx, tl, T=T, chunk=chunk, ws=sws, loss_tok=loss, lse=lse, loss_mean=mean,
                                   dH=dH, dW=dW, profile=profile)
         single()
         torch.cuda.synchronize()
         ms1, k1 = timed_steps(fckl, single, args.steps, nchunks)
+        del sws
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         log("single call: %.2f ms/step, %.0f tokens/s" % (ms1, N * 1e3 / ms1))
         out["single_call"] = {
             "value": round(N * 1e3 / ms1, 1), "unit": "tokens/s", "ms_per_step": round(ms1, 3),
-            "flops_per_step": 6.0 * N * V * H,
+            "flops_per_step": 6.0 * N * V * H, "workspace_gib": round(sws_bytes / GiB, 3),
             "mfma_frac": round(6.0 * N * V * H / (ms1 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "kernels": {k: {"launches": v["launches"], "ms_per_step": round(v["ms"] / args.steps, 4)}
                         for k, v in k1.items()},
@@ -353,11 +382,18 @@ def main():
         del fws, h_t, W_t
         ws = None
 
-    if args.dense:
+    if not args.no_slope:
+        del ws
+        ws = None
+        out["memory_slope"] = memory_slope(W, K, chunk)
+
+    if not args.no_dense:
         # the fused path's workspace and outputs are released first: the dense loss is
         # measured with only the inputs resident
         del ws, loss, lse, mean, dH, dW
         out["dense_baseline"] = dense_baseline(h, W, idx, tl, T)
+        if out["dense_baseline"].get("ok"):
+            out["dense_baseline"]["fused_peak_gib"] = out["peak_gib"]
 
     if args.cpu_tokens > 0:
         out["cpu_baseline"] = cpu_baseline(x, wl, args.cpu_tokens)
@@ -469,6 +505,53 @@ def measured_traffic(workload, chunk, kernel):
         if name.startswith(KERNEL_NAMES[kernel]):
             return round(v["read_bytes"] + v["write_bytes"])
     return None
+
+
+def memory_slope(W, K, chunk, Ns=(32768, 65536, 131072, 262144), seed=7):
+    """Peak device memory of one fwd+bwd step at growing N with a fixed chunk, the head W
+    resident throughout.  Inputs are drawn on the device from a seeded generator (their
+    values do not change the memory): h ~ N(0,1), K distinct indices per token
+    (a random offset plus k * (V // K), modulo V), logits N(0, 3^2) sorted descending.
+    Fits peak = a + b N by least squares; b is the per-token cost, to compare with the
+    inputs and outputs alone (2H + 4H + 6K + 8 bytes) and with the 4 V bytes per token
+    that one fp32 logit row would add."""
+    import numpy as np
+    import torch
+    import chunked_top_kl_chunk_amd as fckl
+    dev = W.device
+    V, H = W.shape
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    points = []
+    for N in Ns:
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        h = torch.randn(N, H, device=dev, dtype=torch.bfloat16, generator=gen)
+        off = torch.randint(0, V, (N, 1), device=dev, generator=gen)
+        idx = ((off + torch.arange(K, device=dev) * (V // K)) % V).to(torch.int32)
+        tl = (torch.randn(N, K, device=dev, generator=gen) * 3.0).sort(dim=1, descending=True).values
+        tl = tl.to(torch.bfloat16)
+        t0 = time.perf_counter()
+        _, lse, _ = fckl.forward(h, W, idx, tl, T=1.0, chunk=chunk)
+        dH, dW = fckl.backward(h, W, idx, tl, lse, T=1.0, chunk=chunk)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3
+        peak = torch.cuda.max_memory_allocated()
+        points.append({"N": N, "peak_gib": round(peak / GiB, 3), "step_peak_minus_resident_gib":
+                       round((peak - base) / GiB, 3), "ms_per_step": round(ms, 1)})
+        log("memory slope: N=%d peak %.2f GiB (%.2f GiB above the resident head), %.1f ms" %
+            (N, peak / GiB, (peak - base) / GiB, ms))
+        del h, off, idx, tl, lse, dH, dW
+    n = np.array([p["N"] for p in points], np.float64)
+    y = np.array([p["peak_gib"] for p in points], np.float64) * GiB
+    b, a = np.polyfit(n, y, 1)
+    torch.cuda.empty_cache()
+    return {"chunk": chunk, "points": points, "bytes_per_token": round(float(b), 1),
+            "intercept_gib": round(float(a) / GiB, 3),
+            "inputs_outputs_bytes_per_token": 2 * H + 4 * H + 6 * K + 8,
+            "one_fp32_logit_row_bytes_per_token": 4 * V}
 
 
 def dense_baseline(h, W, idx, tl, T, reps=2):

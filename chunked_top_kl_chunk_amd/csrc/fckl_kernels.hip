@@ -19,7 +19,8 @@
 //                    g^T [V, C], the operand of both products below
 //   dh               dH_chunk^T = W^T . g^T over the vocabulary (g^T read through
 //                    transposing LDS reads; split over the vocabulary, fixed-order reduce)
-//   dw               dW += g^T . h_chunk (fp32 read-modify-write, chunk after chunk)
+//   dw               dW += g^T . h_chunk (fp32, chunk after chunk: the first chunk stores,
+//                    the others add with fp32 atomics at L2, one adder per element)
 //   transpose        W -> W^T once per backward call, h_chunk -> h_chunk^T per chunk
 //
 // GEMM core: 256 x 256 tiles, 512 threads = 8 wave64s, each wave owns a 128 x 64 block
@@ -1993,29 +1994,26 @@ __global__ __launch_bounds__(G::NT) void dw_kernel(DwParams p)
                                       p.rows, acc);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = G::wm_of(wave), wn = G::wn_of(wave);
-    // Each lane owns one hidden column of 16 * MB rows per fragment column.  When
-    // accumulating, all old values of a fragment column are read before any is written,
-    // so the reads are in flight together instead of each waiting behind the store
-    // before it.
+    // Each lane owns one hidden column of 16 * MB rows per fragment column.  Every dW
+    // element is written by one work-group per launch, and the launches run chunk after
+    // chunk, so adding with a hardware fp32 atomic (no return value) gives the same sum
+    // as a read-modify-write without waiting for the old value.
 #pragma unroll
     for (int j = 0; j < G::NB; ++j) {
         const int col = n0 + G::col_of(wn, j, lane);
         if (col < p.H) {
-            float old[G::MB][16];
 #pragma unroll
             for (int i = 0; i < G::MB; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = m0 + G::row_of(wm, i, r, lane);
-                    old[i][r] = (p.accumulate && row < p.V) ? p.dW[(size_t)row * p.H + col] : 0.0f;
-                }
-#pragma unroll
-            for (int i = 0; i < G::MB; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + G::row_of(wm, i, r, lane);
-                    if (row < p.V)
-                        p.dW[(size_t)row * p.H + col] = old[i][r] + acc[i][j][r];
+                    if (row < p.V) {
+                        float *dst = p.dW + (size_t)row * p.H + col;
+                        if (p.accumulate)
+                            unsafeAtomicAdd(dst, acc[i][j][r]);
+                        else
+                            *dst = acc[i][j][r];
+                    }
                 }
         }
     }

@@ -182,26 +182,32 @@ def test_full_teacher_at_full_size():
 
 
 def test_peak_memory_has_no_tokens_times_vocab_term():
-    """Peak device memory of fwd+bwd at the 32K shape's H, V, K for growing N, fixed chunk:
-    linear in N with the per-token cost of the inputs and outputs only."""
+    """Peak device memory of fwd+bwd at the 32K shape's H, V, K for growing N up to 256K
+    tokens, fixed chunk: linear in N with the per-token cost of the inputs and outputs
+    only."""
     dev = device()
     H, V, K, chunk = 2880, 201088, 100, 4096
-    W = (torch.randn(V, H, device=dev) * 0.02).to(torch.bfloat16)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(31)
+    W = (torch.randn(V, H, device=dev, generator=gen) * 0.02).to(torch.bfloat16)
     peaks = []
-    Ns = (4096, 16384, 32768)
+    Ns = (4096, 16384, 32768, 65536, 131072, 262144)
     for N in Ns:
+        say("case: peak memory N=%d" % N)
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         torch.cuda.reset_peak_memory_stats()
         base = torch.cuda.memory_allocated()
-        h = torch.randn(N, H, device=dev, dtype=torch.bfloat16)
-        idx = torch.randint(0, V, (N, K), device=dev, dtype=torch.int32)
-        tl = torch.randn(N, K, device=dev, dtype=torch.bfloat16)
+        h = torch.randn(N, H, device=dev, dtype=torch.bfloat16, generator=gen)
+        # K distinct indices per token: a random offset plus k (V // K), modulo V
+        off = torch.randint(0, V, (N, 1), device=dev, generator=gen)
+        idx = ((off + torch.arange(K, device=dev) * (V // K)) % V).to(torch.int32)
+        tl = torch.randn(N, K, device=dev, dtype=torch.bfloat16, generator=gen)
         loss, lse, _ = fckl.forward(h, W, idx, tl, T=1.0, chunk=chunk)
         dH, dW = fckl.backward(h, W, idx, tl, lse, T=1.0, chunk=chunk)
         torch.cuda.synchronize()
         peaks.append(torch.cuda.max_memory_allocated() - base)
-        del h, idx, tl, loss, lse, dH, dW
+        del h, off, idx, tl, loss, lse, dH, dW
     per_token = [(peaks[i + 1] - peaks[i]) / (Ns[i + 1] - Ns[i]) for i in range(len(Ns) - 1)]
     expect = 2 * H + 4 * H + K * (4 + 2) + 4 + 4          # h, dH, idx, logits, loss, lse
     say("peak bytes %s, per-token slope %s (expected %d, an N x V term would add %d)"
