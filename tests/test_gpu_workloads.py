@@ -3,15 +3,25 @@
 
 At these sizes the oracle cannot run every token, so:
   * per-token outputs (loss, lse and dH rows) are compared with the oracle on a seeded
-    sample of tokens (the oracle computes each token on its own, normalising dH by
-    the full N); the sample includes the large-norm rows of the stress workload;
+    sample of 512 tokens (the oracle computes each token on its own, normalising dH by
+    the full N); the sample includes 64 of the stress workload's large-norm rows;
   * dW is compared element by element, over the full vocabulary and hidden size, on a
-    separate run of the same shapes restricted to a sampled subset of tokens;
+    separate run of the same shapes restricted to a sampled subset of 512 tokens, run in
+    four chunks of 128 so that the fp32 accumulation of dW across chunks is checked
+    against the oracle;
   * at full size, properties that hold at any size are checked: every per-token loss
     is >= 0, the mean equals the average of the per-token losses, the rows of dW sum
     to zero (the softmax part of the gradient sums to the teacher mass it removes),
-    and <dW, W> = <dH, h> (both equal sum_i <g_i, z_i>).
+    and <dW, W> = <dH, h> (both equal sum_i <g_i, z_i>);
+  * the 256K-token workload runs at chunks of 1024, 2048, 4096 and 8192 tokens: the
+    per-token loss and lse do not depend on the chunk, bit for bit, and dH and dW agree
+    to fp32 reordering (32 to 256 chunks of accumulation).
+An oracle check of dW rows over all N tokens would need every token's lse, 2 N V H
+flop in fp64 on the host (about 9 minutes at 32K tokens, over an hour at 256K), so
+the multi-chunk accumulation is pinned by the subset run and the chunk sweep instead.
 """
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -24,8 +34,17 @@ from gpu_util import GRAD_TOL, LSE_ATOL, check_grad, check_loss, device, say, up
 pytestmark = [pytest.mark.gpu, pytest.mark.slow,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
 
-SAMPLE_ROWS = 48
-DW_TOKENS = 48
+SAMPLE_ROWS = 512
+SCALED_ROWS = 64        # of the stress workload's x20 rows, always in the sample
+DW_TOKENS = 512
+DW_CHUNK = 128          # the subset's dW accumulates over four chunks
+
+
+@functools.lru_cache(maxsize=2)
+def inputs(key):
+    """The workload's seeded inputs, drawn once per session (the 256K-token ones take
+    seconds to draw)."""
+    return synth.make_inputs(synth.WORKLOADS[key], device=device())
 
 
 def _run_full(wl, x):
@@ -46,7 +65,7 @@ def _run_full(wl, x):
     ip_h = (dH.double() * h.double()).sum().item()
     out = dict(loss=loss.cpu().numpy(), lse=lse.cpu().numpy(), mean=float(mean.item()), chunk=chunk,
                sum_rows=sum_rows, scale_rows=scale_rows, ip_w=ip_w, ip_h=ip_h)
-    rows = synth.sample_rows(wl, SAMPLE_ROWS, must_include=synth.scaled_rows(wl)[:8])
+    rows = synth.sample_rows(wl, SAMPLE_ROWS, must_include=synth.scaled_rows(wl)[:SCALED_ROWS])
     out["rows"] = rows
     out["dH_rows"] = dH[torch.from_numpy(rows).to(dev)].cpu().numpy()
     del dH, dW, ws, h, W, idx, tl, loss, lse
@@ -57,7 +76,7 @@ def _run_full(wl, x):
 def _check_workload(key):
     wl = synth.WORKLOADS[key]
     say("case: full workload", key, wl.name)
-    x = synth.make_inputs(wl, device=device())
+    x = inputs(key)
     g = _run_full(wl, x)
     # properties at full size
     assert np.isfinite(g["loss"]).all()
@@ -77,20 +96,20 @@ def _check_workload(key):
     e_dH = check_grad(g["dH_rows"], ref_dH, key + " dH rows")
     say("%s: chunk %d, sampled %d rows: loss %.2e lse %.2e dH %.2e; sum_v dW %.1e of %.1e; <dW,W> %.6e <dH,h> %.6e"
         % (key, g["chunk"], rows.size, e_loss, e_lse, e_dH, g["sum_rows"], g["scale_rows"], g["ip_w"], g["ip_h"]))
-    # dW over the full vocabulary x hidden size, on a token subset
+    # dW over the full vocabulary x hidden size, on a token subset run in several chunks
     sub = synth.sample_rows(wl, DW_TOKENS)
     dev = device()
     hb = torch.from_numpy(x.h_bits[sub].view(np.int16)).to(dev).view(torch.bfloat16)
     Wb = torch.from_numpy(x.W_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     ib = torch.from_numpy(np.ascontiguousarray(x.idx[sub])).to(dev)
     tb = torch.from_numpy(x.tl_bits[sub].view(np.int16)).to(dev).view(torch.bfloat16)
-    _, lse_s, _ = fckl.forward(hb, Wb, ib, tb, T=wl.T, chunk=g["chunk"])
-    dH_s, dW_s = fckl.backward(hb, Wb, ib, tb, lse_s, T=wl.T, chunk=g["chunk"])
+    _, lse_s, _ = fckl.forward(hb, Wb, ib, tb, T=wl.T, chunk=DW_CHUNK)
+    dH_s, dW_s = fckl.backward(hb, Wb, ib, tb, lse_s, T=wl.T, chunk=DW_CHUNK)
     torch.cuda.synchronize()
     ref_dHs, ref_dWs = oracle.backward(x.h[sub], W64, x.idx[sub], x.tl[sub], wl.T)
     e_dHs = check_grad(dH_s.cpu().numpy(), ref_dHs, key + " subset dH")
     e_dWs = check_grad(dW_s.cpu().numpy(), ref_dWs, key + " subset dW")
-    say("%s: %d-token subset, full V x H: dH %.2e dW %.2e" % (key, sub.size, e_dHs, e_dWs))
+    say("%s: %d-token subset in chunks of %d, full V x H: dH %.2e dW %.2e" % (key, sub.size, DW_CHUNK, e_dHs, e_dWs))
 
 
 @pytest.mark.timeout(900)
@@ -99,13 +118,44 @@ def test_full_workload(key):
     _check_workload(key)
 
 
-def test_single_call_at_full_size():
-    """fckl_forward_backward on the 32K-token workload: the forward outputs equal the
-    two-call path's bit for bit, the gradients agree with it to the gradient tolerance,
-    and the size-independent identities hold."""
-    wl = synth.WORKLOADS["c3"]
+@pytest.mark.timeout(900)
+def test_long_context_chunk_sweep():
+    """The 256K-token workload (T = 2) at every chunk size the long-context configuration
+    sweeps: per-token loss and lse bit for bit equal across chunks (each token's logits
+    come from the same tiles whatever chunk holds it), dH and dW equal to fp32 reordering
+    (the dH vocabulary splits and the number of dW accumulation steps depend on the chunk)."""
+    key = "c4"
+    wl = synth.WORKLOADS[key]
+    x = inputs(key)
+    dev = device()
+    h, W, idx, tl = upload(x, dev)
+    ref = None
+    for chunk in (8192, 4096, 2048, 1024):
+        say("case: chunk sweep", key, "chunk", chunk)
+        loss, lse, mean = fckl.forward(h, W, idx, tl, T=wl.T, chunk=chunk)
+        dH, dW = fckl.backward(h, W, idx, tl, lse, T=wl.T, chunk=chunk)
+        torch.cuda.synchronize()
+        if ref is None:
+            ref = (loss, lse, mean, dH, dW)
+            continue
+        assert torch.equal(loss, ref[0]) and torch.equal(lse, ref[1]), "chunk %d: per-token outputs differ" % chunk
+        e_mean = abs(float(mean.item()) - float(ref[2].item())) / abs(float(ref[2].item()))
+        e_dH = float((dH - ref[3]).abs().max() / ref[3].abs().max())
+        e_dW = float((dW - ref[4]).abs().max() / ref[4].abs().max())
+        say("chunk %d against 8192: mean %.1e dH %.1e dW %.1e" % (chunk, e_mean, e_dH, e_dW))
+        assert e_mean <= 1e-6 and e_dH <= 1e-5 and e_dW <= 1e-5
+        del loss, lse, mean, dH, dW
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("key", ["c3", "c4"])
+def test_single_call_at_full_size(key):
+    """fckl_forward_backward on the 32K- and 256K-token workloads: the forward outputs
+    equal the two-call path's bit for bit, the gradients agree with it to the gradient
+    tolerance, and the size-independent identities hold."""
+    wl = synth.WORKLOADS[key]
     say("case: single call, full workload", wl.name)
-    x = synth.make_inputs(wl, device=device())
+    x = inputs(key)
     h, W, idx, tl = upload(x, device())
     desc = fckl.desc_for(h, W, idx, tl, wl.T)
     chunk, _ = fckl.plan(desc)
@@ -130,14 +180,15 @@ def test_single_call_at_full_size():
 
 
 @pytest.mark.timeout(900)
-def test_full_teacher_at_full_size():
-    """fckl_full_forward_backward on the 32K-token shape, teacher of the same shape (a
-    perturbed copy of the student), in the launch configuration the benchmark uses:
-    size-independent identities at full size, sampled tokens against the oracle, and
-    dW over the full vocabulary x hidden size on a token subset."""
-    wl = synth.WORKLOADS["c3"]
+@pytest.mark.parametrize("key", ["c3", "c4"])
+def test_full_teacher_at_full_size(key):
+    """fckl_full_forward_backward on the 32K- and 256K-token shapes, teacher of the same
+    shape (a perturbed copy of the student), in the launch configuration the benchmark
+    uses: size-independent identities at full size, sampled tokens against the oracle,
+    and dW over the full vocabulary x hidden size on a token subset."""
+    wl = synth.WORKLOADS[key]
     say("case: full teacher, full workload", wl.name)
-    x = synth.make_inputs(wl, device=device())
+    x = inputs(key)
     tch = synth.full_teacher(wl, x)
     dev = device()
 
