@@ -4,6 +4,8 @@ here return before any HIP call)."""
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -26,6 +28,45 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(fckl.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
+
+
+# Writable data that the toolchain puts into any HIP shared library: the C runtime's and
+# the dynamic linker's bookkeeping and the registration of the embedded GPU code.
+TOOLCHAIN_DATA = re.compile(
+    r"^(?:_DYNAMIC|_GLOBAL_OFFSET_TABLE_|__dso_handle|__init|__fini|__TMC_END__|DW\.ref\..*"
+    r"|__do_init\..*|__do_fini\..*|completed\.\d+|__hip_fatbin_wrapper|__hip_gpubin_handle_\w+"
+    r"|__hip_cuid_\w+|__do_global_dtors_aux_fini_array_entry|__frame_dummy_init_array_entry)$")
+# The host-side handle of each kernel: an object whose address names the kernel at launch.
+KERNEL_HANDLE = re.compile(r"^(?:void )?fckl::\(anonymous namespace\)::\w+_kernel(?:<.*>)?\(.*\)$")
+# The allocation-free forward's device array and its per-device address table.
+NOALLOC_STATE = {"fckl::scratch", "fckl::g_scratch_once", "fckl::g_scratch_ptr", "fckl::g_scratch_err"}
+
+
+def test_no_writable_global_state_beyond_the_noalloc_table():
+    """The library keeps no mutable globals: no cached device properties, default
+    budgets or handles that one call could leave for the next.  Its writable data
+    symbols are the toolchain's, the kernels' host handles, and the allocation-free
+    forward's device array with its per-device address table."""
+    fckl.load()
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm (binutils) is not installed")
+    out = subprocess.run([nm, "-C", "--defined-only", fckl.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    writable, noalloc = [], set()
+    for line in out.splitlines():
+        parts = line.split(None, 2)
+        if len(parts) != 3 or parts[1] not in "bBdDvVu":
+            continue
+        name = parts[2]
+        if TOOLCHAIN_DATA.match(name) or KERNEL_HANDLE.match(name):
+            continue
+        if name in NOALLOC_STATE:
+            noalloc.add(name)
+            continue
+        writable.append(line)
+    assert not writable, "writable globals in libfckl.so:\n" + "\n".join(writable)
+    assert noalloc == NOALLOC_STATE
 
 
 def test_status_strings_and_version():
