@@ -184,26 +184,29 @@ def main():
         pass_ms[name] = (time.perf_counter() - t0) * 1e3 / reps
     log("forward %.2f ms, backward %.2f ms" % (pass_ms["forward"], pass_ms["backward"]))
     gemms = ("fwd_logits", "bwd_logits", "dh", "dw")
-    # the products that stream the LM head read its V H bf16 values once per launch
+    # the products that stream the LM head read the V H bf16 values of the vocabulary rows
+    # they cover (the backward ones one slab at a time): W bytes per chunk
     w_bytes = 2.0 * V * H
-    w_stream = {"bytes_per_launch": w_bytes,
-                "note": "algorithmic W bytes (W, W, W^T) over the live mean launch time; the L2-miss bytes "
+    w_stream = {"bytes_per_chunk": w_bytes,
+                "note": "algorithmic W bytes (W, W, W^T: 2 V H per chunk each, the backward's launches one "
+                        "vocabulary slab at a time) over the kernel's live time; the L2-miss bytes "
                         "per launch (FETCH_SIZE / TCC_EA0_RDREQ_DRAM count requests to the memory side, which the "
                         "256 MB MALL serves in part, so an upper bound on HBM bytes: no counter on this GPU "
                         "separates MALL hits from HBM reads) are in profiles/hbm_bytes_<workload>.md"}
     for name in ("fwd_logits", "bwd_logits", "dh"):
         d = kernels[name]
-        w_stream[name + "_gb_per_s"] = round(w_bytes / (d["ms"] / d["launches"] * 1e-3) / 1e9, 1)
+        w_stream[name + "_gb_per_s"] = round(2.0 * H * d["vrows"] / (d["ms"] * 1e-3) / 1e9, 1)
     for name, d in kernels.items():
         d["avg_ms"] = d["ms"] / d["launches"]
         d["ms_per_step"] = d["ms"] / args.steps
         if name in gemms:
-            flops = 2.0 * d["tokens"] * V * H
+            # 2 flop per token, vocabulary row and hidden entry of each launch
+            flops = 2.0 * d["token_rows"] * H
             d["tflops"] = flops / (d["ms"] * 1e-3) / 1e12
             d["mfma_frac"] = d["tflops"] / PEAK_BF16_TFLOPS
     dom = max(gemms, key=lambda n: kernels[n]["ms"])
     kd = kernels[dom]
-    flops_per_launch = 2.0 * (kd["tokens"] / kd["launches"]) * V * H
+    flops_per_launch = 2.0 * kd["token_rows"] / kd["launches"] * H
     achieved = flops_per_launch / (kd["avg_ms"] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -455,12 +458,14 @@ def timed_steps(fckl, step, steps, nchunks, clock=None):
     per-kernel {launches, ms, tokens})."""
     import torch
     ev = HipEvents()
-    per_step = nchunks * len(fckl.KERNELS) + 4
+    # the backward launches three of its kernels once per vocabulary slab
+    per_step = nchunks * (len(fckl.KERNELS) + 3 * 16) + 4
     cap = per_step * max(steps, 1)
     events = ev.create(2 * cap)
     kid = (ctypes.c_int32 * cap)()
     work = (ctypes.c_int32 * cap)()
-    prof = fckl.Profile((1 << len(fckl.KERNELS)) - 1, cap, 0, events, kid, work)
+    vrows = (ctypes.c_int32 * cap)()
+    prof = fckl.Profile((1 << len(fckl.KERNELS)) - 1, cap, 0, events, kid, work, vrows)
     torch.cuda.synchronize()
     sampler = ClockSampler() if clock is not None else None
     if sampler:
@@ -477,10 +482,12 @@ def timed_steps(fckl, step, steps, nchunks, clock=None):
     kernels = {}
     for i in range(prof.count):
         name = fckl.KERNELS[kid[i]]
-        d = kernels.setdefault(name, {"launches": 0, "ms": 0.0, "tokens": 0})
+        d = kernels.setdefault(name, {"launches": 0, "ms": 0.0, "tokens": 0, "vrows": 0, "token_rows": 0})
         d["launches"] += 1
         d["ms"] += ev.elapsed_ms(events[2 * i], events[2 * i + 1])
         d["tokens"] += work[i]
+        d["vrows"] += vrows[i]
+        d["token_rows"] += work[i] * vrows[i]
     ev.destroy(events)
     return elapsed * 1e3 / steps, kernels
 

@@ -47,14 +47,14 @@ class Profile(ctypes.Structure):
     """Mirror of struct fckl_profile (per-kernel hipEvent brackets)."""
     _fields_ = [("kernel_mask", ctypes.c_uint32), ("capacity", ctypes.c_int32), ("count", ctypes.c_int32),
                 ("events", ctypes.POINTER(ctypes.c_void_p)), ("kernel_ids", ctypes.POINTER(ctypes.c_int32)),
-                ("work", ctypes.POINTER(ctypes.c_int32))]
+                ("work", ctypes.POINTER(ctypes.c_int32)), ("vocab_rows", ctypes.POINTER(ctypes.c_int32))]
 
 
 class Desc(ctypes.Structure):
     """Mirror of struct fckl_desc."""
     _fields_ = [("N", ctypes.c_int64), ("H", ctypes.c_int32), ("V", ctypes.c_int32), ("K", ctypes.c_int32),
                 ("T", ctypes.c_float), ("chunk", ctypes.c_int32), ("logit_dtype", ctypes.c_int32),
-                ("flags", ctypes.c_uint32), ("profile", ctypes.POINTER(Profile))]
+                ("flags", ctypes.c_uint32), ("profile", ctypes.POINTER(Profile)), ("vocab_slab", ctypes.c_int32)]
 
 
 class FCKLError(RuntimeError):
@@ -114,10 +114,13 @@ def version() -> int:
 
 
 def make_desc(N: int, H: int, V: int, K: int, T: float = 1.0, chunk: int = 0, logit_dtype: int = DTYPE_BF16,
-              flags: int = 0, profile: Optional[Profile] = None) -> Desc:
+              flags: int = 0, profile: Optional[Profile] = None, vocab_slab: int = 0) -> Desc:
+    """vocab_slab: vocabulary rows per slab of the two-pass backward (a multiple of 256;
+    0 = the library's choice)."""
     d = Desc(int(N), int(H), int(V), int(K), float(T), int(chunk), int(logit_dtype), int(flags))
     if profile is not None:
         d.profile = ctypes.pointer(profile)
+    d.vocab_slab = int(vocab_slab)
     return d
 
 
@@ -193,10 +196,11 @@ def _check_inputs(h, W, topk_idx, topk_logit):
 
 
 def desc_for(h, W, topk_idx, topk_logit, T: float, chunk: int = 0, flags: int = 0,
-             profile: Optional[Profile] = None) -> Desc:
+             profile: Optional[Profile] = None, vocab_slab: int = 0) -> Desc:
     import torch
     ld = DTYPE_F32 if topk_logit.dtype == torch.float32 else DTYPE_BF16
-    return make_desc(h.shape[0], h.shape[1], W.shape[0], topk_idx.shape[1], T, chunk, ld, flags, profile)
+    return make_desc(h.shape[0], h.shape[1], W.shape[0], topk_idx.shape[1], T, chunk, ld, flags, profile,
+                     vocab_slab)
 
 
 def _stream_handle(stream):
@@ -246,12 +250,13 @@ def _ptr(t):
 
 def forward(h, W, topk_idx, topk_logit, T: float = 1.0, chunk: int = 0, ws=None, validate: bool = False,
             loss_tok=None, lse=None, loss_mean=None, stream=None, profile: Optional[Profile] = None,
-            weights=None):
+            weights=None, vocab_slab: int = 0):
     """Per-token loss, saved lse (log-sum-exp of z/T) and the mean loss (weighted when
-    `weights` is given), via fckl_forward / fckl_forward_ex."""
+    `weights` is given), via fckl_forward / fckl_forward_ex.  vocab_slab only sizes the
+    workspace (the backward's slabs), so that one workspace serves both passes."""
     _check_inputs(h, W, topk_idx, topk_logit)
     dev = h.device
-    desc = desc_for(h, W, topk_idx, topk_logit, T, chunk, FLAG_VALIDATE if validate else 0, profile)
+    desc = desc_for(h, W, topk_idx, topk_logit, T, chunk, FLAG_VALIDATE if validate else 0, profile, vocab_slab)
     ws = _workspace(desc, ws, dev)
     N = h.shape[0]
     weights = _weights(weights, N, dev)
@@ -289,17 +294,18 @@ def forward_noalloc(h, W, topk_idx, topk_logit, loss_tok, lse, loss_mean=None, T
 
 def backward(h, W, topk_idx, topk_logit, lse, T: float = 1.0, grad_scale: float = 1.0, chunk: int = 0, ws=None,
              dH=None, dW=None, accumulate: bool = False, validate: bool = False, stream=None,
-             profile: Optional[Profile] = None, weights=None, grad_scale_dev=None):
+             profile: Optional[Profile] = None, weights=None, grad_scale_dev=None, vocab_slab: int = 0):
     """dH [N,H] and dW [V,H] (float32) of grad_scale * (weighted) mean loss, via
     fckl_backward / fckl_backward_ex.  grad_scale_dev (float32 [1] on the device) further
-    multiplies grad_scale without a host read-back."""
+    multiplies grad_scale without a host read-back.  vocab_slab: vocabulary rows per
+    slab (a multiple of 256, 0 = the library's choice)."""
     import torch
     _check_inputs(h, W, topk_idx, topk_logit)
     if lse.dtype != torch.float32 or tuple(lse.shape) != (h.shape[0],) or lse.device != h.device:
         raise ValueError("lse must be float32 [N] on the inputs' device")
     dev = h.device
     flags = (FLAG_VALIDATE if validate else 0) | (FLAG_DW_ACCUMULATE if accumulate else 0)
-    desc = desc_for(h, W, topk_idx, topk_logit, T, chunk, flags, profile)
+    desc = desc_for(h, W, topk_idx, topk_logit, T, chunk, flags, profile, vocab_slab)
     ws = _workspace(desc, ws, dev)
     weights = _weights(weights, h.shape[0], dev)
     if grad_scale_dev is not None and (grad_scale_dev.dtype != torch.float32 or grad_scale_dev.numel() != 1

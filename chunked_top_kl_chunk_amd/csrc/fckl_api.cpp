@@ -1,6 +1,7 @@
 // fckl_api.cpp -- the C ABI declared in include/fckl.h: argument checks, the chunk
 // loop and the launch sequence.  No device memory is allocated here; every buffer,
 // including the workspace, belongs to the caller.
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include "fckl_internal.h"
@@ -48,6 +49,9 @@ ChunkArgs chunk_args(const fckl_desc *d, const void *h, const void *W, const int
     a.T = d->T;
     a.ws = reinterpret_cast<char *>(ws);
     a.L = L;
+    a.vt0 = 0;
+    a.nvt = L->nVt;
+    a.split0 = 0;
     return a;
 }
 
@@ -73,10 +77,19 @@ fckl_status validate_indices(const fckl_desc *d, const void *h, const void *W, c
     return host ? FCKL_ERR_INDEX : FCKL_OK;
 }
 
+// Kernels with a vocabulary dimension: by default a launch covers all V rows of it.
+constexpr uint32_t kVocabKernels = (1u << FCKL_KERNEL_FWD_LOGITS) | (1u << FCKL_KERNEL_COMBINE) |
+                                   (1u << FCKL_KERNEL_BWD_LOGITS) | (1u << FCKL_KERNEL_DH) | (1u << FCKL_KERNEL_DW) |
+                                   (1u << FCKL_KERNEL_SOFTMAX_GRAD) | (1u << FCKL_KERNEL_FULL_TEACHER) |
+                                   (1u << FCKL_KERNEL_FULL_STUDENT) | (1u << FCKL_KERNEL_FULL_COMBINE) |
+                                   (1u << FCKL_KERNEL_FULL_GRAD);
+
 // Brackets one launch with the caller's events when fckl_desc.profile selects it.
+// vrows: the vocabulary rows the launch covers (-1: V for a kernel with a vocabulary
+// dimension, else 0).
 class Timed {
   public:
-    Timed(const fckl_desc *d, int kernel, int work, void *stream)
+    Timed(const fckl_desc *d, int kernel, int work, void *stream, int vrows = -1)
         : p_(d->profile), s_(reinterpret_cast<hipStream_t>(stream))
     {
         if (p_ && p_->events && ((p_->kernel_mask >> kernel) & 1u) && p_->count >= 0 &&
@@ -86,6 +99,8 @@ class Timed {
                 p_->kernel_ids[slot_] = kernel;
             if (p_->work)
                 p_->work[slot_] = work;
+            if (p_->vocab_rows)
+                p_->vocab_rows[slot_] = vrows >= 0 ? vrows : ((kVocabKernels >> kernel) & 1u) ? d->V : 0;
             (void)hipEventRecord(reinterpret_cast<hipEvent_t>(p_->events[2 * slot_]), s_);
         }
     }
@@ -179,27 +194,37 @@ fckl_status forward_impl(const fckl_desc *desc, const void *h, const void *W, co
     return forward_chunks(desc, h, W, topk_idx, topk_logit, weights, loss_tok, lse, loss_mean, ws, L, stream);
 }
 
-// dH, dH reduce and dW of one chunk whose g (both layouts) and h^T are in the workspace.
-fckl_status chunk_products(const fckl_desc *desc, const ChunkArgs &a, int64_t c0, float *dH, float *dW,
-                           void *stream)
+// dH partial sums and dW rows of the slab of `a`, whose g^T and the chunk's h^T are in
+// the workspace.
+fckl_status slab_products(const fckl_desc *desc, const ChunkArgs &a, int64_t c0, float *dW, void *stream)
 {
+    const int vrows = std::min(a.V - a.vt0 * kVocabTile, a.nvt * kVocabTile);
     {
-        Timed t(desc, FCKL_KERNEL_DH, a.rows, stream);
+        Timed t(desc, FCKL_KERNEL_DH, a.rows, stream, vrows);
         if (launch_dh(a, stream))
             return FCKL_ERR_HIP;
     }
     {
-        Timed t(desc, FCKL_KERNEL_DH_REDUCE, a.rows, stream);
-        if (launch_dh_reduce(a, dH + (size_t)c0 * desc->H, stream))
-            return FCKL_ERR_HIP;
-    }
-    {
-        Timed t(desc, FCKL_KERNEL_DW, a.rows, stream);
+        Timed t(desc, FCKL_KERNEL_DW, a.rows, stream, vrows);
         const bool accumulate = (desc->flags & FCKL_FLAG_DW_ACCUMULATE) != 0 || c0 > 0;
         if (launch_dw(a, dW, accumulate, stream))
             return FCKL_ERR_HIP;
     }
     return FCKL_OK;
+}
+
+fckl_status dh_reduce(const fckl_desc *desc, const ChunkArgs &a, int64_t c0, float *dH, void *stream)
+{
+    Timed t(desc, FCKL_KERNEL_DH_REDUCE, a.rows, stream);
+    return launch_dh_reduce(a, dH + (size_t)c0 * desc->H, stream) ? FCKL_ERR_HIP : FCKL_OK;
+}
+
+// dH and dW of one chunk whose g^T (the whole vocabulary) and h^T are in the workspace.
+fckl_status chunk_products(const fckl_desc *desc, const ChunkArgs &a, int64_t c0, float *dH, float *dW,
+                           void *stream)
+{
+    fckl_status st = slab_products(desc, a, c0, dW, stream);
+    return st != FCKL_OK ? st : dh_reduce(desc, a, c0, dH, stream);
 }
 
 fckl_status backward_impl(const fckl_desc *desc, const void *h, const void *W, const int32_t *topk_idx,
@@ -242,12 +267,20 @@ fckl_status backward_impl(const fckl_desc *desc, const void *h, const void *W, c
             if (launch_transpose_chunk(a, stream))
                 return FCKL_ERR_HIP;
         }
-        {
-            Timed t(desc, FCKL_KERNEL_BWD_LOGITS, a.rows, stream);
-            if (launch_backward_logits(a, lse + c0, stream))
-                return FCKL_ERR_HIP;
+        // One vocabulary slab at a time: its logits and g^T, its dH splits, its dW rows.
+        for (int32_t s = 0; s < L.nslab; ++s) {
+            slab_tiles_of(L, s, &a.vt0, &a.nvt);
+            a.split0 = dh_partials(L, a.V, a.H, s);
+            const int vrows = std::min(a.V - a.vt0 * kVocabTile, a.nvt * kVocabTile);
+            {
+                Timed t(desc, FCKL_KERNEL_BWD_LOGITS, a.rows, stream, vrows);
+                if (launch_backward_logits(a, lse + c0, stream))
+                    return FCKL_ERR_HIP;
+            }
+            if ((st = slab_products(desc, a, c0, dW, stream)) != FCKL_OK)
+                return st;
         }
-        if ((st = chunk_products(desc, a, c0, dH, dW, stream)) != FCKL_OK)
+        if ((st = dh_reduce(desc, a, c0, dH, stream)) != FCKL_OK)
             return st;
     }
     return FCKL_OK;
@@ -621,6 +654,6 @@ const char *fckl_status_string(fckl_status s)
     return "unknown status";
 }
 
-int32_t fckl_version(void) { return 300; }
+int32_t fckl_version(void) { return 400; }
 
 }  // extern "C"

@@ -26,6 +26,12 @@ constexpr int kTopkSortSub = 2048;  // slice maxima per token up to which the th
 constexpr int kTopkMaxSub = 65536;
 constexpr int32_t kMaxChunk = 8192;
 constexpr size_t kDefaultBudget = size_t(12) << 30;  // 12 GiB of the 288 GB HBM3E
+// The two-pass backward works through a chunk's vocabulary in slabs whose g^T holds at
+// most about this many bytes, in whole multiples of 64 vocabulary tiles (unless the
+// descriptor sets the slab).  64 tiles times a hidden size of 12 or 16 tiles gives dW
+// launches of whole rounds of 256 work-groups.
+constexpr size_t kSlabBytes = size_t(1250) << 20;
+constexpr int32_t kSlabTileStep = 64;
 
 // Kernel limits.  The GEMM operand loaders keep each lane's offset inside a 256-row
 // tile in 32 bits (up to 255 rows of the operand's pitch; the transposed g^T operand of
@@ -54,7 +60,10 @@ struct Layout {
     int32_t nVt = 0;        // vocabulary tiles: ceil(V / kVocabTile)
     int32_t Vpad = 0;       // nVt * kVocabTile (row pitch of g)
     int32_t cnt_stride = 0; // bytes per token of the per-tile entry-count table
-    int32_t dh_splits = 0;  // vocabulary splits of the dH product
+    int32_t dh_splits = 0;  // vocabulary splits of the dH product, over all slabs
+    int32_t nslab = 1;      // vocabulary slabs of the two-pass backward (1 in the other layouts)
+    int32_t slab_tiles = 0; // vocabulary tiles per slab; the last slab takes the remainder
+    int32_t gT_tiles = 0;   // vocabulary tiles of the largest slab (rows of g^T / kVocabTile)
     size_t off_idx = 0;     // int32 [Cpad, K]   cached indices, sorted ascending per token
     size_t off_p = 0;       // f32   [Cpad, K]   teacher probabilities in the same order
     size_t off_zk = 0;      // f32   [Cpad, K]   student logit at each sorted index
@@ -66,8 +75,8 @@ struct Layout {
                             //       kept with the exponentials (keep layouts only)
     size_t off_wsum = 0;    // f32   [2]         sum of the token weights and its inverse
     size_t off_ex = 0;      // bf16  [Cpad, Vpad] kept 2^(z/T log2 e - m) (keep layouts only)
-    size_t off_gT = 0;      // bf16  [Vpad, Cpad] chunk gradient w.r.t. the logits, vocabulary-major
-                            //       (the operand of both the dH and the dW product)
+    size_t off_gT = 0;      // bf16  [gT_tiles * 256, Cpad] chunk gradient w.r.t. the logits of
+                            //       one slab, vocabulary-major (the operand of both products)
     size_t off_hT = 0;      // bf16  [H, Cpad]    chunk hidden states, transposed (dW operand)
     size_t off_WT = 0;      // bf16  [H, Vpad]    LM head, transposed (dH operand)
     size_t off_dhp = 0;     // f32   [dh_splits, Cpad, H] split partial sums of dH
@@ -109,6 +118,17 @@ fckl_status make_full_layout(const fckl_desc *d, int32_t Ht, int32_t chunk, Full
 fckl_status plan_full_chunk(const fckl_desc *d, int32_t Ht, size_t budget, FullLayout *L);
 fckl_status make_layout(const fckl_desc *d, int32_t chunk, Layout *L, LayoutKind kind = LayoutKind::TwoPass);
 fckl_status plan_chunk(const fckl_desc *d, size_t budget, Layout *L, LayoutKind kind = LayoutKind::TwoPass);
+// Slab s of L (0 <= s < L.nslab): its first vocabulary tile and its tile count.
+void slab_tiles_of(const Layout &L, int32_t s, int32_t *vt0, int32_t *nvt);
+// dH splits of a slab of nvt vocabulary tiles with Cpad tokens and hidden size H.
+int32_t slab_split_count(int32_t Cpad, int32_t H, int32_t nvt);
+// The dH product's k-step (vocabulary rows); a split is a whole number of them.
+constexpr int32_t kDhStep = 64;
+// Slab s's dH splits: vocabulary rows per split and the number of splits holding at
+// least one row of the V-row vocabulary (the slab's partial sums are that many).
+void slab_split_rows(const Layout &L, int32_t V, int32_t H, int32_t s, int32_t *ksplit, int32_t *used);
+// dH partial sums of the first nslabs slabs (all of them: the count the reduce sums).
+int32_t dh_partials(const Layout &L, int32_t V, int32_t H, int32_t nslabs);
 
 // The allocation-free forward pass (fckl_forward_noalloc) runs in a device array of the
 // library instead of a caller's workspace: its size, and the lookup of its address on the
@@ -130,6 +150,10 @@ struct ChunkArgs {
     float T;
     char *ws;
     const Layout *L;
+    // The vocabulary slab the backward launches cover: its first tile, its tile count and
+    // the index of its first dH split (the whole vocabulary and 0 outside the two-pass
+    // backward).
+    int32_t vt0 = 0, nvt = 0, split0 = 0;
 };
 
 // Per-token scale of the gradient with respect to z: coef * w[i] * (*inv_wsum) with

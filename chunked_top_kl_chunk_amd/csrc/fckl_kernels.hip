@@ -1131,12 +1131,13 @@ __global__ __launch_bounds__(1024) void weight_sum_kernel(const float *w, int64_
 struct BwdParams {
     const uint16_t *W, *h;
     int H, V, rows, Cpad, Vpad, K, nVt, nNt, cnt_stride;
+    int vt0;                // first vocabulary tile of the slab; nVt tiles from there
     float scale2;           // log2(e) / T
     const float *lse;       // chunk's first token (natural log, z/T units)
     const int32_t *idx_s;
     const float *p_s, *psum;    // stored times each token's gradient scale
     const uint8_t *cnt;
-    uint16_t *gT;           // [Vpad, Cpad] bf16
+    uint16_t *gT;           // [nVt * 256, Cpad] bf16: the slab's rows
 };
 
 __device__ __forceinline__ void backward_tile(const BwdParams &p, char *smem, int t)
@@ -1144,6 +1145,7 @@ __device__ __forceinline__ void backward_tile(const BwdParams &p, char *smem, in
     using G = LogitGemm;
     int tm, tn;
     map_tile(t, p.nVt, p.nNt, 4, tm, tn);
+    tm += p.vt0;
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = G::wm_of(wave), wn = G::wn_of(wave);
@@ -1211,7 +1213,7 @@ __device__ __forceinline__ void backward_tile(const BwdParams &p, char *smem, in
     // The bf16 tile, [vocab][token], the operand of both the dH and the dW product.  (The
     // main loop ended with a barrier, so the operand buffers are free.)
     stage_token_major<G>(acc, smem);
-    store_vocab_major<G::BN, G::NT / 64>(smem, p.gT, (size_t)p.Cpad, m0, n0);
+    store_vocab_major<G::BN, G::NT / 64>(smem, p.gT, (size_t)p.Cpad, m0 - p.vt0 * G::BM, n0);
 }
 
 __global__ __launch_bounds__(LogitGemm::NT) void backward_logits_kernel(BwdParams p)
@@ -1904,10 +1906,11 @@ __global__ __launch_bounds__(64) void topk_select_kernel(const uint64_t *cand, c
 // ------------------------------------------------------------------ dH = g . W
 
 struct DhParams {
-    const uint16_t *gT;     // [Vpad, Cpad]
-    const uint16_t *WT;     // [H, Vpad]
-    int H, V, Vpad, rows, Cpad, nMt, nNt, ksplit;
+    const uint16_t *gT;     // [V rows of the slab, Cpad]
+    const uint16_t *WT;     // the slab's first column of W^T [H, row pitch Vpad]
+    int H, V, Vpad, rows, Cpad, nMt, nNt, ksplit;   // V: the slab's vocabulary rows
     int GM;                 // hidden tiles per group of the tile order
+    int split0;             // index of the slab's first split among all partial sums
     float *part;            // [splits, Cpad, H]
 };
 
@@ -1930,7 +1933,7 @@ __global__ __launch_bounds__(G::NT) void dh_kernel(DhParams p)
                                       k_end, acc);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = G::wm_of(wave), wn = G::wn_of(wave);
-    float *out = p.part + (size_t)blockIdx.y * p.Cpad * p.H;
+    float *out = p.part + (size_t)(p.split0 + blockIdx.y) * p.Cpad * p.H;
     // each lane holds 4 consecutive hidden entries of one token per (i, j, q)
 #pragma unroll
     for (int j = 0; j < G::NB; ++j) {
@@ -1971,10 +1974,10 @@ __global__ __launch_bounds__(256) void dh_reduce_kernel(const float *part, int s
 // ------------------------------------------------------------------ dW += g^T . h
 
 struct DwParams {
-    const uint16_t *gT;     // [Vpad, Cpad]
+    const uint16_t *gT;     // [Vpad, Cpad]: the slab's rows, Vpad = its tiles * 256
     const uint16_t *hT;     // [H, Cpad]
-    int H, V, Vpad, Cpad, rows, nMt, nNt, accumulate;
-    float *dW;              // [V, H]
+    int H, V, Vpad, Cpad, rows, nMt, nNt, accumulate;   // V: the slab's vocabulary rows
+    float *dW;              // the slab's first row of dW [V, H]
 };
 
 template <class G>
@@ -2288,7 +2291,8 @@ int launch_backward_logits(const ChunkArgs &a, const float *lse, void *stream)
     p.Cpad = L.Cpad;
     p.Vpad = L.Vpad;
     p.K = a.K;
-    p.nVt = L.nVt;
+    p.nVt = a.nvt;
+    p.vt0 = a.vt0;
     p.nNt = (a.rows + LogitGemm::BN - 1) / LogitGemm::BN;
     p.cnt_stride = L.cnt_stride;
     p.scale2 = kLog2e / a.T;
@@ -2302,30 +2306,31 @@ int launch_backward_logits(const ChunkArgs &a, const float *lse, void *stream)
     return (int)hipGetLastError();
 }
 
-// Vocabulary splits of the dH product: rows of W per split (a multiple of the k-step)
-// and the number of splits that hold at least one row.
-static void dh_splits(const ChunkArgs &a, int &ksplit, int &used)
+// The slab a covers: its index among the layout's slabs.
+static int32_t slab_index(const ChunkArgs &a)
 {
-    const Layout &L = *a.L;
-    ksplit = ((L.Vpad + L.dh_splits - 1) / L.dh_splits + DGemm::BK - 1) / DGemm::BK * DGemm::BK;
-    used = (a.V + ksplit - 1) / ksplit;
+    return a.L->slab_tiles > 0 ? a.vt0 / a.L->slab_tiles : 0;
 }
 
 int launch_dh(const ChunkArgs &a, void *stream)
 {
+    static_assert(DGemm::BK == kDhStep, "dH splits are whole k-steps");
     const Layout &L = *a.L;
+    const int v0 = a.vt0 * kVocabTile;
     DhParams p;
     p.gT = reinterpret_cast<const uint16_t *>(a.ws + L.off_gT);
-    p.WT = reinterpret_cast<const uint16_t *>(a.ws + L.off_WT);
+    p.WT = reinterpret_cast<const uint16_t *>(a.ws + L.off_WT) + v0;
     p.H = a.H;
-    p.V = a.V;
+    p.V = std::min(a.V - v0, a.nvt * kVocabTile);
     p.Vpad = L.Vpad;
     p.rows = a.rows;
     p.Cpad = L.Cpad;
     p.nMt = (a.H + kHiddenTile - 1) / kHiddenTile;
     p.nNt = (a.rows + 255) / 256;
-    int used = 0;
-    dh_splits(a, p.ksplit, used);
+    int32_t ksplit = 0, used = 0;
+    slab_split_rows(L, a.V, a.H, slab_index(a), &ksplit, &used);
+    p.ksplit = ksplit;
+    p.split0 = a.split0;
     // Tile order.  A dH work-group waits on its global -> LDS loads (a part-filled hidden
     // tile takes as long as a full one), so the order is chosen for L2 hits.  Each XCD
     // takes one eighth of a split's tiles; with groups of GM hidden tiles, GM the smallest
@@ -2354,8 +2359,7 @@ int launch_dh(const ChunkArgs &a, void *stream)
 int launch_dh_reduce(const ChunkArgs &a, float *dH, void *stream)
 {
     const Layout &L = *a.L;
-    int ksplit = 0, used = 0;
-    dh_splits(a, ksplit, used);
+    const int32_t used = dh_partials(L, a.V, a.H, L.nslab);
     const float *part = reinterpret_cast<const float *>(a.ws + L.off_dhp);
     const size_t n4 = (size_t)a.rows * a.H / 4;
     hipLaunchKernelGGL(dh_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, S(stream), part, used,
@@ -2366,18 +2370,19 @@ int launch_dh_reduce(const ChunkArgs &a, float *dH, void *stream)
 int launch_dw(const ChunkArgs &a, float *dW, bool accumulate, void *stream)
 {
     const Layout &L = *a.L;
+    const int v0 = a.vt0 * kVocabTile;
     DwParams p;
     p.gT = reinterpret_cast<const uint16_t *>(a.ws + L.off_gT);
     p.hT = reinterpret_cast<const uint16_t *>(a.ws + L.off_hT);
     p.H = a.H;
-    p.V = a.V;
-    p.Vpad = L.Vpad;
+    p.V = std::min(a.V - v0, a.nvt * kVocabTile);
+    p.Vpad = a.nvt * kVocabTile;
     p.Cpad = L.Cpad;
     p.rows = a.rows;
-    p.nMt = L.nVt;
+    p.nMt = a.nvt;
     p.nNt = (a.H + kHiddenTile - 1) / kHiddenTile;
     p.accumulate = accumulate ? 1 : 0;
-    p.dW = dW;
+    p.dW = dW + (size_t)v0 * a.H;
     dim3 grid(p.nMt * p.nNt);
     hipLaunchKernelGGL(dw_kernel<WGemm>, grid, dim3(WGemm::NT), 0, S(stream), p);
     return (int)hipGetLastError();

@@ -25,7 +25,7 @@ fckl_status check_desc(const fckl_desc *d)
         return FCKL_ERR_INVALID_ARG;
     if (!(d->T > 0.0f) || !std::isfinite(d->T))
         return FCKL_ERR_INVALID_ARG;
-    if (d->K > d->V || d->chunk < 0)
+    if (d->K > d->V || d->chunk < 0 || d->vocab_slab < 0 || d->vocab_slab % kVocabTile != 0)
         return FCKL_ERR_INVALID_ARG;
     if (d->logit_dtype != FCKL_DTYPE_BF16 && d->logit_dtype != FCKL_DTYPE_F32)
         return FCKL_ERR_INVALID_ARG;
@@ -77,6 +77,67 @@ static int32_t dh_split_count(int32_t Cpad, int32_t H, int32_t Vpad)
     return (int32_t)best;
 }
 
+int32_t slab_split_count(int32_t Cpad, int32_t H, int32_t nvt)
+{
+    return dh_split_count(Cpad, H, nvt * kVocabTile);
+}
+
+void slab_tiles_of(const Layout &L, int32_t s, int32_t *vt0, int32_t *nvt)
+{
+    *vt0 = s * L.slab_tiles;
+    *nvt = s + 1 < L.nslab ? L.slab_tiles : L.nVt - *vt0;
+}
+
+void slab_split_rows(const Layout &L, int32_t V, int32_t H, int32_t s, int32_t *ksplit, int32_t *used)
+{
+    int32_t vt0, nvt;
+    slab_tiles_of(L, s, &vt0, &nvt);
+    const int32_t splits = slab_split_count(L.Cpad, H, nvt);
+    const int32_t rows = nvt * kVocabTile, vrows = std::min(V - vt0 * kVocabTile, rows);
+    *ksplit = ((rows + splits - 1) / splits + kDhStep - 1) / kDhStep * kDhStep;
+    *used = (vrows + *ksplit - 1) / *ksplit;
+}
+
+int32_t dh_partials(const Layout &L, int32_t V, int32_t H, int32_t nslabs)
+{
+    int32_t total = 0;
+    for (int32_t s = 0; s < nslabs; ++s) {
+        int32_t ksplit = 0, used = 0;
+        slab_split_rows(L, V, H, s, &ksplit, &used);
+        total += used;
+    }
+    return total;
+}
+
+// Slabs of the two-pass backward: the descriptor's, else whole multiples of
+// kSlabTileStep tiles whose g^T holds at most about kSlabBytes, as many as round
+// nVt / slab to the nearest (the last slab takes the remainder).
+static void plan_slabs(const fckl_desc *d, Layout &o)
+{
+    int32_t st = o.nVt;
+    if (d->vocab_slab > 0) {
+        st = d->vocab_slab / kVocabTile;
+    } else {
+        const size_t tile_bytes = (size_t)kVocabTile * (size_t)o.Cpad * 2;
+        st = std::max<int32_t>(kSlabTileStep, (int32_t)(kSlabBytes / tile_bytes) / kSlabTileStep * kSlabTileStep);
+    }
+    if (st >= o.nVt) {
+        o.nslab = 1;
+        o.slab_tiles = o.nVt;
+    } else {
+        o.nslab = d->vocab_slab > 0 ? o.nVt / st : std::max<int32_t>(1, (o.nVt + st / 2) / st);
+        o.slab_tiles = o.nslab > 1 ? st : o.nVt;
+    }
+    o.gT_tiles = 0;
+    o.dh_splits = 0;
+    for (int32_t s = 0; s < o.nslab; ++s) {
+        int32_t vt0, nvt;
+        slab_tiles_of(o, s, &vt0, &nvt);
+        o.gT_tiles = std::max(o.gT_tiles, nvt);
+        o.dh_splits += slab_split_count(o.Cpad, d->H, nvt);
+    }
+}
+
 fckl_status make_layout(const fckl_desc *d, int32_t chunk, Layout *L, LayoutKind kind)
 {
     fckl_status st = check_desc(d);
@@ -95,6 +156,10 @@ fckl_status make_layout(const fckl_desc *d, int32_t chunk, Layout *L, LayoutKind
     o.Vpad = o.nVt * kVocabTile;
     o.cnt_stride = (int32_t)align_up((size_t)o.nVt + 1, 16);
     o.dh_splits = dh_split_count(o.Cpad, d->H, o.Vpad);
+    o.nslab = 1;
+    o.slab_tiles = o.gT_tiles = o.nVt;
+    if (kind == LayoutKind::TwoPass)
+        plan_slabs(d, o);
     const size_t Cp = (size_t)o.Cpad, K = (size_t)d->K;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -119,7 +184,7 @@ fckl_status make_layout(const fckl_desc *d, int32_t chunk, Layout *L, LayoutKind
     o.off_mw = keep ? take((size_t)o.nVt * 2 * Cp * 4) : 0;
     o.off_wsum = take(16);
     o.off_ex = keep ? take(Cp * (size_t)o.Vpad * 2) : 0;
-    o.off_gT = take(Cp * (size_t)o.Vpad * 2);
+    o.off_gT = take(Cp * (size_t)o.gT_tiles * kVocabTile * 2);
     o.off_hT = take(Cp * (size_t)d->H * 2);
     o.off_WT = take((size_t)o.Vpad * (size_t)d->H * 2);
     o.off_dhp = take((size_t)o.dh_splits * Cp * (size_t)d->H * 4);

@@ -106,8 +106,11 @@ enum {
  * the call's stream, using events[2*i] and events[2*i+1] for the i-th bracketed launch
  * (i = count, then count is incremented; launches beyond capacity are not timed).  The
  * caller creates the hipEvent_t handles (passed as void*) and reads the elapsed times
- * after synchronising.  kernel_ids[i] receives the FCKL_KERNEL_* id of launch i and
- * work[i] the number of tokens that launch processed.
+ * after synchronising.  kernel_ids[i] receives the FCKL_KERNEL_* id of launch i,
+ * work[i] the number of tokens that launch processed and, when vocab_rows is not NULL,
+ * vocab_rows[i] the vocabulary rows it covered: V, except for the launches of the
+ * two-pass backward, which run one vocabulary slab at a time (fckl_desc.vocab_slab), and
+ * 0 for kernels without a vocabulary dimension (transposes, reductions, weights).
  */
 typedef struct fckl_profile {
     uint32_t kernel_mask;
@@ -116,6 +119,7 @@ typedef struct fckl_profile {
     void **events;           /* host array of 2 * capacity hipEvent_t */
     int32_t *kernel_ids;     /* host array of capacity */
     int32_t *work;           /* host array of capacity */
+    int32_t *vocab_rows;     /* host array of capacity, or NULL */
 } fckl_profile;
 
 /* Problem description shared by every call. */
@@ -129,6 +133,8 @@ typedef struct fckl_desc {
     int32_t logit_dtype;  /* FCKL_DTYPE_BF16 or FCKL_DTYPE_F32 */
     uint32_t flags;       /* FCKL_FLAG_* */
     fckl_profile *profile;/* optional kernel timing, NULL = none */
+    int32_t vocab_slab;   /* vocabulary rows per slab of the two-pass backward: a multiple
+                             of 256, or 0 = the library's choice (see fckl_backward) */
 } fckl_desc;
 
 /*
@@ -177,7 +183,15 @@ fckl_status fckl_forward(const fckl_desc *desc, const void *h, const void *W,
  * Backward pass: gradients of grad_scale * loss_mean with respect to h and W.  Each
  * chunk's logits are recomputed with the same tiles as the forward pass; the chunk's
  * gradient g (bf16, written once, vocabulary-major, in the workspace) feeds the dH and
- * dW products.
+ * dW products (the backward pass repeats the projection per chunk: axbrief.com,
+ * "Breaking the Bottleneck with Offline Caching and Chunked Loss").  A chunk is worked
+ * through in slabs of the vocabulary: the logits, g, the slab's share of dH and its
+ * rows of dW of one slab before the next, so the workspace holds g for one slab only.
+ * desc->vocab_slab sets the slab (rows, a multiple of 256; the last slab also takes
+ * the remainder, up to twice that); 0 lets the planner choose slabs of 64-tile
+ * multiples holding at most about 1.25 GB of g each (at 8192 tokens per chunk: 65536
+ * rows, so three slabs at V = 201088), and one slab when that is the whole vocabulary.
+ * The slabs change the order of the dH sum only; loss, lse and dW do not depend on them.
  *   lse        device, f32 [N]         the lse written by fckl_forward for these inputs
  *   grad_scale                         upstream gradient of loss_mean (1 for a plain loss)
  *   dH         device, f32 [N,H]       out: overwritten (16-byte aligned)

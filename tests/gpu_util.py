@@ -51,11 +51,11 @@ def arrays(h, W, idx, tl):
             torch.from_numpy(tb.view(np.int16)).to(dev).view(torch.bfloat16))
 
 
-def run(h, W, idx, tl, T, chunk=0, grad_scale=1.0, backward=True):
-    loss, lse, mean = fckl.forward(h, W, idx, tl, T=T, chunk=chunk)
+def run(h, W, idx, tl, T, chunk=0, grad_scale=1.0, backward=True, vocab_slab=0):
+    loss, lse, mean = fckl.forward(h, W, idx, tl, T=T, chunk=chunk, vocab_slab=vocab_slab)
     out = {"loss": loss, "lse": lse, "mean": mean}
     if backward:
-        dH, dW = fckl.backward(h, W, idx, tl, lse, T=T, grad_scale=grad_scale, chunk=chunk)
+        dH, dW = fckl.backward(h, W, idx, tl, lse, T=T, grad_scale=grad_scale, chunk=chunk, vocab_slab=vocab_slab)
         out.update(dH=dH, dW=dW)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}

@@ -3,6 +3,7 @@
 // function and checks the layout invariants -- regions 256-byte aligned, in order, not
 // overlapping, inside the total; a planned workspace within its budget -- so that
 // AddressSanitizer and UndefinedBehaviorSanitizer see overflow and out-of-range paths.
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <vector>
@@ -51,8 +52,28 @@ static void check_layout(const fckl_desc &d, const Layout &L)
     regions.push_back({L.off_wsum, 8});
     if (keep)
         regions.push_back({L.off_ex, Cp * (size_t)L.Vpad * 2});
+    // vocabulary slabs: contiguous, covering every tile, g^T sized for the largest, dH
+    // partial sums for every split that holds a row (a keep layout has one slab)
+    CHECK(L.nslab >= 1 && L.slab_tiles >= 1 && L.gT_tiles >= 1 && L.gT_tiles <= L.nVt);
+    CHECK(L.kind == LayoutKind::TwoPass || (L.nslab == 1 && L.gT_tiles == L.nVt));
+    int32_t next = 0, biggest = 0;
+    for (int32_t s = 0; s < L.nslab; ++s) {
+        int32_t vt0 = -1, nvt = -1;
+        slab_tiles_of(L, s, &vt0, &nvt);
+        CHECK(vt0 == next && nvt >= 1);
+        CHECK(s + 1 == L.nslab ? nvt < 2 * L.slab_tiles || L.nslab == 1 : nvt == L.slab_tiles);
+        int32_t ksplit = 0, used = 0;
+        slab_split_rows(L, d.V, d.H, s, &ksplit, &used);
+        CHECK(ksplit % kDhStep == 0 && ksplit >= kDhStep && used >= 1);
+        CHECK((int64_t)used * ksplit >= (int64_t)std::min(d.V - vt0 * kVocabTile, nvt * kVocabTile));
+        CHECK((int64_t)(used - 1) * ksplit < (int64_t)std::min(d.V - vt0 * kVocabTile, nvt * kVocabTile));
+        next = vt0 + nvt;
+        biggest = std::max(biggest, nvt);
+    }
+    CHECK(next == L.nVt && biggest == L.gT_tiles);
+    CHECK(dh_partials(L, d.V, d.H, L.nslab) <= L.dh_splits);
     for (const auto &r : std::vector<std::pair<size_t, size_t>>{
-             {L.off_gT, (size_t)L.Vpad * Cp * 2}, {L.off_hT, (size_t)d.H * Cp * 2},
+             {L.off_gT, (size_t)L.gT_tiles * kVocabTile * Cp * 2}, {L.off_hT, (size_t)d.H * Cp * 2},
              {L.off_WT, (size_t)d.H * (size_t)L.Vpad * 2},
              {L.off_dhp, (size_t)L.dh_splits * Cp * (size_t)d.H * 4}, {L.off_err, 16}})
         regions.push_back(r);
@@ -108,6 +129,22 @@ int main()
                                            {F.off_ls2, Cp * 4}},
                                           F.total);
                             CHECK(F.off_at >= F.base.total);
+                        }
+                    }
+                    for (int32_t slab : {256, 512, 65536, 100, -256}) {
+                        fckl_desc ds = d;
+                        ds.vocab_slab = slab;
+                        if (slab % 256 != 0 || slab < 0) {
+                            CHECK(check_desc(&ds) == FCKL_ERR_INVALID_ARG);
+                            continue;
+                        }
+                        for (int32_t chunk : {256, 8192}) {
+                            Layout L;
+                            if (make_layout(&ds, chunk, &L, LayoutKind::TwoPass) == FCKL_OK) {
+                                check_layout(ds, L);
+                                CHECK(L.nslab == std::max<int32_t>(1, L.nVt / (slab / 256)));
+                                CHECK(L.slab_tiles == (L.nslab > 1 ? slab / 256 : L.nVt));
+                            }
                         }
                     }
                     for (int32_t chunk : {1, 256, 1000, 8192, 1 << 20, (1 << 24) + 1}) {

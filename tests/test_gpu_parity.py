@@ -104,6 +104,36 @@ def test_deterministic_and_chunk_invariant():
         assert rel_max(c["dW"], a["dW"]) < 1e-5
 
 
+SLAB_CASES = [
+    # seed, N, H, V, K, T, chunk, vocab_slab: 6 slabs of 2 tiles, the last with a ragged
+    # tile of 184 rows, 3 chunks; 2 slabs, the last of 3 tiles; a 1-tile slab per tile
+    (31, 1100, 264, 3000, 12, 1.3, 512, 512),
+    (32, 700, 2880, 1400, 20, 1.0, 0, 512),
+    (33, 300, 128, 1800, 7, 0.7, 256, 256),
+]
+
+
+@pytest.mark.parametrize("case", SLAB_CASES, ids=["slab512-ragged", "slab512-H2880", "slab256"])
+def test_vocabulary_slabs(case):
+    """The backward taken one vocabulary slab at a time (the slab set by the caller):
+    against the oracle, and against one slab for the whole vocabulary.  The slabs only
+    regroup the dH sum: loss, lse and dW are bit for bit those of one slab."""
+    seed, N, H, V, K, T, chunk, slab = case
+    say("case: vocabulary slabs", case)
+    h, W, idx, tl = synthetic(seed, N, H, V, K, T)
+    t = arrays(h, W, idx, tl)
+    g = run(*t, T=T, chunk=chunk, vocab_slab=slab)
+    compare_all(g, h, W, idx, tl, T, what="slabs%d" % seed)
+    whole = run(*t, T=T, chunk=chunk, vocab_slab=(V + 255) // 256 * 256)
+    for k in ("loss", "lse", "mean", "dW"):
+        np.testing.assert_array_equal(g[k], whole[k], err_msg=k)
+    assert rel_max(g["dH"], whole["dH"]) < 1e-5
+    # deterministic
+    again = run(*t, T=T, chunk=chunk, vocab_slab=slab)
+    for k in g:
+        np.testing.assert_array_equal(g[k], again[k], err_msg=k)
+
+
 def test_loss_nonnegative():
     h, W, idx, tl = synthetic(13, 800, 256, 2000, 50, 2.0, z_sigma=6.0)
     g = run(*arrays(h, W, idx, tl), T=2.0, backward=False)

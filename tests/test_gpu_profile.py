@@ -2,8 +2,8 @@
 
 bench.py derives its live per-kernel times and the roofline from it, so it is checked
 here on its own: every selected launch is bracketed, in launch order, with the token
-count it processed; unselected kernels and launches past the capacity are left out;
-and profiling changes no result.
+count and the vocabulary rows it processed; unselected kernels and launches past the
+capacity are left out; and profiling changes no result.
 """
 import ctypes
 
@@ -43,11 +43,13 @@ class Events:
             self.hip.hipEventDestroy(e)
 
 
-def profile(mask, capacity):
+def profile(mask, capacity, vocab_rows=None):
     ev = Events(2 * capacity)
     kid = (ctypes.c_int32 * capacity)()
     work = (ctypes.c_int32 * capacity)()
-    return fckl.Profile(mask, capacity, 0, ev.arr, kid, work), ev, kid, work
+    if vocab_rows is None:
+        return fckl.Profile(mask, capacity, 0, ev.arr, kid, work), ev, kid, work
+    return fckl.Profile(mask, capacity, 0, ev.arr, kid, work, vocab_rows), ev, kid, work
 
 
 def problem():
@@ -68,7 +70,7 @@ def test_profile_brackets_every_selected_launch():
         want += [("prepare", r), ("fwd_logits", r), ("combine", r)]
     want += [("mean", N), ("transpose", 0)]                  # W^T once per backward call
     for r in rows:
-        want += [("prepare", r), ("transpose", r), ("bwd_logits", r), ("dh", r), ("dh_reduce", r), ("dw", r)]
+        want += [("prepare", r), ("transpose", r), ("bwd_logits", r), ("dh", r), ("dw", r), ("dh_reduce", r)]
     assert got == want
     times = [ev.ms(i) for i in range(prof.count)]
     assert all(x >= 0.0 for x in times)
@@ -109,4 +111,32 @@ def test_profile_mask_and_capacity():
     fckl.forward(*t, T=T, chunk=C, profile=prof)
     torch.cuda.synchronize()
     assert prof.count == 0
+    ev.close()
+
+
+def test_profile_reports_vocabulary_rows_per_slab():
+    """With slabs of 512 vocabulary rows (V = 3000: 6 slabs, the last of 440 rows) the
+    backward's logit, dH and dW launches run once per slab and report the slab's rows;
+    the other launches report V or, without a vocabulary dimension, 0."""
+    t, T, C, rows = problem()
+    V = t[1].shape[0]
+    slabs = [512] * 5 + [V - 5 * 512]
+    cap = 128
+    vr = (ctypes.c_int32 * cap)()
+    prof, ev, kid, work = profile((1 << len(fckl.KERNELS)) - 1, cap, vr)
+    loss, lse, mean = fckl.forward(*t, T=T, chunk=C, profile=prof, vocab_slab=512)
+    fckl.backward(*t, lse, T=T, chunk=C, profile=prof, vocab_slab=512)
+    torch.cuda.synchronize()
+    got = [(fckl.KERNELS[kid[i]], work[i], vr[i]) for i in range(prof.count)]
+    N = t[0].shape[0]
+    want = []
+    for r in rows:
+        want += [("prepare", r, 0), ("fwd_logits", r, V), ("combine", r, V)]
+    want += [("mean", N, 0), ("transpose", 0, 0)]
+    for r in rows:
+        want += [("prepare", r, 0), ("transpose", r, 0)]
+        for v in slabs:
+            want += [("bwd_logits", r, v), ("dh", r, v), ("dw", r, v)]
+        want += [("dh_reduce", r, 0)]
+    assert got == want
     ev.close()

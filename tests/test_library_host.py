@@ -99,8 +99,12 @@ def test_workspace_independent_of_tokens():
     assert len(sizes) == 1
 
 
+VPAD3 = (C3["V"] + 255) // 256 * 256
+
+
 def test_workspace_grows_with_chunk():
-    d = fckl.make_desc(**C3)
+    # one backward slab (the whole vocabulary): the workspace grows with the chunk
+    d = fckl.make_desc(**C3, vocab_slab=VPAD3)
     w = [fckl.workspace_size(d, c) for c in (256, 1024, 4096, 8192, 16384)]
     assert all(a < b for a, b in zip(w, w[1:]))
     # dominated by the bf16 chunk gradient, kept once (2*C*V bytes), and the transposed
@@ -113,6 +117,29 @@ def test_workspace_grows_with_chunk():
     chunk, single = fckl.single_plan(d, 0)
     assert chunk == C
     assert single == w[2] + 2 * C * ((V + 255) // 256 * 256) + 8 * C * ((V + 255) // 256)
+
+
+def test_backward_slabs_bound_the_gradient_buffer():
+    # The planner's slabs at 8192 tokens per chunk: 256, 256 and 274 of the 786
+    # vocabulary tiles.  g^T is held for the largest slab only; the 274-tile slab takes
+    # 4 dH splits and the others 2 each, 8 partial sums in all against 6 for one slab.
+    C, H, nVt = 8192, C3["H"], VPAD3 // 256
+    auto = fckl.workspace_size(fckl.make_desc(**C3), C)
+    whole = fckl.workspace_size(fckl.make_desc(**C3, vocab_slab=VPAD3), C)
+    assert whole - auto == 2 * C * 256 * (nVt - 274) - (8 - 6) * C * H * 4
+    # at 4096 tokens the whole vocabulary's g^T is within the slab size: one slab
+    assert fckl.workspace_size(fckl.make_desc(**C3), 4096) == fckl.workspace_size(
+        fckl.make_desc(**C3, vocab_slab=VPAD3), 4096)
+    # a slab set by the caller: 512 rows, the last slab takes the remainder (3 tiles)
+    small = dict(N=3000, H=264, V=1800, K=20, T=1.0)
+    one = fckl.workspace_size(fckl.make_desc(**small, vocab_slab=2048), 1024)
+    two = fckl.workspace_size(fckl.make_desc(**small, vocab_slab=512), 1024)
+    assert two < one
+    # not a multiple of 256, or negative: refused before any HIP call
+    for bad in (100, -256):
+        with pytest.raises(fckl.FCKLError) as e:
+            fckl.workspace_size(fckl.make_desc(**small, vocab_slab=bad), 1024)
+        assert e.value.status == fckl.ERR_INVALID_ARG
 
 
 def test_plan_explicit_chunk_and_small_budget():
