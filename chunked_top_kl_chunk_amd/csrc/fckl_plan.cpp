@@ -56,7 +56,10 @@ static bool chunk_supported(int64_t Cpad, int32_t H)
 static int32_t dh_split_count(int32_t Cpad, int32_t H, int32_t Vpad)
 {
     const int64_t tiles = (int64_t)(Cpad / kTokenTile) * ((H + kHiddenTile - 1) / kHiddenTile);
-    const int64_t slice_cap = (int64_t)192 << 20;                    // bytes of W per split
+    // bytes of W per split: inside the 256 MB last-level cache; 224 rather than 192 MB lets
+    // a 274-tile vocabulary slab at H = 2880 (404 MB) take 2 splits rather than 4 (-0.17 ms
+    // per step at 32K tokens, and two fewer partial sums)
+    const int64_t slice_cap = (int64_t)224 << 20;
     int64_t smin = ((int64_t)Vpad * H * 2 + slice_cap - 1) / slice_cap;
     int64_t smax = std::min<int64_t>(32, Vpad / 256);
     smin = std::max<int64_t>(1, std::min(smin, smax));
