@@ -144,9 +144,10 @@ typedef struct fckl_desc {
  * host function, no HIP call.
  * Chooses the number of tokens per chunk for `desc` so that the workspace fits in
  * `budget_bytes` (0 = the library default, 12 GiB), preferring the largest chunk up to
- * 8192 tokens (beyond that the saving in re-streamed W and dW read-modify-write is
- * small and the chunk gradient keeps growing) and then evening out the chunks.  If
- * desc->chunk > 0 that chunk is kept and only its workspace size is reported.
+ * 8192 tokens (beyond that the saving in re-streamed W and in dW's per-chunk fp32
+ * additions is small, and the logit products' grids grow past where they gain) and then
+ * evening out the chunks.  If desc->chunk > 0 that chunk is kept and only its workspace
+ * size is reported.
  *   chunk_out    host, may be NULL: tokens per chunk.
  *   ws_bytes_out host, may be NULL: workspace bytes fckl_forward/fckl_backward need.
  * Returns FCKL_ERR_WORKSPACE when even the smallest chunk does not fit.
@@ -156,8 +157,8 @@ fckl_status fckl_plan(const fckl_desc *desc, size_t budget_bytes, int32_t *chunk
 
 /*
  * Workspace bytes needed for `desc` run with `chunk` tokens per chunk (chunk >= 1).
- * The workspace depends on chunk, H, V and K only, never on N: peak memory has no
- * N x V term.  Pure host function.
+ * The workspace depends on chunk, H, V, K and desc->vocab_slab only, never on N: peak
+ * memory has no N x V term.  Pure host function.
  */
 fckl_status fckl_workspace_size(const fckl_desc *desc, int32_t chunk, size_t *ws_bytes_out);
 

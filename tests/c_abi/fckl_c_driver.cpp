@@ -147,6 +147,28 @@ int main()
     fetch(l2, m2, gh2, gw2);
     CHECK(l1 == l2 && m1 == m2 && gh1 == gh2 && gw1 == gw2);   // bitwise repeatable
 
+    // the backward in vocabulary slabs of 512 rows (8 slabs, the last with the 4-row
+    // tile): the same loss and dW bit for bit, dH up to the order of its split sum
+    {
+        fckl_desc ds = d;
+        ds.vocab_slab = 512;
+        size_t slab_ws = 0;
+        CHECK(fckl_workspace_size(&ds, chunk, &slab_ws) == FCKL_OK && slab_ws < ws_bytes);
+        ds.chunk = chunk;
+        CHECK(fckl_forward(&ds, dh, dW_in, didx, dtl, loss, lse, mean, ws, slab_ws, s) == FCKL_OK);
+        CHECK(fckl_backward(&ds, dh, dW_in, didx, dtl, lse, 1.0f, dH, dW, ws, slab_ws, s) == FCKL_OK);
+        fetch(l2, m2, gh2, gw2);
+        CHECK(l1 == l2 && m1 == m2 && gw1 == gw2);
+        double e = 0.0, m = 0.0;
+        for (size_t q = 0; q < gh1.size(); ++q) {
+            e = std::fmax(e, std::fabs(gh1[q] - gh2[q]));
+            m = std::fmax(m, std::fabs(gh1[q]));
+        }
+        CHECK(e <= 1e-5 * m);
+        ds.vocab_slab = 100;     // not a multiple of 256
+        CHECK(fckl_backward(&ds, dh, dW_in, didx, dtl, lse, 1.0f, dH, dW, ws, ws_bytes, s) == FCKL_ERR_INVALID_ARG);
+    }
+
     double lmax = 0.0, lsum = 0.0;
     for (float x : l1) {
         CHECK(std::isfinite(x));
