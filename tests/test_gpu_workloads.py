@@ -18,7 +18,10 @@ At these sizes the oracle cannot run every token, so:
     to fp32 reordering (32 to 256 chunks of accumulation).
 An oracle check of dW rows over all N tokens would need every token's lse, 2 N V H
 flop in fp64 on the host (about 9 minutes at 32K tokens, over an hour at 256K), so
-the multi-chunk accumulation is pinned by the subset run and the chunk sweep instead.
+the multi-chunk accumulation is pinned by the subset run and the chunk sweep, and every
+output at full size (all tokens, all of dH and dW) is compared with the same definition
+computed densely in float32 by torch's own GEMMs on the GPU, a route pinned against the
+oracle on the CPU (tests/test_dense_reference.py).
 """
 import functools
 
@@ -29,7 +32,7 @@ import torch
 import chunked_top_kl_chunk_amd as fckl
 import oracle
 import synth
-from gpu_util import GRAD_TOL, LSE_ATOL, check_grad, check_loss, device, say, upload
+from gpu_util import GRAD_TOL, LOSS_RTOL, LSE_ATOL, check_grad, check_loss, device, say, upload
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
@@ -116,6 +119,76 @@ def _check_workload(key):
 @pytest.mark.parametrize("key", ["c2", "c3", "c4", "c5"])
 def test_full_workload(key):
     _check_workload(key)
+
+
+def _dense_fp32(h, W, idx, tl, T, block=4096):
+    """The definition written out densely in torch float32 on the GPU (its own GEMMs, not
+    this library), a block of tokens at a time: teacher softmax over the K cached
+    entries, z = h W^T, lse over the vocabulary, the per-token KL, g, dH = g W and
+    dW = g^T h accumulated over the blocks in float32.  The bf16 inputs are upcast
+    exactly.  Returns (loss, lse, dH, dW) as float32 tensors on the GPU."""
+    N, H = h.shape
+    V = W.shape[0]
+    Wf = W.float()
+    loss = torch.empty(N, dtype=torch.float32, device=h.device)
+    lse = torch.empty(N, dtype=torch.float32, device=h.device)
+    dH = torch.empty(N, H, dtype=torch.float32, device=h.device)
+    dW = torch.zeros(V, H, dtype=torch.float32, device=h.device)
+    for c0 in range(0, N, block):
+        c1 = min(N, c0 + block)
+        hc = h[c0:c1].float()
+        ic = idx[c0:c1].long()
+        a = tl[c0:c1].float() / T
+        lp = a - torch.logsumexp(a, dim=1, keepdim=True)
+        p = lp.exp()
+        s = torch.mm(hc, Wf.t()) / T
+        l = torch.logsumexp(s, dim=1)
+        zk = s.gather(1, ic)
+        loss[c0:c1] = T * T * (p * (lp - zk + l[:, None])).sum(1)
+        lse[c0:c1] = l
+        g = (s - l[:, None]).exp_()
+        g *= p.sum(1, keepdim=True)
+        g.scatter_add_(1, ic, -p)
+        g *= T / N
+        dH[c0:c1] = torch.mm(g, Wf)
+        dW += torch.mm(g.t().contiguous(), hc)
+        del s, g, zk
+    return loss, lse, dH, dW
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("key", ["c3", "c4"])
+def test_dense_fp32_reference_at_full_size(key):
+    """Every output at full size (all tokens' loss and lse, all of dH and dW after the
+    fp32 accumulation over every chunk and vocabulary slab) against the plain dense
+    definition computed in float32 by torch on the GPU: a second, independent route at
+    the sizes the oracle cannot run whole.  Tolerances as for the oracle."""
+    wl = synth.WORKLOADS[key]
+    say("case: dense float32 reference", key, wl.name)
+    x = inputs(key)
+    dev = device()
+    h, W, idx, tl = upload(x, dev)
+    desc = fckl.desc_for(h, W, idx, tl, wl.T)
+    chunk, ws_bytes = fckl.plan(desc)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    loss, lse, mean = fckl.forward(h, W, idx, tl, T=wl.T, chunk=chunk, ws=ws)
+    dH, dW = fckl.backward(h, W, idx, tl, lse, T=wl.T, chunk=chunk, ws=ws)
+    torch.cuda.synchronize()
+    del ws
+    r_loss, r_lse, r_dH, r_dW = _dense_fp32(h, W, idx, tl, wl.T)
+    torch.cuda.synchronize()
+    e_loss = ((loss.double() - r_loss.double()).abs() / r_loss.double().abs().clamp_min(1e-30)).max().item()
+    e_lse = (lse - r_lse).abs().max().item()
+    e_mean = abs(float(mean.item()) - r_loss.double().mean().item()) / abs(r_loss.double().mean().item())
+    e_dH = ((dH - r_dH).abs().max() / r_dH.abs().max()).item()
+    e_dW = ((dW - r_dW).abs().max() / r_dW.abs().max()).item()
+    say("%s vs dense float32 (chunk %d, %d chunks): loss %.2e lse %.2e mean %.2e dH %.2e dW %.2e"
+        % (key, chunk, -(-wl.N // chunk), e_loss, e_lse, e_mean, e_dH, e_dW))
+    assert e_loss <= LOSS_RTOL and e_mean <= LOSS_RTOL
+    assert e_lse <= LSE_ATOL
+    assert e_dH <= GRAD_TOL and e_dW <= GRAD_TOL
+    del h, W, idx, tl, loss, lse, dH, dW, r_loss, r_lse, r_dH, r_dW
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.timeout(900)
