@@ -157,7 +157,7 @@ def _dense_fp32(h, W, idx, tl, T, block=4096):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("key", ["c3", "c4"])
+@pytest.mark.parametrize("key", ["c2", "c3", "c4", "c5"])
 def test_dense_fp32_reference_at_full_size(key):
     """Every output at full size (all tokens' loss and lse, all of dH and dW after the
     fp32 accumulation over every chunk and vocabulary slab) against the plain dense
