@@ -138,6 +138,7 @@ def main():
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     torch.cuda.reset_peak_memory_stats()
+    free_before = torch.cuda.mem_get_info()[0]        # hipMemGetInfo, the device's own count
     h = torch.from_numpy(x.h_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     W = torch.from_numpy(x.W_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     idx = torch.from_numpy(np.ascontiguousarray(x.idx)).to(dev)
@@ -164,6 +165,10 @@ def main():
         torch.cuda.synchronize()
         log("warmup step %d done" % i)
     peak_bytes = torch.cuda.max_memory_allocated()
+    # cross-check from the device side: the drop in free device memory since before the
+    # inputs were uploaded (the allocator's reservations, so the peak rounded up to its
+    # blocks, plus the runtime's own)
+    device_used = free_before - torch.cuda.mem_get_info()[0]
 
     clock = {}
     ms_step, kernels = timed_steps(fckl, step, args.steps, nchunks, clock)
@@ -232,6 +237,7 @@ def main():
         "forward_ms": round(pass_ms["forward"], 3), "backward_ms": round(pass_ms["backward"], 3),
         "step_tflops": round(step_tflops, 1),
         "peak_gib": round(peak_bytes / GiB, 3),
+        "device_used_gib": round(device_used / GiB, 3),
         "workspace_gib": round(ws_bytes / GiB, 3),
         "w_stream": w_stream,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
