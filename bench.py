@@ -119,6 +119,8 @@ def main():
 
     fckl.load()
     dev = torch.device("cuda:0")
+    # the device's own count of free memory (hipMemGetInfo) before anything of this run
+    free_start = torch.cuda.mem_get_info(dev)[0]
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -136,9 +138,12 @@ def main():
     x = synth.make_inputs(wl, device=dev)
     log("inputs ready in %.1fs" % (time.time() - t0))
     torch.cuda.synchronize()
+    # the generator's products leave torch's BLAS workspace allocated, which pins a cached
+    # segment: release both, so that the step's own allocations are what the device sees
+    if hasattr(torch._C, "_cuda_clearCublasWorkspaces"):
+        torch._C._cuda_clearCublasWorkspaces()
     torch.cuda.empty_cache()
     torch.cuda.reset_peak_memory_stats()
-    free_before = torch.cuda.mem_get_info()[0]        # hipMemGetInfo, the device's own count
     h = torch.from_numpy(x.h_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     W = torch.from_numpy(x.W_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     idx = torch.from_numpy(np.ascontiguousarray(x.idx)).to(dev)
@@ -165,10 +170,10 @@ def main():
         torch.cuda.synchronize()
         log("warmup step %d done" % i)
     peak_bytes = torch.cuda.max_memory_allocated()
-    # cross-check from the device side: the drop in free device memory since before the
-    # inputs were uploaded (the allocator's reservations, so the peak rounded up to its
-    # blocks, plus the runtime's own)
-    device_used = free_before - torch.cuda.mem_get_info()[0]
+    # cross-check from the device side: the drop in free device memory since the start
+    # of the run.  An upper bound of the peak: it also holds the allocator's rounding to
+    # its segments, what input generation left reserved and the runtime's code objects.
+    device_used = free_start - torch.cuda.mem_get_info(dev)[0]
 
     clock = {}
     ms_step, kernels = timed_steps(fckl, step, args.steps, nchunks, clock)
