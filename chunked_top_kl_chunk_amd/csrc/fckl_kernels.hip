@@ -13,14 +13,17 @@
 //                    picked logits per token leave the chip.
 //   combine          per token: logsumexp over the tiles, the KL term, the loss
 //   backward_logits  the same MFMA tiles recompute z (the extra projection in the
-//                    backward pass that the chunked loss pays for, axbrief.com);
-//                    the epilogue forms g = c((sum p) softmax(z/T) - scatter(p, idx)),
-//                    rounds it to bf16 and writes the chunk's g once, vocabulary-major
-//                    g^T [V, C], the operand of both products below
-//   dh               dH_chunk^T = W^T . g^T over the vocabulary (g^T read through
-//                    transposing LDS reads; split over the vocabulary, fixed-order reduce)
-//   dw               dW += g^T . h_chunk (fp32, chunk after chunk: the first chunk stores,
-//                    the others add with fp32 atomics at L2, one adder per element)
+//                    backward pass that the chunked loss pays for, axbrief.com) over one
+//                    vocabulary slab of the chunk; the epilogue forms
+//                    g = c((sum p) softmax(z/T) - scatter(p, idx)), rounds it to bf16 and
+//                    writes the slab's g once, vocabulary-major g^T [slab rows, C], the
+//                    operand of both products below
+//   dh               the slab's share of dH_chunk^T = W^T . g^T over the vocabulary (g^T
+//                    read through transposing LDS reads; split over the slab's rows; one
+//                    fixed-order reduce of every slab's splits after the last slab)
+//   dw               the slab's rows of dW += g^T . h_chunk (fp32, chunk after chunk: the
+//                    first chunk stores, the others add with fp32 atomics at L2, one adder
+//                    per element)
 //   transpose        W -> W^T once per backward call, h_chunk -> h_chunk^T per chunk
 //
 // GEMM core: 256 x 256 tiles, 512 threads = 8 wave64s, each wave owns a 128 x 64 block
