@@ -955,15 +955,17 @@ __device__ __forceinline__ void forward_tile(const FwdParams &p, char *smem, int
         constexpr bool interior = decltype(interior_c)::value;
 #pragma unroll
         for (int j = 0; j < G::NB; ++j) {
+            // the scale log2(e)/T is positive, so scaling the largest value gives the
+            // largest scaled value, bit for bit
             float mx = kNegInf;
 #pragma unroll
             for (int i = 0; i < G::MB; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const bool in = interior || 32 * i + 8 * (r >> 2) + (r & 3) < lim;
-                    mx = fmaxf(mx, in ? acc[i][j][r] * p.scale2 : kNegInf);
+                    mx = fmaxf(mx, in ? acc[i][j][r] : kNegInf);
                 }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale2;
             const float ms = (mx == kNegInf) ? 0.0f : mx;
             float sum = 0.0f;
 #pragma unroll
