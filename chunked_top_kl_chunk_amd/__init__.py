@@ -327,13 +327,13 @@ def backward(h, W, topk_idx, topk_logit, lse, T: float = 1.0, grad_scale: float 
 def forward_backward(h, W, topk_idx, topk_logit, T: float = 1.0, grad_scale: float = 1.0, weights=None,
                      chunk: int = 0, ws=None, loss_tok=None, lse=None, loss_mean=None, dH=None, dW=None,
                      accumulate: bool = False, validate: bool = False, stream=None,
-                     profile: Optional[Profile] = None):
+                     profile: Optional[Profile] = None, vocab_slab: int = 0):
     """Loss and gradients in one call (fckl_forward_backward): the logits of each chunk
-    are formed once.  Returns (loss_tok, lse, loss_mean, dH, dW)."""
+    are formed once.  vocab_slab as for backward.  Returns (loss_tok, lse, loss_mean, dH, dW)."""
     _check_inputs(h, W, topk_idx, topk_logit)
     dev = h.device
     flags = (FLAG_VALIDATE if validate else 0) | (FLAG_DW_ACCUMULATE if accumulate else 0)
-    desc = desc_for(h, W, topk_idx, topk_logit, T, chunk, flags, profile)
+    desc = desc_for(h, W, topk_idx, topk_logit, T, chunk, flags, profile, vocab_slab)
     ws = _workspace(desc, ws, dev, single=True)
     N = h.shape[0]
     weights = _weights(weights, N, dev)
@@ -408,10 +408,11 @@ def full_plan(desc: Desc, H_teacher: int, budget_bytes: int = 0) -> Tuple[int, i
 
 def full_forward_backward(h, W, h_t, W_t, T: float = 1.0, grad_scale: float = 1.0, weights=None, chunk: int = 0,
                           budget_bytes: int = 0, ws=None, loss_tok=None, lse=None, loss_mean=None, dH=None, dW=None,
-                          accumulate: bool = False, stream=None, profile: Optional[Profile] = None):
+                          accumulate: bool = False, stream=None, profile: Optional[Profile] = None,
+                          vocab_slab: int = 0):
     """Online distillation against the teacher's full distribution
     (fckl_full_forward_backward): the student (h, W) and the teacher (h_t, W_t) share the
-    vocabulary.  Returns (loss_tok, lse, loss_mean, dH, dW)."""
+    vocabulary.  vocab_slab as for backward.  Returns (loss_tok, lse, loss_mean, dH, dW)."""
     import torch
     for name, t in (("h", h), ("W", W), ("h_t", h_t), ("W_t", W_t)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
@@ -424,7 +425,7 @@ def full_forward_backward(h, W, h_t, W_t, T: float = 1.0, grad_scale: float = 1.
         raise ValueError("expected h[N,H], W[V,H], h_t[N,Ht], W_t[V,Ht]")
     dev = h.device
     flags = FLAG_DW_ACCUMULATE if accumulate else 0
-    desc = make_desc(N, H, V, 1, T, chunk, DTYPE_BF16, flags, profile)
+    desc = make_desc(N, H, V, 1, T, chunk, DTYPE_BF16, flags, profile, vocab_slab)
     desc.chunk, need = full_plan(desc, Ht, budget_bytes if budget_bytes else device_budget(dev))
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)

@@ -219,12 +219,29 @@ fckl_status dh_reduce(const fckl_desc *desc, const ChunkArgs &a, int64_t c0, flo
     return launch_dh_reduce(a, dH + (size_t)c0 * desc->H, stream) ? FCKL_ERR_HIP : FCKL_OK;
 }
 
-// dH and dW of one chunk whose g^T (the whole vocabulary) and h^T are in the workspace.
-fckl_status chunk_products(const fckl_desc *desc, const ChunkArgs &a, int64_t c0, float *dH, float *dW,
-                           void *stream)
+// The chunk's gradient products, one vocabulary slab at a time: `grad` launches the kernel
+// that writes the slab's g^T (`kernel`, for the profile), then come the slab's dH splits
+// and dW rows; the dH splits of every slab are summed after the last.  The chunk's h^T is
+// in the workspace.
+template <class Grad>
+fckl_status slabbed_products(const fckl_desc *desc, ChunkArgs a, int64_t c0, float *dH, float *dW, int kernel,
+                             void *stream, Grad grad)
 {
-    fckl_status st = slab_products(desc, a, c0, dW, stream);
-    return st != FCKL_OK ? st : dh_reduce(desc, a, c0, dH, stream);
+    const Layout &L = *a.L;
+    for (int32_t s = 0; s < L.nslab; ++s) {
+        slab_tiles_of(L, s, &a.vt0, &a.nvt);
+        a.split0 = dh_partials(L, a.V, a.H, s);
+        const int vrows = std::min(a.V - a.vt0 * kVocabTile, a.nvt * kVocabTile);
+        {
+            Timed t(desc, kernel, a.rows, stream, vrows);
+            if (grad(a))
+                return FCKL_ERR_HIP;
+        }
+        const fckl_status st = slab_products(desc, a, c0, dW, stream);
+        if (st != FCKL_OK)
+            return st;
+    }
+    return dh_reduce(desc, a, c0, dH, stream);
 }
 
 fckl_status backward_impl(const fckl_desc *desc, const void *h, const void *W, const int32_t *topk_idx,
@@ -267,20 +284,10 @@ fckl_status backward_impl(const fckl_desc *desc, const void *h, const void *W, c
             if (launch_transpose_chunk(a, stream))
                 return FCKL_ERR_HIP;
         }
-        // One vocabulary slab at a time: its logits and g^T, its dH splits, its dW rows.
-        for (int32_t s = 0; s < L.nslab; ++s) {
-            slab_tiles_of(L, s, &a.vt0, &a.nvt);
-            a.split0 = dh_partials(L, a.V, a.H, s);
-            const int vrows = std::min(a.V - a.vt0 * kVocabTile, a.nvt * kVocabTile);
-            {
-                Timed t(desc, FCKL_KERNEL_BWD_LOGITS, a.rows, stream, vrows);
-                if (launch_backward_logits(a, lse + c0, stream))
-                    return FCKL_ERR_HIP;
-            }
-            if ((st = slab_products(desc, a, c0, dW, stream)) != FCKL_OK)
-                return st;
-        }
-        if ((st = dh_reduce(desc, a, c0, dH, stream)) != FCKL_OK)
+        // one vocabulary slab at a time: its logits recomputed into g^T, its products
+        st = slabbed_products(desc, a, c0, dH, dW, FCKL_KERNEL_BWD_LOGITS, stream,
+                              [&](const ChunkArgs &sa) { return launch_backward_logits(sa, lse + c0, stream); });
+        if (st != FCKL_OK)
             return st;
     }
     return FCKL_OK;
@@ -425,16 +432,14 @@ fckl_status fckl_forward_backward(const fckl_desc *desc, const void *h, const vo
                 return FCKL_ERR_HIP;
         }
         {
-            Timed t(desc, FCKL_KERNEL_SOFTMAX_GRAD, a.rows, stream);
-            if (launch_softmax_grad(a, lse + c0, gs, stream))
-                return FCKL_ERR_HIP;
-        }
-        {
             Timed t(desc, FCKL_KERNEL_TRANSPOSE, a.rows, stream);
             if (launch_transpose_chunk(a, stream))
                 return FCKL_ERR_HIP;
         }
-        if ((st = chunk_products(desc, a, c0, dH, dW, stream)) != FCKL_OK)
+        // one vocabulary slab at a time: g^T from the kept exponentials, its products
+        st = slabbed_products(desc, a, c0, dH, dW, FCKL_KERNEL_SOFTMAX_GRAD, stream,
+                              [&](const ChunkArgs &sa) { return launch_softmax_grad(sa, lse + c0, gs, stream); });
+        if (st != FCKL_OK)
             return st;
     }
     return loss_mean ? mean_of(desc, loss_tok, weights, loss_mean, stream) : FCKL_OK;
@@ -529,16 +534,14 @@ fckl_status fckl_full_forward_backward(const fckl_desc *desc, int32_t H_teacher,
                 return FCKL_ERR_HIP;
         }
         {
-            Timed t(&d, FCKL_KERNEL_FULL_GRAD, a.rows, stream);
-            if (launch_full_grad(a, F, gs, stream))
-                return FCKL_ERR_HIP;
-        }
-        {
             Timed t(&d, FCKL_KERNEL_TRANSPOSE, a.rows, stream);
             if (launch_transpose_chunk(a, stream))
                 return FCKL_ERR_HIP;
         }
-        if ((st = chunk_products(&d, a, c0, dH, dW, stream)) != FCKL_OK)
+        // one vocabulary slab at a time: g^T from the kept values and a_t, its products
+        st = slabbed_products(&d, a, c0, dH, dW, FCKL_KERNEL_FULL_GRAD, stream,
+                              [&](const ChunkArgs &sa) { return launch_full_grad(sa, F, gs, stream); });
+        if (st != FCKL_OK)
             return st;
     }
     return loss_mean ? mean_of(&d, loss_tok, weights, loss_mean, stream) : FCKL_OK;

@@ -61,7 +61,7 @@ struct Layout {
     int32_t Vpad = 0;       // nVt * kVocabTile (row pitch of g)
     int32_t cnt_stride = 0; // bytes per token of the per-tile entry-count table
     int32_t dh_splits = 0;  // vocabulary splits of the dH product, over all slabs
-    int32_t nslab = 1;      // vocabulary slabs of the two-pass backward (1 in the other layouts)
+    int32_t nslab = 1;      // vocabulary slabs of the gradient products (1 in a forward-only layout)
     int32_t slab_tiles = 0; // vocabulary tiles per slab; the last slab takes the remainder
     int32_t gT_tiles = 0;   // vocabulary tiles of the largest slab (rows of g^T / kVocabTile)
     size_t off_idx = 0;     // int32 [Cpad, K]   cached indices, sorted ascending per token

@@ -1234,7 +1234,8 @@ __global__ __launch_bounds__(LogitGemm::NT) void backward_logits_kernel(BwdParam
 
 struct SoftGradParams {
     const uint16_t *ex;     // [Cpad, Vpad] bf16: the kept 2^(z/T log2 e - m)
-    uint16_t *gT;           // [Vpad, Cpad] bf16 out
+    uint16_t *gT;           // [slab rows, Cpad] bf16 out
+    int vt0;                // first vocabulary tile of the slab
     const float *mw;        // [2 nVt, Cpad] the half-tile maxima m (base 2)
     const float *lse;       // chunk's first token (natural log, z/T units)
     const float *psum;      // [Cpad] sum_k p
@@ -1260,7 +1261,7 @@ __global__ __launch_bounds__(kSgThreads) void softmax_grad_kernel(SoftGradParams
     __shared__ __attribute__((aligned(16))) char smem[kSgTok * kGStagePitch];
     constexpr int kStride = kSgThreads / 32;
     constexpr int kRows = kSgTok / kStride;     // token rows per thread
-    const int tm = blockIdx.x, n0 = blockIdx.y * kSgTok, m0 = tm * 256;
+    const int tm = p.vt0 + blockIdx.x, n0 = blockIdx.y * kSgTok, m0 = tm * 256;
     const int c = threadIdx.x & 31;     // 16-byte piece of the tile row
     const int half = c >> 4;            // its 128-row half of the vocabulary tile
     const int r0 = threadIdx.x >> 5;
@@ -1308,7 +1309,7 @@ __global__ __launch_bounds__(kSgThreads) void softmax_grad_kernel(SoftGradParams
         *reinterpret_cast<u32x4 *>(smem + rl * kGStagePitch + 16 * c) = out;
     }
     __syncthreads();
-    store_vocab_major<kSgTok, kSgThreads / 64>(smem, p.gT, (size_t)p.Cpad, m0, n0);
+    store_vocab_major<kSgTok, kSgThreads / 64>(smem, p.gT, (size_t)p.Cpad, m0 - p.vt0 * 256, n0);
 }
 
 // ------------------------------------------------------------------ full teacher distribution
@@ -1542,7 +1543,8 @@ __global__ __launch_bounds__(256) void full_combine_kernel(const float2 *part, c
 
 struct FullGradParams {
     const uint16_t *ex;     // [Cpad, Vpad] the student's kept exponentials
-    uint16_t *gT;           // [Vpad, Cpad] out
+    uint16_t *gT;           // [slab rows, Cpad] out
+    int vt0;                // first vocabulary tile of the slab
     const float *at;        // a_t in fragment order (at_frag)
     const float *mw;        // [2 nVt, Cpad]
     const float *ls2, *lt2; // [Cpad] L_s, L_t
@@ -1563,7 +1565,7 @@ __global__ __launch_bounds__(256) void full_grad_kernel(FullGradParams p)
     using G = LogitGemm;
     constexpr int kTok = 64;
     __shared__ __attribute__((aligned(16))) char smem[kTok * kGStagePitch];
-    const int tm = blockIdx.x, n0 = blockIdx.y * kTok, m0 = tm * 256;
+    const int tm = p.vt0 + blockIdx.x, n0 = blockIdx.y * kTok, m0 = tm * 256;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int wm = wv >> 1, j = wv & 1;
     const int tn = n0 / G::BN, wn = (n0 % G::BN) / G::WTN;
@@ -1604,7 +1606,7 @@ __global__ __launch_bounds__(256) void full_grad_kernel(FullGradParams p)
         cell[1] = pack_bf16x2(g[2], g[3]);
     }
     __syncthreads();
-    store_vocab_major<kTok, 4>(smem, p.gT, (size_t)p.Cpad, m0, n0);
+    store_vocab_major<kTok, 4>(smem, p.gT, (size_t)p.Cpad, m0 - p.vt0 * 256, n0);
 }
 
 // ------------------------------------------------------------------ teacher top-K
@@ -2279,7 +2281,8 @@ int launch_softmax_grad(const ChunkArgs &a, const float *lse, const GradScale &g
     p.w = gs.w;
     p.inv_wsum = gs.inv_wsum;
     p.mul = gs.mul;
-    hipLaunchKernelGGL(softmax_grad_kernel, dim3(L.nVt, (a.rows + kSgTok - 1) / kSgTok), dim3(kSgThreads), 0,
+    p.vt0 = a.vt0;
+    hipLaunchKernelGGL(softmax_grad_kernel, dim3(a.nvt, (a.rows + kSgTok - 1) / kSgTok), dim3(kSgThreads), 0,
                        S(stream), p);
     return (int)hipGetLastError();
 }
@@ -2517,7 +2520,8 @@ int launch_full_grad(const ChunkArgs &a, const FullLayout &F, const GradScale &g
     p.coef = gs.coef;
     p.w = gs.w;
     p.inv_wsum = gs.inv_wsum;
-    hipLaunchKernelGGL(full_grad_kernel, dim3(L.nVt, (a.rows + 63) / 64), dim3(256), 0, S(stream), p);
+    p.vt0 = a.vt0;
+    hipLaunchKernelGGL(full_grad_kernel, dim3(a.nvt, (a.rows + 63) / 64), dim3(256), 0, S(stream), p);
     return (int)hipGetLastError();
 }
 

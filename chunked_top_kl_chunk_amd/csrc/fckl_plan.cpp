@@ -161,7 +161,7 @@ fckl_status make_layout(const fckl_desc *d, int32_t chunk, Layout *L, LayoutKind
     o.dh_splits = dh_split_count(o.Cpad, d->H, o.Vpad);
     o.nslab = 1;
     o.slab_tiles = o.gT_tiles = o.nVt;
-    if (kind == LayoutKind::TwoPass)
+    if (kind != LayoutKind::ForwardOnly)
         plan_slabs(d, o);
     const size_t Cp = (size_t)o.Cpad, K = (size_t)d->K;
     size_t off = 0;

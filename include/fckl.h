@@ -257,11 +257,11 @@ fckl_status fckl_forward_noalloc(const fckl_desc *desc, const void *h, const voi
  * of a 256-row vocabulary tile, and once the chunk's lse is known a streaming kernel
  * turns those values into g.  That is 6 N V H flop instead of 8.  g differs from the
  * two-call path by the bf16 rounding of the kept values, which has the same relative size
- * as the rounding of g itself.  Workspace: the kept values (2 V bytes per token of the
- * chunk) and g for the whole vocabulary, as the kept values span it (the single call
- * takes the vocabulary as one slab; desc->vocab_slab is not used).  fckl_single_plan gives
- * the size (and, with desc->chunk = 0, the chunk as fckl_plan chooses it for that layout),
- * and the call uses the chunk fckl_single_plan(desc, ws_bytes) reports.
+ * as the rounding of g itself.  g, dH and dW are formed one vocabulary slab at a time, as
+ * in fckl_backward (desc->vocab_slab).  Workspace: the kept values take 2 V bytes per
+ * token of the chunk more than the two-call path needs; fckl_single_plan gives the size
+ * (and, with desc->chunk = 0, the chunk as fckl_plan chooses it for that layout), and the
+ * call uses the chunk fckl_single_plan(desc, ws_bytes) reports.
  */
 fckl_status fckl_single_plan(const fckl_desc *desc, size_t budget_bytes, int32_t *chunk_out,
                              size_t *ws_bytes_out);
@@ -333,7 +333,8 @@ fckl_status fckl_topk_async(const fckl_desc *desc, const void *h, const void *W,
  * fp32 (4 V bytes per token of workspace) and the student product keeps 2^(z/T log2 e - m)
  * in bf16, as fckl_forward_backward does, so the logits of each model are formed once:
  * 2 N V Ht + 6 N V H flop.
- *   desc       N, H (the student's), V, T, chunk, flags (FCKL_FLAG_DW_ACCUMULATE), profile;
+ *   desc       N, H (the student's), V, T, chunk, flags (FCKL_FLAG_DW_ACCUMULATE), profile,
+ *              vocab_slab (g, dH and dW one vocabulary slab at a time, as in fckl_backward);
  *              K and logit_dtype are not read; FCKL_FLAG_VALIDATE has no effect
  *   H_teacher  the teacher's hidden size (a multiple of 8, at most 65536)
  *   h, W       device, bf16 [N,H], [V,H]            the student

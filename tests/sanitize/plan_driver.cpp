@@ -55,7 +55,6 @@ static void check_layout(const fckl_desc &d, const Layout &L)
     // vocabulary slabs: contiguous, covering every tile, g^T sized for the largest, dH
     // partial sums for every split that holds a row (a keep layout has one slab)
     CHECK(L.nslab >= 1 && L.slab_tiles >= 1 && L.gT_tiles >= 1 && L.gT_tiles <= L.nVt);
-    CHECK(L.kind == LayoutKind::TwoPass || (L.nslab == 1 && L.gT_tiles == L.nVt));
     int32_t next = 0, biggest = 0;
     for (int32_t s = 0; s < L.nslab; ++s) {
         int32_t vt0 = -1, nvt = -1;
@@ -138,14 +137,15 @@ int main()
                             CHECK(check_desc(&ds) == FCKL_ERR_INVALID_ARG);
                             continue;
                         }
-                        for (int32_t chunk : {256, 8192}) {
-                            Layout L;
-                            if (make_layout(&ds, chunk, &L, LayoutKind::TwoPass) == FCKL_OK) {
-                                check_layout(ds, L);
-                                CHECK(L.nslab == std::max<int32_t>(1, L.nVt / (slab / 256)));
-                                CHECK(L.slab_tiles == (L.nslab > 1 ? slab / 256 : L.nVt));
+                        for (int32_t chunk : {256, 8192})
+                            for (LayoutKind kind : {LayoutKind::TwoPass, LayoutKind::Keep}) {
+                                Layout L;
+                                if (make_layout(&ds, chunk, &L, kind) == FCKL_OK) {
+                                    check_layout(ds, L);
+                                    CHECK(L.nslab == std::max<int32_t>(1, L.nVt / (slab / 256)));
+                                    CHECK(L.slab_tiles == (L.nslab > 1 ? slab / 256 : L.nVt));
+                                }
                             }
-                        }
                     }
                     for (int32_t chunk : {1, 256, 1000, 8192, 1 << 20, (1 << 24) + 1}) {
                         Layout L;

@@ -154,3 +154,31 @@ def test_full_teacher_module():
     with torch.no_grad():
         l2 = FullTeacherKLLoss(temperature=T, chunk=256)(hb, Wb, htb, dWt, mask=mask)
     assert float(l2) == float(loss.detach())
+
+
+def test_full_teacher_in_vocabulary_slabs():
+    """g, dH and dW one vocabulary slab at a time (slabs of 2 tiles over V = 4100, the
+    last slab of 3 tiles ending in a 4-row tile), weighted, two chunks: the oracle's
+    results, and bit for bit those of one slab except for the order of the dH sum."""
+    N, Hs, Ht, V, T = 600, 256, 384, 4100, 1.2
+    say("case: full teacher, vocabulary slabs")
+    h, W, ht, Wt = models(90, N, Hs, Ht, V)
+    w = weights_for(190, N)
+    wt = torch.from_numpy(w).to(device())
+    t = to_dev(h, W, ht, Wt)
+    a = fckl.full_forward_backward(*t, T=T, grad_scale=0.8, weights=wt, chunk=512, vocab_slab=512)
+    b = fckl.full_forward_backward(*t, T=T, grad_scale=0.8, weights=wt, chunk=512,
+                                   vocab_slab=(V + 255) // 256 * 256)
+    torch.cuda.synchronize()
+    for k, x, y in zip(("loss", "lse", "mean", "dH", "dW"), a, b):
+        if k == "dH":
+            d = (x - y).abs().max().item() / y.abs().max().item()
+            assert d < 1e-5, d
+        else:
+            assert torch.equal(x, y), k
+    loss, lse, mean, dH, dWg = (x.cpu().numpy() for x in a)
+    r_loss, r_lse, r_mean, r_dH, r_dW = oracle.full(h, W, ht, Wt, T, w=w, grad_scale=0.8)
+    check_loss(loss, r_loss, "full-slab")
+    assert float(np.abs(lse - r_lse).max()) <= LSE_ATOL
+    check_grad(dH, r_dH, "full-slab dH")
+    check_grad(dWg, r_dW, "full-slab dW")

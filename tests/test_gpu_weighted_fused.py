@@ -282,3 +282,26 @@ def test_masked_rows_with_non_finite_cached_logits():
         out = mod(hl.to(torch.bfloat16), Wl.to(torch.bfloat16), di, dt, weights=wt)
         out.backward()
         check(loss, lse, out.detach().reshape(1), hl.grad, Wl.grad, "module single_call=%s" % single)
+
+
+@pytest.mark.parametrize("slab", [512, 256])
+def test_single_call_in_vocabulary_slabs(slab):
+    """The single call forms g, dH and dW one vocabulary slab at a time (V = 3000: slabs
+    of 2 tiles or 1 tile, the last holding the 184-row tail), with weights, over three
+    chunks: the oracle's results, and bit for bit those of one slab except for the order
+    of the dH sum."""
+    N, H, V, K, T = 700, 264, 3000, 12, 1.3
+    say("case: single call, vocabulary slab", slab)
+    h, W, idx, tl = synthetic(151, N, H, V, K, T)
+    w = weights_for(152, N)
+    t = arrays(h, W, idx, tl)
+    wt = torch.from_numpy(w).to(device())
+    a = fckl.forward_backward(*t, T=T, grad_scale=0.5, weights=wt, chunk=256, vocab_slab=slab)
+    b = fckl.forward_backward(*t, T=T, grad_scale=0.5, weights=wt, chunk=256, vocab_slab=(V + 255) // 256 * 256)
+    torch.cuda.synchronize()
+    for k, x, y in zip(("loss", "lse", "mean"), a[:3], b[:3]):
+        assert torch.equal(x, y), k
+    assert torch.equal(a[4], b[4]), "dW"
+    assert rel_max(a[3].cpu().numpy(), b[3].cpu().numpy()) < 1e-5
+    g = {k: v.cpu().numpy() for k, v in zip(("loss", "lse", "mean", "dH", "dW"), a)}
+    check_weighted(g, h, W, idx, tl, T, w, 0.5, "single-slab%d" % slab)
