@@ -33,20 +33,23 @@ def check_replays(graph, outs, ref, what):
     say("%s: %d replays equal the eager call" % (what, REPLAYS))
 
 
-def test_two_passes_in_a_graph():
+@pytest.mark.parametrize("slab", [0, 512], ids=["planner-slab", "slabs-of-512"])
+def test_two_passes_in_a_graph(slab):
+    """With slabs of 512 vocabulary rows the backward launches its three kernels six
+    times per chunk: the graph holds all of them."""
     N, H, V, K, T = 600, 256, 3000, 10, 1.5
     h, W, idx, tl = synthetic(90, N, H, V, K, T)
     dh, dW_, di, dt = arrays(h, W, idx, tl)
     dev = device()
-    desc = fckl.desc_for(dh, dW_, di, dt, T, 256)
+    desc = fckl.desc_for(dh, dW_, di, dt, T, 256, vocab_slab=slab)
     ws = torch.empty(fckl.workspace_size(desc, 256), dtype=torch.uint8, device=dev)
     outs = [torch.empty(N, device=dev), torch.empty(N, device=dev), torch.empty(1, device=dev),
             torch.empty(N, H, device=dev), torch.empty(V, H, device=dev)]
     loss, lse, mean, dH, dW = outs
 
     def step():
-        fckl.forward(dh, dW_, di, dt, T=T, chunk=256, ws=ws, loss_tok=loss, lse=lse, loss_mean=mean)
-        fckl.backward(dh, dW_, di, dt, lse, T=T, grad_scale=0.5, chunk=256, ws=ws, dH=dH, dW=dW)
+        fckl.forward(dh, dW_, di, dt, T=T, chunk=256, ws=ws, loss_tok=loss, lse=lse, loss_mean=mean, vocab_slab=slab)
+        fckl.backward(dh, dW_, di, dt, lse, T=T, grad_scale=0.5, chunk=256, ws=ws, dH=dH, dW=dW, vocab_slab=slab)
 
     step()
     torch.cuda.synchronize()
