@@ -1916,8 +1916,9 @@ struct DhParams {
     const uint16_t *gT;     // [V rows of the slab, Cpad]
     const uint16_t *WT;     // the slab's first column of W^T [H, row pitch Vpad]
     int H, V, Vpad, rows, Cpad, nMt, nNt, ksplit;   // V: the slab's vocabulary rows
-    int GM;                 // hidden tiles per group of the tile order
+    int GM;                 // hidden tiles per group of the fallback tile order
     int split0;             // index of the slab's first split among all partial sums
+    int xblk;               // 1: XCD blocks of 4 hidden x 8 token tiles (see dh_kernel)
     float *part;            // [splits, Cpad, H]
 };
 
@@ -1925,11 +1926,29 @@ template <class G>
 __global__ __launch_bounds__(G::NT) void dh_kernel(DhParams p)
 {
     __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
-    int tm, tn;
-    // groups of GM hidden tiles with all token tiles, hidden tile fastest
-    map_tile(blockIdx.x, p.nMt, p.nNt, p.GM, tm, tn);
+    int tm, tn, split;
+    if (p.xblk) {
+        // Work-group L of the launch runs on XCD L % 8.  The launch is cut into blocks of
+        // 4 hidden x 8 token tiles of one split (splits outermost, then token groups, then
+        // hidden groups), and the w-th work-group of an XCD takes tile w % 32 (hidden
+        // fastest) of block (w / 32) * 8 + L % 8.  The 32 work-groups an XCD runs at a
+        // time then read 4 row blocks of W^T and 8 column blocks of g^T per k-step, and
+        // the eight XCDs of a round read the same split.
+        const int L = blockIdx.y * gridDim.x + blockIdx.x;
+        const int w = L >> 3, q = w & 31;
+        const int beta = (w >> 5) * 8 + (L & 7);
+        const int hgs = p.nMt >> 2, bps = hgs * (p.nNt >> 3);
+        split = beta / bps;
+        const int b = beta - split * bps;
+        tm = (b % hgs) * 4 + (q & 3);
+        tn = (b / hgs) * 8 + (q >> 2);
+    } else {
+        // groups of GM hidden tiles with all token tiles, hidden tile fastest
+        map_tile(blockIdx.x, p.nMt, p.nNt, p.GM, tm, tn);
+        split = blockIdx.y;
+    }
     const int m0 = tm * G::BM, n0 = tn * G::BN;     // m: hidden, n: tokens
-    const int k_begin = blockIdx.y * p.ksplit;
+    const int k_begin = split * p.ksplit;
     const int k_end = min(p.V, k_begin + p.ksplit);
     f32x16 acc[G::MB][G::NB];
     // dH^T tile: A(m = hidden, k = vocab) = WT[m][k]; B(n = token, k = vocab) = gT[k][n].
@@ -1940,7 +1959,7 @@ __global__ __launch_bounds__(G::NT) void dh_kernel(DhParams p)
                                       k_end, acc);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = G::wm_of(wave), wn = G::wn_of(wave);
-    float *out = p.part + (size_t)(p.split0 + blockIdx.y) * p.Cpad * p.H;
+    float *out = p.part + (size_t)(p.split0 + split) * p.Cpad * p.H;
     // each lane holds 4 consecutive hidden entries of one token per (i, j, q)
 #pragma unroll
     for (int j = 0; j < G::NB; ++j) {
@@ -2340,7 +2359,10 @@ int launch_dh(const ChunkArgs &a, void *stream)
     p.ksplit = ksplit;
     p.split0 = a.split0;
     // Tile order.  A dH work-group waits on its global -> LDS loads (a part-filled hidden
-    // tile takes as long as a full one), so the order is chosen for L2 hits.  Each XCD
+    // tile takes as long as a full one), so the order is chosen for L2 hits.  When the
+    // launch divides into whole rounds of 4 x 8-tile blocks, one per XCD (H = 2880 and
+    // 4096 at a chunk of 8192 do), each XCD works on such blocks: 22% fewer L2-miss bytes
+    // than the order below, and no slower.  Otherwise each XCD
     // takes one eighth of a split's tiles; with groups of GM hidden tiles, GM the smallest
     // whole multiple of nMt / gcd(nMt, 8) (so that no XCD's share straddles two groups)
     // that is at least nMt / 4, an XCD pair covers a quarter of the hidden tiles and half
@@ -2358,6 +2380,7 @@ int launch_dh(const ChunkArgs &a, void *stream)
         p.GM = base * std::max(1, (p.nMt / 4 + base - 1) / base);
         p.GM = std::min(p.GM, p.nMt);
     }
+    p.xblk = (p.nMt % 4 == 0 && p.nNt % 8 == 0 && ((p.nMt / 4) * (p.nNt / 8) * used) % 8 == 0) ? 1 : 0;
     p.part = reinterpret_cast<float *>(a.ws + L.off_dhp);
     dim3 grid(p.nMt * p.nNt, used);
     hipLaunchKernelGGL(dh_kernel<DGemm>, grid, dim3(DGemm::NT), 0, S(stream), p);

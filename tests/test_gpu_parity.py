@@ -134,6 +134,31 @@ def test_vocabulary_slabs(case):
         np.testing.assert_array_equal(g[k], again[k], err_msg=k)
 
 
+# Shapes whose dH launch takes the XCD block order (blocks of 4 hidden x 8 token tiles,
+# whole rounds of one block per XCD): one chunk of 8 token tiles, V = 2048 (8 vocabulary
+# tiles, so the planner's split count may reach 8), and H with 4 hidden tiles (1024) or 12
+# with a quarter-full last tile (2880).  For both, 8 splits are the first count that fills
+# whole waves of 256 work-groups (32 x 8 and 96 x 8 work-groups), each split 256 rows.
+XBLOCK_CASES = [
+    (41, 2000, 1024, 2048, 16, 1.0),
+    (42, 1900, 2880, 2048, 16, 1.5),
+]
+
+
+@pytest.mark.parametrize("case", XBLOCK_CASES, ids=["H1024", "H2880-tail"])
+def test_dh_xcd_block_order(case):
+    """dH with its work-groups dealt to the XCDs in blocks of tiles, against the oracle;
+    bitwise repeatable."""
+    seed, N, H, V, K, T = case
+    say("case: dH XCD block order", case)
+    h, W, idx, tl = synthetic(seed, N, H, V, K, T)
+    t = arrays(h, W, idx, tl)
+    g = run(*t, T=T)
+    compare_all(g, h, W, idx, tl, T, what="xblock%d" % seed)
+    again = run(*t, T=T)
+    np.testing.assert_array_equal(g["dH"], again["dH"])
+
+
 def test_loss_nonnegative():
     h, W, idx, tl = synthetic(13, 800, 256, 2000, 50, 2.0, z_sigma=6.0)
     g = run(*arrays(h, W, idx, tl), T=2.0, backward=False)
