@@ -29,6 +29,10 @@ one step at N = 32K .. 256K tokens with the step's chunk and fits peak = a + b N
 per-token cost of the inputs and outputs, with no N x V term.  `dense_baseline` is the
 same loss with the N x V logits materialised in eager torch (peak memory and step time),
 run last with only the inputs resident.
+`library_gemm` is context for the roofline, not part of the loss: the platform BLAS
+library's bf16 GEMM (torch.nn.functional.linear, which calls hipBLASLt) on one logit
+product's shape, a chunk of h times W^T with bf16 output, timed on the same GPU with its
+shader clock sampled as for the main measurement.
 """
 from __future__ import annotations
 
@@ -100,6 +104,8 @@ def main():
     ap.add_argument("--sweep", default="4096",
                     help="comma-separated chunk sizes: also time the step and its peak memory at each (default "
                          "4096, the chunk at which the 32K-token step peaks under 7 GiB; '' = none)")
+    ap.add_argument("--no-library-gemm", action="store_true",
+                    help="skip timing the BLAS library's bf16 GEMM on one logit product's shape")
     ap.add_argument("--no-module", action="store_true",
                     help="skip the torch autograd module leg (FusedChunkedKLLoss, both modes)")
     ap.add_argument("--no-full", action="store_true",
@@ -276,6 +282,12 @@ def main():
                         for k, v in k1.items()},
         }
 
+    if not args.no_library_gemm:
+        out["library_gemm"] = library_gemm(h, W, chunk)
+        log("library bf16 GEMM %s: %.3f ms, %.1f TFLOP/s" % (
+            "x".join(str(out["library_gemm"][k]) for k in ("m", "n", "k")), out["library_gemm"]["ms"],
+            out["library_gemm"]["tflops"]))
+
     if args.sweep:
         # The chunk scheduler's trade-off: the same step at other chunk sizes, each with
         # its own workspace, peak memory measured from the inputs and outputs alone.
@@ -412,6 +424,37 @@ def main():
     if args.cpu_tokens > 0:
         out["cpu_baseline"] = cpu_baseline(x, wl, args.cpu_tokens)
     print(json.dumps(out), flush=True)
+
+
+def library_gemm(h, W, rows, reps=40):
+    """The BLAS library's bf16 GEMM on one logit product's shape: h[:rows] W^T, bf16 in and
+    out with fp32 accumulation, `reps` back-to-back calls between two events on torch's
+    stream, the shader clock sampled meanwhile."""
+    import torch
+    import torch.nn.functional as F
+    a = h[:rows]
+    V, H = W.shape
+    for _ in range(3):
+        c = F.linear(a, W)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with ClockSampler() as cs:
+        e0.record()
+        for _ in range(reps):
+            c = F.linear(a, W)
+        e1.record()
+        torch.cuda.synchronize()
+    del c
+    ms = e0.elapsed_time(e1) / reps
+    tf = 2.0 * rows * V * H / (ms * 1e-3) / 1e12
+    res = {"op": "torch.nn.functional.linear (hipBLASLt), bf16 in and out, fp32 accumulation",
+           "m": int(rows), "n": int(V), "k": int(H), "ms": round(ms, 4), "tflops": round(tf, 1),
+           "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    mhz = cs.mean_mhz()
+    if mhz:
+        res["sustained_clock_mhz"] = round(mhz, 1)
+        res["frac_at_sustained_clock"] = round(tf / (PEAK_BF16_TFLOPS * mhz / 2400.0), 4)
+    return res
 
 
 class ClockSampler:
