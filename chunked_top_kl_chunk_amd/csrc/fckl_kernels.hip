@@ -51,6 +51,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -133,11 +134,27 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 // global_load_lds_dwordx4: each lane of the wave copies 16 bytes from `src` to LDS at
-// lds_wave_base + 16 * lane (lds_wave_base is the same for the whole wave).
+// lds_wave_base + 16 * lane (lds_wave_base is the same for the whole wave; M0 holds it).
+// ASM: written as inline asm, so that the compiler does not see an LDS write through a
+// global instruction.  While it sees one in flight it waits for every LDS read
+// (lgkmcnt(0)) wherever a fragment read's result is used, which the 16x16x32 loop, with
+// fragment reads a full row group ahead, cannot afford.  The copies' completion is then
+// tracked by hand: every LDS read of copied data follows an explicit vmcnt wait and a
+// barrier.  No other code here uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <bool ASM = false>
 __device__ __forceinline__ void copy16_to_lds(const void *src, char *lds_wave_base)
 {
-    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)lds_wave_base, 16, 0, 0);
+    if constexpr (ASM) {
+        const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m)
+                     : "memory", "m0");
+    } else {
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t *)lds_wave_base, 16, 0, 0);
+    }
 }
+#pragma clang diagnostic pop
 
 // global_load_lds_dword: 4 bytes per lane to lds_wave_base + 4 * lane.
 __device__ __forceinline__ void copy4_to_lds(const void *src, char *lds_wave_base)
@@ -216,13 +233,14 @@ struct KTile {
     }
     // Piece i of the k-slice [k0, k0 + BKK) into `tile` (a piece past k_valid or past
     // the last row comes from the zero page).
+    template <bool ASM = false>
     __device__ __forceinline__ static void issue_one(const Src &s, int i, int k0, int k_valid, char *tile)
     {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const bool ok = RSTRIDE * i < s.rlim && k0 + s.kc8 < k_valid;
         const void *src = ok ? static_cast<const void *>(s.base + s.off0 + (uint32_t)i * s.step)
                              : static_cast<const void *>(kZeroPage);
-        copy16_to_lds(src, tile + (i * (NT / 64) + wave) * 1024);
+        copy16_to_lds<ASM>(src, tile + (i * (NT / 64) + wave) * 1024);
     }
     // Move the source to the next k-slice.
     __device__ __forceinline__ static void advance(Src &s, int64_t) { s.base += BKK; }
@@ -273,13 +291,14 @@ struct KTileT {
         s.step = (uint32_t)(RSTRIDE * ld);
         s.nok = n0 + 8 * gc < n_valid;
     }
+    template <bool ASM = false>
     __device__ __forceinline__ static void issue_one(const Src &s, int i, int k0, int k_valid, char *tile)
     {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const bool ok = s.nok && k0 + s.krow0 + RSTRIDE * i < k_valid;
         const void *src = ok ? static_cast<const void *>(s.base + s.off0 + (uint32_t)i * s.step)
                              : static_cast<const void *>(kZeroPage);
-        copy16_to_lds(src, tile + (i * (NT / 64) + wave) * 1024);
+        copy16_to_lds<ASM>(src, tile + (i * (NT / 64) + wave) * 1024);
     }
     __device__ __forceinline__ static void advance(Src &s, int64_t ld) { s.base += (int64_t)BKK * ld; }
     // The MFMA operand of one lane for the 32 columns starting at nb and the 16 k-rows
@@ -306,7 +325,16 @@ struct NoHook {
     __device__ __forceinline__ void operator()() const {}
 };
 
-template <int BM_, int BN_, int WM_, int WN_, int BKK, int S, bool SPREAD = false, bool BTR = false>
+// Swaps the odd 16-lane rows of x with the even 16-lane rows of y (gfx950
+// v_permlane16_swap_b32): lane l of x with l in [16,32) or [48,64) takes y from lane
+// l - 16, and lane l of y with l in [0,16) or [32,48) takes x from lane l + 16.  Written
+// as asm: the compiler merges distinct calls of its builtin for this instruction.
+__device__ __forceinline__ void permlane16_swap(float &x, float &y)
+{
+    asm volatile("v_permlane16_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+}
+
+template <int BM_, int BN_, int WM_, int WN_, int BKK, int S, bool SPREAD = false, bool BTR = false, bool MI16 = !BTR>
 struct GemmD {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BKK;
     static constexpr int NT = WM * WN * 64;
@@ -418,6 +446,317 @@ struct GemmD {
                                const uint16_t *B, int64_t ldb, int n0, int n_valid, int kb_valid, int k_begin,
                                int k_end, f32x16 (&acc)[MB][NB], const Hook &hook = Hook())
     {
+        if constexpr (MI16)
+            run16<Hook, TAIL>(smem, A, lda, m0, m_valid, ka_valid, B, ldb, n0, n_valid, kb_valid, k_begin, k_end, acc,
+                              hook);
+        else
+            run32<Hook, TAIL>(smem, A, lda, m0, m_valid, ka_valid, B, ldb, n0, n_valid, kb_valid, k_begin, k_end, acc,
+                              hook);
+    }
+
+    // ---- 16x16x32 form.  Under the board's power limit gfx950 sustains more bf16 flops
+    // with v_mfma_f32_16x16x32_bf16 than with the 32x32x16 form (in register-only loops
+    // over every compute unit, about 2.2 against 1.95 PFLOP/s: the clock settles higher).
+    // Each 32 x 32 accumulator block is computed as four 16 x 16 blocks (R, C) and, after
+    // the k loop, moved into the 32x32x16 output layout, which the epilogues index:
+    // lane l, element r holds row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
+    //   A 16x16x32 product leaves lane l with rows 4 (l / 16) + 0..3 of column l % 16.
+    //   Block (R, C) takes the block's columns 16 C .. 16 C + 15 and, for its row rho,
+    //   block row phi_R(rho) = 16 R + 8 ((rho / 4) % 2) + 4 (rho / 8) + rho % 4.  Lane l
+    //   (16-lane row g = l / 16) then holds its own column in block (R, g % 2) and the
+    //   column of lane l ^ 16 in block (R, 1 - g % 2); one permlane16 swap per register
+    //   pair trades those, after which both registers hold the lane's column, at block
+    //   rows 16 R + 4 (g / 2) + r and 16 R + 8 + 4 (g / 2) + r: elements 8 R + r and
+    //   8 R + 4 + r of the 32x32x16 layout.
+    static constexpr int SUB32 = BKK / 32;
+    static_assert(SUB32 * 32 == BKK && (SUB32 == 1 || SUB32 == 2), "k-steps of 32 or 64");
+    // The fragment rows of the first BAR row blocks of a step's last substep run before
+    // the step's barrier, the others after it, covering the reads of the next step's
+    // first fragments.
+    static constexpr int BAR = MB / 2;
+    // EARLY: the copies of step kb + S are issued right after step kb's barrier (the
+    // stage they fill was last read before it), spread over the fragment rows that follow
+    // it, so that they have a whole step to land; otherwise the copies of step kb + S - 1
+    // go with the first COPY_ROWS rows of step kb.
+    static constexpr bool EARLY = true;
+    static constexpr int COPY_ROWS = EARLY ? 2 * (MB - BAR) : 2;
+    static constexpr int CPRW = (L + COPY_ROWS - 1) / COPY_ROWS;   // copies per such row
+    static_assert(EARLY || SUB32 == 2 || COPY_ROWS <= 2 * BAR, "copies before the barrier");
+    __device__ __forceinline__ static int phi(int R, int rho)
+    {
+        return 16 * R + 8 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3);
+    }
+    // The 16-byte k-chunk of the step that 16-lane row g = lane / 16 of a fragment holds
+    // in 32-deep substep ks; A and B use the same map, so each MFMA still pairs equal k.
+    // The LDS serves a 16-byte read in passes that take lanes l and l + 32 together, and
+    // the map puts the two lanes of a pass in different bank groups both for A's row
+    // order phi and for B's consecutive rows under the tile's swizzle:
+    //   64-deep steps (8 chunks a row): substep ks takes chunks ks, ks + 2 (rows 0, 1)
+    //   and their XOR with 5 (rows 2, 3);
+    //   32-deep steps (4 chunks): rows 0 .. 3 take chunks 0, 1, 3, 2.
+    __device__ __forceinline__ static int kchunk16(int ks, int lane)
+    {
+        const int g = lane >> 4;
+        if constexpr (SUB32 == 2)
+            return (2 * (g & 1) + ks) ^ (5 * (g >> 1));
+        else
+            return g ^ (g >> 1);
+    }
+    __device__ __forceinline__ static bf16x8 frag_a16(const char *stage, int wm, int i, int R, int ks, int lane)
+    {
+        return AT::frag(stage, wm * WTM + 32 * i + phi(R, lane & 15), kchunk16(ks, lane));
+    }
+    __device__ __forceinline__ static bf16x8 frag_b16(const char *stage, int wn, int j, int C, int ks, int lane)
+    {
+        return BT::frag(stage + AT::BYTES, col_of(wn, j, 0) + 16 * C + (lane & 15), kchunk16(ks, lane));
+    }
+
+    template <class Hook = NoHook, bool TAIL = false>
+    __device__ static void run16(char *smem, const uint16_t *A, int64_t lda, int m0, int m_valid, int ka_valid,
+                                 const uint16_t *B, int64_t ldb, int n0, int n_valid, int kb_valid, int k_begin,
+                                 int k_end, f32x16 (&acc)[MB][NB], const Hook &hook)
+    {
+        static_assert(!BTR, "k-major operands");
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int wm = wm_of(wave), wn = wn_of(wave);
+        uint32_t ilive = ~0u, jlive = ~0u;
+        if constexpr (TAIL) {
+            const int live_cols = n_valid - n0, live_rows = m_valid - m0;
+            ilive = jlive = 0u;
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+                if (wm * WTM + i * 32 < live_rows)
+                    ilive |= 1u << i;
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                if (col_of(wn, j, 0) < live_cols)
+                    jlive |= 1u << j;
+            ilive = __builtin_amdgcn_readfirstlane(ilive);
+            jlive = __builtin_amdgcn_readfirstlane(jlive);
+        }
+        const auto ion = [&](int i) { return !TAIL || ((ilive >> i) & 1u); };
+        const auto jon = [&](int j) { return !TAIL || ((jlive >> j) & 1u); };
+        f32x4 q[MB][NB][2][2];
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int R = 0; R < 2; ++R)
+#pragma unroll
+                    for (int C = 0; C < 2; ++C)
+                        q[i][j][R][C] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        const int nk = (k_end - k_begin + BKK - 1) / BKK;
+        if (nk > 0) {
+            typename AT::Src sa;
+            typename BT::Src sb;
+            AT::init(sa, A, lda, m0, m_valid, k_begin);
+            BT::init(sb, B, ldb, n0, n_valid, k_begin);
+            auto issue = [&](int step) {
+                char *st = smem + (step % S) * STAGE;
+                const int k0 = k_begin + step * BKK;
+#pragma unroll
+                for (int x = 0; x < AT::PER; ++x)
+                    AT::template issue_one<true>(sa, x, k0, ka_valid, st);
+#pragma unroll
+                for (int x = 0; x < BT::PER; ++x)
+                    BT::template issue_one<true>(sb, x, k0, kb_valid, st + AT::BYTES);
+                AT::advance(sa, lda);
+                BT::advance(sb, ldb);
+            };
+#pragma unroll
+            for (int st = 0; st + 1 < S; ++st)
+                issue(st);
+            wait_vmcnt<(S - 2) * L>();
+            __builtin_amdgcn_s_barrier();
+            hook();
+            // stage S - 1 has never been read
+            if constexpr (EARLY)
+                issue(S - 1);
+            bf16x8 fa[MB][2], fb[NB][2], fbn[NB][2];
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int R = 0; R < 2; ++R)
+                    if (ion(i))
+                        fa[i][R] = frag_a16(smem, wm, i, R, 0, lane);
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int C = 0; C < 2; ++C)
+                    if (jon(j))
+                        fb[j][C] = frag_b16(smem, wn, j, C, 0, lane);
+            // The MFMAs of fragment row (i, R): one per column block (j, C).
+            auto mma_row = [&](int i, int R) {
+                if (ion(i)) {
+#pragma unroll
+                    for (int j = 0; j < NB; ++j)
+#pragma unroll
+                        for (int C = 0; C < 2; ++C)
+                            if (jon(j))
+                                q[i][j][R][C] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i][R], fb[j][C],
+                                                                                        q[i][j][R][C], 0, 0, 0);
+                }
+            };
+            auto load_b = [&](const char *stage, int ks) {
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+#pragma unroll
+                    for (int C = 0; C < 2; ++C)
+                        if (jon(j))
+                            fbn[j][C] = frag_b16(stage, wn, j, C, ks, lane);
+            };
+            auto load_a_row = [&](const char *stage, int ks, int i, int R) {
+                if (ion(i))
+                    fa[i][R] = frag_a16(stage, wm, i, R, ks, lane);
+            };
+            auto take_b = [&]() {
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+#pragma unroll
+                    for (int C = 0; C < 2; ++C)
+                        fb[j][C] = fbn[j][C];
+            };
+            constexpr int ROWMMA = NB * 2;     // MFMAs per fragment row
+            // One fragment row: its MFMAs, then (optionally) one global->LDS copy and the
+            // read that refills the row's A fragment for the next substep.  The fence
+            // after it keeps the rows in this order: a refill then has the other 2 MB - 1
+            // rows of MFMAs to land before its next use.
+            auto row_group = [&](auto has_vm, auto has_ds) {
+                if constexpr (!TAIL) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, ROWMMA, 0);
+                    if constexpr (decltype(has_vm)::value)
+                        __builtin_amdgcn_sched_group_barrier(0x020, CPRW, 0);
+                    if constexpr (decltype(has_ds)::value)
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            auto step = [&](int kb, auto last_c) {
+                constexpr bool last = decltype(last_c)::value;
+                const char *cur = smem + (kb % S) * STAGE;
+                const int cstep = EARLY ? kb + S : kb + S - 1;    // the step these copies fill
+                char *nxt_dst = smem + (cstep % S) * STAGE;
+                const int k0n = k_begin + cstep * BKK;
+                // the copies of step kb + S - 1 that go with fragment row `row` of the
+                // step's first substep (A pieces first, then B pieces)
+                auto copies = [&](auto rowc) {
+                    constexpr int row = decltype(rowc)::value;
+                    static_for<CPRW>([&](auto cc) {
+                        constexpr int x = row * CPRW + decltype(cc)::value;
+                        if constexpr (row < COPY_ROWS && x < L) {
+                            if constexpr (x < AT::PER)
+                                AT::template issue_one<true>(sa, x, k0n, ka_valid, nxt_dst);
+                            else
+                                BT::template issue_one<true>(sb, x - AT::PER, k0n, kb_valid, nxt_dst + AT::BYTES);
+                        }
+                    });
+                    if constexpr (row + 1 == COPY_ROWS) {
+                        AT::advance(sa, lda);
+                        BT::advance(sb, ldb);
+                    }
+                };
+                static_for<SUB32>([&](auto ksc) {
+                    constexpr int ks = decltype(ksc)::value;
+                    constexpr bool first = ks == 0;
+                    if constexpr (ks + 1 < SUB32) {
+                        // next substep's B fragments first
+                        load_b(cur, ks + 1);
+                        __builtin_amdgcn_sched_barrier(0);
+                        static_for<2 * MB>([&](auto rc) {
+                            constexpr int row = decltype(rc)::value;
+                            constexpr bool vm = !EARLY && first && row < COPY_ROWS;
+                            mma_row(row / 2, row % 2);
+                            if constexpr (vm)
+                                copies(rc);
+                            load_a_row(cur, ks + 1, row / 2, row % 2);
+                            row_group(std::bool_constant<vm>{}, std::true_type{});
+                        });
+                        take_b();
+                    } else if constexpr (!last) {
+                        static_for<2 * BAR>([&](auto rc) {
+                            constexpr int row = decltype(rc)::value;
+                            constexpr bool vm = !EARLY && first && row < COPY_ROWS;
+                            mma_row(row / 2, row % 2);
+                            if constexpr (vm)
+                                copies(rc);
+                            row_group(std::bool_constant<vm>{}, std::false_type{});
+                        });
+                        // step kb + 1 has landed for this wave (later steps may stay in
+                        // flight), and every read of stage kb is done; after the barrier
+                        // that holds for all waves
+                        wait_vmcnt<(S - 2) * L>();
+                        wait_lgkmcnt0();
+                        __builtin_amdgcn_s_barrier();
+                        const char *nst = smem + ((kb + 1) % S) * STAGE;
+                        load_b(nst, 0);
+#pragma unroll
+                        for (int i = 0; i < BAR; ++i)
+#pragma unroll
+                            for (int R = 0; R < 2; ++R)
+                                load_a_row(nst, 0, i, R);
+                        __builtin_amdgcn_sched_barrier(0);
+                        static_for<2 * (MB - BAR)>([&](auto rc) {
+                            constexpr int row = 2 * BAR + decltype(rc)::value;
+                            mma_row(row / 2, row % 2);
+                            if constexpr (EARLY)
+                                copies(rc);
+                            load_a_row(nst, 0, row / 2, row % 2);
+                            row_group(std::bool_constant<EARLY>{}, std::true_type{});
+                        });
+                        take_b();
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < MB; ++i)
+#pragma unroll
+                            for (int R = 0; R < 2; ++R)
+                                mma_row(i, R);
+                    }
+                });
+            };
+            for (int kb = 0; kb + 1 < nk; ++kb)
+                step(kb, std::false_type{});
+            step(nk - 1, std::true_type{});
+        } else {
+            hook();
+        }
+        // every wave is done reading LDS (and no load is in flight) before the caller reuses it
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        // Into the 32x32x16 layout.  The fence keeps every MFMA above it, and the waits
+        // give the last MFMA results time to land before the swaps read them.
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int R = 0; R < 2; ++R)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float x = q[i][j][R][0][r], y = q[i][j][R][1][r];
+                        permlane16_swap(x, y);
+                        acc[i][j][8 * R + r] = x;
+                        acc[i][j][8 * R + 4 + r] = y;
+                    }
+    }
+
+    // ---- 32x32x16 form (the logit products and the transposed-B product)
+    // Issue priority falls over a step's substeps (3 in the first, 0 in the last): of the
+    // two waves that share a SIMD, the one further behind in the step wins the issue
+    // slots, so that both reach the step's barrier about together (-0.5% per step against
+    // none; rising or two-level orders were slower).
+    template <int SS>
+    __device__ __forceinline__ static void wave_priority()
+    {
+        __builtin_amdgcn_s_setprio(SS < 3 ? 3 - SS : 0);
+    }
+    template <class Hook = NoHook, bool TAIL = false>
+    __device__ static void run32(char *smem, const uint16_t *A, int64_t lda, int m0, int m_valid, int ka_valid,
+                                 const uint16_t *B, int64_t ldb, int n0, int n_valid, int kb_valid, int k_begin,
+                                 int k_end, f32x16 (&acc)[MB][NB], const Hook &hook)
+    {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int wm = wm_of(wave), wn = wn_of(wave);
         uint32_t ilive = ~0u, jlive = ~0u;
@@ -485,6 +824,7 @@ struct GemmD {
             const int next = kb + S - 1;
             static_for<SUB>([&](auto ssc) {
                 constexpr int ss = decltype(ssc)::value;
+                wave_priority<ss>();
                 constexpr int lo = ss * P < L ? ss * P : L;
                 constexpr int hi = (ss + 1) * P < L ? (ss + 1) * P : L;
                 if constexpr (lo < hi)
@@ -540,6 +880,7 @@ struct GemmD {
                 const int next = kb + S - 1;
                 static_for<SUB>([&](auto ssc) {
                     constexpr int ss = decltype(ssc)::value;
+                    wave_priority<ss>();
                     constexpr int lo = ss * P < L ? ss * P : L;
                     constexpr int hi = (ss + 1) * P < L ? (ss + 1) * P : L;
                     if constexpr (lo < hi)
@@ -575,6 +916,7 @@ struct GemmD {
                 stepT(kb, std::false_type{});
             stepT(nk - 1, std::true_type{});
         }
+        __builtin_amdgcn_s_setprio(0);
         // every wave is done reading LDS (and no load is in flight) before the caller reuses it
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -582,7 +924,7 @@ struct GemmD {
 };
 
 // The logit GEMM: rows = vocabulary (W), columns = tokens (h), k = hidden.
-using LogitGemm = GemmD<256, 256, 2, 4, 64, 2>;
+using LogitGemm = GemmD<256, 256, 2, 4, 64, 2, false, false, false>;
 static_assert(LogitGemm::BM == kVocabTile, "entry counts are kept per 256-row vocabulary tile");
 static_assert(kTokenTile % LogitGemm::BN == 0, "chunk padding covers whole token tiles");
 constexpr int kGStagePitch = 256 * 2 + 16;   // bytes per token row of the staged bf16 g tile
