@@ -259,7 +259,7 @@ struct KTile {
 // 4 rows k .. k+3 of column n + l.  Half a wave (two groups) reads 4 rows x 4
 // consecutive 16-byte chunks; the chunk index is XOR-swizzled by 4 (row % 4) so those
 // 16 chunks fall on 16 different bank groups.
-template <int COLS, int BKK, int NT>
+template <int COLS, int BKK, int NT, bool SW16 = false>
 struct KTileT {
     static constexpr int CPR = COLS / 8;         // 16-byte chunks per k-row
     static constexpr int RB = COLS * 2;          // bytes per k-row
@@ -270,14 +270,22 @@ struct KTileT {
     static constexpr int BYTES = CHUNKS * 16;
     static constexpr int RSTRIDE = NT / CPR;     // k-rows between a lane's pieces
     static_assert(RSTRIDE % 4 == 0, "swizzle invariant across pieces");
-    __device__ __forceinline__ static int sw(int krow) { return (krow & 3) << 2; }
+    // SW16 (the 16x16x32 reads, below): bit 4 of the row also flips bit 1 of the chunk,
+    // which separates the two 8-row k blocks that one half-wave reads at once.  A
+    // lane's pieces lie RSTRIDE = 16 rows apart, so their chunk alternates with i.
+    static_assert(!SW16 || RSTRIDE == 16, "pieces alternate bit 4 of the row");
+    __device__ __forceinline__ static int sw(int krow)
+    {
+        return SW16 ? (((krow & 3) << 2) ^ (((krow >> 4) & 1) << 1)) : ((krow & 3) << 2);
+    }
 
     struct Src {
         const uint16_t *base;   // row k of the current slice, column n0
         uint32_t off0;          // element offset of piece 0 from base
+        int32_t odd;            // SW16: element offset of odd pieces' chunk from piece 0's
         uint32_t step;          // element offset between pieces (RSTRIDE rows)
         int krow0;              // k-row of piece 0 within the slice
-        bool nok;               // the lane's 8 columns start inside the operand
+        bool nok, nok_odd;      // the lane's 8 columns start inside the operand
     };
     __device__ __forceinline__ static void init(Src &s, const uint16_t *base, int64_t ld, int n0, int n_valid,
                                                 int k_begin)
@@ -290,13 +298,17 @@ struct KTileT {
         s.off0 = (uint32_t)(s.krow0 * ld + 8 * gc);
         s.step = (uint32_t)(RSTRIDE * ld);
         s.nok = n0 + 8 * gc < n_valid;
+        const int gco = SW16 ? gc ^ 2 : gc;
+        s.odd = 8 * (gco - gc);
+        s.nok_odd = n0 + 8 * gco < n_valid;
     }
     template <bool ASM = false>
     __device__ __forceinline__ static void issue_one(const Src &s, int i, int k0, int k_valid, char *tile)
     {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        const bool ok = s.nok && k0 + s.krow0 + RSTRIDE * i < k_valid;
-        const void *src = ok ? static_cast<const void *>(s.base + s.off0 + (uint32_t)i * s.step)
+        const bool odd = SW16 && (i & 1);
+        const bool ok = (odd ? s.nok_odd : s.nok) && k0 + s.krow0 + RSTRIDE * i < k_valid;
+        const void *src = ok ? static_cast<const void *>(s.base + (s.off0 + (odd ? s.odd : 0)) + (uint32_t)i * s.step)
                              : static_cast<const void *>(kZeroPage);
         copy16_to_lds<ASM>(src, tile + (i * (NT / 64) + wave) * 1024);
     }
@@ -312,6 +324,23 @@ struct KTileT {
         typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a + 4 * RB));
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(bf16x8, v);
+    }
+    // The 16x16x32 operand of one lane: column nb + lane % 16, the 8 k-rows of block kb8
+    // (rows 8 kb8 .. 8 kb8 + 7).  Each 16-lane row reads its own block; with SW16 the two
+    // blocks a half-wave reads (16 rows apart) fall on different bank groups.
+    __device__ __forceinline__ static bf16x8 frag16(const char *tile, int nb, int kb8, int lane)
+    {
+        const int gl = lane & 15;
+        const int n = nb + 4 * (gl & 3);
+        const int k = 8 * kb8 + (gl >> 2);
+        const char *a = tile + k * RB + (((n >> 3) ^ sw(k)) << 4) + (n & 7) * 2;
+        const char *b = tile + (k + 4) * RB + (((n >> 3) ^ sw(k + 4)) << 4) + (n & 7) * 2;
+        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(b));
         typedef short i16x8 __attribute__((ext_vector_type(8)));
         const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         return __builtin_bit_cast(bf16x8, v);
@@ -342,7 +371,7 @@ struct GemmD {
     static constexpr int MB = WTM / 32, NB = WTN / 32;
     static_assert(MB * 32 == WTM && NB * 32 == WTN, "wave tile");
     using AT = KTile<BM, BKK, NT>;
-    using BT = std::conditional_t<BTR, KTileT<BN, BKK, NT>, KTile<BN, BKK, NT>>;
+    using BT = std::conditional_t<BTR, KTileT<BN, BKK, NT, MI16>, KTile<BN, BKK, NT>>;
     static constexpr int STAGE = AT::BYTES + BT::BYTES;
     static constexpr int LDS_BYTES = S * STAGE;
     static constexpr int L = AT::PER + BT::PER;     // DMA loads per thread per k-step
@@ -508,7 +537,10 @@ struct GemmD {
     }
     __device__ __forceinline__ static bf16x8 frag_b16(const char *stage, int wn, int j, int C, int ks, int lane)
     {
-        return BT::frag(stage + AT::BYTES, col_of(wn, j, 0) + 16 * C + (lane & 15), kchunk16(ks, lane));
+        if constexpr (BTR)
+            return BT::frag16(stage + AT::BYTES, col_of(wn, j, 0) + 16 * C, kchunk16(ks, lane), lane);
+        else
+            return BT::frag(stage + AT::BYTES, col_of(wn, j, 0) + 16 * C + (lane & 15), kchunk16(ks, lane));
     }
 
     template <class Hook = NoHook, bool TAIL = false>
@@ -516,7 +548,6 @@ struct GemmD {
                                  const uint16_t *B, int64_t ldb, int n0, int n_valid, int kb_valid, int k_begin,
                                  int k_end, f32x16 (&acc)[MB][NB], const Hook &hook)
     {
-        static_assert(!BTR, "k-major operands");
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int wm = wm_of(wave), wn = wn_of(wave);
         uint32_t ilive = ~0u, jlive = ~0u;
@@ -2391,7 +2422,7 @@ __global__ __launch_bounds__(G::NT) void dw_kernel(DwParams p)
     }
 }
 
-using DGemm = GemmD<kHiddenTile, 256, 2, 4, 64, 2, false, true>;   // dH^T: hidden x tokens, k = vocabulary
+using DGemm = GemmD<kHiddenTile, 256, 2, 4, 64, 2, false, true, true>;   // dH^T: hidden x tokens, k = vocabulary
 using WGemm = GemmD<256, kHiddenTile, 2, 4, 64, 2, true>;   // dW: vocabulary x hidden, k = tokens
 
 // dst[c][r] = src[r][c] for r < rows, c < cols; dst[c][r] = 0 for rows <= r < rpad.
