@@ -27,13 +27,16 @@
 //   transpose        W -> W^T once per backward call, h_chunk -> h_chunk^T per chunk
 //
 // GEMM core: 256 x 256 tiles, 512 threads = 8 wave64s, each wave owns a 128 x 64 block
-// of v_mfma_f32_32x32x16_bf16 accumulators.  Operands are read k-major (contiguous
-// along the reduction), which is why the backward products use W^T and h_chunk^T; the
-// one exception is g^T in the dH product, whose fragments come from gfx950's transposing
-// LDS reads.  Each lane's 16-byte piece goes from
-// global memory straight into LDS (global_load_lds_dwordx4, no register staging); two
-// LDS stages of 64-deep k-steps, one barrier per step, and an XOR swizzle of the
-// 16-byte chunks that keeps the MFMA operand reads free of bank conflicts.
+// of fp32 accumulators in the v_mfma_f32_32x32x16_bf16 output layout.  The logit
+// products run 32x32x16 MFMAs; dH and dW run v_mfma_f32_16x16x32_bf16, which holds a
+// higher clock under the board's power limit, and move their accumulators into the
+// 32x32x16 layout after the k loop, so every epilogue indexes one layout.  Operands are
+// read k-major (contiguous along the reduction), which is why the backward products use
+// W^T and h_chunk^T; the one exception is g^T in the dH product, whose fragments come
+// from gfx950's transposing LDS reads.  Each lane's 16-byte piece goes from global
+// memory straight into LDS (global_load_lds_dwordx4, no register staging); two LDS
+// stages of 64-deep k-steps, one barrier per step, and an XOR swizzle of the 16-byte
+// chunks that keeps the MFMA operand reads free of bank conflicts.
 // The two logit kernels are persistent (one work-group per compute unit looping over
 // tiles), which removes the per-work-group dispatch gap between tiles.
 #include <hip/hip_runtime.h>
