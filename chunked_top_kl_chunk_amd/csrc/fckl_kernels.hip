@@ -500,39 +500,30 @@ struct GemmD {
     //   pair trades those, after which both registers hold the lane's column, at block
     //   rows 16 R + 4 (g / 2) + r and 16 R + 8 + 4 (g / 2) + r: elements 8 R + r and
     //   8 R + 4 + r of the 32x32x16 layout.
-    static constexpr int SUB32 = BKK / 32;
-    static_assert(SUB32 * 32 == BKK && (SUB32 == 1 || SUB32 == 2), "k-steps of 32 or 64");
+    static_assert(!MI16 || BKK == 64, "64-deep k-steps: two 32-deep substeps");
     // The fragment rows of the first BAR row blocks of a step's last substep run before
     // the step's barrier, the others after it, covering the reads of the next step's
     // first fragments.
     static constexpr int BAR = MB / 2;
-    // EARLY: the copies of step kb + S are issued right after step kb's barrier (the
-    // stage they fill was last read before it), spread over the fragment rows that follow
-    // it, so that they have a whole step to land; otherwise the copies of step kb + S - 1
-    // go with the first COPY_ROWS rows of step kb.
-    static constexpr bool EARLY = true;
-    static constexpr int COPY_ROWS = EARLY ? 2 * (MB - BAR) : 2;
+    // The copies of step kb + S are issued right after step kb's barrier (the stage they
+    // fill was last read before it), spread over the COPY_ROWS fragment rows that follow
+    // it, so that they have a whole step to land.
+    static constexpr int COPY_ROWS = 2 * (MB - BAR);
     static constexpr int CPRW = (L + COPY_ROWS - 1) / COPY_ROWS;   // copies per such row
-    static_assert(EARLY || SUB32 == 2 || COPY_ROWS <= 2 * BAR, "copies before the barrier");
     __device__ __forceinline__ static int phi(int R, int rho)
     {
         return 16 * R + 8 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3);
     }
-    // The 16-byte k-chunk of the step that 16-lane row g = lane / 16 of a fragment holds
-    // in 32-deep substep ks; A and B use the same map, so each MFMA still pairs equal k.
-    // The LDS serves a 16-byte read in passes that take lanes l and l + 32 together, and
-    // the map puts the two lanes of a pass in different bank groups both for A's row
-    // order phi and for B's consecutive rows under the tile's swizzle:
-    //   64-deep steps (8 chunks a row): substep ks takes chunks ks, ks + 2 (rows 0, 1)
-    //   and their XOR with 5 (rows 2, 3);
-    //   32-deep steps (4 chunks): rows 0 .. 3 take chunks 0, 1, 3, 2.
+    // The 16-byte k-chunk (of the step's 8) that 16-lane row g = lane / 16 of a fragment
+    // holds in 32-deep substep ks; A and B use the same map, so each MFMA still pairs
+    // equal k.  The LDS serves a 16-byte read in passes that take lanes l and l + 32
+    // together: substep ks takes chunks ks, ks + 2 (rows 0, 1) and their XOR with 5 (rows
+    // 2, 3), which puts the two lanes of a pass in different bank groups both for A's row
+    // order phi and for B's consecutive rows under the tile's swizzle.
     __device__ __forceinline__ static int kchunk16(int ks, int lane)
     {
         const int g = lane >> 4;
-        if constexpr (SUB32 == 2)
-            return (2 * (g & 1) + ks) ^ (5 * (g >> 1));
-        else
-            return g ^ (g >> 1);
+        return (2 * (g & 1) + ks) ^ (5 * (g >> 1));
     }
     __device__ __forceinline__ static bf16x8 frag_a16(const char *stage, int wm, int i, int R, int ks, int lane)
     {
@@ -605,8 +596,7 @@ struct GemmD {
             __builtin_amdgcn_s_barrier();
             hook();
             // stage S - 1 has never been read
-            if constexpr (EARLY)
-                issue(S - 1);
+            issue(S - 1);
             bf16x8 fa[MB][2], fb[NB][2], fbn[NB][2];
 #pragma unroll
             for (int i = 0; i < MB; ++i)
@@ -666,23 +656,26 @@ struct GemmD {
                 }
                 __builtin_amdgcn_sched_barrier(0);
             };
+            // One 64-deep step: substep 0 runs every fragment row and refills its A fragment
+            // (and all B fragments) for substep 1 from the same stage; substep 1 runs its
+            // first BAR row blocks, crosses the step's barrier, then runs the others while
+            // the next step's first fragments are read and the copies of step kb + S go out.
             auto step = [&](int kb, auto last_c) {
                 constexpr bool last = decltype(last_c)::value;
                 const char *cur = smem + (kb % S) * STAGE;
-                const int cstep = EARLY ? kb + S : kb + S - 1;    // the step these copies fill
-                char *nxt_dst = smem + (cstep % S) * STAGE;
-                const int k0n = k_begin + cstep * BKK;
-                // the copies of step kb + S - 1 that go with fragment row `row` of the
-                // step's first substep (A pieces first, then B pieces)
+                char *cdst = smem + ((kb + S) % S) * STAGE;       // the stage step kb + S fills
+                const int k0c = k_begin + (kb + S) * BKK;
+                // the copies that go with fragment row `row` after the barrier (A pieces
+                // first, then B pieces)
                 auto copies = [&](auto rowc) {
                     constexpr int row = decltype(rowc)::value;
                     static_for<CPRW>([&](auto cc) {
                         constexpr int x = row * CPRW + decltype(cc)::value;
-                        if constexpr (row < COPY_ROWS && x < L) {
+                        if constexpr (x < L) {
                             if constexpr (x < AT::PER)
-                                AT::template issue_one<true>(sa, x, k0n, ka_valid, nxt_dst);
+                                AT::template issue_one<true>(sa, x, k0c, ka_valid, cdst);
                             else
-                                BT::template issue_one<true>(sb, x - AT::PER, k0n, kb_valid, nxt_dst + AT::BYTES);
+                                BT::template issue_one<true>(sb, x - AT::PER, k0c, kb_valid, cdst + AT::BYTES);
                         }
                     });
                     if constexpr (row + 1 == COPY_ROWS) {
@@ -690,63 +683,52 @@ struct GemmD {
                         BT::advance(sb, ldb);
                     }
                 };
-                static_for<SUB32>([&](auto ksc) {
-                    constexpr int ks = decltype(ksc)::value;
-                    constexpr bool first = ks == 0;
-                    if constexpr (ks + 1 < SUB32) {
-                        // next substep's B fragments first
-                        load_b(cur, ks + 1);
-                        __builtin_amdgcn_sched_barrier(0);
-                        static_for<2 * MB>([&](auto rc) {
-                            constexpr int row = decltype(rc)::value;
-                            constexpr bool vm = !EARLY && first && row < COPY_ROWS;
-                            mma_row(row / 2, row % 2);
-                            if constexpr (vm)
-                                copies(rc);
-                            load_a_row(cur, ks + 1, row / 2, row % 2);
-                            row_group(std::bool_constant<vm>{}, std::true_type{});
-                        });
-                        take_b();
-                    } else if constexpr (!last) {
-                        static_for<2 * BAR>([&](auto rc) {
-                            constexpr int row = decltype(rc)::value;
-                            constexpr bool vm = !EARLY && first && row < COPY_ROWS;
-                            mma_row(row / 2, row % 2);
-                            if constexpr (vm)
-                                copies(rc);
-                            row_group(std::bool_constant<vm>{}, std::false_type{});
-                        });
-                        // step kb + 1 has landed for this wave (later steps may stay in
-                        // flight), and every read of stage kb is done; after the barrier
-                        // that holds for all waves
-                        wait_vmcnt<(S - 2) * L>();
-                        wait_lgkmcnt0();
-                        __builtin_amdgcn_s_barrier();
-                        const char *nst = smem + ((kb + 1) % S) * STAGE;
-                        load_b(nst, 0);
-#pragma unroll
-                        for (int i = 0; i < BAR; ++i)
-#pragma unroll
-                            for (int R = 0; R < 2; ++R)
-                                load_a_row(nst, 0, i, R);
-                        __builtin_amdgcn_sched_barrier(0);
-                        static_for<2 * (MB - BAR)>([&](auto rc) {
-                            constexpr int row = 2 * BAR + decltype(rc)::value;
-                            mma_row(row / 2, row % 2);
-                            if constexpr (EARLY)
-                                copies(rc);
-                            load_a_row(nst, 0, row / 2, row % 2);
-                            row_group(std::bool_constant<EARLY>{}, std::true_type{});
-                        });
-                        take_b();
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < MB; ++i)
-#pragma unroll
-                            for (int R = 0; R < 2; ++R)
-                                mma_row(i, R);
-                    }
+                // substep 0
+                load_b(cur, 1);
+                __builtin_amdgcn_sched_barrier(0);
+                static_for<2 * MB>([&](auto rc) {
+                    constexpr int row = decltype(rc)::value;
+                    mma_row(row / 2, row % 2);
+                    load_a_row(cur, 1, row / 2, row % 2);
+                    row_group(std::false_type{}, std::true_type{});
                 });
+                take_b();
+                // substep 1
+                if constexpr (!last) {
+                    static_for<2 * BAR>([&](auto rc) {
+                        constexpr int row = decltype(rc)::value;
+                        mma_row(row / 2, row % 2);
+                        row_group(std::false_type{}, std::false_type{});
+                    });
+                    // step kb + 1 has landed for this wave (later steps may stay in
+                    // flight), and every read of stage kb is done; after the barrier that
+                    // holds for all waves
+                    wait_vmcnt<(S - 2) * L>();
+                    wait_lgkmcnt0();
+                    __builtin_amdgcn_s_barrier();
+                    const char *nst = smem + ((kb + 1) % S) * STAGE;
+                    load_b(nst, 0);
+#pragma unroll
+                    for (int i = 0; i < BAR; ++i)
+#pragma unroll
+                        for (int R = 0; R < 2; ++R)
+                            load_a_row(nst, 0, i, R);
+                    __builtin_amdgcn_sched_barrier(0);
+                    static_for<COPY_ROWS>([&](auto rc) {
+                        constexpr int row = 2 * BAR + decltype(rc)::value;
+                        mma_row(row / 2, row % 2);
+                        copies(rc);
+                        load_a_row(nst, 0, row / 2, row % 2);
+                        row_group(std::true_type{}, std::true_type{});
+                    });
+                    take_b();
+                } else {
+#pragma unroll
+                    for (int i = 0; i < MB; ++i)
+#pragma unroll
+                        for (int R = 0; R < 2; ++R)
+                            mma_row(i, R);
+                }
             };
             for (int kb = 0; kb + 1 < nk; ++kb)
                 step(kb, std::false_type{});
